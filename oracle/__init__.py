@@ -1,0 +1,234 @@
+"""CPU oracle for the tile-binned splat rasterizer (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may import this package. The
+product path (``tile_binned_gaussian_amd``) never imports, links or runs it, and this package never imports the
+product path: the two share only the seeded inputs from ``tile_binned_gaussian_amd.synth``.
+
+The arithmetic lives in ``gs_oracle.c`` (plain C, float32 where the pages compute in float, no contraction);
+this module marshals numpy arrays into it. Definitions are cited in the C file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gs_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, ERR_INVALID_ARG, ERR_OUT_OF_GRID, ERR_NOMEM = 0, 1, 2, 3
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no contraction, no fast-math: float32 results are reproducible)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
+                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        lib.orc_bits_for.argtypes, lib.orc_bits_for.restype = [I64], I32
+        lib.orc_bounds.argtypes = [F, F, F, F, I32, I32, I32, P]
+        lib.orc_bounds.restype = None
+        lib.orc_isect_count.argtypes = [P, P, I32, I64, I64, I32, I32, I32, P, P]
+        lib.orc_isect_count.restype = I64
+        lib.orc_isect_emit.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, P]
+        lib.orc_isect_emit.restype = I32
+        lib.orc_sort_pairs.argtypes, lib.orc_sort_pairs.restype = [P, P, I64], I32
+        lib.orc_tile_offsets.argtypes, lib.orc_tile_offsets.restype = [P, I64, I64, I32, I32, P], I32
+        lib.orc_exp_neg.argtypes, lib.orc_exp_neg.restype = [F], F
+        lib.orc_exp_neg_array.argtypes, lib.orc_exp_neg_array.restype = [P, P, I64], None
+        lib.orc_composite_pixel.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, P, P, P, P]
+        lib.orc_composite_pixel.restype = None
+        lib.orc_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F, F,
+                                          P, I64, P, P, P, P]
+        lib.orc_rasterize_fwd.restype = I64
+        lib.orc_tile_lists.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, I64, P, P]
+        lib.orc_tile_lists.restype = I64
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def bits_for(count: int) -> int:
+    """Smallest b >= 0 with 2^b >= count (tile_bits for count = w*h, camera bits for count = C)."""
+    return int(_load().orc_bits_for(int(count)))
+
+
+def bounds(mean_x, mean_y, radius_x, radius_y, tile_size, tile_width, tile_height):
+    out = np.zeros(4, np.int32)
+    _load().orc_bounds(float(mean_x), float(mean_y), float(radius_x), float(radius_y), int(tile_size),
+                       int(tile_width), int(tile_height), _p(out))
+    return tuple(int(v) for v in out)
+
+
+@dataclass
+class Isect:
+    tiles_per_gauss: np.ndarray  # [C, N] int32
+    gauss_offsets: np.ndarray  # [C*N] int64, exclusive prefix of the counts
+    keys: np.ndarray  # [n] uint64
+    flatten_ids: np.ndarray  # [n] int32
+    n_isects: int
+
+
+def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True) -> Isect:
+    """Intersections of every (camera, splat) with the tile grid, as the pages' isect_tiles returns them."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    radii = _c(radii, np.float32)
+    depths = _c(depths, np.float32)
+    C, N = means2d.shape[0], means2d.shape[1]
+    rpg = 2 if radii.ndim == 3 else 1
+    tiles_per = np.zeros((C, N), np.int32)
+    goff = np.zeros(C * N, np.int64)
+    n = int(lib.orc_isect_count(_p(means2d), _p(radii), rpg, C, N, tile_size, tile_width, tile_height,
+                                _p(tiles_per), _p(goff)))
+    keys = np.zeros(n, np.uint64)
+    ids = np.zeros(n, np.int32)
+    lib.orc_isect_emit(_p(means2d), _p(radii), rpg, _p(depths), C, N, tile_size, tile_width, tile_height,
+                       _p(keys), _p(ids))
+    if sort and n > 1:
+        rc = lib.orc_sort_pairs(_p(keys), _p(ids), n)
+        if rc != OK:
+            raise MemoryError("oracle sort allocation failed")
+    return Isect(tiles_per, goff, keys, ids, n)
+
+
+def sort_pairs(keys, ids):
+    """Stable ascending sort by the unsigned key; returns new arrays."""
+    k = np.array(keys, dtype=np.uint64, copy=True)
+    i = np.array(ids, dtype=np.int32, copy=True)
+    if _load().orc_sort_pairs(_p(k), _p(i), k.size) != OK:
+        raise MemoryError("oracle sort allocation failed")
+    return k, i
+
+
+def tile_offsets(keys, C, tile_width, tile_height):
+    """Per-tile exclusive offsets [C, th, tw] int32; raises ValueError for a key outside the tile grid."""
+    k = _c(keys, np.uint64)
+    out = np.zeros((C, tile_height, tile_width), np.int32)
+    rc = _load().orc_tile_offsets(_p(k), k.size, C, tile_width, tile_height, _p(out))
+    if rc == ERR_OUT_OF_GRID:
+        raise ValueError("intersection key is outside the tile grid")
+    if rc != OK:
+        raise MemoryError("oracle offsets allocation failed")
+    return out
+
+
+def exp_neg(sigma) -> np.ndarray:
+    """The oracle's float32 e^-sigma, elementwise."""
+    s = np.ascontiguousarray(sigma, dtype=np.float32)
+    out = np.empty(s.shape, np.float32)
+    _load().orc_exp_neg_array(_p(s), _p(out), s.size)
+    return out
+
+
+def composite_pixel(means2d, conics, colors, opacities, list_ids, x, y, alpha_cutoff, alpha_clamp,
+                    transmittance_threshold):
+    """Composite one pixel over an explicit front-to-back list of flat splat ids.
+
+    Returns (acc[K], T, last_position, n_eval); last_position indexes ``list_ids`` (-1 if none composited)."""
+    lib = _load()
+    means2d = _c(means2d, np.float32).reshape(-1, 2)
+    conics = _c(conics, np.float32).reshape(-1, 3)
+    K = colors.shape[-1]
+    colors = _c(colors, np.float32).reshape(-1, K)
+    opacities = _c(opacities, np.float32).reshape(-1)
+    lst = _c(list_ids, np.int32)
+    acc = np.zeros(K, np.float32)
+    T = np.zeros(1, np.float32)
+    last = np.zeros(1, np.int64)
+    ne = np.zeros(1, np.int64)
+    lib.orc_composite_pixel(_p(means2d), _p(conics), _p(colors), _p(opacities), K, _p(lst), 0, lst.size, int(x),
+                            int(y), float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
+                            _p(acc), _p(T), _p(last), _p(ne))
+    return acc, float(T[0]), int(last[0]), int(ne[0])
+
+
+@dataclass
+class Raster:
+    render_colors: np.ndarray  # [C, H, W, K]
+    render_alphas: np.ndarray  # [C, H, W] = 1 - T
+    render_T: np.ndarray  # [C, H, W]
+    last_ids: np.ndarray  # [C, H, W] int32
+    n_eval: int
+
+
+def rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
+                  flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, tiles=None) -> Raster:
+    """Front-to-back compositing over every tile (or only the listed global tiles; other pixels stay NaN)."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    C = means2d.shape[0]
+    K = colors.shape[-1]
+    off = _c(isect_offsets, np.int32)
+    th, tw = off.shape[1], off.shape[2]
+    colors = _c(colors, np.float32)
+    bg = None if backgrounds is None else _c(backgrounds, np.float32)
+    out_c = np.full((C, height, width, K), np.nan, np.float32)
+    out_a = np.full((C, height, width), np.nan, np.float32)
+    out_t = np.full((C, height, width), np.nan, np.float32)
+    out_l = np.full((C, height, width), -2, np.int32)
+    tl = None if tiles is None else _c(tiles, np.int64)
+    n_eval = lib.orc_rasterize_fwd(_p(means2d), _p(_c(conics, np.float32)), _p(colors),
+                                   _p(_c(opacities, np.float32)), _p(bg), C, K, width, height, tile_size, tw, th,
+                                   _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects), float(alpha_cutoff),
+                                   float(alpha_clamp), float(transmittance_threshold), _p(tl),
+                                   0 if tl is None else tl.size, _p(out_c), _p(out_a), _p(out_t), _p(out_l))
+    if n_eval < 0:
+        raise ValueError("invalid rasterize arguments")
+    return Raster(out_c, out_a, out_t, out_l, int(n_eval))
+
+
+def tile_lists(means2d, radii, depths, tile_size, tile_width, tile_height, tiles):
+    """For each listed global tile: flat ids of the splats whose rectangle contains it, by (depth bits, id)."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    radii = _c(radii, np.float32)
+    depths = _c(depths, np.float32)
+    C, N = means2d.shape[0], means2d.shape[1]
+    rpg = 2 if radii.ndim == 3 else 1
+    tl = _c(tiles, np.int64)
+    counts = np.zeros(tl.size, np.int64)
+    total = lib.orc_tile_lists(_p(means2d), _p(radii), rpg, _p(depths), C, N, tile_size, tile_width, tile_height,
+                               _p(tl), tl.size, _p(counts), None)
+    ids = np.zeros(max(total, 0), np.int32)
+    lib.orc_tile_lists(_p(means2d), _p(radii), rpg, _p(depths), C, N, tile_size, tile_width, tile_height,
+                       _p(tl), tl.size, _p(counts), _p(ids))
+    out, pos = [], 0
+    for c in counts:
+        out.append(ids[pos:pos + int(c)])
+        pos += int(c)
+    return out
+
+
+def scene_pipeline(scene, sort=True):
+    """Whole path on the CPU for a synth.Scene: intersections, offsets and the composite."""
+    it = isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                     scene.tile_height, sort=sort)
+    off = tile_offsets(it.keys, scene.C, scene.tile_width, scene.tile_height)
+    ras = rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
+                        scene.width, scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects,
+                        scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold)
+    return it, off, ras

@@ -1,0 +1,399 @@
+/*
+ * Plain, slow CPU oracle for the tile-binned splat rasterizer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU-baseline leg use
+ * this file. It shares no code, header, table or constant with the HIP library; the two meet only at the
+ * seeded synthetic inputs.
+ *
+ * Sources (the pages the method is defined on):
+ *   [gsplat] gsplat 1.0.0 Ruby gem, native C extension, file intersections.c: gs_tile_bits, gs_clamp_tile,
+ *            gs_bounds, gs_radix_sort_without_gvl, gs_isect_tiles, gs_offset_encode.
+ *   [gsplat-bwd] same gem, raster_backward.c: gs_raster_backward_pixel and gs_raster_backward_without_gvl,
+ *            whose per-splat quantities (pixel centre, delta, quadratic form, alpha, clamp, skip test, range
+ *            end) fix what the forward computes; the forward itself is not on the pages and is read as the
+ *            front-to-back inverse of that backward.
+ *   [rlx-metal] rlx-metal 0.2.9 splat_training.rs, training_forward_metal_traced: names alpha_cutoff and
+ *            transmittance_threshold as forward parameters, and a cutoff default of 1/255.
+ *
+ * Arithmetic: float32 wherever the pages compute in float (all of the above do), evaluated in the pages'
+ * expression order with no contraction (build with -ffp-contract=off, never -ffast-math); fmaf appears only
+ * where the exponential below names it. Integer work is exact.
+ *
+ * Parity pins: every function here is checked by the CPU test suite against closed forms, brute-force
+ * enumerations, library routines and invariants; none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ERR_INVALID_ARG 1
+#define ORC_ERR_OUT_OF_GRID 2
+#define ORC_ERR_NOMEM 3
+
+/* Smallest b >= 0 with 2^b >= count: [gsplat] gs_tile_bits (ceil(log2(w*h)); 0 for one tile).
+ * The same rule gives the camera field width from C. */
+int orc_bits_for(int64_t count)
+{
+    int bits = 0;
+    uint64_t capacity = 1;
+    while (capacity < (uint64_t)count) {
+        capacity <<= 1;
+        bits += 1;
+    }
+    return bits;
+}
+
+/* floor/ceil result -> tile index clamped to [0, maximum] ([gsplat] gs_clamp_tile). The clamp is taken on the
+ * float before the int conversion so that huge or non-finite values are defined (NaN maps to 0); for finite
+ * in-range values this equals converting first and clamping after. */
+static int orc_clamp_tile(float value, int maximum)
+{
+    if (!(value > 0.0f)) return 0;
+    if (value > (float)maximum) return maximum;
+    return (int)value;
+}
+
+/* Tile rectangle [x0,x1) x [y0,y1) of one splat ([gsplat] gs_bounds). A non-positive radius gives the empty
+ * rectangle. The division is by the tile size converted to float, as in the pages. */
+void orc_bounds(float mean_x, float mean_y, float radius_x, float radius_y, int tile_size, int tile_width,
+                int tile_height, int32_t bounds[4])
+{
+    if (radius_x <= 0.0f || radius_y <= 0.0f) {
+        bounds[0] = bounds[1] = bounds[2] = bounds[3] = 0;
+        return;
+    }
+    float ts = (float)tile_size;
+    bounds[0] = orc_clamp_tile(floorf((mean_x - radius_x) / ts), tile_width);
+    bounds[1] = orc_clamp_tile(floorf((mean_y - radius_y) / ts), tile_height);
+    bounds[2] = orc_clamp_tile(ceilf((mean_x + radius_x) / ts), tile_width);
+    bounds[3] = orc_clamp_tile(ceilf((mean_y + radius_y) / ts), tile_height);
+}
+
+static void orc_bounds_of(const float *means2d, const float *radii, int radii_per_gauss, int64_t index,
+                          int tile_size, int tile_width, int tile_height, int32_t bounds[4])
+{
+    float rx = radii[index * radii_per_gauss];
+    float ry = radii_per_gauss == 2 ? radii[index * 2 + 1] : rx;
+    orc_bounds(means2d[index * 2], means2d[index * 2 + 1], rx, ry, tile_size, tile_width, tile_height, bounds);
+}
+
+/* Step 1 of [gsplat] gs_isect_tiles: per (camera, splat) tile count = clamped rectangle area, in row-major
+ * [C, N] order, and the running write index (exclusive prefix) at which each splat's keys start.
+ * Returns the total number of intersections. */
+int64_t orc_isect_count(const float *means2d, const float *radii, int radii_per_gauss, int64_t C, int64_t N,
+                        int tile_size, int tile_width, int tile_height, int32_t *tiles_per_gauss,
+                        int64_t *gauss_offsets)
+{
+    int64_t total = 0;
+    for (int64_t index = 0; index < C * N; ++index) {
+        int32_t b[4];
+        orc_bounds_of(means2d, radii, radii_per_gauss, index, tile_size, tile_width, tile_height, b);
+        int64_t count = (int64_t)(b[2] - b[0]) * (int64_t)(b[3] - b[1]);
+        if (tiles_per_gauss) tiles_per_gauss[index] = (int32_t)count;
+        if (gauss_offsets) gauss_offsets[index] = total;
+        total += count;
+    }
+    return total;
+}
+
+/* Step 2 of [gsplat] gs_isect_tiles: in (camera, splat, tile row, tile column) order write
+ *   key = ((camera << tile_bits) | (ty * tile_width + tx)) << 32 | bit pattern of the depth,
+ *   id  = camera * N + splat.
+ * Writes exactly n_isects entries; returns 0. */
+int orc_isect_emit(const float *means2d, const float *radii, int radii_per_gauss, const float *depths,
+                   int64_t C, int64_t N, int tile_size, int tile_width, int tile_height, uint64_t *keys,
+                   int32_t *flatten_ids)
+{
+    int tile_bits = orc_bits_for((int64_t)tile_width * tile_height);
+    int64_t write_index = 0;
+    for (int64_t camera = 0; camera < C; ++camera) {
+        for (int64_t splat = 0; splat < N; ++splat) {
+            int64_t index = camera * N + splat;
+            int32_t b[4];
+            orc_bounds_of(means2d, radii, radii_per_gauss, index, tile_size, tile_width, tile_height, b);
+            uint32_t depth_bits;
+            memcpy(&depth_bits, &depths[index], sizeof depth_bits);
+            uint64_t upper_camera = (uint64_t)camera << tile_bits;
+            for (int ty = b[1]; ty < b[3]; ++ty) {
+                for (int tx = b[0]; tx < b[2]; ++tx) {
+                    uint64_t tile = (uint64_t)ty * (uint64_t)tile_width + (uint64_t)tx;
+                    keys[write_index] = ((upper_camera | tile) << 32) | (uint64_t)depth_bits;
+                    flatten_ids[write_index] = (int32_t)index;
+                    write_index += 1;
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Stable ascending sort of (key, id) pairs by the unsigned key. [gsplat] gs_radix_sort_without_gvl is a
+ * stable LSD radix sort over all 64 bits, so its result is the stable order by key; written here as a plain
+ * bottom-up merge sort, which is stable by construction (ties take the left run first). */
+int orc_sort_pairs(uint64_t *keys, int32_t *ids, int64_t n)
+{
+    if (n < 2) return ORC_OK;
+    uint64_t *tk = (uint64_t *)malloc((size_t)n * sizeof(uint64_t));
+    int32_t *ti = (int32_t *)malloc((size_t)n * sizeof(int32_t));
+    if (!tk || !ti) {
+        free(tk);
+        free(ti);
+        return ORC_ERR_NOMEM;
+    }
+    uint64_t *sk = keys, *dk = tk;
+    int32_t *si = ids, *di = ti;
+    for (int64_t width = 1; width < n; width *= 2) {
+        for (int64_t lo = 0; lo < n; lo += 2 * width) {
+            int64_t mid = lo + width < n ? lo + width : n;
+            int64_t hi = lo + 2 * width < n ? lo + 2 * width : n;
+            int64_t a = lo, b = mid, o = lo;
+            while (a < mid && b < hi) {
+                if (sk[b] < sk[a]) {
+                    dk[o] = sk[b];
+                    di[o++] = si[b++];
+                } else {
+                    dk[o] = sk[a];
+                    di[o++] = si[a++];
+                }
+            }
+            while (a < mid) {
+                dk[o] = sk[a];
+                di[o++] = si[a++];
+            }
+            while (b < hi) {
+                dk[o] = sk[b];
+                di[o++] = si[b++];
+            }
+        }
+        uint64_t *xk = sk;
+        sk = dk;
+        dk = xk;
+        int32_t *xi = si;
+        si = di;
+        di = xi;
+    }
+    if (sk != keys) {
+        memcpy(keys, sk, (size_t)n * sizeof(uint64_t));
+        memcpy(ids, si, (size_t)n * sizeof(int32_t));
+    }
+    free(tk);
+    free(ti);
+    return ORC_OK;
+}
+
+/* [gsplat] gs_offset_encode: histogram of intersections per global tile camera * (w*h) + (upper & mask), with
+ * upper = key >> 32 and camera = upper >> tile_bits, then an exclusive prefix into offsets[C, h, w].
+ * A key whose camera or tile falls outside the grid is an error (the pages raise ArgError). */
+int orc_tile_offsets(const uint64_t *keys, int64_t n, int64_t C, int tile_width, int tile_height,
+                     int32_t *offsets)
+{
+    int tile_bits = orc_bits_for((int64_t)tile_width * tile_height);
+    uint64_t mask = tile_bits == 0 ? 0 : ((1ULL << tile_bits) - 1);
+    uint64_t per_camera = (uint64_t)tile_width * (uint64_t)tile_height;
+    int64_t tiles = C * (int64_t)per_camera;
+    int64_t *counts = (int64_t *)calloc((size_t)(tiles > 0 ? tiles : 1), sizeof(int64_t));
+    if (!counts) return ORC_ERR_NOMEM;
+    for (int64_t i = 0; i < n; ++i) {
+        uint64_t upper = keys[i] >> 32;
+        uint64_t camera = upper >> tile_bits;
+        uint64_t tile = upper & mask;
+        if (camera >= (uint64_t)C || tile >= per_camera) {
+            free(counts);
+            return ORC_ERR_OUT_OF_GRID;
+        }
+        counts[camera * per_camera + tile] += 1;
+    }
+    int64_t running = 0;
+    for (int64_t t = 0; t < tiles; ++t) {
+        offsets[t] = (int32_t)running;
+        running += counts[t];
+    }
+    free(counts);
+    return ORC_OK;
+}
+
+/* e^(-sigma) in float32 by Cody-Waite range reduction and a Taylor polynomial (W. J. Cody and W. Waite,
+ * "Software Manual for the Elementary Functions", 1980, exponential chapter):
+ *   k = nearest integer to -sigma / ln 2,   r = -sigma - k ln 2 (ln 2 split in a high part with trailing zero
+ *   bits and a low correction, both applied with fmaf),   e^(-sigma) = 2^k * sum_{j<=7} r^j / j!.
+ * Any sigma above 80 (or NaN) returns 0: e^-80 is far below any usable alpha, and the cut keeps every returned
+ * value a normal float (k >= -116). The pages call the C library expf; this reading fixes one exponential
+ * so that alpha, and every decision made on it, is reproducible to the bit. */
+static const float ORC_LOG2E = 1.44269502162933349609375f;         /* nearest float to 1/ln 2 */
+static const float ORC_LN2_HI = 0.693145751953125f;                /* ln 2 to 15 significant bits */
+static const float ORC_LN2_LO = 1.428606765330187045037746429443359375e-6f; /* ln 2 - ORC_LN2_HI, rounded */
+
+float orc_exp_neg(float sigma)
+{
+    if (!(sigma <= 80.0f)) return 0.0f;
+    float t = -sigma;
+    float k = rintf(t * ORC_LOG2E);
+    float r = fmaf(-k, ORC_LN2_HI, t);
+    r = fmaf(-k, ORC_LN2_LO, r);
+    float p = 1.0f / 5040.0f;
+    p = fmaf(p, r, 1.0f / 720.0f);
+    p = fmaf(p, r, 1.0f / 120.0f);
+    p = fmaf(p, r, 1.0f / 24.0f);
+    p = fmaf(p, r, 1.0f / 6.0f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)k);
+}
+
+/* Elementwise orc_exp_neg over an array (for sweeps in the tests). */
+void orc_exp_neg_array(const float *sigma, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_exp_neg(sigma[i]);
+}
+
+/* Front-to-back compositing of one pixel over list[start, end) (the forward read from [gsplat-bwd]):
+ *   centre (x + 0.5, y + 0.5); d = mean - centre;
+ *   sigma = 0.5 * (a dx dx + c dy dy) + b dx dy with the conic (a, b, c), each product and sum rounded to float;
+ *   sigma < 0 -> skip; alpha = min(clamp, opacity * e^-sigma); alpha < cutoff -> skip;
+ *   T' = T (1 - alpha); T' <= threshold -> stop before this splat ([rlx-metal] transmittance_threshold);
+ *   otherwise colour += colour_g * (alpha T), T = T', last = position.
+ * Writes acc[K], the final transmittance and the last composited position (-1 if none); counts every
+ * evaluation of sigma (including the stopping one) into *n_eval. */
+void orc_composite_pixel(const float *means2d, const float *conics, const float *colors,
+                         const float *opacities, int K, const int32_t *list, int64_t start, int64_t end,
+                         int x, int y, float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                         float *acc, float *T_out, int64_t *last_out, int64_t *n_eval)
+{
+    float px = (float)x + 0.5f;
+    float py = (float)y + 0.5f;
+    float T = 1.0f;
+    int64_t last = -1;
+    for (int k = 0; k < K; ++k) acc[k] = 0.0f;
+    for (int64_t i = start; i < end; ++i) {
+        int64_t g = list[i];
+        float dx = means2d[g * 2] - px;
+        float dy = means2d[g * 2 + 1] - py;
+        float a = conics[g * 3], b = conics[g * 3 + 1], c = conics[g * 3 + 2];
+        float sigma = 0.5f * (a * dx * dx + c * dy * dy) + b * dx * dy;
+        if (n_eval) *n_eval += 1;
+        if (sigma < 0.0f) continue;
+        float alpha = opacities[g] * orc_exp_neg(sigma);
+        if (alpha > alpha_clamp) alpha = alpha_clamp;
+        if (alpha < alpha_cutoff) continue;
+        float T_next = T * (1.0f - alpha);
+        if (T_next <= transmittance_threshold) break;
+        float v = alpha * T;
+        for (int k = 0; k < K; ++k) acc[k] = acc[k] + colors[g * K + k] * v;
+        T = T_next;
+        last = i;
+    }
+    *T_out = T;
+    *last_out = last;
+}
+
+/* Forward rasterization over tiles ([gsplat-bwd] gs_raster_backward_without_gvl for the tile walk): global
+ * tile t = (camera * th + ty) * tw + tx, its range [offsets[t], t + 1 < T ? offsets[t + 1] : n), the tile's
+ * pixels clipped to width x height. Outputs per pixel: colour = acc + T * background (0 without one),
+ * alpha = 1 - T, T, and last id (global intersection index, -1 if nothing composited).
+ * tiles == NULL processes every tile; otherwise only the n_tiles listed (other pixels are left untouched).
+ * Returns the number of sigma evaluations. */
+int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
+                          const float *opacities, const float *backgrounds, int64_t C, int K, int width,
+                          int height, int tile_size, int tile_width, int tile_height, const int32_t *offsets,
+                          const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
+                          float transmittance_threshold, const int64_t *tiles, int64_t n_tiles,
+                          float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids)
+{
+    int64_t per_camera = (int64_t)tile_width * tile_height;
+    int64_t total_tiles = C * per_camera;
+    int64_t count = tiles ? n_tiles : total_tiles;
+    int64_t n_eval = 0;
+    float acc[64];
+    if (K < 1 || K > 64) return -1;
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t t = tiles ? tiles[j] : j;
+        if (t < 0 || t >= total_tiles) return -1;
+        int64_t camera = t / per_camera;
+        int64_t local = t % per_camera;
+        int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
+        int64_t start = offsets[t];
+        int64_t end = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
+        for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
+            for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
+                float T;
+                int64_t last;
+                orc_composite_pixel(means2d, conics, colors, opacities, K, flatten_ids, start, end, x, y,
+                                    alpha_cutoff, alpha_clamp, transmittance_threshold, acc, &T, &last, &n_eval);
+                int64_t pixel = (camera * height + y) * (int64_t)width + x;
+                for (int k = 0; k < K; ++k) {
+                    float bg = backgrounds ? backgrounds[camera * K + k] : 0.0f;
+                    render_colors[pixel * K + k] = acc[k] + T * bg;
+                }
+                render_alphas[pixel] = 1.0f - T;
+                if (render_T) render_T[pixel] = T;
+                if (last_ids) last_ids[pixel] = (int32_t)last;
+            }
+        }
+    }
+    return n_eval;
+}
+
+/* Per-tile lists straight from the definition, for sampled checks at sizes where a full sort is too slow:
+ * for each requested global tile, every (camera, splat) whose rectangle contains it, ordered by
+ * (depth bit pattern, flat id). Call once with out_ids == NULL to fill out_counts[n_tiles] and get the total,
+ * then again with out_ids sized to that total (tile by tile, in the order of `tiles`). */
+int64_t orc_tile_lists(const float *means2d, const float *radii, int radii_per_gauss, const float *depths,
+                       int64_t C, int64_t N, int tile_size, int tile_width, int tile_height, const int64_t *tiles,
+                       int64_t n_tiles, int64_t *out_counts, int32_t *out_ids)
+{
+    int64_t per_camera = (int64_t)tile_width * tile_height;
+    int64_t *cursor = (int64_t *)calloc((size_t)(n_tiles > 0 ? n_tiles : 1), sizeof(int64_t));
+    if (!cursor) return -1;
+    if (out_ids) {
+        int64_t running = 0;
+        for (int64_t j = 0; j < n_tiles; ++j) {
+            cursor[j] = running;
+            running += out_counts[j];
+        }
+    } else {
+        for (int64_t j = 0; j < n_tiles; ++j) out_counts[j] = 0;
+    }
+    for (int64_t index = 0; index < C * N; ++index) {
+        int64_t camera = index / N;
+        int32_t b[4];
+        orc_bounds_of(means2d, radii, radii_per_gauss, index, tile_size, tile_width, tile_height, b);
+        if (b[0] == b[2] || b[1] == b[3]) continue;
+        for (int64_t j = 0; j < n_tiles; ++j) {
+            int64_t t = tiles[j];
+            if (t / per_camera != camera) continue;
+            int64_t local = t % per_camera;
+            int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
+            if (tx >= b[0] && tx < b[2] && ty >= b[1] && ty < b[3]) {
+                if (out_ids) out_ids[cursor[j]++] = (int32_t)index;
+                else out_counts[j] += 1;
+            }
+        }
+    }
+    int64_t total = 0;
+    for (int64_t j = 0; j < n_tiles; ++j) {
+        int64_t start = total;
+        total += out_counts[j];
+        if (!out_ids) continue;
+        /* insertion sort of this tile's ids by (depth bits, id); ids arrive ascending, so equal depths keep
+         * ascending id */
+        for (int64_t i = start + 1; i < total; ++i) {
+            int32_t v = out_ids[i];
+            uint32_t dv;
+            memcpy(&dv, &depths[v], sizeof dv);
+            int64_t p = i;
+            while (p > start) {
+                uint32_t du;
+                memcpy(&du, &depths[out_ids[p - 1]], sizeof du);
+                if (du <= dv) break;
+                out_ids[p] = out_ids[p - 1];
+                --p;
+            }
+            out_ids[p] = v;
+        }
+    }
+    free(cursor);
+    return total;
+}
