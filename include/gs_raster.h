@@ -1,0 +1,158 @@
+/*
+ * gs_raster.h: C ABI of the MI355X (gfx950) tile-binned splat rasterizer.
+ *
+ * One frame runs four steps, each an entry point below:
+ *   gs_isect_tiles    splat -> tile intersections and their 64-bit keys (optionally sorted),
+ *   gs_sort_keys      stable radix sort of (key, id) pairs over the populated low key bits,
+ *   gs_tile_ranges    per-tile [start, end) ranges of a sorted key array,
+ *   gs_rasterize_fwd  per-tile front-to-back alpha compositing.
+ *
+ * Definitions follow these pages:
+ *   [gsplat]     gsplat 1.0.0 Ruby gem, native C extension, intersections.c (gs_tile_bits, gs_bounds,
+ *                gs_radix_sort_without_gvl, gs_isect_tiles, gs_offset_encode);
+ *   [gsplat-bwd] the same gem's raster_backward.c (gs_raster_backward_pixel, gs_raster_backward_without_gvl),
+ *                whose per-splat terms fix what the forward computes, and raster_backward_bridge.c
+ *                (gs_raster_backward), which lists the forward's arguments;
+ *   [rlx-metal]  rlx-metal 0.2.9 splat_training.rs (training_forward_metal_traced): alpha_cutoff and
+ *                transmittance_threshold as forward parameters.
+ *
+ * Conventions for every entry point.
+ *   - Device pointers point to memory on the current HIP device; every array is dense and C-ordered.
+ *     The caller allocates and owns every buffer, workspace included; the library never allocates or frees
+ *     device memory and keeps no state between calls except a thread-local error message.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls are asynchronous on it unless
+ *     stated otherwise; inputs must stay valid until the stream has run the work.
+ *   - On any error nothing is launched (argument checks run on the host first), the return value says why,
+ *     and gs_last_error() describes it. GS_ERR_DEVICE means a HIP runtime call or launch failed.
+ *   - Keys are 64-bit unsigned; callers holding them in int64 storage (as the pages do) pass the same bits.
+ *   - Floating-point results are float32 with a fixed operation order (no contraction), so the same inputs
+ *     give the same bits on every run.
+ */
+#ifndef GS_RASTER_H
+#define GS_RASTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gs_status {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARG = 1, /* bad shape, size, pointer or option ([gsplat] raises ArgError for these) */
+    GS_ERR_OUT_OF_GRID = 2, /* a key decodes outside the tile grid ([gsplat] gs_offset_encode) */
+    GS_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than the matching *_workspace_bytes() */
+    GS_ERR_DEVICE = 4       /* a HIP runtime call or kernel launch failed */
+} gs_status;
+
+/* Message for the last non-OK status returned on this thread ("" if none). Valid until the next call. */
+const char *gs_last_error(void);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Intersections ([gsplat] gs_isect_tiles, with gs_bounds and gs_tile_bits).
+ *
+ * For every camera c < C and splat g < N (flat index i = c*N + g) the tile rectangle is
+ *   x0 = clamp(floor((mx - rx) / ts), 0, tw)    x1 = clamp(ceil((mx + rx) / ts), 0, tw)
+ *   y0 = clamp(floor((my - ry) / ts), 0, th)    y1 = clamp(ceil((my + ry) / ts), 0, th)
+ * in float32 with IEEE division (empty when rx <= 0 or ry <= 0, or when an input is NaN), its tile count is
+ * (x1 - x0) * (y1 - y0), and each covered tile (ty, tx) yields one intersection
+ *   key = ((c << tile_bits) | (ty * tw + tx)) << 32 | bits(depth[i]),   id = i,
+ * with tile_bits = ceil(log2(tw * th)) (0 for one tile). Unsorted output is in (c, g, ty, tx) order; sorted
+ * output is the stable ascending order by key, i.e. by (camera, tile, depth bits, id).
+ *
+ * Two phases, because the output size depends on the data:
+ *   1. keys == NULL: count. Writes tiles_per_gauss[C*N] (int32), gauss_offsets[C*N] (int32 exclusive prefix
+ *      of the counts, the first output slot of each splat) and *n_isects_out (host memory), then SYNCHRONISES
+ *      the stream to return the count. n_isects is ignored.
+ *   2. keys != NULL: emit. Needs gauss_offsets from phase 1 unchanged and n_isects = phase 1's count; writes
+ *      keys[n_isects] and flatten_ids[n_isects]; when sort != 0 and n_isects > 1 also sorts them (as
+ *      gs_sort_keys with end_bit = 32 + tile_bits + camera_bits). Asynchronous. tiles_per_gauss and
+ *      n_isects_out are ignored.
+ *
+ * means2d     [C, N, 2] float32 (pixel coordinates)
+ * radii       [C, N] float32 if radii_per_gauss == 1 (isotropic), [C, N, 2] if 2 (x and y extents)
+ * depths      [C, N] float32; only the bit pattern is used (it forms the key's low 32 bits)
+ * tile_size   > 0 pixels; tile_width, tile_height > 0 tiles (any grid; not tied to an image size here)
+ * Limits (GS_ERR_INVALID_ARG): C >= 1, N >= 0, C*N < 2^31, tile_width*tile_height < 2^31,
+ *   tile_bits + camera_bits <= 32 (camera_bits = ceil(log2 C)), total intersections < 2^31 (phase 1 returns
+ *   the error and still writes *n_isects_out), and with sort != 0 at most 2^30 - 1 intersections.
+ * workspace: gs_isect_workspace_bytes(C, N, n, tile_width, tile_height, sort) bytes; n = 0 sizes phase 1.
+ */
+size_t gs_isect_workspace_bytes(int64_t C, int64_t N, int64_t n_isects, int tile_width, int tile_height, int sort);
+
+gs_status gs_isect_tiles(const float *means2d, const float *radii, int radii_per_gauss, const float *depths,
+                         int64_t C, int64_t N, int tile_size, int tile_width, int tile_height, int sort,
+                         int32_t *tiles_per_gauss, int32_t *gauss_offsets, int64_t *n_isects_out,
+                         uint64_t *keys, int32_t *flatten_ids, int64_t n_isects,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Stable sort ([gsplat] gs_radix_sort_without_gvl: a stable LSD radix sort of (key, id) pairs).
+ *
+ * Reorders keys[n] and flatten_ids[n] in place into ascending order of (key mod 2^end_bit); equal values keep
+ * their input order, so the result is unique. Bits at and above end_bit take no part and travel with their
+ * key (for intersection keys they are zero). 0 <= end_bit <= 64; n <= 2^30 - 1. Passes of at most 8 bits
+ * cover [0, end_bit); the workspace holds the alternate buffers and the per-pass counters.
+ */
+size_t gs_sort_workspace_bytes(int64_t n, int end_bit);
+
+gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_bit, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Tile ranges ([gsplat] gs_offset_encode for the output, [gsplat-bwd] gs_raster_backward_without_gvl for how
+ * a range is read).
+ *
+ * For keys sorted by their upper 32 bits, writes isect_offsets[C, th, tw] (int32): entry t is the number of
+ * keys whose global tile camera * (tw * th) + (upper & (2^tile_bits - 1)) is below t, with
+ * upper = key >> 32 and camera = upper >> tile_bits. Tile t's intersections are then
+ * [offsets[t], t + 1 < C*th*tw ? offsets[t + 1] : n). Computed by boundary detection over the sorted keys.
+ * validate != 0: also checks every key decodes inside the grid (camera < C, tile < tw * th) and that the
+ *   keys' global tiles do not decrease, then SYNCHRONISES; returns GS_ERR_OUT_OF_GRID or GS_ERR_INVALID_ARG
+ *   (unsorted) if not. validate == 0 trusts the input (writes stay in bounds either way) and is asynchronous.
+ * n may be 0 (all offsets 0). workspace: gs_tile_ranges_workspace_bytes() bytes (an error flag).
+ */
+size_t gs_tile_ranges_workspace_bytes(void);
+
+gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int64_t C, int tile_width, int tile_height,
+                         int32_t *isect_offsets, int validate, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Forward compositing (the front-to-back inverse of [gsplat-bwd] gs_raster_backward_pixel, with the
+ * [rlx-metal] alpha_cutoff and transmittance_threshold).
+ *
+ * For each camera c, tile t = (c * th + ty) * tw + tx and pixel (x, y) of the tile inside width x height,
+ * walking i over [offsets[t], end of t) with g = flatten_ids[i], starting from T = 1, colour 0, last = -1:
+ *   dx = means2d[g].x - (x + 0.5),  dy = means2d[g].y - (y + 0.5),
+ *   sigma = 0.5 * (a dx dx + c dy dy) + b dx dy  with (a, b, c) = conics[g], each operation rounded to float;
+ *   skip if sigma < 0;  alpha = min(alpha_clamp, opacities[g] * E(sigma));  skip if alpha < alpha_cutoff;
+ *   T' = T * (1 - alpha); stop before this splat if T' <= transmittance_threshold;
+ *   colour += colors[g] * (alpha * T); T = T'; last = i.
+ * E(sigma) is e^-sigma computed as: 0 if sigma > 80 or NaN, else k = rint(-sigma * log2 e),
+ * r = fma(-k, ln2_hi, -sigma), r = fma(-k, ln2_lo, r), a degree-7 Taylor polynomial of e^r by fma (Horner),
+ * times 2^k (Cody and Waite's reduction) - the same bits on any IEEE float32 machine.
+ * Outputs per pixel: render_colors [C, H, W, K] = colour + T * backgrounds[c] (backgrounds [C, K], NULL = 0),
+ * render_alphas [C, H, W] = 1 - T, render_T [C, H, W] = T (nullable), last_ids [C, H, W] = last (nullable;
+ * a global intersection index, -1 if nothing composited).
+ * conics [C, N, 3] = (inv00, inv01, inv11) of the 2D covariance; colors [C, N, K]; opacities [C, N].
+ * Limits: 1 <= K <= 4; 1 <= tile_size <= 32; tile_width == ceil(width / tile_size) and
+ *   tile_height == ceil(height / tile_size); flatten_ids must index [0, C*N) (not checked on the device).
+ * workspace: gs_rasterize_workspace_bytes(C, tile_width, tile_height) bytes (tile scheduling order).
+ */
+size_t gs_rasterize_workspace_bytes(int64_t C, int tile_width, int tile_height);
+
+gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
+                           const float *backgrounds, int64_t C, int64_t N, int K, int width, int height,
+                           int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
+                           const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
+                           float transmittance_threshold, float *render_colors, float *render_alphas,
+                           float *render_T, int32_t *last_ids, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_RASTER_H */

@@ -59,6 +59,10 @@ def _load():
         lib.orc_rasterize_fwd.restype = I64
         lib.orc_tile_lists.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, I64, P, P]
         lib.orc_tile_lists.restype = I64
+        lib.orc_rasterize_tile.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, P, I64, F, F, F, P, P,
+                                           P]
+        lib.orc_rasterize_tile.restype = I64
+        lib.orc_rects.argtypes, lib.orc_rects.restype = [P, P, I32, I64, I32, I32, I32, P], None
         _lib = lib
     return _lib
 
@@ -220,6 +224,37 @@ def tile_lists(means2d, radii, depths, tile_size, tile_width, tile_height, tiles
     for c in counts:
         out.append(ids[pos:pos + int(c)])
         pos += int(c)
+    return out
+
+
+def rasterize_tile(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, tile_width,
+                   tile_height, tile, list_ids, alpha_cutoff, alpha_clamp, transmittance_threshold):
+    """Composite one global tile over an explicit front-to-back list of flat ids.
+
+    Returns (colors [ts, ts, K], T [ts, ts], last_pos [ts, ts] indexing list_ids, n_eval); pixels outside the image
+    hold NaN / -2."""
+    lib = _load()
+    K = colors.shape[-1]
+    lst = _c(list_ids, np.int32)
+    oc = np.full((tile_size, tile_size, K), np.nan, np.float32)
+    ot = np.full((tile_size, tile_size), np.nan, np.float32)
+    ol = np.full((tile_size, tile_size), -2, np.int64)
+    bg = None if backgrounds is None else _c(backgrounds, np.float32)
+    ne = lib.orc_rasterize_tile(_p(_c(means2d, np.float32)), _p(_c(conics, np.float32)), _p(_c(colors, np.float32)),
+                                _p(_c(opacities, np.float32)), _p(bg), K, width, height, tile_size, tile_width,
+                                tile_height, int(tile), _p(lst), lst.size, float(alpha_cutoff), float(alpha_clamp),
+                                float(transmittance_threshold), _p(oc), _p(ot), _p(ol))
+    return oc, ot, ol, int(ne)
+
+
+def rects(means2d, radii, tile_size, tile_width, tile_height):
+    """[C*N, 4] int32 tile rectangles (x0, y0, x1, y1)."""
+    means2d = _c(means2d, np.float32)
+    radii = _c(radii, np.float32)
+    M = means2d.shape[0] * means2d.shape[1]
+    out = np.zeros((M, 4), np.int32)
+    _load().orc_rects(_p(means2d), _p(radii), 2 if radii.ndim == 3 else 1, M, tile_size, tile_width, tile_height,
+                      _p(out))
     return out
 
 

@@ -336,6 +336,50 @@ int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float
     return n_eval;
 }
 
+/* Composite the pixels of one global tile over an explicit front-to-back list of flat ids (the same per-pixel
+ * rule as orc_rasterize_fwd). Outputs are [ts*ts] per-tile arrays in row-major pixel order; pixels outside the
+ * image are left untouched. last_pos indexes `list` (-1 if nothing composited). Returns the evaluation count. */
+int64_t orc_rasterize_tile(const float *means2d, const float *conics, const float *colors, const float *opacities,
+                           const float *backgrounds, int K, int width, int height, int tile_size, int tile_width,
+                           int tile_height, int64_t tile, const int32_t *list, int64_t count, float alpha_cutoff,
+                           float alpha_clamp, float transmittance_threshold, float *out_colors, float *out_T,
+                           int64_t *out_last_pos)
+{
+    int64_t per_camera = (int64_t)tile_width * tile_height;
+    int64_t camera = tile / per_camera;
+    int64_t local = tile % per_camera;
+    int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
+    int64_t n_eval = 0;
+    float acc[64];
+    if (K < 1 || K > 64) return -1;
+    for (int ly = 0; ly < tile_size; ++ly) {
+        for (int lx = 0; lx < tile_size; ++lx) {
+            int x = tx * tile_size + lx, y = ty * tile_size + ly;
+            if (x >= width || y >= height) continue;
+            float T;
+            int64_t last;
+            orc_composite_pixel(means2d, conics, colors, opacities, K, list, 0, count, x, y, alpha_cutoff,
+                                alpha_clamp, transmittance_threshold, acc, &T, &last, &n_eval);
+            int64_t q = (int64_t)ly * tile_size + lx;
+            for (int k = 0; k < K; ++k) {
+                float bg = backgrounds ? backgrounds[camera * K + k] : 0.0f;
+                out_colors[q * K + k] = acc[k] + T * bg;
+            }
+            out_T[q] = T;
+            out_last_pos[q] = last;
+        }
+    }
+    return n_eval;
+}
+
+/* Tile rectangles [x0, y0, x1, y1] of every (camera, splat), for vectorised membership checks. */
+void orc_rects(const float *means2d, const float *radii, int radii_per_gauss, int64_t M, int tile_size,
+               int tile_width, int tile_height, int32_t *rects)
+{
+    for (int64_t i = 0; i < M; ++i)
+        orc_bounds_of(means2d, radii, radii_per_gauss, i, tile_size, tile_width, tile_height, rects + 4 * i);
+}
+
 /* Per-tile lists straight from the definition, for sampled checks at sizes where a full sort is too slow:
  * for each requested global tile, every (camera, splat) whose rectangle contains it, ordered by
  * (depth bit pattern, flat id). Call once with out_ids == NULL to fill out_counts[n_tiles] and get the total,

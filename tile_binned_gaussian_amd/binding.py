@@ -1,0 +1,212 @@
+"""Thin ctypes binding of libgs_raster (C ABI in include/gs_raster.h), one Python function per entry point.
+
+Argument marshalling only: every step runs in the HIP library. PyTorch supplies device memory (tensors on a ROCm
+device) and the stream (torch's current stream unless one is passed). The library must be built
+(``python -m tile_binned_gaussian_amd.build``); loading fails loudly otherwise, and there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loads the HIP runtime first, so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgs_raster.so")
+
+GS_OK, GS_ERR_INVALID_ARG, GS_ERR_OUT_OF_GRID, GS_ERR_WORKSPACE, GS_ERR_DEVICE = range(5)
+_STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPACE", 4: "GS_ERR_DEVICE"}
+
+EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
+           "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
+           "gs_rasterize_fwd")
+
+
+class GsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libgs_raster.so and declares every exported signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m tile_binned_gaussian_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gs_last_error.argtypes, lib.gs_last_error.restype = [], ctypes.c_char_p
+    lib.gs_isect_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, I32]
+    lib.gs_isect_workspace_bytes.restype = SZ
+    lib.gs_isect_tiles.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, I32, P, P, P, P, P, I64, P, SZ, P]
+    lib.gs_isect_tiles.restype = I32
+    lib.gs_sort_workspace_bytes.argtypes, lib.gs_sort_workspace_bytes.restype = [I64, I32], SZ
+    lib.gs_sort_keys.argtypes, lib.gs_sort_keys.restype = [P, P, I64, I32, P, SZ, P], I32
+    lib.gs_tile_ranges_workspace_bytes.argtypes, lib.gs_tile_ranges_workspace_bytes.restype = [], SZ
+    lib.gs_tile_ranges.argtypes = [P, I64, I64, I32, I32, P, I32, P, SZ, P]
+    lib.gs_tile_ranges.restype = I32
+    lib.gs_rasterize_workspace_bytes.argtypes = [I64, I32, I32]
+    lib.gs_rasterize_workspace_bytes.restype = SZ
+    lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F, F,
+                                     P, P, P, P, P, SZ, P]
+    lib.gs_rasterize_fwd.restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GS_OK:
+        raise GsError(status, _lib.gs_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _req(t, name, dtype, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Intersections:
+    tiles_per_gauss: torch.Tensor  # [C, N] int32
+    gauss_offsets: torch.Tensor  # [C*N] int32
+    isect_ids: torch.Tensor  # [n] int64 (the u64 key bits)
+    flatten_ids: torch.Tensor  # [n] int32
+    n_isects: int
+
+
+def gs_isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True, stream=None,
+                   workspace=None) -> Intersections:
+    """Both phases of gs_isect_tiles: count (synchronises once for the size), then emit (and sort)."""
+    lib = load_library()
+    dev = means2d.device
+    _req(means2d, "means2d", torch.float32, dev)
+    if means2d.dim() != 3 or means2d.shape[2] != 2:
+        raise ValueError("means2d must be [C, N, 2]")
+    C, N = means2d.shape[0], means2d.shape[1]
+    _req(radii, "radii", torch.float32, dev)
+    if tuple(radii.shape) == (C, N):
+        rpg = 1
+    elif tuple(radii.shape) == (C, N, 2):
+        rpg = 2
+    else:
+        raise ValueError(f"radii must be [C, N] or [C, N, 2] (got {tuple(radii.shape)})")
+    _req(depths, "depths", torch.float32, dev, (C, N))
+    s = _stream(stream)
+    tiles_per = torch.empty((C, N), dtype=torch.int32, device=dev)
+    goff = torch.empty(C * N, dtype=torch.int32, device=dev)
+    n_out = ctypes.c_int64(0)
+    ws = workspace if workspace is not None else _workspace(
+        lib.gs_isect_workspace_bytes(C, N, 0, tile_width, tile_height, int(bool(sort))), dev)
+    _check(lib.gs_isect_tiles(_ptr(means2d), _ptr(radii), rpg, _ptr(depths), C, N, tile_size, tile_width,
+                              tile_height, int(bool(sort)), _ptr(tiles_per), _ptr(goff), ctypes.byref(n_out), None,
+                              None, 0, _ptr(ws), ws.numel(), s))
+    n = int(n_out.value)
+    keys = torch.empty(n, dtype=torch.int64, device=dev)
+    ids = torch.empty(n, dtype=torch.int32, device=dev)
+    if n == 0:
+        return Intersections(tiles_per, goff, keys, ids, n)
+    need = lib.gs_isect_workspace_bytes(C, N, n, tile_width, tile_height, int(bool(sort)))
+    if ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check(lib.gs_isect_tiles(_ptr(means2d), _ptr(radii), rpg, _ptr(depths), C, N, tile_size, tile_width,
+                              tile_height, int(bool(sort)), None, _ptr(goff), None, _ptr(keys), _ptr(ids), n,
+                              _ptr(ws), ws.numel(), s))
+    return Intersections(tiles_per, goff, keys, ids, n)
+
+
+def gs_sort_keys(keys, flatten_ids, end_bit=64, stream=None, workspace=None):
+    """Stable in-place sort of (keys, flatten_ids) by bits [0, end_bit) of the keys."""
+    lib = load_library()
+    _req(keys, "keys", torch.int64)
+    _req(flatten_ids, "flatten_ids", torch.int32, keys.device, (keys.numel(),))
+    n = keys.numel()
+    ws = workspace if workspace is not None else _workspace(lib.gs_sort_workspace_bytes(n, end_bit), keys.device)
+    _check(lib.gs_sort_keys(_ptr(keys), _ptr(flatten_ids), n, end_bit, _ptr(ws), ws.numel(), _stream(stream)))
+    return keys, flatten_ids
+
+
+def gs_tile_ranges(sorted_keys, C, tile_width, tile_height, validate=False, out=None, stream=None,
+                   workspace=None):
+    """Per-tile offsets [C, th, tw] int32 of sorted keys (boundary detection)."""
+    lib = load_library()
+    _req(sorted_keys, "sorted_keys", torch.int64)
+    dev = sorted_keys.device
+    if out is None:
+        out = torch.empty((C, tile_height, tile_width), dtype=torch.int32, device=dev)
+    _req(out, "isect_offsets", torch.int32, dev, (C, tile_height, tile_width))
+    ws = workspace if workspace is not None else _workspace(lib.gs_tile_ranges_workspace_bytes(), dev)
+    _check(lib.gs_tile_ranges(_ptr(sorted_keys), sorted_keys.numel(), C, tile_width, tile_height, _ptr(out),
+                              int(bool(validate)), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+@dataclass
+class Render:
+    render_colors: torch.Tensor  # [C, H, W, K]
+    render_alphas: torch.Tensor  # [C, H, W]
+    render_T: torch.Tensor  # [C, H, W]
+    last_ids: torch.Tensor  # [C, H, W] int32
+
+
+def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
+                     flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
+                     transmittance_threshold=1e-4, out=None, stream=None, workspace=None) -> Render:
+    """Front-to-back compositing of every tile; returns colours, 1 - T, T and the last composited index."""
+    lib = load_library()
+    dev = means2d.device
+    _req(means2d, "means2d", torch.float32, dev)
+    C, N = means2d.shape[0], means2d.shape[1]
+    _req(conics, "conics", torch.float32, dev, (C, N, 3))
+    _req(colors, "colors", torch.float32, dev)
+    if colors.dim() != 3 or tuple(colors.shape[:2]) != (C, N):
+        raise ValueError("colors must be [C, N, K]")
+    K = colors.shape[2]
+    _req(opacities, "opacities", torch.float32, dev, (C, N))
+    if backgrounds is not None:
+        _req(backgrounds, "backgrounds", torch.float32, dev, (C, K))
+    _req(isect_offsets, "isect_offsets", torch.int32, dev)
+    th, tw = isect_offsets.shape[1], isect_offsets.shape[2]
+    _req(flatten_ids, "flatten_ids", torch.int32, dev)
+    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    if out is None:
+        out = Render(torch.empty((C, height, width, K), dtype=torch.float32, device=dev),
+                     torch.empty((C, height, width), dtype=torch.float32, device=dev),
+                     torch.empty((C, height, width), dtype=torch.float32, device=dev),
+                     torch.empty((C, height, width), dtype=torch.int32, device=dev))
+    ws = workspace if workspace is not None else _workspace(lib.gs_rasterize_workspace_bytes(C, tw, th), dev)
+    _check(lib.gs_rasterize_fwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
+                                K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
+                                float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
+                                _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
+                                _ptr(out.last_ids), _ptr(ws), ws.numel(), _stream(stream)))
+    return out

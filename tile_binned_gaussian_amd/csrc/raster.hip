@@ -1,0 +1,238 @@
+// Per-tile front-to-back alpha compositing on gfx950. One workgroup per tile, one pixel per thread (tiles up to
+// 16x16; 4 pixels per thread up to 32x32). The tile's splats are staged in batches through LDS (mean, conic,
+// opacity, colour), every lane reads the same LDS word (a broadcast), and a pixel stops at the transmittance
+// early-out; a workgroup vote ends the tile once every pixel has stopped. No matrix cores: nothing here is a
+// dense contraction.
+//
+// Definitions: the front-to-back inverse of gsplat 1.0.0 raster_backward.c (gs_raster_backward_pixel: pixel
+// centre, delta, quadratic form, alpha clamp, skip test, render alpha = 1 - T; gs_raster_backward_without_gvl:
+// tile walk and range end), with alpha_cutoff and transmittance_threshold from rlx-metal 0.2.9
+// splat_training.rs (training_forward_metal_traced).
+#include "gs_internal.hpp"
+
+namespace gs {
+namespace {
+
+constexpr int kMaxThreads = 256;
+
+// e^-sigma in float32: Cody and Waite's range reduction (k = rint(-sigma / ln 2), r = -sigma - k ln 2 with ln 2
+// split into a 15-bit high part and a low correction, both by fma) and the degree-7 Taylor polynomial of e^r
+// evaluated by fma, scaled by 2^k. sigma > 80 (or NaN) gives 0, which also keeps 2^k a normal scale.
+__device__ __forceinline__ float exp_neg(float sigma) {
+    if (!(sigma <= 80.0f)) return 0.0f;
+    const float t = -sigma;
+    const float k = __builtin_rintf(t * 0x1.715476p+0f);  // 1 / ln 2
+    float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);         // ln 2, high 15 bits
+    r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);             // ln 2 - high part
+    float q = 0x1.a01a02p-13f;                              // 1/7!
+    q = __builtin_fmaf(q, r, 0x1.6c16c2p-10f);              // 1/6!
+    q = __builtin_fmaf(q, r, 0x1.111112p-7f);               // 1/5!
+    q = __builtin_fmaf(q, r, 0x1.555556p-5f);               // 1/4!
+    q = __builtin_fmaf(q, r, 0x1.555556p-3f);               // 1/3!
+    q = __builtin_fmaf(q, r, 0.5f);
+    q = __builtin_fmaf(q, r, 1.0f);
+    q = __builtin_fmaf(q, r, 1.0f);
+    return __builtin_ldexpf(q, static_cast<int>(k));
+}
+
+struct RasterArgs {
+    const float2 *means;
+    const float *conics;
+    const float *colors;
+    const float *opacities;
+    const float *backgrounds;
+    const int32_t *offsets;
+    const int32_t *ids;
+    const int32_t *tile_order;  // nullable: launch order of tiles
+    int64_t n_isects;
+    int total_tiles, width, height, tile_size, tile_width, tile_height;
+    float alpha_cutoff, alpha_clamp, transmittance_threshold;
+    float *out_colors, *out_alphas, *out_T;
+    int32_t *out_last;
+};
+
+template <int K, int PPT>
+__global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
+    __shared__ float2 s_xy[kMaxThreads];
+    __shared__ float4 s_abco[kMaxThreads];
+    __shared__ float s_rgb[kMaxThreads * K];
+
+    const int tile = a.tile_order ? a.tile_order[blockIdx.x] : static_cast<int>(blockIdx.x);
+    const int per_camera = a.tile_width * a.tile_height;
+    const int camera = tile / per_camera;
+    const int local = tile - camera * per_camera;
+    const int ty = local / a.tile_width;
+    const int tx = local - ty * a.tile_width;
+    const int start = a.offsets[tile];
+    const int end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects);
+    const int ts = a.tile_size;
+    const int nthreads = blockDim.x;
+
+    float px[PPT], py[PPT], T[PPT], acc[PPT][K];
+    int last[PPT], xs[PPT], ys[PPT];
+    bool done[PPT];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+        const int pix = threadIdx.x + q * nthreads;
+        const int lx = pix % ts, ly = pix / ts;
+        xs[q] = tx * ts + lx;
+        ys[q] = ty * ts + ly;
+        done[q] = !(pix < ts * ts && xs[q] < a.width && ys[q] < a.height);
+        px[q] = static_cast<float>(xs[q]) + 0.5f;
+        py[q] = static_cast<float>(ys[q]) + 0.5f;
+        T[q] = 1.0f;
+        last[q] = -1;
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc[q][k] = 0.0f;
+    }
+
+    for (int base = start; base < end; base += nthreads) {
+        bool mine_done = true;
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) mine_done = mine_done && done[q];
+        if (__syncthreads_and(mine_done)) break;  // also orders the previous batch's LDS reads before refilling
+        const int idx = base + static_cast<int>(threadIdx.x);
+        if (idx < end) {
+            const int g = a.ids[idx];
+            s_xy[threadIdx.x] = a.means[g];
+            const float *cg = a.conics + 3 * static_cast<int64_t>(g);
+            s_abco[threadIdx.x] = make_float4(cg[0], cg[1], cg[2], a.opacities[g]);
+#pragma unroll
+            for (int k = 0; k < K; ++k) s_rgb[threadIdx.x * K + k] = a.colors[static_cast<int64_t>(g) * K + k];
+        }
+        __syncthreads();
+        const int count = end - base < nthreads ? end - base : nthreads;
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            if (done[q]) continue;
+            for (int j = 0; j < count; ++j) {
+                const float2 m = s_xy[j];
+                const float4 c = s_abco[j];
+                const float dx = m.x - px[q];
+                const float dy = m.y - py[q];
+                const float sigma = 0.5f * (c.x * dx * dx + c.z * dy * dy) + c.y * dx * dy;
+                if (sigma < 0.0f) continue;
+                float alpha = c.w * exp_neg(sigma);
+                if (alpha > a.alpha_clamp) alpha = a.alpha_clamp;
+                if (alpha < a.alpha_cutoff) continue;
+                const float t_next = T[q] * (1.0f - alpha);
+                if (t_next <= a.transmittance_threshold) {
+                    done[q] = true;
+                    break;
+                }
+                const float v = alpha * T[q];
+#pragma unroll
+                for (int k = 0; k < K; ++k) acc[q][k] = acc[q][k] + s_rgb[j * K + k] * v;
+                T[q] = t_next;
+                last[q] = base + j;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+        const int pix = threadIdx.x + q * nthreads;
+        if (!(pix < ts * ts && xs[q] < a.width && ys[q] < a.height)) continue;
+        const int64_t p = (static_cast<int64_t>(camera) * a.height + ys[q]) * a.width + xs[q];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float bg = a.backgrounds ? a.backgrounds[camera * K + k] : 0.0f;
+            a.out_colors[p * K + k] = acc[q][k] + T[q] * bg;
+        }
+        a.out_alphas[p] = 1.0f - T[q];
+        if (a.out_T) a.out_T[p] = T[q];
+        if (a.out_last) a.out_last[p] = last[q];
+    }
+}
+
+template <int K>
+gs_status launch_k(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(args.total_tiles)), block(static_cast<unsigned>(threads));
+    if (ppt == 1) hipLaunchKernelGGL((raster_fwd_kernel<K, 1>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4>), grid, block, 0, stream, args);
+    GS_LAUNCH_TRY("raster_fwd_kernel");
+    return ok();
+}
+
+}  // namespace
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" size_t gs_rasterize_workspace_bytes(int64_t C, int tile_width, int tile_height) {
+    if (C < 1 || tile_width < 1 || tile_height < 1) return 0;
+    return align_up(static_cast<size_t>(C) * tile_width * tile_height * sizeof(int32_t), 256);
+}
+
+extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
+                                      const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
+                                      int width, int height, int tile_size, int tile_width, int tile_height,
+                                      const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
+                                      float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                                      float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
+                                      void *workspace, size_t workspace_bytes, void *stream_handle) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+    if (C < 1 || N < 0 || C * N >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: need C >= 1, N >= 0 and C*N < 2^31");
+    if (K < 1 || K > 4) return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: K = %d channels outside [1, 4]", K);
+    if (width < 1 || height < 1 || tile_size < 1 || tile_size > 32)
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: need width, height >= 1 and 1 <= tile_size <= 32");
+    if (tile_width != (width + tile_size - 1) / tile_size || tile_height != (height + tile_size - 1) / tile_size)
+        return fail(GS_ERR_INVALID_ARG,
+                    "gs_rasterize_fwd: tile grid %dx%d does not match ceil(%d/%d) x ceil(%d/%d)", tile_width,
+                    tile_height, width, tile_size, height, tile_size);
+    const int64_t total_tiles = C * tile_width * tile_height;
+    if (total_tiles >= (int64_t(1) << 31) || C * height * width * K >= (int64_t(1) << 40))
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: image batch too large");
+    if (n_isects < 0 || n_isects >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: n_isects = %lld outside [0, 2^31)", (long long)n_isects);
+    if (!isect_offsets || !render_colors || !render_alphas || (n_isects > 0 && !flatten_ids) ||
+        (N > 0 && (!means2d || !conics || !colors || !opacities)))
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: a required pointer is NULL");
+    if (!(alpha_cutoff >= 0.0f) || !(alpha_clamp > 0.0f) || !(transmittance_threshold >= 0.0f))
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: alpha_cutoff >= 0, alpha_clamp > 0 and "
+                                        "transmittance_threshold >= 0 are required");
+    const size_t need = gs_rasterize_workspace_bytes(C, tile_width, tile_height);
+    if (workspace_bytes > 0 && workspace_bytes < need)
+        return fail(GS_ERR_WORKSPACE, "gs_rasterize_fwd: needs %zu workspace bytes (got %zu)", need, workspace_bytes);
+
+    RasterArgs args{};
+    args.means = reinterpret_cast<const float2 *>(means2d);
+    args.conics = conics;
+    args.colors = colors;
+    args.opacities = opacities;
+    args.backgrounds = backgrounds;
+    args.offsets = isect_offsets;
+    args.ids = flatten_ids;
+    args.tile_order = nullptr;
+    args.n_isects = n_isects;
+    args.total_tiles = static_cast<int>(total_tiles);
+    args.width = width;
+    args.height = height;
+    args.tile_size = tile_size;
+    args.tile_width = tile_width;
+    args.tile_height = tile_height;
+    args.alpha_cutoff = alpha_cutoff;
+    args.alpha_clamp = alpha_clamp;
+    args.transmittance_threshold = transmittance_threshold;
+    args.out_colors = render_colors;
+    args.out_alphas = render_alphas;
+    args.out_T = render_T;
+    args.out_last = last_ids;
+
+    const int pixels = tile_size * tile_size;
+    int threads, ppt;
+    if (pixels <= kMaxThreads) {
+        threads = (pixels + kWave - 1) / kWave * kWave;
+        ppt = 1;
+    } else {
+        threads = kMaxThreads;
+        ppt = 4;
+    }
+    switch (K) {
+        case 1: return launch_k<1>(args, threads, ppt, stream);
+        case 2: return launch_k<2>(args, threads, ppt, stream);
+        case 3: return launch_k<3>(args, threads, ppt, stream);
+        default: return launch_k<4>(args, threads, ppt, stream);
+    }
+}
