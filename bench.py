@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of one frame of the tile-binned splat rasterizer on one MI355X.
+
+A step is the whole hot path on one batch of synthetic input already resident in HBM: intersection count (one
+8-byte readback for the size), key emission, stable key sort, tile ranges and compositing. The default workload is
+the 1M-splat 1920x1080 frame (64-component clustered mixture, tile 16). Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config config3] [--no-cpu-baseline]
+
+Only one GPU is supported: --gpus above 1 (or a multi-rank launch) exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "isect keys sorted/s; rasterized Mpix/s (1M splats, 1920x1080, 1 GPU)"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+# non-packed FP32 VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T lane-operations per second
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# lane-operations per evaluation of the composite's definition:
+#   every evaluation: 2 (delta) + 9 (quadratic form) + 1 (sign test) + 14 (exponential incl. the >80 test)
+#                     + 1 (opacity product) + 1 (clamp) + 1 (cutoff test) = 29
+#   alpha >= cutoff:  1 (1 - alpha) + 1 (T product) + 1 (threshold test) = 3
+#   composited:       1 (alpha T) + 2 K (colour multiply-add, unfused) = 7 for K = 3
+OPS_EVAL, OPS_PASS = 29, 3
+
+WORKLOADS = {
+    "tiny": "tiny: 1 camera, 256 splats, 64x64, tile 16",
+    "config2": "1 camera, 200k splats (uniform, elliptical radii), 800x800, tile 16",
+    "config3": "1 camera, 1M splats (64-component clustered mixture), 1920x1080 (120x68 tiles), tile 16",
+    "config4": "4 cameras x 3M splats (per-camera mixtures, 1% radius 0), 1600x1064, tile 16",
+    "config5": "1 camera, 6M splats (uniform, r median 6 px, 10% duplicate depths, half opacity < 1/255), "
+               "3840x2160, tile 16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="config3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tile-stride", type=int, default=4,
+                    help="CPU baseline composites every k-th tile (then scales to the frame)")
+    return ap.parse_args()
+
+
+def stage_bytes(scene, n, passes):
+    """Algorithmic HBM bytes per stage (what each step must read and write at least once)."""
+    M = scene.C * scene.N
+    rb = 8 if scene.radii.ndim == 3 else 4
+    pixels = scene.C * scene.width * scene.height
+    K = scene.colors.shape[-1]
+    return {
+        "count": M * (8 + rb + 4 + 4),  # means, radii -> tiles_per_gauss, gauss_offsets
+        "emit": M * (8 + rb + 4 + 4) + n * 12,  # means, radii, depth, offset -> key + id
+        "sort": n * 8 + passes * n * 24,  # histogram read, then read+write of key and id per pass
+        "ranges": n * 8 + scene.C * scene.tile_width * scene.tile_height * 4,
+        "composite": n * (4 + 8 + 12 + 4 + 4 * K) + pixels * (4 * K + 4 + 4 + 4),
+    }
+
+
+def cpu_baseline(scene, stride):
+    """The oracle as it stands (single thread): intersections, sort and offsets on the whole frame, the composite
+    on every stride-th tile, scaled to the frame."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    it = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                            scene.tile_height, sort=True)
+    off = oracle.tile_offsets(it.keys, scene.C, scene.tile_width, scene.tile_height)
+    t1 = time.perf_counter()
+    tiles = np.arange(0, off.size, stride, dtype=np.int64)
+    ras = oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
+                               scene.width, scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects,
+                               scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold, tiles=tiles)
+    t2 = time.perf_counter()
+    frame_s = (t1 - t0) + (t2 - t1) * off.size / tiles.size
+    pixels = scene.C * scene.width * scene.height
+    return {
+        "value": pixels / frame_s / 1e6, "unit": "Mpix/s", "cores": 1, "kind": "oracle",
+        "sample": f"whole frame for intersections+sort+offsets ({t1 - t0:.2f} s), composite on every {stride}-th "
+                  f"tile ({tiles.size} of {off.size}, {t2 - t1:.2f} s) scaled to all tiles; single thread",
+        "frame_s_estimate": round(frame_s, 3), "isect_sort_offsets_s": round(t1 - t0, 3),
+        "keys_sorted_per_s": it.n_isects / (t1 - t0),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the frame is "
+              f"not sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tile_binned_gaussian_amd import frame, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    scene = synth.CONFIGS[args.config]()
+    ds = frame.to_device(scene, "cuda:0")
+    plan = frame.FramePlan(ds)
+
+    # untimed: count the work the composite's definition implies on this frame
+    counts = torch.zeros(3, dtype=torch.int64, device="cuda:0")
+    plan.run(eval_counts=counts)
+    torch.cuda.synchronize()
+    n_eval, n_pass, n_comp = (int(v) for v in counts.cpu())
+
+    for _ in range(args.warmup):
+        plan.run()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        plan.run(events=events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = plan.n_isects
+
+    names = ["count", "emit", "sort", "ranges", "composite"]
+    stage_ms = {nm: statistics.median(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
+                for i, nm in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    pixels = scene.C * scene.width * scene.height
+    passes = (plan.end_bit + 7) // 8
+    nbytes = stage_bytes(scene, n, passes)
+    K = scene.colors.shape[-1]
+    ops = OPS_EVAL * n_eval + OPS_PASS * n_pass + (1 + 2 * K) * n_comp
+    stages = {}
+    for nm in names:
+        gbs = nbytes[nm] / (stage_ms[nm] * 1e-3) / 1e9
+        stages[nm] = {"ms": round(stage_ms[nm], 4), "bytes": nbytes[nm], "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    comp_tops = ops / (stage_ms["composite"] * 1e-3) / 1e12
+    stages["composite"].update({"lane_ops": ops, "Tops/s": round(comp_tops, 3),
+                                "valu_frac": round(comp_tops / PEAK_VALU_TOPS, 4)})
+    dominant = max(names, key=lambda nm: stage_ms[nm])
+    if dominant == "composite":
+        roofline = {"bound": "alu", "kernel": "raster_fwd_kernel", "achieved": round(comp_tops, 3),
+                    "peak": round(PEAK_VALU_TOPS, 2), "unit": "Tops/s (FP32 VALU lane-ops)",
+                    "frac": round(comp_tops / PEAK_VALU_TOPS, 4), "traffic": None}
+    else:
+        gbs = nbytes[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": round(pixels / (ms_per_step * 1e-3) / 1e6, 2),
+        "unit": "Mpix/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config, "cameras": scene.C, "splats": scene.N,
+                   "width": scene.width, "height": scene.height, "tile_size": scene.tile_size,
+                   "n_isects": n, "sort_end_bit": plan.end_bit, "sort_passes": passes},
+        "isect_keys_sorted_per_s": round(n / (stage_ms["sort"] * 1e-3), 1),
+        "isect_keys_sorted_per_s_frame": round(n / (ms_per_step * 1e-3), 1),
+        "rasterized_mpix_per_s_composite_only": round(pixels / (stage_ms["composite"] * 1e-3) / 1e6, 2),
+        "composite_work": {"evaluations": n_eval, "alpha_ge_cutoff": n_pass, "composited": n_comp},
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(scene, args.cpu_tile_stride)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,6 +137,10 @@ gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int64_t C, int 
  * render_alphas [C, H, W] = 1 - T, render_T [C, H, W] = T (nullable), last_ids [C, H, W] = last (nullable;
  * a global intersection index, -1 if nothing composited).
  * conics [C, N, 3] = (inv00, inv01, inv11) of the 2D covariance; colors [C, N, K]; opacities [C, N].
+ * eval_counts: nullable device uint64[3]; when set, the launch ADDS the work the definition implies: [0] every
+ * evaluation of sigma (per pixel, each splat of its range up to and including the one that stops it), [1] the
+ * evaluations with alpha >= alpha_cutoff, [2] the splats composited. The counting variant is a separate kernel
+ * build; with NULL nothing is counted.
  * Limits: 1 <= K <= 4; 1 <= tile_size <= 32; tile_width == ceil(width / tile_size) and
  *   tile_height == ceil(height / tile_size); flatten_ids must index [0, C*N) (not checked on the device).
  * workspace: gs_rasterize_workspace_bytes(C, tile_width, tile_height) bytes (tile scheduling order).
@@ -148,8 +152,8 @@ gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const floa
                            int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
                            const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
                            float transmittance_threshold, float *render_colors, float *render_alphas,
-                           float *render_T, int32_t *last_ids, void *workspace, size_t workspace_bytes,
-                           void *stream);
+                           float *render_T, int32_t *last_ids, uint64_t *eval_counts, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -46,6 +46,15 @@ def gpu_frame(scene):
     return fr
 
 
+def last_splat(last, ids):
+    """Splat named by each last-composited index (-1 where nothing was composited)."""
+    last = np.asarray(last, np.int64)
+    if ids.size == 0:
+        assert (last == -1).all()
+        return last
+    return np.where(last >= 0, ids[np.maximum(last, 0)], -1)
+
+
 def assert_raster_equal(scene, fr_gpu, ras_orc, orc_ids):
     """Bit-exact colours, alphas and T; last ids compared as the splat they name."""
     np.testing.assert_array_equal(host(fr_gpu.render.render_colors), ras_orc.render_colors)
@@ -54,8 +63,7 @@ def assert_raster_equal(scene, fr_gpu, ras_orc, orc_ids):
     g_last = host(fr_gpu.render.last_ids).astype(np.int64)
     o_last = ras_orc.last_ids.astype(np.int64)
     g_ids = host(fr_gpu.isect.flatten_ids)
-    np.testing.assert_array_equal(np.where(g_last >= 0, g_ids[np.maximum(g_last, 0)], -1),
-                                  np.where(o_last >= 0, orc_ids[np.maximum(o_last, 0)], -1))
+    np.testing.assert_array_equal(last_splat(g_last, g_ids), last_splat(o_last, orc_ids))
     # within tolerance too (the bar stated for colour and transmittance)
     np.testing.assert_allclose(host(fr_gpu.render.render_colors), ras_orc.render_colors, atol=1e-4, rtol=0)
 
@@ -96,7 +104,5 @@ def check_tiles_against_oracle(scene, fr_gpu, tiles):
         np.testing.assert_array_equal(T_g[cam, y0:y1, x0:x1], oT[: y1 - y0, : x1 - x0], err_msg=f"tile {t}")
         gl = last_g[cam, y0:y1, x0:x1].astype(np.int64)
         olp = ol[: y1 - y0, : x1 - x0]
-        np.testing.assert_array_equal(np.where(gl >= 0, ids_g[np.maximum(gl, 0)], -1),
-                                      np.where(olp >= 0, lst[np.maximum(olp, 0)] if lst.size else -1, -1),
-                                      err_msg=f"tile {t} last ids")
+        np.testing.assert_array_equal(last_splat(gl, ids_g), last_splat(olp, lst), err_msg=f"tile {t} last ids")
         assert ((gl == -1) | ((gl >= s) & (gl < e))).all()

@@ -106,7 +106,7 @@ def test_rasterize_argument_errors(lib):
 
     def call(C=1, N=4, K=3, W=64, H=64, ts=16, tw=4, th=4, n=10, cut=1 / 255, clamp=0.99, thr=1e-4, ptr=fake):
         return lib.gs_rasterize_fwd(ptr, ptr, ptr, ptr, None, C, N, K, W, H, ts, tw, th, ptr, ptr, n, F(cut),
-                                    F(clamp), F(thr), ptr, ptr, None, None, None, 0, None)
+                                    F(clamp), F(thr), ptr, ptr, None, None, None, None, 0, None)
     assert call(K=0) == GS_ERR_INVALID_ARG
     assert call(K=5) == GS_ERR_INVALID_ARG
     assert call(ts=33, tw=2, th=2) == GS_ERR_INVALID_ARG

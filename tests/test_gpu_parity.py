@@ -141,3 +141,23 @@ def test_ranges_validation_errors():
     # without validation the same input is accepted and the writes stay inside the offsets array
     binding.gs_tile_ranges(dev(bad.view(np.int64)), 1, tw, th, validate=False)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["tiny", "dense-early-out", "ts32-ppt4", "multicam-ragged-elliptical", "K1"])
+def test_eval_counter_matches_oracle(name):
+    # the composite's optional work counter: evaluations per pixel up to and including the stopping splat
+    scene = SCENES[name]()
+    it_o, off_o, ras_o = oracle.scene_pipeline(scene)
+    from tile_binned_gaussian_amd import frame
+    ds = frame.to_device(scene)
+    it = binding.gs_isect_tiles(ds.means2d, ds.radii, ds.depths, ds.tile_size, ds.tile_width, ds.tile_height)
+    off = binding.gs_tile_ranges(it.isect_ids, ds.C, ds.tile_width, ds.tile_height)
+    counts = torch.zeros(3, dtype=torch.int64, device="cuda")
+    ren = binding.gs_rasterize_fwd(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, ds.width,
+                                   ds.height, ds.tile_size, off, it.flatten_ids, it.n_isects, eval_counts=counts)
+    c = host(counts)
+    assert c[0] == ras_o.n_eval
+    assert c[0] >= c[1] >= c[2]
+    # every pixel with a last id composited at least one splat
+    assert c[2] >= int((host(ren.last_ids) >= 0).sum())
+    np.testing.assert_array_equal(host(ren.render_T), ras_o.render_T)

@@ -54,7 +54,7 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_workspace_bytes.argtypes = [I64, I32, I32]
     lib.gs_rasterize_workspace_bytes.restype = SZ
     lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F, F,
-                                     P, P, P, P, P, SZ, P]
+                                     P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd.restype = I32
     _lib = lib
     return lib
@@ -180,8 +180,10 @@ class Render:
 
 def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
-                     transmittance_threshold=1e-4, out=None, stream=None, workspace=None) -> Render:
-    """Front-to-back compositing of every tile; returns colours, 1 - T, T and the last composited index."""
+                     transmittance_threshold=1e-4, out=None, stream=None, workspace=None, eval_counts=None) -> Render:
+    """Front-to-back compositing of every tile; returns colours, 1 - T, T and the last composited index.
+
+    eval_counts: optional int64 [3] device tensor that the launch adds (evaluations, alpha >= cutoff, composited)."""
     lib = load_library()
     dev = means2d.device
     _req(means2d, "means2d", torch.float32, dev)
@@ -208,5 +210,5 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
                                 K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
                                 float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
                                 _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
-                                _ptr(out.last_ids), _ptr(ws), ws.numel(), _stream(stream)))
+                                _ptr(out.last_ids), _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
     return out

@@ -49,9 +49,10 @@ struct RasterArgs {
     float alpha_cutoff, alpha_clamp, transmittance_threshold;
     float *out_colors, *out_alphas, *out_T;
     int32_t *out_last;
+    unsigned long long *eval_counts;  // nullable: [evaluations, alpha >= cutoff, composited]
 };
 
-template <int K, int PPT>
+template <int K, int PPT, bool COUNT>
 __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float2 s_xy[kMaxThreads];
     __shared__ float4 s_abco[kMaxThreads];
@@ -69,8 +70,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     const int nthreads = blockDim.x;
 
     float px[PPT], py[PPT], T[PPT], acc[PPT][K];
-    int last[PPT], xs[PPT], ys[PPT];
+    int last[PPT], xs[PPT], ys[PPT], stop[PPT];
     bool done[PPT];
+    unsigned long long n_pass = 0, n_comp = 0;
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const int pix = threadIdx.x + q * nthreads;
@@ -82,6 +84,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         py[q] = static_cast<float>(ys[q]) + 0.5f;
         T[q] = 1.0f;
         last[q] = -1;
+        stop[q] = end;
 #pragma unroll
         for (int k = 0; k < K; ++k) acc[q][k] = 0.0f;
     }
@@ -115,11 +118,14 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
                 float alpha = c.w * exp_neg(sigma);
                 if (alpha > a.alpha_clamp) alpha = a.alpha_clamp;
                 if (alpha < a.alpha_cutoff) continue;
+                if (COUNT) ++n_pass;
                 const float t_next = T[q] * (1.0f - alpha);
                 if (t_next <= a.transmittance_threshold) {
                     done[q] = true;
+                    if (COUNT) stop[q] = base + j + 1;
                     break;
                 }
+                if (COUNT) ++n_comp;
                 const float v = alpha * T[q];
 #pragma unroll
                 for (int k = 0; k < K; ++k) acc[q][k] = acc[q][k] + s_rgb[j * K + k] * v;
@@ -143,15 +149,34 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         if (a.out_T) a.out_T[p] = T[q];
         if (a.out_last) a.out_last[p] = last[q];
     }
+    if (COUNT) {
+        // evaluations under the definition: every splat of the range up to and including the one that stops
+        // the pixel (the whole range otherwise), for each pixel inside the image
+        unsigned long long n_eval = 0;
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            const int pix = threadIdx.x + q * nthreads;
+            if (pix < ts * ts && xs[q] < a.width && ys[q] < a.height) n_eval += static_cast<unsigned>(stop[q] - start);
+        }
+        atomicAdd(&a.eval_counts[0], n_eval);
+        atomicAdd(&a.eval_counts[1], n_pass);
+        atomicAdd(&a.eval_counts[2], n_comp);
+    }
+}
+
+template <int K, bool COUNT>
+gs_status launch_kc(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(args.total_tiles)), block(static_cast<unsigned>(threads));
+    if (ppt == 1) hipLaunchKernelGGL((raster_fwd_kernel<K, 1, COUNT>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4, COUNT>), grid, block, 0, stream, args);
+    GS_LAUNCH_TRY("raster_fwd_kernel");
+    return ok();
 }
 
 template <int K>
 gs_status launch_k(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(args.total_tiles)), block(static_cast<unsigned>(threads));
-    if (ppt == 1) hipLaunchKernelGGL((raster_fwd_kernel<K, 1>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4>), grid, block, 0, stream, args);
-    GS_LAUNCH_TRY("raster_fwd_kernel");
-    return ok();
+    return args.eval_counts ? launch_kc<K, true>(args, threads, ppt, stream)
+                            : launch_kc<K, false>(args, threads, ppt, stream);
 }
 
 }  // namespace
@@ -170,7 +195,8 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
                                       const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
                                       float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
                                       float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
-                                      void *workspace, size_t workspace_bytes, void *stream_handle) {
+                                      uint64_t *eval_counts, void *workspace, size_t workspace_bytes,
+                                      void *stream_handle) {
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
     if (C < 1 || N < 0 || C * N >= (int64_t(1) << 31))
         return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: need C >= 1, N >= 0 and C*N < 2^31");
@@ -219,6 +245,7 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
     args.out_alphas = render_alphas;
     args.out_T = render_T;
     args.out_last = last_ids;
+    args.eval_counts = reinterpret_cast<unsigned long long *>(eval_counts);
 
     const int pixels = tile_size * tile_size;
     int threads, ppt;

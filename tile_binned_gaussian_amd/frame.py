@@ -4,6 +4,7 @@ Marshalling only: intersections (count, emit and sort), tile ranges, then compos
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 
 import torch
@@ -58,3 +59,96 @@ def render_frame(ds: DeviceScene, stream=None) -> FrameResult:
                                    ds.height, ds.tile_size, off, it.flatten_ids, it.n_isects, ds.alpha_cutoff,
                                    ds.alpha_clamp, ds.transmittance_threshold, stream=stream)
     return FrameResult(it, off, ren)
+
+
+class FramePlan:
+    """Preallocated buffers for repeated frames of one scene, so that a timed loop allocates nothing.
+
+    run() issues: count (one synchronisation for the intersection count), emit, sort, tile ranges, composite, with
+    optional torch events recorded between the steps on the same stream."""
+
+    def __init__(self, ds: DeviceScene, stream=None):
+        self.ds = ds
+        self.lib = binding.load_library()
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        dev = ds.means2d.device
+        C, N = ds.C, ds.N
+        self.rpg = 2 if ds.radii.dim() == 3 else 1
+        self.tile_bits = _bits_for(ds.tile_width * ds.tile_height)
+        self.end_bit = 32 + self.tile_bits + _bits_for(C)
+        self.tiles_per = torch.empty((C, N), dtype=torch.int32, device=dev)
+        self.goff = torch.empty(C * N, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty((C, ds.tile_height, ds.tile_width), dtype=torch.int32, device=dev)
+        K = ds.colors.shape[2]
+        self.render = binding.Render(torch.empty((C, ds.height, ds.width, K), dtype=torch.float32, device=dev),
+                                     torch.empty((C, ds.height, ds.width), dtype=torch.float32, device=dev),
+                                     torch.empty((C, ds.height, ds.width), dtype=torch.float32, device=dev),
+                                     torch.empty((C, ds.height, ds.width), dtype=torch.int32, device=dev))
+        self.ws_count = torch.empty(max(self.lib.gs_isect_workspace_bytes(C, N, 0, ds.tile_width, ds.tile_height, 0),
+                                        1), dtype=torch.uint8, device=dev)
+        self.ws_ranges = torch.empty(self.lib.gs_tile_ranges_workspace_bytes(), dtype=torch.uint8, device=dev)
+        self.ws_raster = torch.empty(max(self.lib.gs_rasterize_workspace_bytes(C, ds.tile_width, ds.tile_height), 1),
+                                     dtype=torch.uint8, device=dev)
+        self.capacity = -1
+        self.n_isects = 0
+
+    def _ensure(self, n):
+        if n <= self.capacity:
+            return
+        dev = self.ds.means2d.device
+        self.keys = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+        self.ids = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+        self.ws_sort = torch.empty(max(self.lib.gs_sort_workspace_bytes(n, self.end_bit), 1), dtype=torch.uint8,
+                                   device=dev)
+        self.ws_emit = torch.empty(max(self.lib.gs_isect_workspace_bytes(self.ds.C, self.ds.N, n, self.ds.tile_width,
+                                                                         self.ds.tile_height, 0), 1),
+                                   dtype=torch.uint8, device=dev)
+        self.capacity = n
+
+    def run(self, events=None, eval_counts=None):
+        """One frame. events: optional list of 6 torch.cuda.Event recorded before count, emit, sort, ranges,
+        composite and after the composite."""
+        ds, lib, P = self.ds, self.lib, binding._ptr
+        s = binding._stream(self.stream)
+        ev = events or [None] * 6
+        n_out = ctypes.c_int64(0)
+        rec = lambda i: ev[i] is not None and ev[i].record(self.stream)  # noqa: E731
+        rec(0)
+        binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
+                                          ds.tile_size, ds.tile_width, ds.tile_height, 0, P(self.tiles_per),
+                                          P(self.goff), ctypes.byref(n_out), None, None, 0, P(self.ws_count),
+                                          self.ws_count.numel(), s))
+        n = int(n_out.value)
+        self._ensure(n)
+        self.n_isects = n
+        rec(1)
+        if n > 0:
+            binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
+                                              ds.tile_size, ds.tile_width, ds.tile_height, 0, None, P(self.goff),
+                                              None, P(self.keys), P(self.ids), n, P(self.ws_emit),
+                                              self.ws_emit.numel(), s))
+        rec(2)
+        binding._check(lib.gs_sort_keys(P(self.keys), P(self.ids), n, self.end_bit, P(self.ws_sort),
+                                        self.ws_sort.numel(), s))
+        rec(3)
+        binding._check(lib.gs_tile_ranges(P(self.keys), n, ds.C, ds.tile_width, ds.tile_height, P(self.offsets), 0,
+                                          P(self.ws_ranges), self.ws_ranges.numel(), s))
+        rec(4)
+        r = self.render
+        binding._check(lib.gs_rasterize_fwd(P(ds.means2d), P(ds.conics), P(ds.colors), P(ds.opacities),
+                                            P(ds.backgrounds), ds.C, ds.N, ds.colors.shape[2], ds.width, ds.height,
+                                            ds.tile_size, ds.tile_width, ds.tile_height, P(self.offsets),
+                                            P(self.ids), n, ctypes.c_float(ds.alpha_cutoff),
+                                            ctypes.c_float(ds.alpha_clamp),
+                                            ctypes.c_float(ds.transmittance_threshold), P(r.render_colors),
+                                            P(r.render_alphas), P(r.render_T), P(r.last_ids), P(eval_counts),
+                                            P(self.ws_raster), self.ws_raster.numel(), s))
+        rec(5)
+        return n
+
+
+def _bits_for(count: int) -> int:
+    bits = 0
+    while (1 << bits) < count:
+        bits += 1
+    return bits

@@ -88,9 +88,9 @@ def _pack(name, C, N, W, H, ts, means, radii, depths, conics, colors, opac, note
         radii=_f32(radii).reshape((C, N, 2) if elliptical else (C, N)),
         depths=_f32(depths).reshape(C, N),
         conics=_f32(conics).reshape(C, N, 3),
-        colors=_f32(colors).reshape(C, N, -1),
+        colors=_f32(colors).reshape(C, N, np.shape(colors)[-1]),
         opacities=_f32(opac).reshape(C, N),
-        backgrounds=None if bg is None else _f32(bg).reshape(C, -1),
+        backgrounds=None if bg is None else _f32(bg).reshape(C, np.shape(bg)[-1]),
         notes=notes or {},
     )
 
