@@ -55,7 +55,7 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes(scene, n, passes):
+def stage_bytes(scene, n, tile_passes, generic_passes):
     """Algorithmic HBM bytes per stage (what each step must read and write at least once)."""
     M = scene.C * scene.N
     rb = 8 if scene.radii.ndim == 3 else 4
@@ -63,10 +63,13 @@ def stage_bytes(scene, n, passes):
     K = scene.colors.shape[-1]
     return {
         "count": M * (8 + rb + 4 + 4),  # means, radii -> tiles_per_gauss, gauss_offsets
-        "emit": M * (8 + rb + 4 + 4) + n * 12,  # means, radii, depth, offset -> key + id
-        "sort": n * 8 + passes * n * 24,  # histogram read, then read+write of key and id per pass
+        # depth order of the splats (one 4-byte histogram read, then 4 passes of 4+4 bytes read and written),
+        # splat reads for the ordered counts and the emission, 12 bytes per intersection emitted, then a histogram
+        # read (8 B) and tile_passes passes of 24 B per intersection
+        "emit_sort": M * (4 + 4 * 16) + 2 * M * (8 + rb + 4 + 4) + n * 12 + n * 8 + tile_passes * n * 24,
         "ranges": n * 8 + scene.C * scene.tile_width * scene.tile_height * 4,
         "composite": n * (4 + 8 + 12 + 4 + 4 * K) + pixels * (4 * K + 4 + 4 + 4),
+        "generic_sort": n * 8 + generic_passes * n * 24 + (n * 24 if generic_passes % 2 else 0),
     }
 
 
@@ -115,14 +118,14 @@ def main():
     plan = frame.FramePlan(ds)
 
     # untimed: count the work the composite's definition implies on this frame
-    counts = torch.zeros(3, dtype=torch.int64, device="cuda:0")
+    counts = torch.zeros(5, dtype=torch.int64, device="cuda:0")
     plan.run(eval_counts=counts)
     torch.cuda.synchronize()
-    n_eval, n_pass, n_comp = (int(v) for v in counts.cpu())
+    n_eval, n_pass, n_comp, n_exec, n_staged = (int(v) for v in counts.cpu())
 
     for _ in range(args.warmup):
         plan.run()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -131,26 +134,33 @@ def main():
     wall = time.perf_counter() - t0
     n = plan.n_isects
 
-    names = ["count", "emit", "sort", "ranges", "composite"]
+    names = ["count", "emit_sort", "ranges", "composite"]
     stage_ms = {nm: statistics.median(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
                 for i, nm in enumerate(names)}
     ms_per_step = wall * 1e3 / args.steps
+    # outside the frame: the stand-alone stable sort of the same intersections over all populated key bits
+    stage_ms["generic_sort"], _ = plan.run_generic_sort(max(5, args.steps // 2))
     pixels = scene.C * scene.width * scene.height
-    passes = (plan.end_bit + 7) // 8
-    nbytes = stage_bytes(scene, n, passes)
+    tile_passes = (plan.end_bit - 32 + 7) // 8
+    generic_passes = (plan.end_bit + 7) // 8
+    nbytes = stage_bytes(scene, n, tile_passes, generic_passes)
     K = scene.colors.shape[-1]
-    ops = OPS_EVAL * n_eval + OPS_PASS * n_pass + (1 + 2 * K) * n_comp
+    # the definition's work, and the work the kernel executes (it skips evaluations its exact cull proves idle)
+    ops_def = OPS_EVAL * n_eval + OPS_PASS * n_pass + (1 + 2 * K) * n_comp
+    ops = OPS_EVAL * n_exec + OPS_PASS * n_pass + (1 + 2 * K) * n_comp
     stages = {}
-    for nm in names:
+    for nm in names + ["generic_sort"]:
         gbs = nbytes[nm] / (stage_ms[nm] * 1e-3) / 1e9
         stages[nm] = {"ms": round(stage_ms[nm], 4), "bytes": nbytes[nm], "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     comp_tops = ops / (stage_ms["composite"] * 1e-3) / 1e12
-    stages["composite"].update({"lane_ops": ops, "Tops/s": round(comp_tops, 3),
-                                "valu_frac": round(comp_tops / PEAK_VALU_TOPS, 4)})
+    stages["composite"].update({"lane_ops_executed": ops, "lane_ops_definition": ops_def,
+                                "Tops/s": round(comp_tops, 3), "valu_frac": round(comp_tops / PEAK_VALU_TOPS, 4),
+                                "definition_Tops/s_equivalent": round(ops_def / (stage_ms["composite"] * 1e-3) / 1e12,
+                                                                      3)})
     dominant = max(names, key=lambda nm: stage_ms[nm])
     if dominant == "composite":
-        roofline = {"bound": "alu", "kernel": "raster_fwd_kernel", "achieved": round(comp_tops, 3),
+        roofline = {"bound": "alu", "kernel": "raster_cull_kernel", "achieved": round(comp_tops, 3),
                     "peak": round(PEAK_VALU_TOPS, 2), "unit": "Tops/s (FP32 VALU lane-ops)",
                     "frac": round(comp_tops / PEAK_VALU_TOPS, 4), "traffic": None}
     else:
@@ -173,11 +183,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "cameras": scene.C, "splats": scene.N,
                    "width": scene.width, "height": scene.height, "tile_size": scene.tile_size,
-                   "n_isects": n, "sort_end_bit": plan.end_bit, "sort_passes": passes},
-        "isect_keys_sorted_per_s": round(n / (stage_ms["sort"] * 1e-3), 1),
+                   "n_isects": n, "sort_end_bit": plan.end_bit, "tile_sort_passes": tile_passes,
+                   "generic_sort_passes": generic_passes},
+        "isect_keys_sorted_per_s": round(n / (stage_ms["emit_sort"] * 1e-3), 1),
+        "isect_keys_sorted_per_s_generic_sort": round(n / (stage_ms["generic_sort"] * 1e-3), 1),
         "isect_keys_sorted_per_s_frame": round(n / (ms_per_step * 1e-3), 1),
         "rasterized_mpix_per_s_composite_only": round(pixels / (stage_ms["composite"] * 1e-3) / 1e6, 2),
-        "composite_work": {"evaluations": n_eval, "alpha_ge_cutoff": n_pass, "composited": n_comp},
+        "composite_work": {"evaluations_definition": n_eval, "evaluations_executed": n_exec,
+                           "alpha_ge_cutoff": n_pass, "composited": n_comp, "splats_staged": n_staged},
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": None,

@@ -137,10 +137,12 @@ gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int64_t C, int 
  * render_alphas [C, H, W] = 1 - T, render_T [C, H, W] = T (nullable), last_ids [C, H, W] = last (nullable;
  * a global intersection index, -1 if nothing composited).
  * conics [C, N, 3] = (inv00, inv01, inv11) of the 2D covariance; colors [C, N, K]; opacities [C, N].
- * eval_counts: nullable device uint64[3]; when set, the launch ADDS the work the definition implies: [0] every
- * evaluation of sigma (per pixel, each splat of its range up to and including the one that stops it), [1] the
- * evaluations with alpha >= alpha_cutoff, [2] the splats composited. The counting variant is a separate kernel
- * build; with NULL nothing is counted.
+ * eval_counts: nullable device uint64[5]; when set, the launch ADDS work counts: [0] the evaluations of sigma the
+ * definition makes (per pixel, each splat of its range up to and including the one that stops it), [1] those
+ * with alpha >= alpha_cutoff, [2] the splats composited, [3] the evaluations the kernel actually made (it skips
+ * splats a conservative bound proves to stay below the cutoff over a wave's pixels, which cannot change any
+ * output), [4] the splats staged per tile. The counting variant is a separate kernel build; with NULL nothing is
+ * counted.
  * Limits: 1 <= K <= 4; 1 <= tile_size <= 32; tile_width == ceil(width / tile_size) and
  *   tile_height == ceil(height / tile_size); flatten_ids must index [0, C*N) (not checked on the device).
  * workspace: gs_rasterize_workspace_bytes(C, tile_width, tile_height) bytes (tile scheduling order).

@@ -47,7 +47,31 @@ def _one_isect():
     return s
 
 
+def _cull_edges():
+    # opacities just above the cutoff, strongly anisotropic conics and means on quadrant borders: the cases where a
+    # conservative per-region cull of the composite would be wrong if its margins were
+    rng = np.random.default_rng(44)
+    s = synth.random_scene(44, 1, 1500, 48, 48, 16, r_range=(1.0, 14.0))
+    cut = np.float32(1.0) / np.float32(255.0)
+    n = s.N
+    s.opacities[0] = np.where(rng.uniform(size=n) < 0.5, cut * rng.uniform(1.0, 1.3, n),
+                              rng.uniform(0.5, 1.0, n)).astype(np.float32)
+    s.opacities[0, :20] = cut
+    edges = np.array([7.5, 8.0, 8.5, 15.5, 16.0, 16.5, 23.5, 24.0, 24.5, 31.5, 32.0, 32.5], np.float32)
+    s.means2d[0, : n // 3] = rng.choice(edges, size=(n // 3, 2))
+    l1 = rng.uniform(0.5, 40.0, n)
+    l2 = l1 / rng.uniform(1.0, 250.0, n)
+    th = rng.uniform(0, np.pi, n)
+    cs, sn = np.cos(th), np.sin(th)
+    sxx, syy, sxy = l1 * cs * cs + l2 * sn * sn, l1 * sn * sn + l2 * cs * cs, (l1 - l2) * cs * sn
+    det = l1 * l2
+    s.conics[0] = np.stack([syy / det, -sxy / det, sxx / det], -1).astype(np.float32)
+    s.radii[0] = (3.0 * np.sqrt(l1)).astype(np.float32)
+    return s
+
+
 SCENES = {
+    "cull-edges": _cull_edges,
     "tiny": lambda: synth.tiny(),
     "tiny-aniso": lambda: synth.tiny(anisotropic=True),
     "multicam-ragged-elliptical": lambda: synth.random_scene(35, 3, 700, 150, 90, 16, elliptical=True,
@@ -143,7 +167,8 @@ def test_ranges_validation_errors():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["tiny", "dense-early-out", "ts32-ppt4", "multicam-ragged-elliptical", "K1"])
+@pytest.mark.parametrize("name", ["tiny", "dense-early-out", "ts32-ppt4", "multicam-ragged-elliptical", "K1",
+                                  "cull-edges", "ts8-margin"])
 def test_eval_counter_matches_oracle(name):
     # the composite's optional work counter: evaluations per pixel up to and including the stopping splat
     scene = SCENES[name]()
@@ -152,12 +177,14 @@ def test_eval_counter_matches_oracle(name):
     ds = frame.to_device(scene)
     it = binding.gs_isect_tiles(ds.means2d, ds.radii, ds.depths, ds.tile_size, ds.tile_width, ds.tile_height)
     off = binding.gs_tile_ranges(it.isect_ids, ds.C, ds.tile_width, ds.tile_height)
-    counts = torch.zeros(3, dtype=torch.int64, device="cuda")
+    counts = torch.zeros(5, dtype=torch.int64, device="cuda")
     ren = binding.gs_rasterize_fwd(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, ds.width,
                                    ds.height, ds.tile_size, off, it.flatten_ids, it.n_isects, eval_counts=counts)
     c = host(counts)
     assert c[0] == ras_o.n_eval
     assert c[0] >= c[1] >= c[2]
+    assert c[0] >= c[3] >= c[1]  # the kernel never evaluates more than the definition, nor skips a contributor
+    assert c[4] <= it.n_isects
     # every pixel with a last id composited at least one splat
     assert c[2] >= int((host(ren.last_ids) >= 0).sum())
     np.testing.assert_array_equal(host(ren.render_T), ras_o.render_T)

@@ -268,3 +268,13 @@ def test_partition_of_unity_and_invariants(orc):
     it, off, ras = orc.scene_pipeline(DENSE())
     assert (ras.render_T > THR).all()
     assert (ras.render_T < 2 * THR).sum() > 100  # the early-out is exercised
+
+
+def test_exp_never_exceeds_one_for_nonnegative_sigma(orc):
+    # alpha = opacity * E(sigma) <= opacity for sigma >= 0: every float in [0, 2^-12] (bit patterns) and a dense
+    # sweep of [0, 2]
+    tiny = np.arange(0, np.array(2.0 ** -12, np.float32).view(np.int32) + 1, 97, dtype=np.int64)
+    e = orc.exp_neg(tiny.astype(np.int32).view(np.float32))
+    assert (e <= 1.0).all()
+    e = orc.exp_neg(np.linspace(0, 2, 3_000_001, dtype=np.float32))
+    assert (e <= 1.0).all()

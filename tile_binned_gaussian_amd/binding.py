@@ -183,7 +183,8 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
                      transmittance_threshold=1e-4, out=None, stream=None, workspace=None, eval_counts=None) -> Render:
     """Front-to-back compositing of every tile; returns colours, 1 - T, T and the last composited index.
 
-    eval_counts: optional int64 [3] device tensor that the launch adds (evaluations, alpha >= cutoff, composited)."""
+    eval_counts: optional int64 [5] device tensor that the launch adds to (evaluations by the definition, alpha >=
+    cutoff, composited, evaluations executed, splats staged)."""
     lib = load_library()
     dev = means2d.device
     _req(means2d, "means2d", torch.float32, dev)

@@ -1,0 +1,35 @@
+// Internal interface of the onesweep radix sort (sort.hip), shared with the intersection step.
+#pragma once
+
+#include "gs_internal.hpp"
+
+namespace gs {
+
+constexpr int kMaxPasses = 8;
+
+// Digit passes over bits [begin_bit, end_bit): pass p sorts `bits[p]` bits starting at `shift[p]`.
+struct PassPlan {
+    int passes;
+    int shift[kMaxPasses];
+    int bits[kMaxPasses];
+};
+
+// Splits [begin_bit, end_bit) evenly into ceil(width / 8) passes of at most 8 bits.
+PassPlan make_pass_plan(int begin_bit, int end_bit);
+
+// Per-sort scratch: digit histograms, partition counters and two look-back arrays sized for n pairs.
+struct SortScratchLayout {
+    size_t hist, counters, status0, status1, bytes;
+    int64_t parts;
+};
+SortScratchLayout sort_scratch_layout(int64_t n);
+
+// Stable LSD sort of n (key, id) pairs. Pass 0 reads (keys_in, ids_in) (ids_in == nullptr: ids are the input
+// positions); pass p writes buffer A when p is even and B when odd, so the result is in B after an even number of
+// passes (*result_in_b = 1) and in A after an odd number. keys_in may alias B but never A.
+template <typename KeyT>
+gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                           KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
+                           hipStream_t stream, int *result_in_b);
+
+}  // namespace gs

@@ -4,7 +4,7 @@
 // slot by a search over the workgroup's offsets in LDS.
 //
 // Definitions: gsplat 1.0.0 native extension, intersections.c (gs_bounds, gs_tile_bits, gs_isect_tiles).
-#include "gs_internal.hpp"
+#include "gs_sort.hpp"
 
 namespace gs {
 namespace {
@@ -79,19 +79,22 @@ __device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t *s_tmp, in
     return before + inc - v;
 }
 
-// Phase 1a: per-splat tile count, and one partial sum per workgroup.
+// Phase 1a: per-splat tile count, and one partial sum per workgroup. With `perm`, position j counts splat
+// perm[j] (the sum is then over that order) and tiles_per_gauss is not written.
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void count_kernel(const float2 *__restrict__ means,
                                                          const float *__restrict__ radii, int M, float ts, int tw,
-                                                         int th, int32_t *__restrict__ tiles_per_gauss,
+                                                         int th, const int32_t *__restrict__ perm,
+                                                         int32_t *__restrict__ tiles_per_gauss,
                                                          int64_t *__restrict__ block_sums) {
     __shared__ int64_t s_tmp[kThreads / kWave];
-    const int i = blockIdx.x * kThreads + threadIdx.x;
+    const int j = blockIdx.x * kThreads + threadIdx.x;
     int64_t count = 0;
-    if (i < M) {
+    if (j < M) {
+        const int i = perm ? perm[j] : j;
         const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
         count = static_cast<int64_t>(r.x1 - r.x0) * static_cast<int64_t>(r.y1 - r.y0);
-        if (tiles_per_gauss) tiles_per_gauss[i] = static_cast<int32_t>(count);
+        if (tiles_per_gauss) tiles_per_gauss[j] = static_cast<int32_t>(count);
     }
     const int64_t total = block_sum(count, s_tmp);
     if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
@@ -114,94 +117,163 @@ __global__ __launch_bounds__(kThreads) void scan_block_sums_kernel(int64_t *__re
     if (threadIdx.x == 0) *total_out = carry;
 }
 
-// Phase 1c: per-splat first output slot = workgroup prefix + exclusive scan of the counts within it.
+// Phase 1c: per-position first output slot = workgroup prefix + exclusive scan of the counts within it (position
+// j holds splat perm[j], or j without a permutation).
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void offsets_kernel(const float2 *__restrict__ means,
                                                            const float *__restrict__ radii, int M, float ts, int tw,
-                                                           int th, const int64_t *__restrict__ block_prefix,
+                                                           int th, const int32_t *__restrict__ perm,
+                                                           const int64_t *__restrict__ block_prefix,
                                                            int32_t *__restrict__ gauss_offsets) {
     __shared__ int64_t s_tmp[kThreads / kWave];
-    const int i = blockIdx.x * kThreads + threadIdx.x;
+    const int j = blockIdx.x * kThreads + threadIdx.x;
     int64_t count = 0;
-    if (i < M) {
+    if (j < M) {
+        const int i = perm ? perm[j] : j;
         const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
         count = static_cast<int64_t>(r.x1 - r.x0) * static_cast<int64_t>(r.y1 - r.y0);
     }
     int64_t unused;
     const int64_t ex = block_exclusive(count, s_tmp, &unused);
-    if (i < M) gauss_offsets[i] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
+    if (j < M) gauss_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
 }
 
-// Phase 2: the workgroup takes 256 consecutive splats; their outputs occupy the contiguous slots
-// [start(g0), start(g0 + 256)). Each thread walks slots with stride 256, finds the owning splat (the last one
-// whose start is <= slot) by binary search in LDS, and writes key and id for tile k of its rectangle in
-// row-major order.
+// Phase 2: the workgroup takes 256 consecutive positions (splat perm[j], or j without a permutation); their
+// outputs occupy the contiguous slots [start(g0), start(g0 + 256)). Each thread walks slots with stride 256,
+// finds the owning position (the last one whose start is <= slot) by binary search in LDS, and writes key and
+// id for tile k of that splat's rectangle in row-major order.
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict__ means,
                                                         const float *__restrict__ radii,
                                                         const uint32_t *__restrict__ depth_bits, int M, int N,
                                                         float ts, int tw, int th, int tile_bits,
+                                                        const int32_t *__restrict__ perm,
                                                         const int32_t *__restrict__ gauss_offsets, int n,
                                                         uint64_t *__restrict__ keys, int32_t *__restrict__ ids) {
     __shared__ int s_start[kThreads + 1];
-    __shared__ int s_x0[kThreads], s_y0[kThreads], s_w[kThreads];
+    __shared__ int s_x0[kThreads], s_y0[kThreads], s_w[kThreads], s_id[kThreads];
     __shared__ uint32_t s_upper_cam[kThreads], s_depth[kThreads];
     const int g0 = blockIdx.x * kThreads;
-    const int i = g0 + threadIdx.x;
-    if (i < M) {
+    const int j = g0 + threadIdx.x;
+    if (j < M) {
+        const int i = perm ? perm[j] : j;
         const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
         s_x0[threadIdx.x] = r.x0;
         s_y0[threadIdx.x] = r.y0;
         s_w[threadIdx.x] = r.x1 - r.x0;
-        s_start[threadIdx.x] = gauss_offsets[i];
+        s_start[threadIdx.x] = gauss_offsets[j];
         s_depth[threadIdx.x] = depth_bits[i];
         s_upper_cam[threadIdx.x] = static_cast<uint32_t>(i / N) << tile_bits;
+        s_id[threadIdx.x] = i;
     } else {
         s_start[threadIdx.x] = n;
         s_w[threadIdx.x] = 1;
         s_x0[threadIdx.x] = s_y0[threadIdx.x] = 0;
         s_depth[threadIdx.x] = s_upper_cam[threadIdx.x] = 0;
+        s_id[threadIdx.x] = 0;
     }
     if (threadIdx.x == 0) s_start[kThreads] = (g0 + kThreads < M) ? gauss_offsets[g0 + kThreads] : n;
     __syncthreads();
     // clamped to [0, n] so that offsets inconsistent with n can never address past the outputs
     const int out_end = min(s_start[kThreads], n);
     const int out_begin = min(s_start[0], out_end);
-    for (int j = out_begin + static_cast<int>(threadIdx.x); j < out_end; j += kThreads) {
-        int lo = 0, hi = kThreads - 1;  // invariant: s_start[lo] <= j, answer in [lo, hi]
+    for (int slot = out_begin + static_cast<int>(threadIdx.x); slot < out_end; slot += kThreads) {
+        int lo = 0, hi = kThreads - 1;  // invariant: s_start[lo] <= slot, answer in [lo, hi]
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (s_start[mid] <= j) lo = mid;
+            if (s_start[mid] <= slot) lo = mid;
             else hi = mid - 1;
         }
-        const int k = j - s_start[lo];
+        const int k = slot - s_start[lo];
         const int w = s_w[lo];
         const int ry = k / w;
         const int rx = k - ry * w;
         const uint32_t tile = static_cast<uint32_t>(s_y0[lo] + ry) * static_cast<uint32_t>(tw) +
                               static_cast<uint32_t>(s_x0[lo] + rx);
         const uint64_t upper = static_cast<uint64_t>(s_upper_cam[lo] | tile);
-        keys[j] = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
-        ids[j] = g0 + lo;
+        keys[slot] = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
+        ids[slot] = s_id[lo];
     }
 }
 
+// Workspace of gs_isect_tiles. Phase 1 uses the workgroup sums and the total. Phase 2 with sorting adds the
+// depth-ordered splat permutation (two u32/i32 ping-pong pairs of M), the per-position offsets in that order, the
+// alternate intersection buffers and the radix-sort scratch (sized for the larger of M and n).
 struct IsectLayout {
-    size_t block_sums, total, sort, bytes;
+    size_t block_sums, total, dkeys_a, dids_a, dkeys_b, dids_b, sorted_offsets, alt_keys, alt_ids, scratch, bytes;
 };
 
-IsectLayout isect_layout(int64_t M, int64_t n, int end_bit, int sort) {
+IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     IsectLayout L{};
     Carver c(nullptr);
     const int64_t blocks = (M + kThreads - 1) / kThreads;
+    L.block_sums = align_up(c.used, 256);
     c.take<int64_t>(static_cast<size_t>(blocks > 0 ? blocks : 1));
-    L.block_sums = 0;
     L.total = align_up(c.used, 256);
     c.take<int64_t>(1);
-    L.sort = align_up(c.used, 256);
-    L.bytes = L.sort;
-    if (sort && n > 1) L.bytes += sort_workspace_layout(n, end_bit);
+    L.bytes = align_up(c.used, 256);
+    if (!(sort && n > 1)) return L;
+    const size_t m = static_cast<size_t>(M > 0 ? M : 1), nn = static_cast<size_t>(n);
+    L.dkeys_a = align_up(c.used, 256);
+    c.take<uint32_t>(m);
+    L.dids_a = align_up(c.used, 256);
+    c.take<int32_t>(m);
+    L.dkeys_b = align_up(c.used, 256);
+    c.take<uint32_t>(m);
+    L.dids_b = align_up(c.used, 256);
+    c.take<int32_t>(m);
+    L.sorted_offsets = align_up(c.used, 256);
+    c.take<int32_t>(m);
+    L.alt_keys = align_up(c.used, 256);
+    c.take<uint64_t>(nn);
+    L.alt_ids = align_up(c.used, 256);
+    c.take<int32_t>(nn);
+    L.scratch = align_up(c.used, 256);
+    L.bytes = L.scratch + sort_scratch_layout(M > n ? M : n).bytes;
     return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+// count -> workgroup sums -> scan -> per-position offsets, over positions 0..M-1 in the order given by perm.
+gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, float ts, int tw, int th,
+                        const int32_t *perm, int32_t *tiles_per_gauss, int64_t *block_sums, int64_t *total,
+                        int32_t *offsets, hipStream_t stream) {
+    const int blocks = (M + kThreads - 1) / kThreads;
+    if (rpg == 2)
+        hipLaunchKernelGGL(count_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th, perm,
+                           tiles_per_gauss, block_sums);
+    else
+        hipLaunchKernelGGL(count_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th, perm,
+                           tiles_per_gauss, block_sums);
+    GS_LAUNCH_TRY("count_kernel");
+    hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks, total);
+    GS_LAUNCH_TRY("scan_block_sums_kernel");
+    if (rpg == 2)
+        hipLaunchKernelGGL(offsets_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
+                           perm, block_sums, offsets);
+    else
+        hipLaunchKernelGGL(offsets_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
+                           perm, block_sums, offsets);
+    GS_LAUNCH_TRY("offsets_kernel");
+    return ok();
+}
+
+gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
+                      int tw, int th, int tile_bits, const int32_t *perm, const int32_t *offsets, int n,
+                      uint64_t *keys, int32_t *ids, hipStream_t stream) {
+    const int blocks = (M + kThreads - 1) / kThreads;
+    if (rpg == 2)
+        hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
+                           th, tile_bits, perm, offsets, n, keys, ids);
+    else
+        hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
+                           th, tile_bits, perm, offsets, n, keys, ids);
+    GS_LAUNCH_TRY("emit_kernel");
+    return ok();
 }
 
 }  // namespace
@@ -211,9 +283,8 @@ using namespace gs;
 
 extern "C" size_t gs_isect_workspace_bytes(int64_t C, int64_t N, int64_t n_isects, int tile_width,
                                            int tile_height, int sort) {
-    if (C < 1 || N < 0 || tile_width < 1 || tile_height < 1) return 0;
-    const int end_bit = 32 + bits_for(static_cast<int64_t>(tile_width) * tile_height) + bits_for(C);
-    return isect_layout(C * N, n_isects, end_bit > 64 ? 64 : end_bit, sort).bytes;
+    if (C < 1 || N < 0 || tile_width < 1 || tile_height < 1 || n_isects < 0) return 0;
+    return isect_layout(C * N, n_isects, sort).bytes;
 }
 
 extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, int radii_per_gauss,
@@ -244,13 +315,12 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: means2d, radii and depths are required");
     if (M > 0 && !gauss_offsets)
         return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: gauss_offsets is required in both phases");
-    const int blocks = (M + kThreads - 1) / kThreads;
     const float ts = static_cast<float>(tile_size);
     const float2 *m2 = reinterpret_cast<const float2 *>(means2d);
 
     if (keys == nullptr) {  // ---------------------------------------------------------------- phase 1: count
         if (!n_isects_out) return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: n_isects_out is required to count");
-        const IsectLayout L = isect_layout(M, 0, 64, 0);
+        const IsectLayout L = isect_layout(M, 0, 0);
         if (!workspace || workspace_bytes < L.bytes)
             return fail(GS_ERR_WORKSPACE, "gs_isect_tiles: count needs %zu workspace bytes (got %zu)", L.bytes,
                         workspace_bytes);
@@ -258,24 +328,11 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             *n_isects_out = 0;
             return ok();
         }
-        int64_t *block_sums = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + L.block_sums);
-        int64_t *total = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + L.total);
-        if (radii_per_gauss == 2)
-            hipLaunchKernelGGL(count_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts,
-                               tile_width, tile_height, tiles_per_gauss, block_sums);
-        else
-            hipLaunchKernelGGL(count_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts,
-                               tile_width, tile_height, tiles_per_gauss, block_sums);
-        GS_LAUNCH_TRY("count_kernel");
-        hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks, total);
-        GS_LAUNCH_TRY("scan_block_sums_kernel");
-        if (radii_per_gauss == 2)
-            hipLaunchKernelGGL(offsets_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts,
-                               tile_width, tile_height, block_sums, gauss_offsets);
-        else
-            hipLaunchKernelGGL(offsets_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts,
-                               tile_width, tile_height, block_sums, gauss_offsets);
-        GS_LAUNCH_TRY("offsets_kernel");
+        int64_t *total = at<int64_t>(workspace, L.total);
+        gs_status st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, nullptr,
+                                     tiles_per_gauss, at<int64_t>(workspace, L.block_sums), total, gauss_offsets,
+                                     stream);
+        if (st != GS_OK) return st;
         int64_t host_total = 0;
         GS_HIP_TRY(hipMemcpyAsync(&host_total, total, sizeof host_total, hipMemcpyDeviceToHost, stream));
         GS_HIP_TRY(hipStreamSynchronize(stream));
@@ -290,26 +347,48 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     if (!flatten_ids) return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: flatten_ids is required to emit");
     if (n_isects < 0 || n_isects >= (int64_t(1) << 31))
         return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: n_isects = %lld out of range", (long long)n_isects);
-    const int end_bit = 32 + tile_bits + cam_bits;
     if (sort && n_isects > 1 && n_isects >= (int64_t(1) << 30))
         return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: sorting supports at most 2^30 - 1 intersections");
-    const IsectLayout L = isect_layout(M, n_isects, end_bit, sort);
+    const IsectLayout L = isect_layout(M, n_isects, sort);
     if (!workspace || workspace_bytes < L.bytes)
         return fail(GS_ERR_WORKSPACE, "gs_isect_tiles: emit needs %zu workspace bytes (got %zu)", L.bytes,
                     workspace_bytes);
     if (M == 0 || n_isects == 0) return ok();
     const uint32_t *dbits = reinterpret_cast<const uint32_t *>(depths);
-    if (radii_per_gauss == 2)
-        hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M,
-                           static_cast<int>(N), ts, tile_width, tile_height, tile_bits, gauss_offsets,
-                           static_cast<int>(n_isects), keys, flatten_ids);
-    else
-        hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M,
-                           static_cast<int>(N), ts, tile_width, tile_height, tile_bits, gauss_offsets,
-                           static_cast<int>(n_isects), keys, flatten_ids);
-    GS_LAUNCH_TRY("emit_kernel");
-    if (sort && n_isects > 1)
-        return sort_pairs_u64(keys, flatten_ids, n_isects, end_bit, static_cast<char *>(workspace) + L.sort,
-                              stream);
-    return ok();
+    const int n = static_cast<int>(n_isects);
+    if (!(sort && n > 1))  // emission in (camera, splat, tile row, tile column) order
+        return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
+                           tile_bits, nullptr, gauss_offsets, n, keys, flatten_ids, stream);
+
+    // Sorted output. Splats are first put in stable (depth bits, flat id) order; emitting each splat's tiles in
+    // that order makes the intersections ordered by (depth bits, id) already, so a stable sort of the camera and
+    // tile bits [32, end_bit) alone completes the order by the whole key - the unique stable order by key.
+    void *scratch = at<char>(workspace, L.scratch);
+    int in_b = 0;
+    gs_status st = radix_sort_pairs<uint32_t>(dbits, nullptr, at<uint32_t>(workspace, L.dkeys_a),
+                                              at<int32_t>(workspace, L.dids_a), at<uint32_t>(workspace, L.dkeys_b),
+                                              at<int32_t>(workspace, L.dids_b), M, make_pass_plan(0, 32), scratch,
+                                              stream, &in_b);
+    if (st != GS_OK) return st;
+    const int32_t *perm = at<int32_t>(workspace, in_b ? L.dids_b : L.dids_a);
+    int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
+    st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, perm, nullptr,
+                       at<int64_t>(workspace, L.block_sums), at<int64_t>(workspace, L.total), sorted_offsets, stream);
+    if (st != GS_OK) return st;
+    const PassPlan tile_plan = make_pass_plan(32, 32 + tile_bits + cam_bits);
+    uint64_t *alt_keys = at<uint64_t>(workspace, L.alt_keys);
+    int32_t *alt_ids = at<int32_t>(workspace, L.alt_ids);
+    // the tile passes alternate buffers; emit where the last pass then lands in the caller's arrays
+    const bool odd = (tile_plan.passes % 2) == 1;
+    uint64_t *emit_keys = odd ? alt_keys : keys;
+    int32_t *emit_ids = odd ? alt_ids : flatten_ids;
+    st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
+                     perm, sorted_offsets, n, emit_keys, emit_ids, stream);
+    if (st != GS_OK) return st;
+    if (tile_plan.passes == 0) return ok();
+    if (odd)
+        return radix_sort_pairs<uint64_t>(alt_keys, alt_ids, keys, flatten_ids, alt_keys, alt_ids, n, tile_plan,
+                                          scratch, stream, &in_b);
+    return radix_sort_pairs<uint64_t>(keys, flatten_ids, alt_keys, alt_ids, keys, flatten_ids, n, tile_plan, scratch,
+                                      stream, &in_b);
 }

@@ -10,6 +10,8 @@
 // splat_training.rs (training_forward_metal_traced).
 #include "gs_internal.hpp"
 
+#include <cmath>
+
 namespace gs {
 namespace {
 
@@ -50,6 +52,7 @@ struct RasterArgs {
     float *out_colors, *out_alphas, *out_T;
     int32_t *out_last;
     unsigned long long *eval_counts;  // nullable: [evaluations, alpha >= cutoff, composited]
+    float log_cutoff;                 // ln(alpha_cutoff), for the conservative cull
 };
 
 template <int K, int PPT, bool COUNT>
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     float px[PPT], py[PPT], T[PPT], acc[PPT][K];
     int last[PPT], xs[PPT], ys[PPT], stop[PPT];
     bool done[PPT];
-    unsigned long long n_pass = 0, n_comp = 0;
+    unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const int pix = threadIdx.x + q * nthreads;
@@ -96,6 +99,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         if (__syncthreads_and(mine_done)) break;  // also orders the previous batch's LDS reads before refilling
         const int idx = base + static_cast<int>(threadIdx.x);
         if (idx < end) {
+            if (COUNT) ++n_staged;
             const int g = a.ids[idx];
             s_xy[threadIdx.x] = a.means[g];
             const float *cg = a.conics + 3 * static_cast<int64_t>(g);
@@ -109,6 +113,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         for (int q = 0; q < PPT; ++q) {
             if (done[q]) continue;
             for (int j = 0; j < count; ++j) {
+                if (COUNT) ++n_exec;
                 const float2 m = s_xy[j];
                 const float4 c = s_abco[j];
                 const float dx = m.x - px[q];
@@ -164,10 +169,207 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     }
 }
 
+// Conservative cull of one splat against a wave's pixel region (pixel-centre box [x0, x1] x [y0, y1]). Returns
+// false only when alpha < cutoff at every pixel of the box, so skipping the splat there leaves every output bit
+// unchanged:
+//  - opacity < cutoff: alpha = opacity * E(sigma) <= opacity since E(sigma) <= 1 for sigma >= 0;
+//  - otherwise alpha >= cutoff needs sigma_exact <= L = ln(opacity / cutoff) + 0.05, and {sigma <= L} lies inside
+//    |dx| <= sqrt(2 L S_xx), |dy| <= sqrt(2 L S_yy) with S = inverse of the conic (the marginal bound of a
+//    quadratic form). The 5% alpha margin covers float32 rounding: with trace^2 <= 1000 det the computed sigma is
+//    within 24 * 2^-24 * trace^2 / det < 0.15% of the exact one, E is within one ulp of e^-sigma, and
+//    0.9985 (ln(o / cutoff) + 0.05) > ln(o / cutoff) for every opacity up to 1e6; the box is padded for the rounding
+//    of its own arithmetic;
+//  - non-positive-definite, badly conditioned or non-finite conics, opacities above 1e6 or NaN, and means beyond
+//    1e6 pixels are never culled.
+struct CullBox {
+    float x0, x1, y0, y1;  // bounding box of the alpha >= cutoff footprint, or +-inf when not culled
+    bool never;            // the splat can reach the cutoff nowhere
+};
+
+__device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c, float o, float alpha_cutoff,
+                                           float log_cutoff) {
+    CullBox box{-INFINITY, INFINITY, -INFINITY, INFINITY, false};
+    if (o < alpha_cutoff) {
+        box.never = true;
+        return box;
+    }
+    const float det = a * c - b * b;
+    const float tr = a + c;
+    if (!(o >= alpha_cutoff) || !(o <= 1.0e6f) || !(det > 0.0f) || !(a > 0.0f) || !(c > 0.0f) ||
+        !(tr * tr <= 1.0e3f * det) || !(fabsf(m.x) < 1.0e6f) || !(fabsf(m.y) < 1.0e6f))
+        return box;
+    const float L = logf(o) - log_cutoff + 0.05f;
+    float rx = sqrtf(2.0f * L * (c / det)) * 1.0001f;
+    float ry = sqrtf(2.0f * L * (a / det)) * 1.0001f;
+    if (!(rx < 1.0e6f) || !(ry < 1.0e6f)) return box;
+    rx += 2.0e-3f + 1.0e-6f * (fabsf(m.x) + rx);
+    ry += 2.0e-3f + 1.0e-6f * (fabsf(m.y) + ry);
+    box.x0 = m.x - rx;
+    box.x1 = m.x + rx;
+    box.y0 = m.y - ry;
+    box.y1 = m.y + ry;
+    return box;
+}
+
+// Tiles up to 16x16, one pixel per thread. With 16x16 tiles each wave owns an 8x8 quadrant; otherwise pixels are
+// row-major and a wave's region is the rows it covers. Each staged splat carries a bit per wave telling whether its
+// alpha >= cutoff footprint can touch that wave's region (cull_box); a wave compacts the batch to the splats with
+// its bit set, in order, and evaluates only those. Skipped splats would have been skipped by the cutoff test at
+// every pixel of the region, so the result is the same to the bit.
+template <int K, bool COUNT>
+__global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) {
+    __shared__ float2 s_xy[kMaxThreads];
+    __shared__ float4 s_abco[kMaxThreads];
+    __shared__ float s_rgb[kMaxThreads * K];
+    __shared__ uint32_t s_mask[kMaxThreads];
+    __shared__ uint16_t s_list[kMaxThreads / kWave][kMaxThreads];
+
+    const int tile = a.tile_order ? a.tile_order[blockIdx.x] : static_cast<int>(blockIdx.x);
+    const int per_camera = a.tile_width * a.tile_height;
+    const int camera = tile / per_camera;
+    const int local = tile - camera * per_camera;
+    const int ty = local / a.tile_width;
+    const int tx = local - ty * a.tile_width;
+    const int start = a.offsets[tile];
+    const int end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects);
+    const int ts = a.tile_size;
+    const int nthreads = blockDim.x;
+    const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const bool quadrants = (ts == 16);
+
+    // this thread's pixel
+    int lx, ly;
+    if (quadrants) {
+        lx = (wave & 1) * 8 + (lane & 7);
+        ly = (wave >> 1) * 8 + (lane >> 3);
+    } else {
+        lx = static_cast<int>(threadIdx.x) % ts;
+        ly = static_cast<int>(threadIdx.x) / ts;
+    }
+    const int x = tx * ts + lx, y = ty * ts + ly;
+    const bool inside = static_cast<int>(threadIdx.x) < ts * ts && x < a.width && y < a.height;
+    const float px = static_cast<float>(x) + 0.5f, py = static_cast<float>(y) + 0.5f;
+
+    // pixel-centre boxes of every wave's region (for the cull bits), in pixel coordinates
+    float rx0[kMaxThreads / kWave], rx1[kMaxThreads / kWave], ry0[kMaxThreads / kWave], ry1[kMaxThreads / kWave];
+#pragma unroll
+    for (int w = 0; w < kMaxThreads / kWave; ++w) {
+        int qx0, qx1, qy0, qy1;
+        if (quadrants) {
+            qx0 = (w & 1) * 8;
+            qx1 = qx0 + 7;
+            qy0 = (w >> 1) * 8;
+            qy1 = qy0 + 7;
+        } else {
+            qx0 = 0;
+            qx1 = ts - 1;
+            qy0 = (w * kWave) / ts;
+            qy1 = (w * kWave + kWave - 1) / ts;
+        }
+        rx0[w] = static_cast<float>(tx * ts + qx0) + 0.5f;
+        rx1[w] = static_cast<float>(tx * ts + qx1) + 0.5f;
+        ry0[w] = static_cast<float>(ty * ts + qy0) + 0.5f;
+        ry1[w] = static_cast<float>(ty * ts + qy1) + 0.5f;
+    }
+
+    float T = 1.0f, acc[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[k] = 0.0f;
+    int last = -1, stop = end;
+    bool done = !inside;
+    unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+
+    for (int base = start; base < end; base += nthreads) {
+        if (__syncthreads_and(done)) break;  // also orders the previous batch's LDS reads before refilling
+        const int idx = base + static_cast<int>(threadIdx.x);
+        if (idx < end) {
+            if (COUNT) ++n_staged;
+            const int g = a.ids[idx];
+            const float2 m = a.means[g];
+            const float *cg = a.conics + 3 * static_cast<int64_t>(g);
+            const float ca = cg[0], cb = cg[1], cc = cg[2], o = a.opacities[g];
+            s_xy[threadIdx.x] = m;
+            s_abco[threadIdx.x] = make_float4(ca, cb, cc, o);
+#pragma unroll
+            for (int k = 0; k < K; ++k) s_rgb[threadIdx.x * K + k] = a.colors[static_cast<int64_t>(g) * K + k];
+            const CullBox box = cull_box(m, ca, cb, cc, o, a.alpha_cutoff, a.log_cutoff);
+            uint32_t bits = 0;
+            if (!box.never) {
+#pragma unroll
+                for (int w = 0; w < kMaxThreads / kWave; ++w) {
+                    const bool touch = box.x1 >= rx0[w] && box.x0 <= rx1[w] && box.y1 >= ry0[w] && box.y0 <= ry1[w];
+                    bits |= (touch ? 1u : 0u) << w;
+                }
+            }
+            s_mask[threadIdx.x] = bits;
+        }
+        __syncthreads();
+        const int count = end - base < nthreads ? end - base : nthreads;
+        // this wave's splats of the batch, in order
+        int listed = 0;
+        for (int c0 = 0; c0 < count; c0 += kWave) {
+            const int j = c0 + lane;
+            const bool keep = j < count && ((s_mask[j] >> wave) & 1u);
+            const uint64_t ballot = __ballot(keep);
+            if (keep) s_list[wave][listed + __popcll(ballot & lt_mask)] = static_cast<uint16_t>(j);
+            listed += __popcll(ballot);
+        }
+        if (done) continue;
+        for (int jj = 0; jj < listed; ++jj) {
+            const int j = s_list[wave][jj];
+            if (COUNT) ++n_exec;
+            const float2 m = s_xy[j];
+            const float4 c = s_abco[j];
+            const float dx = m.x - px;
+            const float dy = m.y - py;
+            const float sigma = 0.5f * (c.x * dx * dx + c.z * dy * dy) + c.y * dx * dy;
+            if (sigma < 0.0f) continue;
+            float alpha = c.w * exp_neg(sigma);
+            if (alpha > a.alpha_clamp) alpha = a.alpha_clamp;
+            if (alpha < a.alpha_cutoff) continue;
+            if (COUNT) ++n_pass;
+            const float t_next = T * (1.0f - alpha);
+            if (t_next <= a.transmittance_threshold) {
+                done = true;
+                if (COUNT) stop = base + j + 1;
+                break;
+            }
+            if (COUNT) ++n_comp;
+            const float v = alpha * T;
+#pragma unroll
+            for (int k = 0; k < K; ++k) acc[k] = acc[k] + s_rgb[j * K + k] * v;
+            T = t_next;
+            last = base + j;
+        }
+    }
+
+    if (inside) {
+        const int64_t p = (static_cast<int64_t>(camera) * a.height + y) * a.width + x;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float bg = a.backgrounds ? a.backgrounds[camera * K + k] : 0.0f;
+            a.out_colors[p * K + k] = acc[k] + T * bg;
+        }
+        a.out_alphas[p] = 1.0f - T;
+        if (a.out_T) a.out_T[p] = T;
+        if (a.out_last) a.out_last[p] = last;
+    }
+    if (COUNT) {
+        const unsigned long long n_eval = inside ? static_cast<unsigned>(stop - start) : 0u;
+        atomicAdd(&a.eval_counts[0], n_eval);
+        atomicAdd(&a.eval_counts[1], n_pass);
+        atomicAdd(&a.eval_counts[2], n_comp);
+        atomicAdd(&a.eval_counts[3], n_exec);
+        atomicAdd(&a.eval_counts[4], n_staged);
+    }
+}
+
 template <int K, bool COUNT>
 gs_status launch_kc(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(args.total_tiles)), block(static_cast<unsigned>(threads));
-    if (ppt == 1) hipLaunchKernelGGL((raster_fwd_kernel<K, 1, COUNT>), grid, block, 0, stream, args);
+    if (ppt == 1) hipLaunchKernelGGL((raster_cull_kernel<K, COUNT>), grid, block, 0, stream, args);
     else hipLaunchKernelGGL((raster_fwd_kernel<K, 4, COUNT>), grid, block, 0, stream, args);
     GS_LAUNCH_TRY("raster_fwd_kernel");
     return ok();
@@ -246,6 +448,7 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
     args.out_T = render_T;
     args.out_last = last_ids;
     args.eval_counts = reinterpret_cast<unsigned long long *>(eval_counts);
+    args.log_cutoff = alpha_cutoff > 0.0f ? static_cast<float>(std::log(static_cast<double>(alpha_cutoff))) : -INFINITY;
 
     const int pixels = tile_size * tile_size;
     int threads, ppt;

@@ -1,14 +1,16 @@
-// Stable LSD radix sort of (64-bit key, int32 id) pairs on gfx950, onesweep style:
-//   1. one read of the keys builds every pass's 256-bucket digit histogram in LDS (global atomics at the end);
-//   2. one kernel per 8-bit digit pass: a workgroup takes the next partition of 4096 pairs (dynamic index, so
-//      every predecessor is already running), ranks its keys stably with wave64 ballot matching, publishes its
-//      per-digit counts, resolves its global per-digit offsets by a decoupled look-back over the predecessors'
-//      published counts, reorders the pairs through LDS by digit and writes runs of consecutive addresses.
-// Only bits [0, end_bit) are sorted; passes over them are ceil(end_bit / 8).
+// Stable LSD radix sort of (key, int32 id) pairs on gfx950, onesweep style:
+//   1. one read of the keys builds every pass's digit histogram (each thread counts runs of equal digits over 16
+//      consecutive keys, so keys that share digits - e.g. one splat's intersections - cost one LDS atomic);
+//   2. one kernel per digit pass: a workgroup takes the next partition of 4096 pairs (dynamic index, so every
+//      predecessor is already running), ranks its keys stably with wave64 ballot matching, publishes its
+//      per-digit counts, resolves its global per-digit offsets by a decoupled look-back that inspects 8
+//      predecessors per load round, reorders the pairs through LDS by digit (keys first, then ids in the same
+//      LDS bytes) and writes runs of consecutive addresses.
+// Only bits [begin_bit, end_bit) are sorted, split evenly into passes of at most 8 bits.
 //
 // Semantics: gsplat 1.0.0 native extension, intersections.c, gs_radix_sort_without_gvl (a stable LSD radix sort
 // of keys with their ids). Stability makes the result unique, so it is compared bit for bit.
-#include "gs_internal.hpp"
+#include "gs_sort.hpp"
 
 namespace gs {
 namespace {
@@ -19,16 +21,21 @@ constexpr int kItems = 16;                    // pairs per thread
 constexpr int kTile = kThreads * kItems;      // pairs per partition
 constexpr int kWaveSpan = kWave * kItems;     // contiguous pairs owned by one wave
 constexpr int kRadix = 256;
-constexpr int kMaxPasses = 8;
 constexpr uint32_t kFlagAggregate = 1u << 30; // partition's own count published
 constexpr uint32_t kFlagInclusive = 2u << 30; // count including every earlier partition published
 constexpr uint32_t kValueMask = (1u << 30) - 1;
+constexpr int kLookWindow = 8;                // predecessors inspected per look-back round
 
 __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void atomic_store_agent(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename KeyT>
+__device__ __forceinline__ uint32_t digit_of(KeyT k, int shift, uint32_t mask) {
+    return static_cast<uint32_t>(k >> shift) & mask;
 }
 
 // Exclusive prefix over the 256 threads of the workgroup (one value each); *total = sum.
@@ -48,27 +55,48 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_
     return before + inc - v;
 }
 
-__global__ __launch_bounds__(kThreads) void histogram_kernel(const uint64_t *__restrict__ keys, int64_t n,
-                                                             int passes, int end_bit, uint32_t *__restrict__ hist) {
+template <typename KeyT>
+__global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restrict__ keys, int64_t n,
+                                                             PassPlan plan, uint32_t *__restrict__ hist) {
     __shared__ uint32_t s_hist[kMaxPasses][kRadix];
-    for (int p = 0; p < passes; ++p) s_hist[p][threadIdx.x] = 0;
+    for (int p = 0; p < plan.passes; ++p) s_hist[p][threadIdx.x] = 0;
     __syncthreads();
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
-#pragma unroll 4
+    const int64_t start = static_cast<int64_t>(blockIdx.x) * kTile + static_cast<int64_t>(threadIdx.x) * kItems;
+    KeyT k[kItems];
+    int count = 0;
+#pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        const int64_t idx = base + i * kThreads + threadIdx.x;
-        if (idx < n) {
-            const uint64_t k = keys[idx];
-            for (int p = 0; p < passes; ++p) {
-                const int shift = 8 * p;
-                const int bits = end_bit - shift < 8 ? end_bit - shift : 8;
-                const uint32_t d = static_cast<uint32_t>(k >> shift) & ((1u << bits) - 1u);
-                atomicAdd(&s_hist[p][d], 1u);
+        if (start + i < n) {
+            k[i] = keys[start + i];
+            count = i + 1;
+        } else {
+            k[i] = 0;
+        }
+    }
+    if (count > 0) {
+        for (int p = 0; p < plan.passes; ++p) {
+            const int shift = plan.shift[p];
+            const uint32_t mask = (1u << plan.bits[p]) - 1u;
+            uint32_t run_digit = digit_of(k[0], shift, mask);
+            uint32_t run = 1;
+#pragma unroll
+            for (int i = 1; i < kItems; ++i) {
+                if (i < count) {
+                    const uint32_t d = digit_of(k[i], shift, mask);
+                    if (d == run_digit) {
+                        ++run;
+                    } else {
+                        atomicAdd(&s_hist[p][run_digit], run);
+                        run_digit = d;
+                        run = 1;
+                    }
+                }
             }
+            atomicAdd(&s_hist[p][run_digit], run);
         }
     }
     __syncthreads();
-    for (int p = 0; p < passes; ++p) {
+    for (int p = 0; p < plan.passes; ++p) {
         const uint32_t c = s_hist[p][threadIdx.x];
         if (c) atomicAdd(&hist[p * kRadix + threadIdx.x], c);
     }
@@ -77,13 +105,17 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const uint64_t *__r
 // One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile); wave w owns the
 // contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at w*kWaveSpan + i*64 + l,
 // so (wave, item, lane) order is input order and the per-wave running counts give a stable rank.
-// status[part][d] holds the look-back words of this pass; status_next[part][d] is cleared for the next pass.
+// ids_in == nullptr means the identity (id = input position). status[part][d] holds this pass's look-back
+// words; status_next[part][d] is cleared for the next pass.
+template <typename KeyT>
 __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
-    const uint64_t *__restrict__ keys_in, const int32_t *__restrict__ ids_in, uint64_t *__restrict__ keys_out,
+    const KeyT *__restrict__ keys_in, const int32_t *__restrict__ ids_in, KeyT *__restrict__ keys_out,
     int32_t *__restrict__ ids_out, int64_t n, int shift, int digit_bits, const uint32_t *__restrict__ hist,
     uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next) {
-    __shared__ uint64_t s_keys[kTile];
-    __shared__ int32_t s_ids[kTile];
+    __shared__ union {
+        KeyT keys[kTile];
+        int32_t ids[kTile];
+    } s_buf;
     __shared__ uint32_t s_wave_hist[kWaves][kRadix];
     __shared__ uint32_t s_local_start[kRadix];
     __shared__ uint32_t s_global_base[kRadix];
@@ -108,16 +140,16 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
 
     // load this wave's span
     const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan;
-    uint64_t k[kItems];
+    KeyT k[kItems];
     int32_t v[kItems];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const int64_t pos = base + i * kWave + lane;
         if (pos < n) {
             k[i] = keys_in[pos];
-            v[i] = ids_in[pos];
+            v[i] = ids_in ? ids_in[pos] : static_cast<int32_t>(pos);
         } else {
-            k[i] = ~0ull;  // past the end: largest digit, ranked after every real pair of this partition
+            k[i] = ~KeyT(0);  // past the end: largest digit, ranked after every real pair of this partition
             v[i] = 0;
         }
     }
@@ -127,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        const uint32_t d = static_cast<uint32_t>(k[i] >> shift) & digit_mask;
+        const uint32_t d = digit_of(k[i], shift, digit_mask);
         uint64_t same = ~0ull;
         for (int b = 0; b < digit_bits; ++b) {
             const bool bit = (d >> b) & 1u;
@@ -153,76 +185,100 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     }
     const uint32_t part_count = running;
     uint32_t *my_status = status + static_cast<size_t>(part) * kRadix + d;
-    if (part == 0) atomic_store_agent(my_status, kFlagInclusive | part_count);
-    else atomic_store_agent(my_status, kFlagAggregate | part_count);
+    atomic_store_agent(my_status, (part == 0 ? kFlagInclusive : kFlagAggregate) | part_count);
 
     uint32_t local_total;
     const uint32_t local_start = block_exclusive_u32(part_count, s_tmp, &local_total);
     s_local_start[d] = local_start;
 
-    // decoupled look-back: sum the predecessors' counts for digit d until one publishes an inclusive count
+    // decoupled look-back for digit d: walk back over the predecessors' published counts, loading a window of
+    // kLookWindow of them at once, until one carries an inclusive count (partition 0 always does)
     uint32_t before = 0;
     if (part > 0) {
         int64_t j = static_cast<int64_t>(part) - 1;
         while (true) {
-            const uint32_t s = atomic_load_agent(status + static_cast<size_t>(j) * kRadix + d);
-            const uint32_t flag = s & ~kValueMask;
-            if (flag == 0) {
-                __builtin_amdgcn_s_sleep(1);
-                continue;
+            uint32_t s[kLookWindow];
+#pragma unroll
+            for (int w = 0; w < kLookWindow; ++w)
+                s[w] = (j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d)
+                                    : kFlagInclusive;
+            int used = 0;
+            bool found = false;
+#pragma unroll
+            for (int w = 0; w < kLookWindow; ++w) {
+                if (found || used < w) continue;  // stop at the first unpublished word or the inclusive one
+                const uint32_t flag = s[w] & ~kValueMask;
+                if (flag == 0) continue;
+                before += s[w] & kValueMask;
+                used = w + 1;
+                if (flag == kFlagInclusive) found = true;
             }
-            before += s & kValueMask;
-            if (flag == kFlagInclusive) break;
-            --j;
+            if (found) break;
+            j -= used;
+            if (used < kLookWindow) __builtin_amdgcn_s_sleep(1);
         }
         atomic_store_agent(my_status, kFlagInclusive | (before + part_count));
     }
     s_global_base[d] = digit_global_start + before;
     __syncthreads();
 
-    // reorder the partition by digit through LDS
+    // reorder the partition's keys by digit through LDS
+    uint32_t lp[kItems];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        const uint32_t dd = static_cast<uint32_t>(k[i] >> shift) & digit_mask;
-        const uint32_t lp = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
-        s_keys[lp] = k[i];
-        s_ids[lp] = v[i];
+        const uint32_t dd = digit_of(k[i], shift, digit_mask);
+        lp[i] = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
+        s_buf.keys[lp[i]] = k[i];
     }
     __syncthreads();
 
-    // write: consecutive local positions of one digit go to consecutive global positions
+    // write keys: consecutive local positions of one digit go to consecutive global positions
     const int64_t valid64 = n - static_cast<int64_t>(part) * kTile;
     const int valid = valid64 < kTile ? static_cast<int>(valid64) : kTile;
+    uint32_t dst[kItems];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        const int lp = i * kThreads + tid;
-        if (lp < valid) {
-            const uint64_t key = s_keys[lp];
-            const uint32_t dd = static_cast<uint32_t>(key >> shift) & digit_mask;
-            const uint32_t dst = s_global_base[dd] + (static_cast<uint32_t>(lp) - s_local_start[dd]);
-            keys_out[dst] = key;
-            ids_out[dst] = s_ids[lp];
-        }
+        const int q = i * kThreads + tid;
+        const KeyT key = s_buf.keys[q];
+        const uint32_t dd = digit_of(key, shift, digit_mask);
+        dst[i] = s_global_base[dd] + (static_cast<uint32_t>(q) - s_local_start[dd]);
+        if (q < valid) keys_out[dst[i]] = key;
+    }
+    __syncthreads();
+
+    // the ids follow through the same LDS bytes
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) s_buf.ids[lp[i]] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int q = i * kThreads + tid;
+        if (q < valid) ids_out[dst[i]] = s_buf.ids[q];
     }
 }
 
-struct SortLayout {
-    size_t alt_keys, alt_ids, hist, counters, status0, status1, bytes;
-    int passes;
-    int64_t parts;
-};
+}  // namespace
 
-SortLayout sort_layout(int64_t n, int end_bit) {
-    SortLayout L{};
-    L.passes = (end_bit + 7) / 8;
+PassPlan make_pass_plan(int begin_bit, int end_bit) {
+    PassPlan plan{};
+    const int total = end_bit - begin_bit;
+    if (total <= 0) return plan;
+    plan.passes = (total + 7) / 8;
+    const int base = total / plan.passes, extra = total % plan.passes;
+    int shift = begin_bit;
+    for (int p = 0; p < plan.passes; ++p) {
+        plan.shift[p] = shift;
+        plan.bits[p] = base + (p < extra ? 1 : 0);
+        shift += plan.bits[p];
+    }
+    return plan;
+}
+
+SortScratchLayout sort_scratch_layout(int64_t n) {
+    SortScratchLayout L{};
     L.parts = (n + kTile - 1) / kTile;
     Carver c(nullptr);
-    const size_t nn = static_cast<size_t>(n > 0 ? n : 1);
-    c.take<uint64_t>(nn);
-    L.alt_keys = 0;
-    L.alt_ids = align_up(c.used, 256);
-    c.take<int32_t>(nn);
-    L.hist = align_up(c.used, 256);
+    L.hist = 0;
     c.take<uint32_t>(kMaxPasses * kRadix);
     L.counters = align_up(c.used, 256);
     c.take<uint32_t>(kMaxPasses);
@@ -235,17 +291,14 @@ SortLayout sort_layout(int64_t n, int end_bit) {
     return L;
 }
 
-}  // namespace
-
-size_t sort_workspace_layout(int64_t n, int end_bit) { return sort_layout(n, end_bit).bytes; }
-
-gs_status sort_pairs_u64(uint64_t *keys, int32_t *ids, int64_t n, int end_bit, void *workspace,
-                         hipStream_t stream) {
-    if (n < 2 || end_bit == 0) return ok();
-    const SortLayout L = sort_layout(n, end_bit);
-    char *ws = static_cast<char *>(workspace);
-    uint64_t *alt_keys = reinterpret_cast<uint64_t *>(ws + L.alt_keys);
-    int32_t *alt_ids = reinterpret_cast<int32_t *>(ws + L.alt_ids);
+template <typename KeyT>
+gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                           KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
+                           hipStream_t stream, int *result_in_b) {
+    *result_in_b = 0;
+    if (plan.passes == 0 || n < 1) return ok();
+    const SortScratchLayout L = sort_scratch_layout(n);
+    char *ws = static_cast<char *>(scratch);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
     uint32_t *status[2] = {reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1)};
@@ -254,34 +307,79 @@ gs_status sort_pairs_u64(uint64_t *keys, int32_t *ids, int64_t n, int end_bit, v
     GS_HIP_TRY(fill_u32(hist, 0, kMaxPasses * kRadix, stream));
     GS_HIP_TRY(fill_u32(counters, 0, kMaxPasses, stream));
     GS_HIP_TRY(fill_u32(status[0], 0, status_words, stream));
-    hipLaunchKernelGGL(histogram_kernel, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0, stream, keys, n,
-                       L.passes, end_bit, hist);
+    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0, stream,
+                       keys_in, n, plan, hist);
     GS_LAUNCH_TRY("histogram_kernel");
 
-    uint64_t *src_k = keys, *dst_k = alt_keys;
-    int32_t *src_i = ids, *dst_i = alt_ids;
-    for (int p = 0; p < L.passes; ++p) {
-        const int shift = 8 * p;
-        const int bits = end_bit - shift < 8 ? end_bit - shift : 8;
+    const KeyT *src_k = keys_in;
+    const int32_t *src_i = ids_in;
+    for (int p = 0; p < plan.passes; ++p) {
+        const bool to_a = (p % 2) == 0;
+        KeyT *dk = to_a ? buf_a_keys : buf_b_keys;
+        int32_t *di = to_a ? buf_a_ids : buf_b_ids;
         uint32_t *st = status[p & 1];
-        uint32_t *st_next = (p + 1 < L.passes) ? status[(p + 1) & 1] : nullptr;
-        hipLaunchKernelGGL(onesweep_pass_kernel, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0, stream,
-                           src_k, src_i, dst_k, dst_i, n, shift, bits, hist + p * kRadix, counters + p, st, st_next);
+        uint32_t *st_next = (p + 1 < plan.passes) ? status[(p + 1) & 1] : nullptr;
+        hipLaunchKernelGGL(onesweep_pass_kernel<KeyT>, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0,
+                           stream, src_k, src_i, dk, di, n, plan.shift[p], plan.bits[p], hist + p * kRadix,
+                           counters + p, st, st_next);
         GS_LAUNCH_TRY("onesweep_pass_kernel");
-        uint64_t *tk = src_k;
-        src_k = dst_k;
-        dst_k = tk;
-        int32_t *ti = src_i;
-        src_i = dst_i;
-        dst_i = ti;
+        src_k = dk;
+        src_i = di;
     }
-    if (src_k != keys) {
-        GS_HIP_TRY(hipMemcpyAsync(keys, src_k, static_cast<size_t>(n) * sizeof(uint64_t), hipMemcpyDeviceToDevice,
-                                  stream));
-        GS_HIP_TRY(hipMemcpyAsync(ids, src_i, static_cast<size_t>(n) * sizeof(int32_t), hipMemcpyDeviceToDevice,
-                                  stream));
-    }
+    *result_in_b = (plan.passes % 2) == 0;
     return ok();
+}
+
+template gs_status radix_sort_pairs<uint32_t>(const uint32_t *, const int32_t *, uint32_t *, int32_t *, uint32_t *,
+                                              int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
+template gs_status radix_sort_pairs<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
+                                              int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
+
+namespace {
+
+struct SortLayout {
+    size_t alt_keys, alt_ids, scratch, bytes;
+};
+
+SortLayout sort_layout(int64_t n) {
+    SortLayout L{};
+    Carver c(nullptr);
+    const size_t nn = static_cast<size_t>(n > 0 ? n : 1);
+    c.take<uint64_t>(nn);
+    L.alt_keys = 0;
+    L.alt_ids = align_up(c.used, 256);
+    c.take<int32_t>(nn);
+    L.scratch = align_up(c.used, 256);
+    L.bytes = L.scratch + sort_scratch_layout(n).bytes;
+    return L;
+}
+
+}  // namespace
+
+size_t sort_workspace_layout(int64_t n, int) { return sort_layout(n).bytes; }
+
+// In-place stable sort of (keys, ids) by bits [0, end_bit): passes alternate between the caller's arrays and the
+// workspace copies; an odd pass count starts with a copy into the workspace so the last pass lands in place.
+gs_status sort_pairs_u64(uint64_t *keys, int32_t *ids, int64_t n, int end_bit, void *workspace,
+                         hipStream_t stream) {
+    if (n < 2 || end_bit == 0) return ok();
+    const SortLayout L = sort_layout(n);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *alt_keys = reinterpret_cast<uint64_t *>(ws + L.alt_keys);
+    int32_t *alt_ids = reinterpret_cast<int32_t *>(ws + L.alt_ids);
+    const PassPlan plan = make_pass_plan(0, end_bit);
+    int in_b = 0;
+    if (plan.passes % 2 == 0) {
+        // keys -> alt -> keys -> ...: the even last pass writes the caller's arrays
+        return radix_sort_pairs<uint64_t>(keys, ids, alt_keys, alt_ids, keys, ids, n, plan, ws + L.scratch, stream,
+                                          &in_b);
+    }
+    GS_HIP_TRY(hipMemcpyAsync(alt_keys, keys, static_cast<size_t>(n) * sizeof(uint64_t), hipMemcpyDeviceToDevice,
+                              stream));
+    GS_HIP_TRY(hipMemcpyAsync(alt_ids, ids, static_cast<size_t>(n) * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                              stream));
+    return radix_sort_pairs<uint64_t>(alt_keys, alt_ids, keys, ids, alt_keys, alt_ids, n, plan, ws + L.scratch,
+                                      stream, &in_b);
 }
 
 }  // namespace gs
@@ -290,7 +388,7 @@ using namespace gs;
 
 extern "C" size_t gs_sort_workspace_bytes(int64_t n, int end_bit) {
     if (n < 0 || end_bit < 0 || end_bit > 64) return 0;
-    return sort_layout(n, end_bit).bytes;
+    return sort_layout(n).bytes;
 }
 
 extern "C" gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_bit, void *workspace,
@@ -301,7 +399,7 @@ extern "C" gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t 
         return fail(GS_ERR_INVALID_ARG, "gs_sort_keys: end_bit = %d outside [0, 64]", end_bit);
     if (n > 0 && (!keys || !flatten_ids)) return fail(GS_ERR_INVALID_ARG, "gs_sort_keys: keys and ids are required");
     if (n < 2 || end_bit == 0) return ok();
-    const size_t need = sort_layout(n, end_bit).bytes;
+    const size_t need = sort_layout(n).bytes;
     if (!workspace || workspace_bytes < need)
         return fail(GS_ERR_WORKSPACE, "gs_sort_keys: needs %zu workspace bytes (got %zu)", need, workspace_bytes);
     return sort_pairs_u64(keys, flatten_ids, n, end_bit, workspace, static_cast<hipStream_t>(stream));

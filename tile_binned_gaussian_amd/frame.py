@@ -64,8 +64,9 @@ def render_frame(ds: DeviceScene, stream=None) -> FrameResult:
 class FramePlan:
     """Preallocated buffers for repeated frames of one scene, so that a timed loop allocates nothing.
 
-    run() issues: count (one synchronisation for the intersection count), emit, sort, tile ranges, composite, with
-    optional torch events recorded between the steps on the same stream."""
+    run() issues: count (one synchronisation for the intersection count), emit with the sort folded in
+    (gs_isect_tiles with sort=1), tile ranges and the composite, with optional torch events recorded between the
+    steps on the same stream. run_generic_sort() times gs_sort_keys alone on the frame's unsorted keys."""
 
     def __init__(self, ds: DeviceScene, stream=None):
         self.ds = ds
@@ -84,7 +85,7 @@ class FramePlan:
                                      torch.empty((C, ds.height, ds.width), dtype=torch.float32, device=dev),
                                      torch.empty((C, ds.height, ds.width), dtype=torch.float32, device=dev),
                                      torch.empty((C, ds.height, ds.width), dtype=torch.int32, device=dev))
-        self.ws_count = torch.empty(max(self.lib.gs_isect_workspace_bytes(C, N, 0, ds.tile_width, ds.tile_height, 0),
+        self.ws_count = torch.empty(max(self.lib.gs_isect_workspace_bytes(C, N, 0, ds.tile_width, ds.tile_height, 1),
                                         1), dtype=torch.uint8, device=dev)
         self.ws_ranges = torch.empty(self.lib.gs_tile_ranges_workspace_bytes(), dtype=torch.uint8, device=dev)
         self.ws_raster = torch.empty(max(self.lib.gs_rasterize_workspace_bytes(C, ds.tile_width, ds.tile_height), 1),
@@ -98,42 +99,45 @@ class FramePlan:
         dev = self.ds.means2d.device
         self.keys = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
         self.ids = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
-        self.ws_sort = torch.empty(max(self.lib.gs_sort_workspace_bytes(n, self.end_bit), 1), dtype=torch.uint8,
-                                   device=dev)
         self.ws_emit = torch.empty(max(self.lib.gs_isect_workspace_bytes(self.ds.C, self.ds.N, n, self.ds.tile_width,
-                                                                         self.ds.tile_height, 0), 1),
+                                                                         self.ds.tile_height, 1), 1),
                                    dtype=torch.uint8, device=dev)
         self.capacity = n
 
-    def run(self, events=None, eval_counts=None):
-        """One frame. events: optional list of 6 torch.cuda.Event recorded before count, emit, sort, ranges,
-        composite and after the composite."""
+    def _count(self, s):
         ds, lib, P = self.ds, self.lib, binding._ptr
-        s = binding._stream(self.stream)
-        ev = events or [None] * 6
         n_out = ctypes.c_int64(0)
-        rec = lambda i: ev[i] is not None and ev[i].record(self.stream)  # noqa: E731
-        rec(0)
         binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
-                                          ds.tile_size, ds.tile_width, ds.tile_height, 0, P(self.tiles_per),
+                                          ds.tile_size, ds.tile_width, ds.tile_height, 1, P(self.tiles_per),
                                           P(self.goff), ctypes.byref(n_out), None, None, 0, P(self.ws_count),
                                           self.ws_count.numel(), s))
-        n = int(n_out.value)
+        return int(n_out.value)
+
+    def _emit(self, s, n, sort):
+        ds, lib, P = self.ds, self.lib, binding._ptr
+        if n > 0:
+            binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
+                                              ds.tile_size, ds.tile_width, ds.tile_height, int(sort), None,
+                                              P(self.goff), None, P(self.keys), P(self.ids), n, P(self.ws_emit),
+                                              self.ws_emit.numel(), s))
+
+    def run(self, events=None, eval_counts=None):
+        """One frame. events: optional list of 5 torch.cuda.Event recorded before count, emit+sort, ranges and
+        the composite, and after the composite."""
+        ds, lib, P = self.ds, self.lib, binding._ptr
+        s = binding._stream(self.stream)
+        ev = events or [None] * 5
+        rec = lambda i: ev[i] is not None and ev[i].record(self.stream)  # noqa: E731
+        rec(0)
+        n = self._count(s)
         self._ensure(n)
         self.n_isects = n
         rec(1)
-        if n > 0:
-            binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
-                                              ds.tile_size, ds.tile_width, ds.tile_height, 0, None, P(self.goff),
-                                              None, P(self.keys), P(self.ids), n, P(self.ws_emit),
-                                              self.ws_emit.numel(), s))
+        self._emit(s, n, sort=True)
         rec(2)
-        binding._check(lib.gs_sort_keys(P(self.keys), P(self.ids), n, self.end_bit, P(self.ws_sort),
-                                        self.ws_sort.numel(), s))
-        rec(3)
         binding._check(lib.gs_tile_ranges(P(self.keys), n, ds.C, ds.tile_width, ds.tile_height, P(self.offsets), 0,
                                           P(self.ws_ranges), self.ws_ranges.numel(), s))
-        rec(4)
+        rec(3)
         r = self.render
         binding._check(lib.gs_rasterize_fwd(P(ds.means2d), P(ds.conics), P(ds.colors), P(ds.opacities),
                                             P(ds.backgrounds), ds.C, ds.N, ds.colors.shape[2], ds.width, ds.height,
@@ -143,8 +147,30 @@ class FramePlan:
                                             ctypes.c_float(ds.transmittance_threshold), P(r.render_colors),
                                             P(r.render_alphas), P(r.render_T), P(r.last_ids), P(eval_counts),
                                             P(self.ws_raster), self.ws_raster.numel(), s))
-        rec(5)
+        rec(4)
         return n
+
+    def run_generic_sort(self, repeats, warmup=2):
+        """Median milliseconds of gs_sort_keys over bits [0, end_bit) on this frame's unsorted keys (each repeat
+        re-emits the unsorted order first, outside the timed interval)."""
+        s = binding._stream(self.stream)
+        n = self._count(s)
+        self._ensure(n)
+        ws = torch.empty(max(self.lib.gs_sort_workspace_bytes(n, self.end_bit), 1), dtype=torch.uint8,
+                         device=self.ds.means2d.device)
+        times = []
+        for r in range(warmup + repeats):
+            self._emit(s, n, sort=False)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            binding._check(self.lib.gs_sort_keys(binding._ptr(self.keys), binding._ptr(self.ids), n, self.end_bit,
+                                                 binding._ptr(ws), ws.numel(), s))
+            b.record(self.stream)
+            b.synchronize()
+            if r >= warmup:
+                times.append(a.elapsed_time(b))
+        times.sort()
+        return times[len(times) // 2], n
 
 
 def _bits_for(count: int) -> int:
