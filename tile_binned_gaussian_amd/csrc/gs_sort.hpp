@@ -24,7 +24,18 @@ struct SortScratchLayout {
 };
 SortScratchLayout sort_scratch_layout(int64_t n);
 
-// Stable LSD sort of n (key, id) pairs. Pass 0 reads (keys_in, ids_in) (ids_in == nullptr: ids are the input
+// Clears the scratch's histograms, partition counters and first look-back array for a sort of n pairs.
+gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream);
+// The scratch's per-pass digit histograms (kMaxPasses x 256 counts) for a sort of n pairs.
+uint32_t *radix_histograms(void *scratch, int64_t n);
+
+// The digit passes alone, after radix_prepare and with the histograms already accumulated by the caller.
+template <typename KeyT>
+gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                       KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
+                       hipStream_t stream, int *result_in_b);
+
+// Stable LSD sort of n (key, id) pairs (prepare + histograms + passes). Pass 0 reads (keys_in, ids_in) (ids_in == nullptr: ids are the input
 // positions); pass p writes buffer A when p is even and B when odd, so the result is in B after an even number of
 // passes (*result_in_b = 1) and in A after an odd number. keys_in may alias B but never A.
 template <typename KeyT>

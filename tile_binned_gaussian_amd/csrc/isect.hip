@@ -149,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                                                         float ts, int tw, int th, int tile_bits,
                                                         const int32_t *__restrict__ perm,
                                                         const int32_t *__restrict__ gauss_offsets, int n,
-                                                        uint64_t *__restrict__ keys, int32_t *__restrict__ ids) {
+                                                        uint64_t *__restrict__ keys, int32_t *__restrict__ ids,
+                                                        uint32_t *__restrict__ hist, PassPlan hplan) {
+    __shared__ uint32_t s_hist[kMaxPasses][kThreads];
     __shared__ int s_start[kThreads + 1];
     __shared__ int s_x0[kThreads], s_y0[kThreads], s_w[kThreads], s_id[kThreads];
     __shared__ uint32_t s_upper_cam[kThreads], s_depth[kThreads];
@@ -173,6 +175,8 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
         s_id[threadIdx.x] = 0;
     }
     if (threadIdx.x == 0) s_start[kThreads] = (g0 + kThreads < M) ? gauss_offsets[g0 + kThreads] : n;
+    if (hist)
+        for (int p = 0; p < hplan.passes; ++p) s_hist[p][threadIdx.x] = 0;
     __syncthreads();
     // clamped to [0, n] so that offsets inconsistent with n can never address past the outputs
     const int out_end = min(s_start[kThreads], n);
@@ -191,8 +195,20 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
         const uint32_t tile = static_cast<uint32_t>(s_y0[lo] + ry) * static_cast<uint32_t>(tw) +
                               static_cast<uint32_t>(s_x0[lo] + rx);
         const uint64_t upper = static_cast<uint64_t>(s_upper_cam[lo] | tile);
-        keys[slot] = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
+        const uint64_t key = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
+        keys[slot] = key;
         ids[slot] = s_id[lo];
+        if (hist)
+            for (int p = 0; p < hplan.passes; ++p)
+                atomicAdd(&s_hist[p][static_cast<uint32_t>(key >> hplan.shift[p]) & ((1u << hplan.bits[p]) - 1u)], 1u);
+    }
+    // digit histograms of the keys just written, for the sort passes that follow
+    if (hist) {
+        __syncthreads();
+        for (int p = 0; p < hplan.passes; ++p) {
+            const uint32_t c = s_hist[p][threadIdx.x];
+            if (c) atomicAdd(&hist[p * kThreads + threadIdx.x], c);
+        }
     }
 }
 
@@ -262,16 +278,17 @@ gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, fl
     return ok();
 }
 
+// hist (nullable): accumulate the digit histograms of the emitted keys for the passes of hplan.
 gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
                       int tw, int th, int tile_bits, const int32_t *perm, const int32_t *offsets, int n,
-                      uint64_t *keys, int32_t *ids, hipStream_t stream) {
+                      uint64_t *keys, int32_t *ids, uint32_t *hist, const PassPlan &hplan, hipStream_t stream) {
     const int blocks = (M + kThreads - 1) / kThreads;
     if (rpg == 2)
         hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, offsets, n, keys, ids);
+                           th, tile_bits, perm, offsets, n, keys, ids, hist, hplan);
     else
         hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, offsets, n, keys, ids);
+                           th, tile_bits, perm, offsets, n, keys, ids, hist, hplan);
     GS_LAUNCH_TRY("emit_kernel");
     return ok();
 }
@@ -358,7 +375,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const int n = static_cast<int>(n_isects);
     if (!(sort && n > 1))  // emission in (camera, splat, tile row, tile column) order
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, nullptr, gauss_offsets, n, keys, flatten_ids, stream);
+                           tile_bits, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr, PassPlan{}, stream);
 
     // Sorted output. Splats are first put in stable (depth bits, flat id) order; emitting each splat's tiles in
     // that order makes the intersections ordered by (depth bits, id) already, so a stable sort of the camera and
@@ -382,13 +399,18 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const bool odd = (tile_plan.passes % 2) == 1;
     uint64_t *emit_keys = odd ? alt_keys : keys;
     int32_t *emit_ids = odd ? alt_ids : flatten_ids;
-    st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
-                     perm, sorted_offsets, n, emit_keys, emit_ids, stream);
+    if (tile_plan.passes == 0)
+        return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
+                           tile_bits, perm, sorted_offsets, n, emit_keys, emit_ids, nullptr, PassPlan{}, stream);
+    // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them
+    st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
-    if (tile_plan.passes == 0) return ok();
+    st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
+                     perm, sorted_offsets, n, emit_keys, emit_ids, radix_histograms(scratch, n), tile_plan, stream);
+    if (st != GS_OK) return st;
     if (odd)
-        return radix_sort_pairs<uint64_t>(alt_keys, alt_ids, keys, flatten_ids, alt_keys, alt_ids, n, tile_plan,
-                                          scratch, stream, &in_b);
-    return radix_sort_pairs<uint64_t>(keys, flatten_ids, alt_keys, alt_ids, keys, flatten_ids, n, tile_plan, scratch,
+        return radix_passes<uint64_t>(alt_keys, alt_ids, keys, flatten_ids, alt_keys, alt_ids, n, tile_plan, scratch,
                                       stream, &in_b);
+    return radix_passes<uint64_t>(keys, flatten_ids, alt_keys, alt_ids, keys, flatten_ids, n, tile_plan, scratch,
+                                  stream, &in_b);
 }

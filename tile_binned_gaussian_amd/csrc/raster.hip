@@ -37,6 +37,27 @@ __device__ __forceinline__ float exp_neg(float sigma) {
     return __builtin_ldexpf(q, static_cast<int>(k));
 }
 
+// The same function without branches (a select replaces the early return), for lock-step loops where every lane
+// evaluates it anyway. Identical bits: the polynomial path is the one above, and any sigma that is not <= 80
+// (including NaN) selects 0.
+__device__ __forceinline__ float exp_neg_select(float sigma) {
+    const float t = -sigma;
+    const float k = __builtin_rintf(t * 0x1.715476p+0f);
+    float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);
+    r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);
+    float q = 0x1.a01a02p-13f;
+    q = __builtin_fmaf(q, r, 0x1.6c16c2p-10f);
+    q = __builtin_fmaf(q, r, 0x1.111112p-7f);
+    q = __builtin_fmaf(q, r, 0x1.555556p-5f);
+    q = __builtin_fmaf(q, r, 0x1.555556p-3f);
+    q = __builtin_fmaf(q, r, 0.5f);
+    q = __builtin_fmaf(q, r, 1.0f);
+    q = __builtin_fmaf(q, r, 1.0f);
+    const int ki = (sigma <= 80.0f) ? static_cast<int>(k) : 0;
+    const float e = __builtin_ldexpf(q, ki);
+    return (sigma <= 80.0f) ? e : 0.0f;
+}
+
 struct RasterArgs {
     const float2 *means;
     const float *conics;
@@ -166,6 +187,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         atomicAdd(&a.eval_counts[0], n_eval);
         atomicAdd(&a.eval_counts[1], n_pass);
         atomicAdd(&a.eval_counts[2], n_comp);
+        atomicAdd(&a.eval_counts[3], n_exec);
+        atomicAdd(&a.eval_counts[4], n_staged);
     }
 }
 
@@ -212,15 +235,16 @@ __device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c,
 }
 
 // Tiles up to 16x16, one pixel per thread. With 16x16 tiles each wave owns an 8x8 quadrant; otherwise pixels are
-// row-major and a wave's region is the rows it covers. Each staged splat carries a bit per wave telling whether its
-// alpha >= cutoff footprint can touch that wave's region (cull_box); a wave compacts the batch to the splats with
-// its bit set, in order, and evaluates only those. Skipped splats would have been skipped by the cutoff test at
-// every pixel of the region, so the result is the same to the bit.
+// row-major and a wave's region is the rows it covers. Each staged splat is one 48-byte LDS record (mean, conic,
+// opacity, intersection index, colour) plus a bit per wave telling whether its alpha >= cutoff footprint can touch
+// that wave's region (cull_box); a wave compacts the batch to the byte offsets of the records with its bit set, in
+// order, and evaluates only those. Skipped splats would have been skipped by the cutoff test at every pixel of the
+// region, so the result is the same to the bit. The evaluation loop runs in lock step without per-lane exits: a
+// pixel that stops only sets `done`, and the wave leaves the loop once every lane is done.
 template <int K, bool COUNT>
 __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) {
-    __shared__ float2 s_xy[kMaxThreads];
-    __shared__ float4 s_abco[kMaxThreads];
-    __shared__ float s_rgb[kMaxThreads * K];
+    constexpr int kRec = 12;  // floats per record: mx my a b | c o index - | colour[4]
+    __shared__ float4 s_rec[kMaxThreads * kRec / 4];
     __shared__ uint32_t s_mask[kMaxThreads];
     __shared__ uint16_t s_list[kMaxThreads / kWave][kMaxThreads];
 
@@ -280,6 +304,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     bool done = !inside;
     unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const char *rec_base = reinterpret_cast<const char *>(s_rec);
 
     for (int base = start; base < end; base += nthreads) {
         if (__syncthreads_and(done)) break;  // also orders the previous batch's LDS reads before refilling
@@ -290,10 +315,15 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
             const float2 m = a.means[g];
             const float *cg = a.conics + 3 * static_cast<int64_t>(g);
             const float ca = cg[0], cb = cg[1], cc = cg[2], o = a.opacities[g];
-            s_xy[threadIdx.x] = m;
-            s_abco[threadIdx.x] = make_float4(ca, cb, cc, o);
-#pragma unroll
-            for (int k = 0; k < K; ++k) s_rgb[threadIdx.x * K + k] = a.colors[static_cast<int64_t>(g) * K + k];
+            float4 col = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            const float *cs = a.colors + static_cast<int64_t>(g) * K;
+            col.x = cs[0];
+            if (K > 1) col.y = cs[1];
+            if (K > 2) col.z = cs[2];
+            if (K > 3) col.w = cs[3];
+            s_rec[threadIdx.x * 3 + 0] = make_float4(m.x, m.y, ca, cb);
+            s_rec[threadIdx.x * 3 + 1] = make_float4(cc, o, __int_as_float(idx), 0.0f);
+            s_rec[threadIdx.x * 3 + 2] = col;
             const CullBox box = cull_box(m, ca, cb, cc, o, a.alpha_cutoff, a.log_cutoff);
             uint32_t bits = 0;
             if (!box.never) {
@@ -307,41 +337,44 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
         }
         __syncthreads();
         const int count = end - base < nthreads ? end - base : nthreads;
-        // this wave's splats of the batch, in order
+        // this wave's splats of the batch, in order, as byte offsets of their records
         int listed = 0;
         for (int c0 = 0; c0 < count; c0 += kWave) {
             const int j = c0 + lane;
             const bool keep = j < count && ((s_mask[j] >> wave) & 1u);
             const uint64_t ballot = __ballot(keep);
-            if (keep) s_list[wave][listed + __popcll(ballot & lt_mask)] = static_cast<uint16_t>(j);
+            if (keep) s_list[wave][listed + __popcll(ballot & lt_mask)] = static_cast<uint16_t>(j * kRec * 4);
             listed += __popcll(ballot);
         }
-        if (done) continue;
         for (int jj = 0; jj < listed; ++jj) {
-            const int j = s_list[wave][jj];
-            if (COUNT) ++n_exec;
-            const float2 m = s_xy[j];
-            const float4 c = s_abco[j];
-            const float dx = m.x - px;
-            const float dy = m.y - py;
-            const float sigma = 0.5f * (c.x * dx * dx + c.z * dy * dy) + c.y * dx * dy;
-            if (sigma < 0.0f) continue;
-            float alpha = c.w * exp_neg(sigma);
-            if (alpha > a.alpha_clamp) alpha = a.alpha_clamp;
-            if (alpha < a.alpha_cutoff) continue;
-            if (COUNT) ++n_pass;
-            const float t_next = T * (1.0f - alpha);
-            if (t_next <= a.transmittance_threshold) {
-                done = true;
-                if (COUNT) stop = base + j + 1;
-                break;
+            if (__ballot(!done) == 0) break;
+            const char *rec = rec_base + s_list[wave][jj];
+            const float4 r0 = *reinterpret_cast<const float4 *>(rec);
+            const float2 r1 = *reinterpret_cast<const float2 *>(rec + 16);
+            const float dx = r0.x - px;
+            const float dy = r0.y - py;
+            const float sigma = 0.5f * (r0.z * dx * dx + r1.x * dy * dy) + r0.w * dx * dy;
+            float alpha = r1.y * exp_neg_select(sigma);
+            alpha = alpha > a.alpha_clamp ? a.alpha_clamp : alpha;
+            if (COUNT && !done) ++n_exec;
+            if (!done && !(sigma < 0.0f) && !(alpha < a.alpha_cutoff)) {
+                if (COUNT) ++n_pass;
+                const float t_next = T * (1.0f - alpha);
+                if (t_next <= a.transmittance_threshold) {
+                    done = true;
+                    if (COUNT) stop = __float_as_int(*reinterpret_cast<const float *>(rec + 24)) + 1;
+                } else {
+                    if (COUNT) ++n_comp;
+                    const float4 col = *reinterpret_cast<const float4 *>(rec + 32);
+                    const float v = alpha * T;
+                    acc[0] = acc[0] + col.x * v;
+                    if (K > 1) acc[1] = acc[1] + col.y * v;
+                    if (K > 2) acc[2] = acc[2] + col.z * v;
+                    if (K > 3) acc[3] = acc[3] + col.w * v;
+                    T = t_next;
+                    last = __float_as_int(*reinterpret_cast<const float *>(rec + 24));
+                }
             }
-            if (COUNT) ++n_comp;
-            const float v = alpha * T;
-#pragma unroll
-            for (int k = 0; k < K; ++k) acc[k] = acc[k] + s_rgb[j * K + k] * v;
-            T = t_next;
-            last = base + j;
         }
     }
 

@@ -55,41 +55,40 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_
     return before + inc - v;
 }
 
+// Digit histograms of every pass. Keys are read coalesced (lane-contiguous) into LDS, then each thread walks 16
+// consecutive keys and adds one count per run of equal digits, so keys that share digits (one splat's
+// intersections share their depth bits) cost one LDS atomic per run instead of one per key.
 template <typename KeyT>
 __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restrict__ keys, int64_t n,
                                                              PassPlan plan, uint32_t *__restrict__ hist) {
+    constexpr int kSkew = kItems + 1;  // row pitch of the transposed tile, breaks LDS bank conflicts
+    __shared__ KeyT s_keys[kThreads * kSkew];
     __shared__ uint32_t s_hist[kMaxPasses][kRadix];
     for (int p = 0; p < plan.passes; ++p) s_hist[p][threadIdx.x] = 0;
-    __syncthreads();
-    const int64_t start = static_cast<int64_t>(blockIdx.x) * kTile + static_cast<int64_t>(threadIdx.x) * kItems;
-    KeyT k[kItems];
-    int count = 0;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
+    const int valid = n - base < kTile ? static_cast<int>(n - base) : kTile;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        if (start + i < n) {
-            k[i] = keys[start + i];
-            count = i + 1;
-        } else {
-            k[i] = 0;
-        }
+        const int q = i * kThreads + threadIdx.x;  // coalesced
+        if (q < valid) s_keys[(q / kItems) * kSkew + (q % kItems)] = keys[base + q];
     }
+    __syncthreads();
+    const int first = threadIdx.x * kItems;
+    const int count = valid - first < kItems ? valid - first : kItems;
     if (count > 0) {
         for (int p = 0; p < plan.passes; ++p) {
             const int shift = plan.shift[p];
             const uint32_t mask = (1u << plan.bits[p]) - 1u;
-            uint32_t run_digit = digit_of(k[0], shift, mask);
+            uint32_t run_digit = digit_of(s_keys[threadIdx.x * kSkew], shift, mask);
             uint32_t run = 1;
-#pragma unroll
-            for (int i = 1; i < kItems; ++i) {
-                if (i < count) {
-                    const uint32_t d = digit_of(k[i], shift, mask);
-                    if (d == run_digit) {
-                        ++run;
-                    } else {
-                        atomicAdd(&s_hist[p][run_digit], run);
-                        run_digit = d;
-                        run = 1;
-                    }
+            for (int i = 1; i < count; ++i) {
+                const uint32_t d = digit_of(s_keys[threadIdx.x * kSkew + i], shift, mask);
+                if (d == run_digit) {
+                    ++run;
+                } else {
+                    atomicAdd(&s_hist[p][run_digit], run);
+                    run_digit = d;
+                    run = 1;
                 }
             }
             atomicAdd(&s_hist[p][run_digit], run);
@@ -107,11 +106,12 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restr
 // so (wave, item, lane) order is input order and the per-wave running counts give a stable rank.
 // ids_in == nullptr means the identity (id = input position). status[part][d] holds this pass's look-back
 // words; status_next[part][d] is cleared for the next pass.
-template <typename KeyT>
+template <typename KeyT, int kDigitBits>
 __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const KeyT *__restrict__ keys_in, const int32_t *__restrict__ ids_in, KeyT *__restrict__ keys_out,
-    int32_t *__restrict__ ids_out, int64_t n, int shift, int digit_bits, const uint32_t *__restrict__ hist,
+    int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ hist,
     uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next) {
+    constexpr int digit_bits = kDigitBits;
     __shared__ union {
         KeyT keys[kTile];
         int32_t ids[kTile];
@@ -138,19 +138,18 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     uint32_t unused_total;
     const uint32_t digit_global_start = block_exclusive_u32(hist[tid], s_tmp, &unused_total);
 
-    // load this wave's span
-    const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan;
+    // load this wave's span of keys (ids are loaded after the keys are written, to keep registers free)
+    const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan + lane;
+    const bool full = static_cast<int64_t>(part + 1) * kTile <= n;
     KeyT k[kItems];
-    int32_t v[kItems];
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const int64_t pos = base + i * kWave + lane;
-        if (pos < n) {
-            k[i] = keys_in[pos];
-            v[i] = ids_in ? ids_in[pos] : static_cast<int32_t>(pos);
-        } else {
-            k[i] = ~KeyT(0);  // past the end: largest digit, ranked after every real pair of this partition
-            v[i] = 0;
+        for (int i = 0; i < kItems; ++i) k[i] = keys_in[base + i * kWave];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+            const int64_t pos = base + i * kWave;
+            k[i] = pos < n ? keys_in[pos] : ~KeyT(0);  // past the end: largest digit, ranked after every real pair
         }
     }
 
@@ -160,12 +159,17 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const uint32_t d = digit_of(k[i], shift, digit_mask);
-        uint64_t same = ~0ull;
+        // lanes whose digit equals this lane's: for every bit, keep the lanes whose bit matches (ballot XNOR the
+        // lane's own bit spread over 32 bits), on both halves of the 64-lane mask
+        uint32_t same_lo = ~0u, same_hi = ~0u;
+#pragma unroll
         for (int b = 0; b < digit_bits; ++b) {
-            const bool bit = (d >> b) & 1u;
-            const uint64_t ballot = __ballot(bit);
-            same &= bit ? ballot : ~ballot;
+            const uint32_t spread = static_cast<uint32_t>(static_cast<int32_t>(d << (31 - b)) >> 31);
+            const uint64_t ballot = __ballot(spread != 0u);
+            same_lo &= ~(static_cast<uint32_t>(ballot) ^ spread);
+            same_hi &= ~(static_cast<uint32_t>(ballot >> 32) ^ spread);
         }
+        const uint64_t same = (static_cast<uint64_t>(same_hi) << 32) | same_lo;
         const uint32_t below = static_cast<uint32_t>(__popcll(same & lt_mask));
         const uint32_t run = s_wave_hist[wave][d];
         rank[i] = run + below;
@@ -242,18 +246,24 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         const KeyT key = s_buf.keys[q];
         const uint32_t dd = digit_of(key, shift, digit_mask);
         dst[i] = s_global_base[dd] + (static_cast<uint32_t>(q) - s_local_start[dd]);
-        if (q < valid) keys_out[dst[i]] = key;
+        if (full || q < valid) keys_out[dst[i]] = key;
+    }
+    // the ids follow through the same LDS bytes
+    int32_t v[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int64_t pos = base + i * kWave;
+        if (ids_in) v[i] = (full || pos < n) ? ids_in[pos] : 0;
+        else v[i] = static_cast<int32_t>(pos);
     }
     __syncthreads();
-
-    // the ids follow through the same LDS bytes
 #pragma unroll
     for (int i = 0; i < kItems; ++i) s_buf.ids[lp[i]] = v[i];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const int q = i * kThreads + tid;
-        if (q < valid) ids_out[dst[i]] = s_buf.ids[q];
+        if (full || q < valid) ids_out[dst[i]] = s_buf.ids[q];
     }
 }
 
@@ -291,10 +301,40 @@ SortScratchLayout sort_scratch_layout(int64_t n) {
     return L;
 }
 
+gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream) {
+    const SortScratchLayout L = sort_scratch_layout(n);
+    char *ws = static_cast<char *>(scratch);
+    GS_HIP_TRY(fill_u32(reinterpret_cast<uint32_t *>(ws + L.hist), 0, kMaxPasses * kRadix, stream));
+    GS_HIP_TRY(fill_u32(reinterpret_cast<uint32_t *>(ws + L.counters), 0, kMaxPasses, stream));
+    GS_HIP_TRY(fill_u32(reinterpret_cast<uint32_t *>(ws + L.status0), 0, static_cast<size_t>(L.parts) * kRadix,
+                        stream));
+    return ok();
+}
+
+uint32_t *radix_histograms(void *scratch, int64_t n) {
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + sort_scratch_layout(n).hist);
+}
+
 template <typename KeyT>
 gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                            KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
                            hipStream_t stream, int *result_in_b) {
+    *result_in_b = 0;
+    if (plan.passes == 0 || n < 1) return ok();
+    gs_status st = radix_prepare(n, scratch, stream);
+    if (st != GS_OK) return st;
+    const SortScratchLayout L = sort_scratch_layout(n);
+    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0, stream,
+                       keys_in, n, plan, radix_histograms(scratch, n));
+    GS_LAUNCH_TRY("histogram_kernel");
+    return radix_passes<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, scratch, stream,
+                              result_in_b);
+}
+
+template <typename KeyT>
+gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                       KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
+                       hipStream_t stream, int *result_in_b) {
     *result_in_b = 0;
     if (plan.passes == 0 || n < 1) return ok();
     const SortScratchLayout L = sort_scratch_layout(n);
@@ -302,14 +342,6 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
     uint32_t *status[2] = {reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1)};
-    const size_t status_words = static_cast<size_t>(L.parts) * kRadix;
-
-    GS_HIP_TRY(fill_u32(hist, 0, kMaxPasses * kRadix, stream));
-    GS_HIP_TRY(fill_u32(counters, 0, kMaxPasses, stream));
-    GS_HIP_TRY(fill_u32(status[0], 0, status_words, stream));
-    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0, stream,
-                       keys_in, n, plan, hist);
-    GS_LAUNCH_TRY("histogram_kernel");
 
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
@@ -319,9 +351,18 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
         int32_t *di = to_a ? buf_a_ids : buf_b_ids;
         uint32_t *st = status[p & 1];
         uint32_t *st_next = (p + 1 < plan.passes) ? status[(p + 1) & 1] : nullptr;
-        hipLaunchKernelGGL(onesweep_pass_kernel<KeyT>, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0,
-                           stream, src_k, src_i, dk, di, n, plan.shift[p], plan.bits[p], hist + p * kRadix,
-                           counters + p, st, st_next);
+        const dim3 grid(static_cast<unsigned>(L.parts)), block(kThreads);
+        const uint32_t *h = hist + p * kRadix;
+        switch (plan.bits[p]) {
+#define GS_PASS(B)                                                                                                  \
+    case B:                                                                                                         \
+        hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B>), grid, block, 0, stream, src_k, src_i, dk, di, n,       \
+                           plan.shift[p], h, counters + p, st, st_next);                                            \
+        break;
+            GS_PASS(1) GS_PASS(2) GS_PASS(3) GS_PASS(4) GS_PASS(5) GS_PASS(6) GS_PASS(7) GS_PASS(8)
+#undef GS_PASS
+            default: return fail(GS_ERR_INVALID_ARG, "radix pass of %d bits", plan.bits[p]);
+        }
         GS_LAUNCH_TRY("onesweep_pass_kernel");
         src_k = dk;
         src_i = di;
@@ -334,6 +375,8 @@ template gs_status radix_sort_pairs<uint32_t>(const uint32_t *, const int32_t *,
                                               int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
 template gs_status radix_sort_pairs<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
                                               int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
+template gs_status radix_passes<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
+                                          int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
 
 namespace {
 
