@@ -191,21 +191,40 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     uint32_t *my_status = status + static_cast<size_t>(part) * kRadix + d;
     atomic_store_agent(my_status, (part == 0 ? kFlagInclusive : kFlagAggregate) | part_count);
 
+    // issue the first look-back window now; its round trip overlaps the local reorder and the id loads below
+    uint32_t s[kLookWindow];
+    int64_t j = static_cast<int64_t>(part) - 1;
+#pragma unroll
+    for (int w = 0; w < kLookWindow; ++w)
+        s[w] = (j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d) : kFlagInclusive;
+
     uint32_t local_total;
     const uint32_t local_start = block_exclusive_u32(part_count, s_tmp, &local_total);
     s_local_start[d] = local_start;
+    __syncthreads();
 
-    // decoupled look-back for digit d: walk back over the predecessors' published counts, loading a window of
-    // kLookWindow of them at once, until one carries an inclusive count (partition 0 always does)
+    // reorder the partition's keys by digit through LDS (local positions need no global offsets)
+    uint32_t lp[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const uint32_t dd = digit_of(k[i], shift, digit_mask);
+        lp[i] = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
+        s_buf.keys[lp[i]] = k[i];
+    }
+    // the ids travel with the keys; load them while the look-back is in flight
+    int32_t v[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int64_t pos = base + i * kWave;
+        if (ids_in) v[i] = (full || pos < n) ? ids_in[pos] : 0;
+        else v[i] = static_cast<int32_t>(pos);
+    }
+
+    // decoupled look-back for digit d: walk back over the predecessors' published counts, a window of kLookWindow
+    // at a time, until one carries an inclusive count (partition 0 always does)
     uint32_t before = 0;
     if (part > 0) {
-        int64_t j = static_cast<int64_t>(part) - 1;
         while (true) {
-            uint32_t s[kLookWindow];
-#pragma unroll
-            for (int w = 0; w < kLookWindow; ++w)
-                s[w] = (j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d)
-                                    : kFlagInclusive;
             int used = 0;
             bool found = false;
 #pragma unroll
@@ -220,20 +239,14 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
             if (found) break;
             j -= used;
             if (used < kLookWindow) __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int w = 0; w < kLookWindow; ++w)
+                s[w] = (j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d)
+                                    : kFlagInclusive;
         }
         atomic_store_agent(my_status, kFlagInclusive | (before + part_count));
     }
     s_global_base[d] = digit_global_start + before;
-    __syncthreads();
-
-    // reorder the partition's keys by digit through LDS
-    uint32_t lp[kItems];
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const uint32_t dd = digit_of(k[i], shift, digit_mask);
-        lp[i] = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
-        s_buf.keys[lp[i]] = k[i];
-    }
     __syncthreads();
 
     // write keys: consecutive local positions of one digit go to consecutive global positions
@@ -249,13 +262,6 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         if (full || q < valid) keys_out[dst[i]] = key;
     }
     // the ids follow through the same LDS bytes
-    int32_t v[kItems];
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const int64_t pos = base + i * kWave;
-        if (ids_in) v[i] = (full || pos < n) ? ids_in[pos] : 0;
-        else v[i] = static_cast<int32_t>(pos);
-    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) s_buf.ids[lp[i]] = v[i];
