@@ -32,6 +32,10 @@ PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 #   alpha >= cutoff:  1 (1 - alpha) + 1 (T product) + 1 (threshold test) = 3
 #   composited:       1 (alpha T) + 2 K (colour multiply-add, unfused) = 7 for K = 3
 OPS_EVAL, OPS_PASS = 29, 3
+# HBM bytes the composite kernel moved per launch on the 1M-splat frame, from two profiler counter runs; valid only
+# while the kernel source is the one the counters were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "raster_cull_kernel_config3_hbm_traffic.txt")
+RASTER_SOURCE = os.path.join(ROOT, "tile_binned_gaussian_amd", "csrc", "raster.hip")
 
 WORKLOADS = {
     "tiny": "tiny: 1 camera, 256 splats, 64x64, tile 16",
@@ -74,6 +78,23 @@ def stage_bytes(scene, n, tile_passes, generic_passes):
         "composite": n * (4 + 8 + 12 + 4 + 4 * K) + pixels * (4 * K + 4 + 4 + 4),
         "generic_sort": n * 8 + generic_passes * n * 24 + (n * 24 if generic_passes % 2 else 0),
     }
+
+
+def measured_traffic(config):
+    """Counter-measured HBM bytes per composite launch, or None if there is no record for this workload or the
+    kernel source changed since the record was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = dict(line.split(":", 1) for line in f.read().splitlines() if ":" in line and not line.startswith(" "))
+        with open(RASTER_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    rec = {k.strip(): v.strip() for k, v in rec.items()}
+    if rec.get("workload") != config or rec.get("kernel_source_sha256") != sha:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(scene, stride):
@@ -165,7 +186,8 @@ def main():
     # pair); the other stages, several kernels each, are reported against HBM in "stages"
     roofline = {"bound": "alu", "kernel": "raster_cull_kernel", "achieved": round(comp_tops, 3),
                 "peak": round(PEAK_VALU_TOPS, 2), "unit": "Tops/s (FP32 VALU lane-ops)",
-                "frac": round(comp_tops / PEAK_VALU_TOPS, 4), "traffic": None}
+                "frac": round(comp_tops / PEAK_VALU_TOPS, 4), "traffic": measured_traffic(args.config),
+                "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": nbytes["composite"]}
 
     result = {
         "metric": METRIC,
