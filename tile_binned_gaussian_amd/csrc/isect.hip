@@ -10,6 +10,8 @@ namespace gs {
 namespace {
 
 constexpr int kThreads = 256;
+// emission workgroups: a few per CU, each striding over chunks of splats
+constexpr int kEmitBlocks = 2048;
 
 // Tile index from a floor/ceil result, clamped to [0, maximum] (gs_clamp_tile). The clamp is applied to the
 // float so NaN and values beyond int range are defined (NaN -> 0).
@@ -138,16 +140,19 @@ __global__ __launch_bounds__(kThreads) void offsets_kernel(const float2 *__restr
     if (j < M) gauss_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
 }
 
-// Phase 2: the workgroup takes 256 consecutive positions (splat perm[j], or j without a permutation); their
-// outputs occupy the contiguous slots [start(g0), start(g0 + 256)). Each thread walks slots with stride 256,
-// finds the owning position (the last one whose start is <= slot) by binary search in LDS, and writes key and
-// id for tile k of that splat's rectangle in row-major order.
+// Phase 2: a chunk is 256 consecutive positions (splat perm[j], or j without a permutation); their outputs occupy
+// the contiguous slots [start(g0), start(g0 + 256)). Each thread walks slots with stride 256, finds the owning
+// position (the last one whose start is <= slot) by binary search in LDS, and writes key and id for tile k of
+// that splat's rectangle in row-major order. With a permutation, sorted_depth[j] holds the depth bits of splat
+// perm[j] (read in order instead of gathered). Workgroups stride over chunks, so the digit histograms (hist
+// non-null) are flushed to global memory once per workgroup.
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict__ means,
                                                         const float *__restrict__ radii,
                                                         const uint32_t *__restrict__ depth_bits, int M, int N,
                                                         float ts, int tw, int th, int tile_bits,
                                                         const int32_t *__restrict__ perm,
+                                                        const uint32_t *__restrict__ sorted_depth,
                                                         const int32_t *__restrict__ gauss_offsets, int n,
                                                         uint64_t *__restrict__ keys, int32_t *__restrict__ ids,
                                                         uint32_t *__restrict__ hist, PassPlan hplan) {
@@ -155,52 +160,76 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
     __shared__ int s_start[kThreads + 1];
     __shared__ int s_x0[kThreads], s_y0[kThreads], s_w[kThreads], s_id[kThreads];
     __shared__ uint32_t s_upper_cam[kThreads], s_depth[kThreads];
-    const int g0 = blockIdx.x * kThreads;
-    const int j = g0 + threadIdx.x;
-    if (j < M) {
-        const int i = perm ? perm[j] : j;
-        const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
-        s_x0[threadIdx.x] = r.x0;
-        s_y0[threadIdx.x] = r.y0;
-        s_w[threadIdx.x] = r.x1 - r.x0;
-        s_start[threadIdx.x] = gauss_offsets[j];
-        s_depth[threadIdx.x] = depth_bits[i];
-        s_upper_cam[threadIdx.x] = static_cast<uint32_t>(i / N) << tile_bits;
-        s_id[threadIdx.x] = i;
-    } else {
-        s_start[threadIdx.x] = n;
-        s_w[threadIdx.x] = 1;
-        s_x0[threadIdx.x] = s_y0[threadIdx.x] = 0;
-        s_depth[threadIdx.x] = s_upper_cam[threadIdx.x] = 0;
-        s_id[threadIdx.x] = 0;
-    }
-    if (threadIdx.x == 0) s_start[kThreads] = (g0 + kThreads < M) ? gauss_offsets[g0 + kThreads] : n;
+    const int lane = __lane_id();
+    const uint64_t above_mask = lane == kWave - 1 ? 0ull : (~0ull << (lane + 1));
     if (hist)
         for (int p = 0; p < hplan.passes; ++p) s_hist[p][threadIdx.x] = 0;
-    __syncthreads();
-    // clamped to [0, n] so that offsets inconsistent with n can never address past the outputs
-    const int out_end = min(s_start[kThreads], n);
-    const int out_begin = min(s_start[0], out_end);
-    for (int slot = out_begin + static_cast<int>(threadIdx.x); slot < out_end; slot += kThreads) {
-        int lo = 0, hi = kThreads - 1;  // invariant: s_start[lo] <= slot, answer in [lo, hi]
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_start[mid] <= slot) lo = mid;
-            else hi = mid - 1;
+    const int chunks = (M + kThreads - 1) / kThreads;
+    for (int chunk = blockIdx.x; chunk < chunks; chunk += gridDim.x) {
+        const int g0 = chunk * kThreads;
+        const int j = g0 + threadIdx.x;
+        __syncthreads();  // the previous chunk's LDS reads are done
+        if (j < M) {
+            const int i = perm ? perm[j] : j;
+            const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
+            s_x0[threadIdx.x] = r.x0;
+            s_y0[threadIdx.x] = r.y0;
+            s_w[threadIdx.x] = r.x1 - r.x0;
+            s_start[threadIdx.x] = gauss_offsets[j];
+            s_depth[threadIdx.x] = sorted_depth ? sorted_depth[j] : depth_bits[i];
+            s_upper_cam[threadIdx.x] = static_cast<uint32_t>(i / N) << tile_bits;
+            s_id[threadIdx.x] = i;
+        } else {
+            s_start[threadIdx.x] = n;
+            s_w[threadIdx.x] = 1;
+            s_x0[threadIdx.x] = s_y0[threadIdx.x] = 0;
+            s_depth[threadIdx.x] = s_upper_cam[threadIdx.x] = 0;
+            s_id[threadIdx.x] = 0;
         }
-        const int k = slot - s_start[lo];
-        const int w = s_w[lo];
-        const int ry = k / w;
-        const int rx = k - ry * w;
-        const uint32_t tile = static_cast<uint32_t>(s_y0[lo] + ry) * static_cast<uint32_t>(tw) +
-                              static_cast<uint32_t>(s_x0[lo] + rx);
-        const uint64_t upper = static_cast<uint64_t>(s_upper_cam[lo] | tile);
-        const uint64_t key = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
-        keys[slot] = key;
-        ids[slot] = s_id[lo];
-        if (hist)
-            for (int p = 0; p < hplan.passes; ++p)
-                atomicAdd(&s_hist[p][static_cast<uint32_t>(key >> hplan.shift[p]) & ((1u << hplan.bits[p]) - 1u)], 1u);
+        if (threadIdx.x == 0) s_start[kThreads] = (g0 + kThreads < M) ? gauss_offsets[g0 + kThreads] : n;
+        __syncthreads();
+        // clamped to [0, n] so that offsets inconsistent with n can never address past the outputs
+        const int out_end = min(s_start[kThreads], n);
+        const int out_begin = min(s_start[0], out_end);
+        // every lane runs every round (the histogram's neighbour exchange needs the whole wave)
+        for (int round = out_begin; round < out_end; round += kThreads) {
+            const int slot = round + static_cast<int>(threadIdx.x);
+            const bool in = slot < out_end;
+            const int sl = in ? slot : out_end - 1;
+            int lo = 0, hi = kThreads - 1;  // invariant: s_start[lo] <= sl, answer in [lo, hi]
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_start[mid] <= sl) lo = mid;
+                else hi = mid - 1;
+            }
+            const int k = sl - s_start[lo];
+            const int w = s_w[lo];
+            const int ry = k / w;
+            const int rx = k - ry * w;
+            const uint32_t tile = static_cast<uint32_t>(s_y0[lo] + ry) * static_cast<uint32_t>(tw) +
+                                  static_cast<uint32_t>(s_x0[lo] + rx);
+            const uint64_t upper = static_cast<uint64_t>(s_upper_cam[lo] | tile);
+            const uint64_t key = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
+            if (in) {
+                keys[slot] = key;
+                ids[slot] = s_id[lo];
+            }
+            if (hist) {
+                // consecutive lanes hold consecutive slots: a run of equal digits adds its length once
+                for (int p = 0; p < hplan.passes; ++p) {
+                    const uint32_t d =
+                        in ? static_cast<uint32_t>(key >> hplan.shift[p]) & ((1u << hplan.bits[p]) - 1u) : 0xffffffffu;
+                    const uint32_t prev = __builtin_amdgcn_update_dpp(0xffffffffu, d, 0x138, 0xf, 0xf, false);
+                    const bool start = lane == 0 || d != prev;
+                    const uint64_t starts = __ballot(start);
+                    if (start && in) {
+                        const uint64_t later = starts & above_mask;
+                        const int next = later ? __builtin_ctzll(later) : kWave;
+                        atomicAdd(&s_hist[p][d], static_cast<uint32_t>(next - lane));
+                    }
+                }
+            }
+        }
     }
     // digit histograms of the keys just written, for the sort passes that follow
     if (hist) {
@@ -280,15 +309,17 @@ gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, fl
 
 // hist (nullable): accumulate the digit histograms of the emitted keys for the passes of hplan.
 gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
-                      int tw, int th, int tile_bits, const int32_t *perm, const int32_t *offsets, int n,
-                      uint64_t *keys, int32_t *ids, uint32_t *hist, const PassPlan &hplan, hipStream_t stream) {
-    const int blocks = (M + kThreads - 1) / kThreads;
+                      int tw, int th, int tile_bits, const int32_t *perm, const uint32_t *sorted_depth,
+                      const int32_t *offsets, int n, uint64_t *keys, int32_t *ids, uint32_t *hist,
+                      const PassPlan &hplan, hipStream_t stream) {
+    const int chunks = (M + kThreads - 1) / kThreads;
+    const int blocks = chunks < kEmitBlocks ? chunks : kEmitBlocks;
     if (rpg == 2)
         hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, offsets, n, keys, ids, hist, hplan);
     else
         hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, offsets, n, keys, ids, hist, hplan);
     GS_LAUNCH_TRY("emit_kernel");
     return ok();
 }
@@ -375,7 +406,8 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const int n = static_cast<int>(n_isects);
     if (!(sort && n > 1))  // emission in (camera, splat, tile row, tile column) order
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr, PassPlan{}, stream);
+                           tile_bits, nullptr, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr, PassPlan{},
+                           stream);
 
     // Sorted output. Splats are first put in stable (depth bits, flat id) order; emitting each splat's tiles in
     // that order makes the intersections ordered by (depth bits, id) already, so a stable sort of the camera and
@@ -388,6 +420,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
                                               stream, &in_b);
     if (st != GS_OK) return st;
     const int32_t *perm = at<int32_t>(workspace, in_b ? L.dids_b : L.dids_a);
+    const uint32_t *sorted_depth = at<uint32_t>(workspace, in_b ? L.dkeys_b : L.dkeys_a);
     int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
     st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, perm, nullptr,
                        at<int64_t>(workspace, L.block_sums), at<int64_t>(workspace, L.total), sorted_offsets, stream);
@@ -401,12 +434,14 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     int32_t *emit_ids = odd ? alt_ids : flatten_ids;
     if (tile_plan.passes == 0)
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, perm, sorted_offsets, n, emit_keys, emit_ids, nullptr, PassPlan{}, stream);
+                           tile_bits, perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, nullptr,
+                           PassPlan{}, stream);
     // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them
     st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
     st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
-                     perm, sorted_offsets, n, emit_keys, emit_ids, radix_histograms(scratch, n), tile_plan, stream);
+                     perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, radix_histograms(scratch, n), tile_plan,
+                     stream);
     if (st != GS_OK) return st;
     if (odd)
         return radix_passes<uint64_t>(alt_keys, alt_ids, keys, flatten_ids, alt_keys, alt_ids, n, tile_plan, scratch,

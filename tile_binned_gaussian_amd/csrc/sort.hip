@@ -55,43 +55,48 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_
     return before + inc - v;
 }
 
-// Digit histograms of every pass. Keys are read coalesced (lane-contiguous) into LDS, then each thread walks 16
-// consecutive keys and adds one count per run of equal digits, so keys that share digits (one splat's
-// intersections share their depth bits) cost one LDS atomic per run instead of one per key.
+constexpr int64_t kHistBlocks = 1024;
+
+// Digit histograms of every pass. Each thread holds 16 keys read lane-contiguous (consecutive lanes hold
+// consecutive keys). Per pass, a lane whose digit differs from the previous lane's starts a run, and only run
+// starts add to the LDS histogram (the run length), so keys that share digits - one splat's intersections share
+// their depth bits - cost one LDS atomic per run.
 template <typename KeyT>
 __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restrict__ keys, int64_t n,
                                                              PassPlan plan, uint32_t *__restrict__ hist) {
-    constexpr int kSkew = kItems + 1;  // row pitch of the transposed tile, breaks LDS bank conflicts
-    __shared__ KeyT s_keys[kThreads * kSkew];
     __shared__ uint32_t s_hist[kMaxPasses][kRadix];
     for (int p = 0; p < plan.passes; ++p) s_hist[p][threadIdx.x] = 0;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
-    const int valid = n - base < kTile ? static_cast<int>(n - base) : kTile;
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const int q = i * kThreads + threadIdx.x;  // coalesced
-        if (q < valid) s_keys[(q / kItems) * kSkew + (q % kItems)] = keys[base + q];
-    }
+    const int lane = __lane_id();
+    // bits above this lane, for the distance to the next run start
+    const uint64_t above_mask = lane == kWave - 1 ? 0ull : (~0ull << (lane + 1));
+    const int64_t tiles = (n + kTile - 1) / kTile;
     __syncthreads();
-    const int first = threadIdx.x * kItems;
-    const int count = valid - first < kItems ? valid - first : kItems;
-    if (count > 0) {
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int64_t base = tile * kTile;
+        const int valid = n - base < kTile ? static_cast<int>(n - base) : kTile;
+        KeyT k[kItems];
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+            const int q = i * kThreads + threadIdx.x;
+            k[i] = q < valid ? keys[base + q] : KeyT(0);
+        }
         for (int p = 0; p < plan.passes; ++p) {
             const int shift = plan.shift[p];
             const uint32_t mask = (1u << plan.bits[p]) - 1u;
-            uint32_t run_digit = digit_of(s_keys[threadIdx.x * kSkew], shift, mask);
-            uint32_t run = 1;
-            for (int i = 1; i < count; ++i) {
-                const uint32_t d = digit_of(s_keys[threadIdx.x * kSkew + i], shift, mask);
-                if (d == run_digit) {
-                    ++run;
-                } else {
-                    atomicAdd(&s_hist[p][run_digit], run);
-                    run_digit = d;
-                    run = 1;
+#pragma unroll
+            for (int i = 0; i < kItems; ++i) {
+                const bool in = i * kThreads + static_cast<int>(threadIdx.x) < valid;
+                const uint32_t d = in ? digit_of(k[i], shift, mask) : 0xffffffffu;
+                // the previous lane's digit (a whole-wave shift right by one lane; lane 0 keeps the all-ones value)
+                const uint32_t prev = __builtin_amdgcn_update_dpp(0xffffffffu, d, 0x138, 0xf, 0xf, false);
+                const bool start = lane == 0 || d != prev;
+                const uint64_t starts = __ballot(start);
+                if (start && in) {
+                    const uint64_t later = starts & above_mask;
+                    const int next = later ? __builtin_ctzll(later) : kWave;
+                    atomicAdd(&s_hist[p][d], static_cast<uint32_t>(next - lane));
                 }
             }
-            atomicAdd(&s_hist[p][run_digit], run);
         }
     }
     __syncthreads();
@@ -330,7 +335,10 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     gs_status st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
     const SortScratchLayout L = sort_scratch_layout(n);
-    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(static_cast<unsigned>(L.parts)), dim3(kThreads), 0, stream,
+    // a few workgroups per CU, each striding over many tiles, so that few per-workgroup flushes hit the 256 x
+    // passes global counters (contended device-scope atomics dominate when every tile flushes its own)
+    const unsigned hist_blocks = static_cast<unsigned>(L.parts < kHistBlocks ? L.parts : kHistBlocks);
+    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(hist_blocks), dim3(kThreads), 0, stream,
                        keys_in, n, plan, radix_histograms(scratch, n));
     GS_LAUNCH_TRY("histogram_kernel");
     return radix_passes<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, scratch, stream,
