@@ -1,11 +1,13 @@
 // Stable LSD radix sort of (key, int32 id) pairs on gfx950, onesweep style:
-//   1. one read of the keys builds every pass's digit histogram (each thread counts runs of equal digits over 16
-//      consecutive keys, so keys that share digits - e.g. one splat's intersections - cost one LDS atomic);
-//   2. one kernel per digit pass: a workgroup takes the next partition of 4096 pairs (dynamic index, so every
-//      predecessor is already running), ranks its keys stably with wave64 ballot matching, publishes its
-//      per-digit counts, resolves its global per-digit offsets by a decoupled look-back that inspects 8
-//      predecessors per load round, reorders the pairs through LDS by digit (keys first, then ids in the same
-//      LDS bytes) and writes runs of consecutive addresses.
+//   1. one read of the keys builds every pass's digit histogram (lanes holding consecutive keys compare digits
+//      with their neighbour and only the first lane of a run of equal digits adds to the LDS histogram, so keys
+//      that share digits - e.g. one splat's intersections - cost one LDS atomic per run);
+//   2. one kernel per digit pass: a workgroup takes the next partition (7168 pairs for 8-byte keys, 4096 for
+//      4-byte keys; dynamic index, so every predecessor is already running), ranks its keys stably with wave64
+//      ballot matching, publishes its per-digit counts, resolves its global per-digit offsets by a decoupled
+//      look-back (a window of predecessors per load round) that overlaps the LDS reorder and the id loads,
+//      reorders the pairs through LDS by digit (keys first, then ids in the same LDS bytes) and writes runs of
+//      consecutive addresses.
 // Only bits [begin_bit, end_bit) are sorted, split evenly into passes of at most 8 bits.
 //
 // Semantics: gsplat 1.0.0 native extension, intersections.c, gs_radix_sort_without_gvl (a stable LSD radix sort
@@ -17,14 +19,26 @@ namespace {
 
 constexpr int kThreads = 256;                 // 4 waves
 constexpr int kWaves = kThreads / kWave;
-constexpr int kItems = 16;                    // pairs per thread
-constexpr int kTile = kThreads * kItems;      // pairs per partition
-constexpr int kWaveSpan = kWave * kItems;     // contiguous pairs owned by one wave
 constexpr int kRadix = 256;
 constexpr uint32_t kFlagAggregate = 1u << 30; // partition's own count published
 constexpr uint32_t kFlagInclusive = 2u << 30; // count including every earlier partition published
 constexpr uint32_t kValueMask = (1u << 30) - 1;
-constexpr int kLookWindow = 8;                // predecessors inspected per look-back round
+
+// Partition shape of a digit pass per key type. 8-byte keys take larger partitions and a shorter look-back
+// window: fewer partitions in flight shorten the look-back walks, whose loads (device-coherent, ~1 us each under
+// load) dominate a partition's life. Measured on 13M frame keys: 28 items and window 4 beat 16 and 8 by ~10%.
+template <typename KeyT>
+struct Tiling {
+    static constexpr int items = sizeof(KeyT) == 8 ? 28 : 16;  // pairs per thread
+    static constexpr int tile = kThreads * items;              // pairs per partition
+    static constexpr int wave_span = kWave * items;            // contiguous pairs owned by one wave
+    static constexpr int window = sizeof(KeyT) == 8 ? 4 : 8;   // predecessors inspected per look-back round
+};
+// the smallest partition of any key type sizes the look-back arrays
+constexpr int kMinTile = kThreads * 16;
+// histogram kernel: keys per thread and per workgroup step
+constexpr int kHistItems = 16;
+constexpr int kHistTile = kThreads * kHistItems;
 
 __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -69,14 +83,14 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restr
     const int lane = __lane_id();
     // bits above this lane, for the distance to the next run start
     const uint64_t above_mask = lane == kWave - 1 ? 0ull : (~0ull << (lane + 1));
-    const int64_t tiles = (n + kTile - 1) / kTile;
+    const int64_t tiles = (n + kHistTile - 1) / kHistTile;
     __syncthreads();
     for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int64_t base = tile * kTile;
-        const int valid = n - base < kTile ? static_cast<int>(n - base) : kTile;
-        KeyT k[kItems];
+        const int64_t base = tile * kHistTile;
+        const int valid = n - base < kHistTile ? static_cast<int>(n - base) : kHistTile;
+        KeyT k[kHistItems];
 #pragma unroll
-        for (int i = 0; i < kItems; ++i) {
+        for (int i = 0; i < kHistItems; ++i) {
             const int q = i * kThreads + threadIdx.x;
             k[i] = q < valid ? keys[base + q] : KeyT(0);
         }
@@ -84,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restr
             const int shift = plan.shift[p];
             const uint32_t mask = (1u << plan.bits[p]) - 1u;
 #pragma unroll
-            for (int i = 0; i < kItems; ++i) {
+            for (int i = 0; i < kHistItems; ++i) {
                 const bool in = i * kThreads + static_cast<int>(threadIdx.x) < valid;
                 const uint32_t d = in ? digit_of(k[i], shift, mask) : 0xffffffffu;
                 // the previous lane's digit (a whole-wave shift right by one lane; lane 0 keeps the all-ones value)
@@ -106,8 +120,8 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restr
     }
 }
 
-// One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile); wave w owns the
-// contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at w*kWaveSpan + i*64 + l,
+// One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling<KeyT>);
+// wave w owns the contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at w*kWaveSpan + i*64 + l,
 // so (wave, item, lane) order is input order and the per-wave running counts give a stable rank.
 // ids_in == nullptr means the identity (id = input position). status[part][d] holds this pass's look-back
 // words; status_next[part][d] is cleared for the next pass.
@@ -117,6 +131,8 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ hist,
     uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next) {
     constexpr int digit_bits = kDigitBits;
+    constexpr int kItems = Tiling<KeyT>::items, kTile = Tiling<KeyT>::tile, kWaveSpan = Tiling<KeyT>::wave_span;
+    constexpr int kLookWindow = Tiling<KeyT>::window;
     __shared__ union {
         KeyT keys[kTile];
         int32_t ids[kTile];
@@ -297,7 +313,7 @@ PassPlan make_pass_plan(int begin_bit, int end_bit) {
 
 SortScratchLayout sort_scratch_layout(int64_t n) {
     SortScratchLayout L{};
-    L.parts = (n + kTile - 1) / kTile;
+    L.parts = (n + kMinTile - 1) / kMinTile;
     Carver c(nullptr);
     L.hist = 0;
     c.take<uint32_t>(kMaxPasses * kRadix);
@@ -334,10 +350,10 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     if (plan.passes == 0 || n < 1) return ok();
     gs_status st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
-    const SortScratchLayout L = sort_scratch_layout(n);
     // a few workgroups per CU, each striding over many tiles, so that few per-workgroup flushes hit the 256 x
     // passes global counters (contended device-scope atomics dominate when every tile flushes its own)
-    const unsigned hist_blocks = static_cast<unsigned>(L.parts < kHistBlocks ? L.parts : kHistBlocks);
+    const int64_t hist_tiles = (n + kHistTile - 1) / kHistTile;
+    const unsigned hist_blocks = static_cast<unsigned>(hist_tiles < kHistBlocks ? hist_tiles : kHistBlocks);
     hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(hist_blocks), dim3(kThreads), 0, stream,
                        keys_in, n, plan, radix_histograms(scratch, n));
     GS_LAUNCH_TRY("histogram_kernel");
@@ -365,7 +381,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
         int32_t *di = to_a ? buf_a_ids : buf_b_ids;
         uint32_t *st = status[p & 1];
         uint32_t *st_next = (p + 1 < plan.passes) ? status[(p + 1) & 1] : nullptr;
-        const dim3 grid(static_cast<unsigned>(L.parts)), block(kThreads);
+        const dim3 grid(static_cast<unsigned>((n + Tiling<KeyT>::tile - 1) / Tiling<KeyT>::tile)), block(kThreads);
         const uint32_t *h = hist + p * kRadix;
         switch (plan.bits[p]) {
 #define GS_PASS(B)                                                                                                  \
