@@ -34,8 +34,9 @@ struct Tiling {
     static constexpr int wave_span = kWave * items;            // contiguous pairs owned by one wave
     static constexpr int window = sizeof(KeyT) == 8 ? 4 : 8;   // predecessors inspected per look-back round
 };
-// the smallest partition of any key type sizes the look-back arrays
-constexpr int kMinTile = kThreads * 16;
+// the smallest partition of any key type sizes the look-back arrays (one status word per digit and partition)
+constexpr int kMinTile = Tiling<uint32_t>::tile < Tiling<uint64_t>::tile ? Tiling<uint32_t>::tile
+                                                                          : Tiling<uint64_t>::tile;
 // histogram kernel: keys per thread and per workgroup step
 constexpr int kHistItems = 16;
 constexpr int kHistTile = kThreads * kHistItems;
@@ -381,7 +382,11 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
         int32_t *di = to_a ? buf_a_ids : buf_b_ids;
         uint32_t *st = status[p & 1];
         uint32_t *st_next = (p + 1 < plan.passes) ? status[(p + 1) & 1] : nullptr;
-        const dim3 grid(static_cast<unsigned>((n + Tiling<KeyT>::tile - 1) / Tiling<KeyT>::tile)), block(kThreads);
+        const int64_t parts = (n + Tiling<KeyT>::tile - 1) / Tiling<KeyT>::tile;
+        if (parts > L.parts)  // the look-back arrays hold L.parts partitions of 256 words
+            return fail(GS_ERR_INVALID_ARG, "radix pass: %lld partitions exceed the look-back arrays (%lld)",
+                        (long long)parts, (long long)L.parts);
+        const dim3 grid(static_cast<unsigned>(parts)), block(kThreads);
         const uint32_t *h = hist + p * kRadix;
         switch (plan.bits[p]) {
 #define GS_PASS(B)                                                                                                  \
