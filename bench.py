@@ -26,7 +26,7 @@ METRIC = "isect keys sorted/s; rasterized Mpix/s (1M splats, 1920x1080, 1 GPU)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # non-packed FP32 VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T lane-operations per second
 PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# lane-operations per evaluation of the composite's definition (see DESIGN.md):
+# lane-operations per evaluation of the composite's definition:
 #   every evaluation: 2 (delta) + 9 (quadratic form) + 1 (sign test) + 14 (exponential incl. the >80 test)
 #                     + 1 (opacity product) + 1 (clamp) + 1 (cutoff test) = 29
 #   alpha >= cutoff:  1 (1 - alpha) + 1 (T product) + 1 (threshold test) = 3
