@@ -76,8 +76,14 @@ const char *gs_last_error(void);
  * tile_size   > 0 pixels; tile_width, tile_height > 0 tiles (any grid; not tied to an image size here)
  * Limits (GS_ERR_INVALID_ARG): C >= 1, N >= 0, C*N < 2^31, tile_width*tile_height < 2^31,
  *   tile_bits + camera_bits <= 32 (camera_bits = ceil(log2 C)), total intersections < 2^31 (phase 1 returns
- *   the error and still writes *n_isects_out), and with sort != 0 at most 2^30 - 1 intersections.
+ *   the error and still writes *n_isects_out), and with sort != 0 at most 2^30 - 1 splats and intersections.
  * workspace: gs_isect_workspace_bytes(C, N, n, tile_width, tile_height, sort) bytes; n = 0 sizes phase 1.
+ *   With sort != 0, phase 1 also puts the splats in (depth bits, id) order and computes each one's first output
+ *   slot in that order, into the first gs_isect_workspace_bytes(C, N, 0, tile_width, tile_height, 1) bytes of
+ *   the workspace; this work is queued behind the count's copy, so it runs while the count reaches the host.
+ *   Phase 2 must then receive a workspace that starts with those bytes unchanged: the same buffer (sized for
+ *   phase 2 from the start), or a larger one into which the caller copied them on the same stream. A workspace
+ *   without them gives a wrong order (never an access outside the buffers).
  */
 size_t gs_isect_workspace_bytes(int64_t C, int64_t N, int64_t n_isects, int tile_width, int tile_height, int sort);
 

@@ -80,7 +80,18 @@ def test_isect_argument_errors(lib):
     assert b"too large" in lib.gs_last_error()
     assert _isect(lib, N=4) == GS_ERR_INVALID_ARG  # required pointers missing
     assert _isect(lib, N=4, means2d=fake, radii=fake, depths=fake, goff=fake, nout=ctypes.byref(n_out),
+                  ws=None, wsb=0) == GS_ERR_INVALID_ARG  # counting needs tiles_per_gauss
+    assert b"tiles_per_gauss" in lib.gs_last_error()
+    assert _isect(lib, N=4, means2d=fake, radii=fake, depths=fake, goff=fake, tpg=fake, nout=ctypes.byref(n_out),
                   ws=None, wsb=0) == GS_ERR_WORKSPACE
+    # the sorted count phase needs the depth-order prefix: a workspace sized for the unsorted count is too small
+    small = lib.gs_isect_workspace_bytes(1, 4, 0, 4, 4, 0)
+    assert small < lib.gs_isect_workspace_bytes(1, 4, 0, 4, 4, 1)
+    assert _isect(lib, N=4, means2d=fake, radii=fake, depths=fake, goff=fake, tpg=fake, nout=ctypes.byref(n_out),
+                  ws=fake, wsb=small, sort=1) == GS_ERR_WORKSPACE
+    assert _isect(lib, C=2, N=1 << 29, means2d=fake, radii=fake, depths=fake, goff=fake, tpg=fake,
+                  nout=ctypes.byref(n_out), sort=1) == GS_ERR_INVALID_ARG
+    assert b"2^30 - 1 splats" in lib.gs_last_error()
     assert _isect(lib, N=4, means2d=fake, radii=fake, depths=fake, goff=fake, keys=fake, ids=fake, n=1 << 31,
                   ws=fake, wsb=1 << 40) == GS_ERR_INVALID_ARG
 

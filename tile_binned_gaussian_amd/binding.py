@@ -137,7 +137,11 @@ def gs_isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, s
         return Intersections(tiles_per, goff, keys, ids, n)
     need = lib.gs_isect_workspace_bytes(C, N, n, tile_width, tile_height, int(bool(sort)))
     if ws.numel() < need:
-        ws = _workspace(need, dev)
+        # phase 1 left the depth order at the start of the workspace; phase 2 reads it there
+        prefix = lib.gs_isect_workspace_bytes(C, N, 0, tile_width, tile_height, int(bool(sort)))
+        grown = _workspace(need, dev)
+        grown[:prefix].copy_(ws[:prefix])
+        ws = grown
     _check(lib.gs_isect_tiles(_ptr(means2d), _ptr(radii), rpg, _ptr(depths), C, N, tile_size, tile_width,
                               tile_height, int(bool(sort)), None, _ptr(goff), None, _ptr(keys), _ptr(ids), n,
                               _ptr(ws), ws.numel(), s))

@@ -81,22 +81,19 @@ __device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t *s_tmp, in
     return before + inc - v;
 }
 
-// Phase 1a: per-splat tile count, and one partial sum per workgroup. With `perm`, position j counts splat
-// perm[j] (the sum is then over that order) and tiles_per_gauss is not written.
+// Phase 1a: per-splat tile count, and one partial sum per workgroup.
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void count_kernel(const float2 *__restrict__ means,
                                                          const float *__restrict__ radii, int M, float ts, int tw,
-                                                         int th, const int32_t *__restrict__ perm,
-                                                         int32_t *__restrict__ tiles_per_gauss,
+                                                         int th, int32_t *__restrict__ tiles_per_gauss,
                                                          int64_t *__restrict__ block_sums) {
     __shared__ int64_t s_tmp[kThreads / kWave];
     const int j = blockIdx.x * kThreads + threadIdx.x;
     int64_t count = 0;
     if (j < M) {
-        const int i = perm ? perm[j] : j;
-        const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
+        const Rect r = rect_of<RPG>(means, radii, j, ts, tw, th);
         count = static_cast<int64_t>(r.x1 - r.x0) * static_cast<int64_t>(r.y1 - r.y0);
-        if (tiles_per_gauss) tiles_per_gauss[j] = static_cast<int32_t>(count);
+        tiles_per_gauss[j] = static_cast<int32_t>(count);
     }
     const int64_t total = block_sum(count, s_tmp);
     if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
@@ -119,25 +116,52 @@ __global__ __launch_bounds__(kThreads) void scan_block_sums_kernel(int64_t *__re
     if (threadIdx.x == 0) *total_out = carry;
 }
 
-// Phase 1c: per-position first output slot = workgroup prefix + exclusive scan of the counts within it (position
-// j holds splat perm[j], or j without a permutation).
-template <int RPG>
-__global__ __launch_bounds__(kThreads) void offsets_kernel(const float2 *__restrict__ means,
-                                                           const float *__restrict__ radii, int M, float ts, int tw,
-                                                           int th, const int32_t *__restrict__ perm,
+// Phase 1c: per-splat first output slot = workgroup prefix + exclusive scan of the counts within it (the counts
+// are read back from phase 1a, coalesced).
+__global__ __launch_bounds__(kThreads) void offsets_kernel(const int32_t *__restrict__ tiles_per_gauss, int M,
                                                            const int64_t *__restrict__ block_prefix,
                                                            int32_t *__restrict__ gauss_offsets) {
     __shared__ int64_t s_tmp[kThreads / kWave];
     const int j = blockIdx.x * kThreads + threadIdx.x;
-    int64_t count = 0;
-    if (j < M) {
-        const int i = perm ? perm[j] : j;
-        const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
-        count = static_cast<int64_t>(r.x1 - r.x0) * static_cast<int64_t>(r.y1 - r.y0);
-    }
+    const int64_t count = j < M ? static_cast<int64_t>(tiles_per_gauss[j]) : 0;
     int64_t unused;
     const int64_t ex = block_exclusive(count, s_tmp, &unused);
     if (j < M) gauss_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
+}
+
+// Count of splat i from the row-major offsets of phase 1 (the next splat's first slot minus its own; the last
+// splat ends at the total). i outside [0, M) - only possible with a corrupted workspace - counts 0.
+__device__ __forceinline__ int64_t count_from_offsets(const int32_t *__restrict__ gauss_offsets,
+                                                      const int64_t *__restrict__ total, int M, int i) {
+    if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) return 0;
+    const int64_t end = i + 1 < M ? static_cast<int64_t>(gauss_offsets[i + 1]) : *total;
+    return end - static_cast<int64_t>(gauss_offsets[i]);
+}
+
+// Counts in depth order: position j holds splat perm[j]; one partial sum per workgroup.
+__global__ __launch_bounds__(kThreads) void perm_count_kernel(const int32_t *__restrict__ perm,
+                                                              const int32_t *__restrict__ gauss_offsets,
+                                                              const int64_t *__restrict__ total, int M,
+                                                              int64_t *__restrict__ block_sums) {
+    __shared__ int64_t s_tmp[kThreads / kWave];
+    const int j = blockIdx.x * kThreads + threadIdx.x;
+    const int64_t count = j < M ? count_from_offsets(gauss_offsets, total, M, perm[j]) : 0;
+    const int64_t sum = block_sum(count, s_tmp);
+    if (threadIdx.x == 0) block_sums[blockIdx.x] = sum;
+}
+
+// First output slot per position in depth order: workgroup prefix + exclusive scan within the workgroup.
+__global__ __launch_bounds__(kThreads) void perm_offsets_kernel(const int32_t *__restrict__ perm,
+                                                                const int32_t *__restrict__ gauss_offsets,
+                                                                const int64_t *__restrict__ total, int M,
+                                                                const int64_t *__restrict__ block_prefix,
+                                                                int32_t *__restrict__ sorted_offsets) {
+    __shared__ int64_t s_tmp[kThreads / kWave];
+    const int j = blockIdx.x * kThreads + threadIdx.x;
+    const int64_t count = j < M ? count_from_offsets(gauss_offsets, total, M, perm[j]) : 0;
+    int64_t unused;
+    const int64_t ex = block_exclusive(count, s_tmp, &unused);
+    if (j < M) sorted_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
 }
 
 // Phase 2: a chunk is 256 consecutive positions (splat perm[j], or j without a permutation); their outputs occupy
@@ -170,7 +194,8 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
         const int j = g0 + threadIdx.x;
         __syncthreads();  // the previous chunk's LDS reads are done
         if (j < M) {
-            const int i = perm ? perm[j] : j;
+            int i = perm ? perm[j] : j;
+            if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) i = 0;  // only with a corrupted workspace
             const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
             s_x0[threadIdx.x] = r.x0;
             s_y0[threadIdx.x] = r.y0;
@@ -203,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                 else hi = mid - 1;
             }
             const int k = sl - s_start[lo];
-            const int w = s_w[lo];
+            const int w = max(s_w[lo], 1);  // a slot never maps to an empty rectangle unless offsets are corrupt
             const int ry = k / w;
             const int rx = k - ry * w;
             const uint32_t tile = static_cast<uint32_t>(s_y0[lo] + ry) * static_cast<uint32_t>(tw) +
@@ -241,11 +266,14 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
     }
 }
 
-// Workspace of gs_isect_tiles. Phase 1 uses the workgroup sums and the total. Phase 2 with sorting adds the
-// depth-ordered splat permutation (two u32/i32 ping-pong pairs of M), the per-position offsets in that order, the
-// alternate intersection buffers and the radix-sort scratch (sized for the larger of M and n).
+// Workspace of gs_isect_tiles. The prefix [0, prefix) depends on M and the sort flag only, so phase 1 and phase 2
+// see it at the same offsets: the workgroup sums, the total and, when sorting, the depth order of the splats
+// (two u32/i32 ping-pong pairs of M), the per-position offsets in that order and the depth sort's scratch. Phase 1
+// fills it; phase 2 reads it and adds, when sorting more than one intersection, the alternate intersection buffers
+// and the tile sort's scratch.
 struct IsectLayout {
-    size_t block_sums, total, dkeys_a, dids_a, dkeys_b, dids_b, sorted_offsets, alt_keys, alt_ids, scratch, bytes;
+    size_t block_sums, total, dkeys_a, dids_a, dkeys_b, dids_b, sorted_offsets, depth_scratch, prefix;
+    size_t alt_keys, alt_ids, tile_scratch, bytes;
 };
 
 IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
@@ -256,25 +284,31 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     c.take<int64_t>(static_cast<size_t>(blocks > 0 ? blocks : 1));
     L.total = align_up(c.used, 256);
     c.take<int64_t>(1);
-    L.bytes = align_up(c.used, 256);
+    if (sort) {
+        const size_t m = static_cast<size_t>(M > 0 ? M : 1);
+        L.dkeys_a = align_up(c.used, 256);
+        c.take<uint32_t>(m);
+        L.dids_a = align_up(c.used, 256);
+        c.take<int32_t>(m);
+        L.dkeys_b = align_up(c.used, 256);
+        c.take<uint32_t>(m);
+        L.dids_b = align_up(c.used, 256);
+        c.take<int32_t>(m);
+        L.sorted_offsets = align_up(c.used, 256);
+        c.take<int32_t>(m);
+        L.depth_scratch = align_up(c.used, 256);
+        c.take<char>(sort_scratch_layout(static_cast<int64_t>(m)).bytes);
+    }
+    L.prefix = L.bytes = align_up(c.used, 256);
     if (!(sort && n > 1)) return L;
-    const size_t m = static_cast<size_t>(M > 0 ? M : 1), nn = static_cast<size_t>(n);
-    L.dkeys_a = align_up(c.used, 256);
-    c.take<uint32_t>(m);
-    L.dids_a = align_up(c.used, 256);
-    c.take<int32_t>(m);
-    L.dkeys_b = align_up(c.used, 256);
-    c.take<uint32_t>(m);
-    L.dids_b = align_up(c.used, 256);
-    c.take<int32_t>(m);
-    L.sorted_offsets = align_up(c.used, 256);
-    c.take<int32_t>(m);
+    const size_t nn = static_cast<size_t>(n);
     L.alt_keys = align_up(c.used, 256);
     c.take<uint64_t>(nn);
     L.alt_ids = align_up(c.used, 256);
     c.take<int32_t>(nn);
-    L.scratch = align_up(c.used, 256);
-    L.bytes = L.scratch + sort_scratch_layout(M > n ? M : n).bytes;
+    L.tile_scratch = align_up(c.used, 256);
+    c.take<char>(sort_scratch_layout(n).bytes);
+    L.bytes = align_up(c.used, 256);
     return L;
 }
 
@@ -283,26 +317,22 @@ T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
-// count -> workgroup sums -> scan -> per-position offsets, over positions 0..M-1 in the order given by perm.
+// count -> workgroup sums -> scan -> per-splat offsets.
 gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, float ts, int tw, int th,
-                        const int32_t *perm, int32_t *tiles_per_gauss, int64_t *block_sums, int64_t *total,
-                        int32_t *offsets, hipStream_t stream) {
+                        int32_t *tiles_per_gauss, int64_t *block_sums, int64_t *total, int32_t *offsets,
+                        hipStream_t stream) {
     const int blocks = (M + kThreads - 1) / kThreads;
     if (rpg == 2)
-        hipLaunchKernelGGL(count_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th, perm,
+        hipLaunchKernelGGL(count_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
                            tiles_per_gauss, block_sums);
     else
-        hipLaunchKernelGGL(count_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th, perm,
+        hipLaunchKernelGGL(count_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
                            tiles_per_gauss, block_sums);
     GS_LAUNCH_TRY("count_kernel");
     hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks, total);
     GS_LAUNCH_TRY("scan_block_sums_kernel");
-    if (rpg == 2)
-        hipLaunchKernelGGL(offsets_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
-                           perm, block_sums, offsets);
-    else
-        hipLaunchKernelGGL(offsets_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
-                           perm, block_sums, offsets);
+    hipLaunchKernelGGL(offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream, tiles_per_gauss, M, block_sums,
+                       offsets);
     GS_LAUNCH_TRY("offsets_kernel");
     return ok();
 }
@@ -359,6 +389,8 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: camera bits %d + tile bits %d exceed the 32 upper key bits",
                     cam_bits, tile_bits);
     const int M = static_cast<int>(C * N);
+    if (sort && M >= (1 << 30))
+        return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: sorting supports at most 2^30 - 1 splats (C*N = %d)", M);
     if (M > 0 && (!means2d || !radii || !depths))
         return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: means2d, radii and depths are required");
     if (M > 0 && !gauss_offsets)
@@ -366,9 +398,15 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const float ts = static_cast<float>(tile_size);
     const float2 *m2 = reinterpret_cast<const float2 *>(means2d);
 
+    // the depth order of the splats lands in the B pair after an even number of 8-bit passes over 32 bits
+    const PassPlan depth_plan = make_pass_plan(0, 32);
+    const bool depth_in_b = depth_plan.passes % 2 == 0;
+
     if (keys == nullptr) {  // ---------------------------------------------------------------- phase 1: count
         if (!n_isects_out) return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: n_isects_out is required to count");
-        const IsectLayout L = isect_layout(M, 0, 0);
+        if (M > 0 && !tiles_per_gauss)
+            return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: tiles_per_gauss is required to count");
+        const IsectLayout L = isect_layout(M, 0, sort);
         if (!workspace || workspace_bytes < L.bytes)
             return fail(GS_ERR_WORKSPACE, "gs_isect_tiles: count needs %zu workspace bytes (got %zu)", L.bytes,
                         workspace_bytes);
@@ -377,13 +415,47 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             return ok();
         }
         int64_t *total = at<int64_t>(workspace, L.total);
-        gs_status st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, nullptr,
-                                     tiles_per_gauss, at<int64_t>(workspace, L.block_sums), total, gauss_offsets,
-                                     stream);
+        int64_t *block_sums = at<int64_t>(workspace, L.block_sums);
+        gs_status st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, tiles_per_gauss,
+                                     block_sums, total, gauss_offsets, stream);
         if (st != GS_OK) return st;
         int64_t host_total = 0;
-        GS_HIP_TRY(hipMemcpyAsync(&host_total, total, sizeof host_total, hipMemcpyDeviceToHost, stream));
-        GS_HIP_TRY(hipStreamSynchronize(stream));
+        hipEvent_t copied = nullptr;
+        GS_HIP_TRY(hipEventCreateWithFlags(&copied, hipEventDisableTiming));
+        hipError_t e = hipMemcpyAsync(&host_total, total, sizeof host_total, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipEventRecord(copied, stream);
+        if (e == hipSuccess && sort) {
+            // The depth order and the offsets in that order need only the splats: queue them behind the copy so
+            // the device works on them while the count travels to the host and the caller prepares phase 2.
+            const uint32_t *dbits = reinterpret_cast<const uint32_t *>(depths);
+            int in_b = 0;
+            st = radix_sort_pairs<uint32_t>(dbits, nullptr, at<uint32_t>(workspace, L.dkeys_a),
+                                            at<int32_t>(workspace, L.dids_a), at<uint32_t>(workspace, L.dkeys_b),
+                                            at<int32_t>(workspace, L.dids_b), M, depth_plan,
+                                            at<char>(workspace, L.depth_scratch), stream, &in_b);
+            const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
+            const int blocks = (M + kThreads - 1) / kThreads;
+            if (st == GS_OK) {
+                hipLaunchKernelGGL(perm_count_kernel, dim3(blocks), dim3(kThreads), 0, stream, perm, gauss_offsets,
+                                   total, M, block_sums);
+                e = hipGetLastError();
+            }
+            if (st == GS_OK && e == hipSuccess) {
+                // the scan rewrites the total with the same value (the same counts in another order)
+                hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks,
+                                   total);
+                e = hipGetLastError();
+            }
+            if (st == GS_OK && e == hipSuccess) {
+                hipLaunchKernelGGL(perm_offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream, perm, gauss_offsets,
+                                   total, M, block_sums, at<int32_t>(workspace, L.sorted_offsets));
+                e = hipGetLastError();
+            }
+        }
+        const hipError_t w = (e == hipSuccess) ? hipEventSynchronize(copied) : e;
+        (void)hipEventDestroy(copied);
+        if (st != GS_OK) return st;
+        if (w != hipSuccess) return fail(GS_ERR_DEVICE, "gs_isect_tiles: %s", hipGetErrorString(w));
         *n_isects_out = host_total;
         if (host_total >= (int64_t(1) << 31))
             return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: %lld intersections exceed the int32 offsets",
@@ -409,22 +481,14 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
                            tile_bits, nullptr, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr, PassPlan{},
                            stream);
 
-    // Sorted output. Splats are first put in stable (depth bits, flat id) order; emitting each splat's tiles in
-    // that order makes the intersections ordered by (depth bits, id) already, so a stable sort of the camera and
-    // tile bits [32, end_bit) alone completes the order by the whole key - the unique stable order by key.
-    void *scratch = at<char>(workspace, L.scratch);
-    int in_b = 0;
-    gs_status st = radix_sort_pairs<uint32_t>(dbits, nullptr, at<uint32_t>(workspace, L.dkeys_a),
-                                              at<int32_t>(workspace, L.dids_a), at<uint32_t>(workspace, L.dkeys_b),
-                                              at<int32_t>(workspace, L.dids_b), M, make_pass_plan(0, 32), scratch,
-                                              stream, &in_b);
-    if (st != GS_OK) return st;
-    const int32_t *perm = at<int32_t>(workspace, in_b ? L.dids_b : L.dids_a);
-    const uint32_t *sorted_depth = at<uint32_t>(workspace, in_b ? L.dkeys_b : L.dkeys_a);
-    int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
-    st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, perm, nullptr,
-                       at<int64_t>(workspace, L.block_sums), at<int64_t>(workspace, L.total), sorted_offsets, stream);
-    if (st != GS_OK) return st;
+    // Sorted output. Phase 1 put the splats in stable (depth bits, flat id) order and computed each position's
+    // first output slot in that order; emitting each splat's tiles in that order makes the intersections ordered
+    // by (depth bits, id) already, so a stable sort of the camera and tile bits [32, end_bit) alone completes the
+    // order by the whole key - the unique stable order by key.
+    const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
+    const uint32_t *sorted_depth = at<uint32_t>(workspace, depth_in_b ? L.dkeys_b : L.dkeys_a);
+    const int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
+    void *scratch = at<char>(workspace, L.tile_scratch);
     const PassPlan tile_plan = make_pass_plan(32, 32 + tile_bits + cam_bits);
     uint64_t *alt_keys = at<uint64_t>(workspace, L.alt_keys);
     int32_t *alt_ids = at<int32_t>(workspace, L.alt_ids);
@@ -437,12 +501,13 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
                            tile_bits, perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, nullptr,
                            PassPlan{}, stream);
     // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them
-    st = radix_prepare(n, scratch, stream);
+    gs_status st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
     st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
-                     perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, radix_histograms(scratch, n), tile_plan,
-                     stream);
+                     perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, radix_histograms(scratch, n),
+                     tile_plan, stream);
     if (st != GS_OK) return st;
+    int in_b = 0;
     if (odd)
         return radix_passes<uint64_t>(alt_keys, alt_ids, keys, flatten_ids, alt_keys, alt_ids, n, tile_plan, scratch,
                                       stream, &in_b);

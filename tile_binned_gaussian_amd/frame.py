@@ -85,7 +85,8 @@ class FramePlan:
                                      torch.empty((C, ds.height, ds.width), dtype=torch.float32, device=dev),
                                      torch.empty((C, ds.height, ds.width), dtype=torch.float32, device=dev),
                                      torch.empty((C, ds.height, ds.width), dtype=torch.int32, device=dev))
-        self.ws_count = torch.empty(max(self.lib.gs_isect_workspace_bytes(C, N, 0, ds.tile_width, ds.tile_height, 1),
+        # one intersection workspace for both phases: phase 1 leaves the depth order at its start for phase 2
+        self.ws_isect = torch.empty(max(self.lib.gs_isect_workspace_bytes(C, N, 0, ds.tile_width, ds.tile_height, 1),
                                         1), dtype=torch.uint8, device=dev)
         self.ws_ranges = torch.empty(self.lib.gs_tile_ranges_workspace_bytes(), dtype=torch.uint8, device=dev)
         self.ws_raster = torch.empty(max(self.lib.gs_rasterize_workspace_bytes(C, ds.tile_width, ds.tile_height), 1),
@@ -99,9 +100,11 @@ class FramePlan:
         dev = self.ds.means2d.device
         self.keys = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
         self.ids = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
-        self.ws_emit = torch.empty(max(self.lib.gs_isect_workspace_bytes(self.ds.C, self.ds.N, n, self.ds.tile_width,
-                                                                         self.ds.tile_height, 1), 1),
-                                   dtype=torch.uint8, device=dev)
+        need = self.lib.gs_isect_workspace_bytes(self.ds.C, self.ds.N, n, self.ds.tile_width, self.ds.tile_height, 1)
+        if need > self.ws_isect.numel():
+            grown = torch.empty(need, dtype=torch.uint8, device=dev)
+            grown[:self.ws_isect.numel()].copy_(self.ws_isect)
+            self.ws_isect = grown
         self.capacity = n
 
     def _count(self, s):
@@ -109,8 +112,8 @@ class FramePlan:
         n_out = ctypes.c_int64(0)
         binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
                                           ds.tile_size, ds.tile_width, ds.tile_height, 1, P(self.tiles_per),
-                                          P(self.goff), ctypes.byref(n_out), None, None, 0, P(self.ws_count),
-                                          self.ws_count.numel(), s))
+                                          P(self.goff), ctypes.byref(n_out), None, None, 0, P(self.ws_isect),
+                                          self.ws_isect.numel(), s))
         return int(n_out.value)
 
     def _emit(self, s, n, sort):
@@ -118,8 +121,8 @@ class FramePlan:
         if n > 0:
             binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
                                               ds.tile_size, ds.tile_width, ds.tile_height, int(sort), None,
-                                              P(self.goff), None, P(self.keys), P(self.ids), n, P(self.ws_emit),
-                                              self.ws_emit.numel(), s))
+                                              P(self.goff), None, P(self.keys), P(self.ids), n, P(self.ws_isect),
+                                              self.ws_isect.numel(), s))
 
     def run(self, events=None, eval_counts=None):
         """One frame. events: optional list of 5 torch.cuda.Event recorded before count, emit+sort, ranges and
