@@ -66,13 +66,12 @@ struct RasterArgs {
     const float *backgrounds;
     const int32_t *offsets;
     const int32_t *ids;
-    const int32_t *tile_order;  // nullable: launch order of tiles
     int64_t n_isects;
     int total_tiles, width, height, tile_size, tile_width, tile_height;
     float alpha_cutoff, alpha_clamp, transmittance_threshold;
     float *out_colors, *out_alphas, *out_T;
     int32_t *out_last;
-    unsigned long long *eval_counts;  // nullable: [evaluations, alpha >= cutoff, composited]
+    unsigned long long *eval_counts;  // nullable: the five work counts of the ABI
     float log_cutoff;                 // ln(alpha_cutoff), for the conservative cull
 };
 
@@ -82,7 +81,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float4 s_abco[kMaxThreads];
     __shared__ float s_rgb[kMaxThreads * K];
 
-    const int tile = a.tile_order ? a.tile_order[blockIdx.x] : static_cast<int>(blockIdx.x);
+    const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
     const int camera = tile / per_camera;
     const int local = tile - camera * per_camera;
@@ -192,26 +191,31 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     }
 }
 
-// Conservative cull of one splat against a wave's pixel region (pixel-centre box [x0, x1] x [y0, y1]). Returns
-// false only when alpha < cutoff at every pixel of the box, so skipping the splat there leaves every output bit
-// unchanged:
+// Conservative cull of one splat against a wave's pixel region (pixel-centre box [x0, x1] x [y0, y1]). The splat
+// is dropped for the region only when alpha < cutoff at every pixel of the box, so skipping it there leaves every
+// output bit unchanged:
 //  - opacity < cutoff: alpha = opacity * E(sigma) <= opacity since E(sigma) <= 1 for sigma >= 0;
-//  - otherwise alpha >= cutoff needs sigma_exact <= L = ln(opacity / cutoff) + 0.05, and {sigma <= L} lies inside
-//    |dx| <= sqrt(2 L S_xx), |dy| <= sqrt(2 L S_yy) with S = inverse of the conic (the marginal bound of a
-//    quadratic form). The 5% alpha margin covers float32 rounding: with trace^2 <= 1000 det the computed sigma is
-//    within 24 * 2^-24 * trace^2 / det < 0.15% of the exact one, E is within one ulp of e^-sigma, and
-//    0.9985 (ln(o / cutoff) + 0.05) > ln(o / cutoff) for every opacity up to 1e6; the box is padded for the rounding
-//    of its own arithmetic;
+//  - otherwise alpha >= cutoff needs sigma_exact <= L = ln(opacity / cutoff) + 0.05. The set {sigma <= L} lies
+//    inside |dx| <= sqrt(2 L S_xx), |dy| <= sqrt(2 L S_yy) with S = inverse of the conic (the marginal bound of a
+//    quadratic form): a box test first; then the minimum of sigma over the region's continuous box (no smaller
+//    than over its pixel centres) must not exceed thr = 1.004 L + 1e-3. The 5% alpha margin in L and the 0.4% in
+//    thr cover float32 rounding: with trace^2 <= 1000 det a computed sigma is within 24 * 2^-24 * trace^2 / det
+//    < 0.15% of the exact one, E is within one ulp of e^-sigma, the minimiser along an edge is found to within
+//    rounding (the quadratic is flat there, so the value moves by a second-order amount the 1e-3 covers), and
+//    0.9985 (ln(o / cutoff) + 0.05) > ln(o / cutoff) for every opacity up to 1e6; the box is padded for the
+//    rounding of its own arithmetic;
 //  - non-positive-definite, badly conditioned or non-finite conics, opacities above 1e6 or NaN, and means beyond
 //    1e6 pixels are never culled.
 struct CullBox {
     float x0, x1, y0, y1;  // bounding box of the alpha >= cutoff footprint, or +-inf when not culled
+    float thr, ra, rc;     // sigma bound for the region test and 1/a, 1/c (finite only when culled)
     bool never;            // the splat can reach the cutoff nowhere
+    bool exact;            // the region test applies
 };
 
 __device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c, float o, float alpha_cutoff,
                                            float log_cutoff) {
-    CullBox box{-INFINITY, INFINITY, -INFINITY, INFINITY, false};
+    CullBox box{-INFINITY, INFINITY, -INFINITY, INFINITY, 0.0f, 0.0f, 0.0f, false, false};
     if (o < alpha_cutoff) {
         box.never = true;
         return box;
@@ -231,7 +235,30 @@ __device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c,
     box.x1 = m.x + rx;
     box.y0 = m.y - ry;
     box.y1 = m.y + ry;
+    box.thr = 1.004f * L + 1.0e-3f;
+    box.ra = 1.0f / a;
+    box.rc = 1.0f / c;
+    box.exact = true;
     return box;
+}
+
+// sigma = 0.5 (a dx^2 + c dy^2) + b dx dy at an offset from the mean
+__device__ __forceinline__ float quad_form(float a, float b, float c, float dx, float dy) {
+    return 0.5f * (a * dx * dx + c * dy * dy) + b * dx * dy;
+}
+
+// Whether sigma can be <= thr somewhere in the box [x0, x1] x [y0, y1]: yes if the mean is inside; otherwise the
+// minimum of the convex quadratic lies on an edge, where it is a one-dimensional quadratic minimised at the
+// clamped stationary point.
+__device__ __forceinline__ bool region_reach(float2 m, float a, float b, float c, float ra, float rc, float thr,
+                                             float x0, float x1, float y0, float y1) {
+    if (m.x >= x0 && m.x <= x1 && m.y >= y0 && m.y <= y1) return true;
+    const float lx = x0 - m.x, hx = x1 - m.x, ly = y0 - m.y, hy = y1 - m.y;
+    float best = quad_form(a, b, c, lx, fminf(fmaxf(-b * lx * rc, ly), hy));
+    best = fminf(best, quad_form(a, b, c, hx, fminf(fmaxf(-b * hx * rc, ly), hy)));
+    best = fminf(best, quad_form(a, b, c, fminf(fmaxf(-b * ly * ra, lx), hx), ly));
+    best = fminf(best, quad_form(a, b, c, fminf(fmaxf(-b * hy * ra, lx), hx), hy));
+    return best <= thr;
 }
 
 // Tiles up to 16x16, one pixel per thread. With 16x16 tiles each wave owns an 8x8 quadrant; otherwise pixels are
@@ -248,7 +275,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     __shared__ uint32_t s_mask[kMaxThreads];
     __shared__ uint16_t s_list[kMaxThreads / kWave][kMaxThreads];
 
-    const int tile = a.tile_order ? a.tile_order[blockIdx.x] : static_cast<int>(blockIdx.x);
+    const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
     const int camera = tile / per_camera;
     const int local = tile - camera * per_camera;
@@ -329,7 +356,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
             if (!box.never) {
 #pragma unroll
                 for (int w = 0; w < kMaxThreads / kWave; ++w) {
-                    const bool touch = box.x1 >= rx0[w] && box.x0 <= rx1[w] && box.y1 >= ry0[w] && box.y0 <= ry1[w];
+                    bool touch = box.x1 >= rx0[w] && box.x0 <= rx1[w] && box.y1 >= ry0[w] && box.y0 <= ry1[w];
+                    if (touch && box.exact)
+                        touch = region_reach(m, ca, cb, cc, box.ra, box.rc, box.thr, rx0[w], rx1[w], ry0[w], ry1[w]);
                     bits |= (touch ? 1u : 0u) << w;
                 }
             }
@@ -465,7 +494,6 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
     args.backgrounds = backgrounds;
     args.offsets = isect_offsets;
     args.ids = flatten_ids;
-    args.tile_order = nullptr;
     args.n_isects = n_isects;
     args.total_tiles = static_cast<int>(total_tiles);
     args.width = width;
