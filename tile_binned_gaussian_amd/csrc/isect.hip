@@ -81,12 +81,13 @@ __device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t *s_tmp, in
     return before + inc - v;
 }
 
-// Phase 1a: per-splat tile count, and one partial sum per workgroup.
+// Phase 1a: per-splat tile count, and one partial sum per workgroup. rects (nullable) receives each splat's
+// rectangle as (x0, y0, width, height) in tiles, for the depth-ordered steps.
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void count_kernel(const float2 *__restrict__ means,
                                                          const float *__restrict__ radii, int M, float ts, int tw,
                                                          int th, int32_t *__restrict__ tiles_per_gauss,
-                                                         int64_t *__restrict__ block_sums) {
+                                                         int4 *__restrict__ rects, int64_t *__restrict__ block_sums) {
     __shared__ int64_t s_tmp[kThreads / kWave];
     const int j = blockIdx.x * kThreads + threadIdx.x;
     int64_t count = 0;
@@ -94,23 +95,46 @@ __global__ __launch_bounds__(kThreads) void count_kernel(const float2 *__restric
         const Rect r = rect_of<RPG>(means, radii, j, ts, tw, th);
         count = static_cast<int64_t>(r.x1 - r.x0) * static_cast<int64_t>(r.y1 - r.y0);
         tiles_per_gauss[j] = static_cast<int32_t>(count);
+        if (rects) rects[j] = make_int4(r.x0, r.y0, r.x1 - r.x0, r.y1 - r.y0);
     }
     const int64_t total = block_sum(count, s_tmp);
     if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
 }
 
-// Phase 1b: exclusive scan of the workgroup sums in place (one workgroup), total to *total_out.
+// Phase 1b: exclusive scan of the workgroup sums in place (one workgroup), total to *total_out. The sums pass
+// through LDS in chunks of 16 per thread: each thread adds its 16 consecutive values, one workgroup scan spreads
+// the partial sums, and each thread writes its 16 prefixes (LDS rows padded by one word against bank conflicts).
+constexpr int kScanPer = 16;
+constexpr int kScanChunk = kThreads * kScanPer;
+__device__ __forceinline__ int scan_slot(int i) { return i + i / kScanPer; }
+
 __global__ __launch_bounds__(kThreads) void scan_block_sums_kernel(int64_t *__restrict__ sums, int count,
                                                                    int64_t *__restrict__ total_out) {
+    __shared__ int64_t s_v[kScanChunk + kScanChunk / kScanPer];
     __shared__ int64_t s_tmp[kThreads / kWave];
     int64_t carry = 0;
-    for (int base = 0; base < count; base += kThreads) {
-        const int i = base + threadIdx.x;
-        const int64_t v = i < count ? sums[i] : 0;
-        int64_t chunk = 0;
-        const int64_t ex = block_exclusive(v, s_tmp, &chunk);
-        if (i < count) sums[i] = carry + ex;
-        carry += chunk;
+    for (int base = 0; base < count; base += kScanChunk) {
+        const int len = count - base < kScanChunk ? count - base : kScanChunk;
+        for (int i = threadIdx.x; i < len; i += kThreads) s_v[scan_slot(i)] = sums[base + i];
+        __syncthreads();
+        const int first = static_cast<int>(threadIdx.x) * kScanPer;
+        int64_t local = 0;
+#pragma unroll
+        for (int i = 0; i < kScanPer; ++i)
+            if (first + i < len) local += s_v[scan_slot(first + i)];
+        int64_t chunk_total;
+        int64_t run = carry + block_exclusive(local, s_tmp, &chunk_total);
+#pragma unroll
+        for (int i = 0; i < kScanPer; ++i) {
+            if (first + i < len) {
+                const int64_t v = s_v[scan_slot(first + i)];
+                s_v[scan_slot(first + i)] = run;
+                run += v;
+            }
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < len; i += kThreads) sums[base + i] = s_v[scan_slot(i)];
+        carry += chunk_total;
         __syncthreads();
     }
     if (threadIdx.x == 0) *total_out = carry;
@@ -129,36 +153,37 @@ __global__ __launch_bounds__(kThreads) void offsets_kernel(const int32_t *__rest
     if (j < M) gauss_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
 }
 
-// Count of splat i from the row-major offsets of phase 1 (the next splat's first slot minus its own; the last
-// splat ends at the total). i outside [0, M) - only possible with a corrupted workspace - counts 0.
-__device__ __forceinline__ int64_t count_from_offsets(const int32_t *__restrict__ gauss_offsets,
-                                                      const int64_t *__restrict__ total, int M, int i) {
-    if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) return 0;
-    const int64_t end = i + 1 < M ? static_cast<int64_t>(gauss_offsets[i + 1]) : *total;
-    return end - static_cast<int64_t>(gauss_offsets[i]);
-}
-
-// Counts in depth order: position j holds splat perm[j]; one partial sum per workgroup.
-__global__ __launch_bounds__(kThreads) void perm_count_kernel(const int32_t *__restrict__ perm,
-                                                              const int32_t *__restrict__ gauss_offsets,
-                                                              const int64_t *__restrict__ total, int M,
+// Depth order, step 1: position j holds splat perm[j]; its rectangle is gathered once into depth order and its
+// count summed per workgroup. A perm entry outside [0, M) - only possible with a corrupted workspace - gives an
+// empty rectangle.
+__global__ __launch_bounds__(kThreads) void perm_rects_kernel(const int32_t *__restrict__ perm,
+                                                              const int4 *__restrict__ rects, int M,
+                                                              int4 *__restrict__ sorted_rects,
                                                               int64_t *__restrict__ block_sums) {
     __shared__ int64_t s_tmp[kThreads / kWave];
     const int j = blockIdx.x * kThreads + threadIdx.x;
-    const int64_t count = j < M ? count_from_offsets(gauss_offsets, total, M, perm[j]) : 0;
+    int64_t count = 0;
+    if (j < M) {
+        const int i = perm[j];
+        const int4 r = static_cast<unsigned>(i) < static_cast<unsigned>(M) ? rects[i] : make_int4(0, 0, 0, 0);
+        sorted_rects[j] = r;
+        count = static_cast<int64_t>(r.z) * static_cast<int64_t>(r.w);
+    }
     const int64_t sum = block_sum(count, s_tmp);
     if (threadIdx.x == 0) block_sums[blockIdx.x] = sum;
 }
 
-// First output slot per position in depth order: workgroup prefix + exclusive scan within the workgroup.
-__global__ __launch_bounds__(kThreads) void perm_offsets_kernel(const int32_t *__restrict__ perm,
-                                                                const int32_t *__restrict__ gauss_offsets,
-                                                                const int64_t *__restrict__ total, int M,
+// Depth order, step 2: first output slot per position = workgroup prefix + exclusive scan within the workgroup.
+__global__ __launch_bounds__(kThreads) void perm_offsets_kernel(const int4 *__restrict__ sorted_rects, int M,
                                                                 const int64_t *__restrict__ block_prefix,
                                                                 int32_t *__restrict__ sorted_offsets) {
     __shared__ int64_t s_tmp[kThreads / kWave];
     const int j = blockIdx.x * kThreads + threadIdx.x;
-    const int64_t count = j < M ? count_from_offsets(gauss_offsets, total, M, perm[j]) : 0;
+    int64_t count = 0;
+    if (j < M) {
+        const int4 r = sorted_rects[j];
+        count = static_cast<int64_t>(r.z) * static_cast<int64_t>(r.w);
+    }
     int64_t unused;
     const int64_t ex = block_exclusive(count, s_tmp, &unused);
     if (j < M) sorted_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
@@ -168,8 +193,9 @@ __global__ __launch_bounds__(kThreads) void perm_offsets_kernel(const int32_t *_
 // the contiguous slots [start(g0), start(g0 + 256)). Each thread walks slots with stride 256, finds the owning
 // position (the last one whose start is <= slot) by binary search in LDS, and writes key and id for tile k of
 // that splat's rectangle in row-major order. With a permutation, sorted_depth[j] holds the depth bits of splat
-// perm[j] (read in order instead of gathered). Workgroups stride over chunks, so the digit histograms (hist
-// non-null) are flushed to global memory once per workgroup.
+// perm[j] (read in order instead of gathered), and sorted_rects[j] its rectangle, so no splat data is gathered.
+// Workgroups stride over chunks, so the digit histograms (hist non-null) are flushed to global memory once per
+// workgroup.
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict__ means,
                                                         const float *__restrict__ radii,
@@ -177,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                                                         float ts, int tw, int th, int tile_bits,
                                                         const int32_t *__restrict__ perm,
                                                         const uint32_t *__restrict__ sorted_depth,
+                                                        const int4 *__restrict__ sorted_rects,
                                                         const int32_t *__restrict__ gauss_offsets, int n,
                                                         uint64_t *__restrict__ keys, int32_t *__restrict__ ids,
                                                         uint32_t *__restrict__ hist, PassPlan hplan) {
@@ -196,10 +223,17 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
         if (j < M) {
             int i = perm ? perm[j] : j;
             if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) i = 0;  // only with a corrupted workspace
-            const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
-            s_x0[threadIdx.x] = r.x0;
-            s_y0[threadIdx.x] = r.y0;
-            s_w[threadIdx.x] = r.x1 - r.x0;
+            if (sorted_rects) {
+                const int4 r = sorted_rects[j];
+                s_x0[threadIdx.x] = r.x;
+                s_y0[threadIdx.x] = r.y;
+                s_w[threadIdx.x] = r.z;
+            } else {
+                const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
+                s_x0[threadIdx.x] = r.x0;
+                s_y0[threadIdx.x] = r.y0;
+                s_w[threadIdx.x] = r.x1 - r.x0;
+            }
             s_start[threadIdx.x] = gauss_offsets[j];
             s_depth[threadIdx.x] = sorted_depth ? sorted_depth[j] : depth_bits[i];
             s_upper_cam[threadIdx.x] = static_cast<uint32_t>(i / N) << tile_bits;
@@ -268,11 +302,13 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
 
 // Workspace of gs_isect_tiles. The prefix [0, prefix) depends on M and the sort flag only, so phase 1 and phase 2
 // see it at the same offsets: the workgroup sums, the total and, when sorting, the depth order of the splats
-// (two u32/i32 ping-pong pairs of M), the per-position offsets in that order and the depth sort's scratch. Phase 1
+// (two u32/i32 ping-pong pairs of M), the rectangles (row-major and in depth order), the per-position offsets in
+// that order and the depth sort's scratch. Phase 1
 // fills it; phase 2 reads it and adds, when sorting more than one intersection, the alternate intersection buffers
 // and the tile sort's scratch.
 struct IsectLayout {
-    size_t block_sums, total, dkeys_a, dids_a, dkeys_b, dids_b, sorted_offsets, depth_scratch, prefix;
+    size_t block_sums, total, dkeys_a, dids_a, dkeys_b, dids_b, rects, sorted_rects, sorted_offsets, depth_scratch,
+        prefix;
     size_t alt_keys, alt_ids, tile_scratch, bytes;
 };
 
@@ -294,6 +330,10 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
         c.take<uint32_t>(m);
         L.dids_b = align_up(c.used, 256);
         c.take<int32_t>(m);
+        L.rects = align_up(c.used, 256);
+        c.take<int4>(m);
+        L.sorted_rects = align_up(c.used, 256);
+        c.take<int4>(m);
         L.sorted_offsets = align_up(c.used, 256);
         c.take<int32_t>(m);
         L.depth_scratch = align_up(c.used, 256);
@@ -319,15 +359,15 @@ T *at(void *ws, size_t off) {
 
 // count -> workgroup sums -> scan -> per-splat offsets.
 gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, float ts, int tw, int th,
-                        int32_t *tiles_per_gauss, int64_t *block_sums, int64_t *total, int32_t *offsets,
-                        hipStream_t stream) {
+                        int32_t *tiles_per_gauss, int4 *rects, int64_t *block_sums, int64_t *total,
+                        int32_t *offsets, hipStream_t stream) {
     const int blocks = (M + kThreads - 1) / kThreads;
     if (rpg == 2)
         hipLaunchKernelGGL(count_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
-                           tiles_per_gauss, block_sums);
+                           tiles_per_gauss, rects, block_sums);
     else
         hipLaunchKernelGGL(count_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
-                           tiles_per_gauss, block_sums);
+                           tiles_per_gauss, rects, block_sums);
     GS_LAUNCH_TRY("count_kernel");
     hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks, total);
     GS_LAUNCH_TRY("scan_block_sums_kernel");
@@ -340,16 +380,16 @@ gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, fl
 // hist (nullable): accumulate the digit histograms of the emitted keys for the passes of hplan.
 gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
                       int tw, int th, int tile_bits, const int32_t *perm, const uint32_t *sorted_depth,
-                      const int32_t *offsets, int n, uint64_t *keys, int32_t *ids, uint32_t *hist,
-                      const PassPlan &hplan, hipStream_t stream) {
+                      const int4 *sorted_rects, const int32_t *offsets, int n, uint64_t *keys, int32_t *ids,
+                      uint32_t *hist, const PassPlan &hplan, hipStream_t stream) {
     const int chunks = (M + kThreads - 1) / kThreads;
     const int blocks = chunks < kEmitBlocks ? chunks : kEmitBlocks;
     if (rpg == 2)
         hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, sorted_depth, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, sorted_rects, offsets, n, keys, ids, hist, hplan);
     else
         hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, sorted_depth, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, sorted_rects, offsets, n, keys, ids, hist, hplan);
     GS_LAUNCH_TRY("emit_kernel");
     return ok();
 }
@@ -416,8 +456,9 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         }
         int64_t *total = at<int64_t>(workspace, L.total);
         int64_t *block_sums = at<int64_t>(workspace, L.block_sums);
+        int4 *rects = sort ? at<int4>(workspace, L.rects) : nullptr;
         gs_status st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, tiles_per_gauss,
-                                     block_sums, total, gauss_offsets, stream);
+                                     rects, block_sums, total, gauss_offsets, stream);
         if (st != GS_OK) return st;
         int64_t host_total = 0;
         hipEvent_t copied = nullptr;
@@ -436,8 +477,8 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
             const int blocks = (M + kThreads - 1) / kThreads;
             if (st == GS_OK) {
-                hipLaunchKernelGGL(perm_count_kernel, dim3(blocks), dim3(kThreads), 0, stream, perm, gauss_offsets,
-                                   total, M, block_sums);
+                hipLaunchKernelGGL(perm_rects_kernel, dim3(blocks), dim3(kThreads), 0, stream, perm, rects, M,
+                                   at<int4>(workspace, L.sorted_rects), block_sums);
                 e = hipGetLastError();
             }
             if (st == GS_OK && e == hipSuccess) {
@@ -447,8 +488,9 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
                 e = hipGetLastError();
             }
             if (st == GS_OK && e == hipSuccess) {
-                hipLaunchKernelGGL(perm_offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream, perm, gauss_offsets,
-                                   total, M, block_sums, at<int32_t>(workspace, L.sorted_offsets));
+                hipLaunchKernelGGL(perm_offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                                   at<int4>(workspace, L.sorted_rects), M, block_sums,
+                                   at<int32_t>(workspace, L.sorted_offsets));
                 e = hipGetLastError();
             }
         }
@@ -478,8 +520,8 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const int n = static_cast<int>(n_isects);
     if (!(sort && n > 1))  // emission in (camera, splat, tile row, tile column) order
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, nullptr, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr, PassPlan{},
-                           stream);
+                           tile_bits, nullptr, nullptr, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr,
+                           PassPlan{}, stream);
 
     // Sorted output. Phase 1 put the splats in stable (depth bits, flat id) order and computed each position's
     // first output slot in that order; emitting each splat's tiles in that order makes the intersections ordered
@@ -488,6 +530,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
     const uint32_t *sorted_depth = at<uint32_t>(workspace, depth_in_b ? L.dkeys_b : L.dkeys_a);
     const int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
+    const int4 *sorted_rects = at<int4>(workspace, L.sorted_rects);
     void *scratch = at<char>(workspace, L.tile_scratch);
     const PassPlan tile_plan = make_pass_plan(32, 32 + tile_bits + cam_bits);
     uint64_t *alt_keys = at<uint64_t>(workspace, L.alt_keys);
@@ -498,14 +541,14 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     int32_t *emit_ids = odd ? alt_ids : flatten_ids;
     if (tile_plan.passes == 0)
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, nullptr,
-                           PassPlan{}, stream);
+                           tile_bits, perm, sorted_depth, sorted_rects, sorted_offsets, n, emit_keys, emit_ids,
+                           nullptr, PassPlan{}, stream);
     // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them
     gs_status st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
     st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
-                     perm, sorted_depth, sorted_offsets, n, emit_keys, emit_ids, radix_histograms(scratch, n),
-                     tile_plan, stream);
+                     perm, sorted_depth, sorted_rects, sorted_offsets, n, emit_keys, emit_ids,
+                     radix_histograms(scratch, n), tile_plan, stream);
     if (st != GS_OK) return st;
     int in_b = 0;
     if (odd)

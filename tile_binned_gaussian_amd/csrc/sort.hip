@@ -331,11 +331,9 @@ SortScratchLayout sort_scratch_layout(int64_t n) {
 
 gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream) {
     const SortScratchLayout L = sort_scratch_layout(n);
-    char *ws = static_cast<char *>(scratch);
-    GS_HIP_TRY(fill_u32(reinterpret_cast<uint32_t *>(ws + L.hist), 0, kMaxPasses * kRadix, stream));
-    GS_HIP_TRY(fill_u32(reinterpret_cast<uint32_t *>(ws + L.counters), 0, kMaxPasses, stream));
-    GS_HIP_TRY(fill_u32(reinterpret_cast<uint32_t *>(ws + L.status0), 0, static_cast<size_t>(L.parts) * kRadix,
-                        stream));
+    // histograms, counters and the first look-back array are consecutive: one fill clears all three
+    const size_t words = L.status0 / sizeof(uint32_t) + static_cast<size_t>(L.parts) * kRadix;
+    GS_HIP_TRY(fill_u32(static_cast<uint32_t *>(scratch), 0, words, stream));
     return ok();
 }
 
