@@ -81,6 +81,8 @@ const char *gs_last_error(void);
  *   With sort != 0, phase 1 also puts the splats in (depth bits, id) order and computes each one's first output
  *   slot in that order, into the first gs_isect_workspace_bytes(C, N, 0, tile_width, tile_height, 1) bytes of
  *   the workspace; this work is queued behind the count's copy, so it runs while the count reaches the host.
+ *   When n_isects_out is page-locked host memory (hipHostMalloc, or a pinned torch tensor) the copy does not
+ *   block the host, so that work is queued before the host waits; with pageable memory the copy call waits.
  *   Phase 2 must then receive a workspace that starts with those bytes unchanged: the same buffer (sized for
  *   phase 2 from the start), or a larger one into which the caller copied them on the same stream. A workspace
  *   without them gives a wrong order (never an access outside the buffers).

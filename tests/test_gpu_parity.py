@@ -124,6 +124,53 @@ def test_frame_end_to_end(name):
     assert_raster_equal(scene, fr, ras_o, it_o.flatten_ids)
 
 
+@pytest.mark.parametrize("name", ["multicam-ragged-elliptical", "tiny", "ts8-margin", "one-isect", "empty"])
+def test_frame_plan_matches_oracle(name):
+    """The preallocated frame path bench.py times: the count read back into page-locked memory (the depth order
+    queued before the host waits), one intersection workspace shared by both phases and grown once, and repeated
+    frames reusing every buffer."""
+    from tile_binned_gaussian_amd import frame
+    scene = SCENES[name]()
+    it_o, off_o, ras_o = oracle.scene_pipeline(scene)
+    plan = frame.FramePlan(frame.to_device(scene))
+    for _ in range(3):
+        n = plan.run()
+        torch.cuda.synchronize()
+        assert n == it_o.n_isects
+        np.testing.assert_array_equal(keys_u64(plan.keys)[:n], it_o.keys)
+        np.testing.assert_array_equal(host(plan.ids)[:n], it_o.flatten_ids)
+        np.testing.assert_array_equal(host(plan.offsets), off_o)
+        fr = frame.FrameResult(binding.Intersections(plan.tiles_per, plan.goff, plan.keys[:n], plan.ids[:n], n),
+                               plan.offsets, plan.render)
+        assert_raster_equal(scene, fr, ras_o, it_o.flatten_ids)
+
+
+def test_count_into_pageable_and_pinned_memory_agree():
+    """Phase 1 writes the same count through both readback paths (pageable: the copy waits; page-locked: the
+    copy is asynchronous and the host waits on an event)."""
+    import ctypes
+    scene = SCENES["multicam-ragged-elliptical"]()
+    lib = binding.load_library()
+    m, r, d = dev(scene.means2d), dev(scene.radii), dev(scene.depths)
+    C, N = scene.C, scene.N
+    rpg = 2 if scene.radii.ndim == 3 else 1
+    ws = torch.empty(lib.gs_isect_workspace_bytes(C, N, 0, scene.tile_width, scene.tile_height, 1),
+                     dtype=torch.uint8, device="cuda")
+    tpg = torch.empty((C, N), dtype=torch.int32, device="cuda")
+    goff = torch.empty(C * N, dtype=torch.int32, device="cuda")
+    s = binding._stream(None)
+    pageable = ctypes.c_int64(-1)
+    pinned = torch.full((1,), -1, dtype=torch.int64, pin_memory=True)
+    for out in (ctypes.byref(pageable), binding._ptr(pinned)):
+        binding._check(lib.gs_isect_tiles(binding._ptr(m), binding._ptr(r), rpg, binding._ptr(d), C, N,
+                                          scene.tile_size, scene.tile_width, scene.tile_height, 1, binding._ptr(tpg),
+                                          binding._ptr(goff), out, None, None, 0, binding._ptr(ws), ws.numel(), s))
+    expected = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                                  scene.tile_height, sort=True).n_isects
+    assert pageable.value == expected
+    assert int(pinned[0]) == expected
+
+
 def test_frame_is_deterministic():
     scene = SCENES["multicam-ragged-elliptical"]()
     a, b = gpu_frame(scene), gpu_frame(scene)

@@ -352,6 +352,16 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     return L;
 }
 
+// Whether p is page-locked host memory the device can write directly (a copy into it does not block the host).
+bool pinned_host(const void *p) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();  // an unknown host pointer is not an error here
+        return false;
+    }
+    return attr.type == hipMemoryTypeHost;
+}
+
 template <typename T>
 T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
@@ -460,10 +470,14 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         gs_status st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, tiles_per_gauss,
                                      rects, block_sums, total, gauss_offsets, stream);
         if (st != GS_OK) return st;
+        // Into page-locked memory the copy is asynchronous, so the depth-order work below is queued before the
+        // host waits; into pageable memory the copy call itself waits for the count.
+        const bool pinned = pinned_host(n_isects_out);
         int64_t host_total = 0;
         hipEvent_t copied = nullptr;
         GS_HIP_TRY(hipEventCreateWithFlags(&copied, hipEventDisableTiming));
-        hipError_t e = hipMemcpyAsync(&host_total, total, sizeof host_total, hipMemcpyDeviceToHost, stream);
+        hipError_t e = hipMemcpyAsync(pinned ? n_isects_out : &host_total, total, sizeof host_total,
+                                      hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess) e = hipEventRecord(copied, stream);
         if (e == hipSuccess && sort) {
             // The depth order and the offsets in that order need only the splats: queue them behind the copy so
@@ -498,6 +512,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         (void)hipEventDestroy(copied);
         if (st != GS_OK) return st;
         if (w != hipSuccess) return fail(GS_ERR_DEVICE, "gs_isect_tiles: %s", hipGetErrorString(w));
+        if (pinned) host_total = *static_cast<volatile int64_t *>(n_isects_out);
         *n_isects_out = host_total;
         if (host_total >= (int64_t(1) << 31))
             return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: %lld intersections exceed the int32 offsets",

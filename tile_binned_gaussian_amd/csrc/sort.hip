@@ -27,12 +27,14 @@ constexpr uint32_t kValueMask = (1u << 30) - 1;
 // Partition shape of a digit pass per key type. 8-byte keys take larger partitions and a shorter look-back
 // window: fewer partitions in flight shorten the look-back walks, whose loads (device-coherent, ~1 us each under
 // load) dominate a partition's life. Measured on 13M frame keys: 28 items and window 4 beat 16 and 8 by ~10%.
+// 4-byte keys sort the splats' depths (about a million, every partition in flight at once): 16 items and window 4
+// measured best there (windows 8, 16 and 32 and 24 or 32 items were 2-25% slower).
 template <typename KeyT>
 struct Tiling {
     static constexpr int items = sizeof(KeyT) == 8 ? 28 : 16;  // pairs per thread
     static constexpr int tile = kThreads * items;              // pairs per partition
     static constexpr int wave_span = kWave * items;            // contiguous pairs owned by one wave
-    static constexpr int window = sizeof(KeyT) == 8 ? 4 : 8;   // predecessors inspected per look-back round
+    static constexpr int window = 4;                            // predecessors inspected per look-back round
 };
 // the smallest partition of any key type sizes the look-back arrays (one status word per digit and partition)
 constexpr int kMinTile = Tiling<uint32_t>::tile < Tiling<uint64_t>::tile ? Tiling<uint32_t>::tile

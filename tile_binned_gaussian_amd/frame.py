@@ -91,6 +91,8 @@ class FramePlan:
         self.ws_ranges = torch.empty(self.lib.gs_tile_ranges_workspace_bytes(), dtype=torch.uint8, device=dev)
         self.ws_raster = torch.empty(max(self.lib.gs_rasterize_workspace_bytes(C, ds.tile_width, ds.tile_height), 1),
                                      dtype=torch.uint8, device=dev)
+        # page-locked host word for the intersection count (the device writes it without blocking the host)
+        self.n_host = torch.zeros(1, dtype=torch.int64, pin_memory=True)
         self.capacity = -1
         self.n_isects = 0
 
@@ -109,12 +111,11 @@ class FramePlan:
 
     def _count(self, s):
         ds, lib, P = self.ds, self.lib, binding._ptr
-        n_out = ctypes.c_int64(0)
         binding._check(lib.gs_isect_tiles(P(ds.means2d), P(ds.radii), self.rpg, P(ds.depths), ds.C, ds.N,
                                           ds.tile_size, ds.tile_width, ds.tile_height, 1, P(self.tiles_per),
-                                          P(self.goff), ctypes.byref(n_out), None, None, 0, P(self.ws_isect),
+                                          P(self.goff), P(self.n_host), None, None, 0, P(self.ws_isect),
                                           self.ws_isect.numel(), s))
-        return int(n_out.value)
+        return int(self.n_host[0])
 
     def _emit(self, s, n, sort):
         ds, lib, P = self.ds, self.lib, binding._ptr
