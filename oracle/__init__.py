@@ -63,6 +63,9 @@ def _load():
                                            P]
         lib.orc_rasterize_tile.restype = I64
         lib.orc_rects.argtypes, lib.orc_rects.restype = [P, P, I32, I64, I32, I32, I32, P], None
+        lib.orc_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F,
+                                          P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.orc_rasterize_bwd.restype = I32
         _lib = lib
     return _lib
 
@@ -256,6 +259,48 @@ def rects(means2d, radii, tile_size, tile_width, tile_height):
     _load().orc_rects(_p(means2d), _p(radii), 2 if radii.ndim == 3 else 1, M, tile_size, tile_width, tile_height,
                       _p(out))
     return out
+
+
+@dataclass
+class RasterGrad:
+    """Gradients of L = sum(grad_colors * render_colors) + sum(grad_alphas * render_alphas) (float64 sums of the
+    float32 terms) and, per entry, the sum of the terms' magnitudes (abs_*)."""
+    means2d: np.ndarray  # [C, N, 2]
+    conics: np.ndarray  # [C, N, 3]
+    colors: np.ndarray  # [C, N, K]
+    opacities: np.ndarray  # [C, N]
+    backgrounds: np.ndarray | None  # [C, K]
+    means2d_abs: np.ndarray  # [C, N, 2]
+    abs_means2d: np.ndarray
+    abs_conics: np.ndarray
+    abs_colors: np.ndarray
+    abs_opacities: np.ndarray
+    abs_backgrounds: np.ndarray | None
+
+
+def rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
+                  flatten_ids, n_isects, alpha_cutoff, alpha_clamp, render_alphas, last_ids, grad_colors,
+                  grad_alphas) -> RasterGrad:
+    """Backward of the composite over every tile (orc_rasterize_bwd)."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    C, N = means2d.shape[0], means2d.shape[1]
+    K = colors.shape[-1]
+    off = _c(isect_offsets, np.int32)
+    th, tw = off.shape[1], off.shape[2]
+    bg = None if backgrounds is None else _c(backgrounds, np.float32)
+    z = lambda *shape: np.zeros(shape, np.float64)  # noqa: E731
+    g = [z(C, N, 2), z(C, N, 3), z(C, N, K), z(C, N), None if bg is None else z(C, K), z(C, N, 2)]
+    a = [z(C, N, 2), z(C, N, 3), z(C, N, K), z(C, N), None if bg is None else z(C, K)]
+    rc = lib.orc_rasterize_bwd(_p(means2d), _p(_c(conics, np.float32)), _p(_c(colors, np.float32)),
+                               _p(_c(opacities, np.float32)), _p(bg), C, N, K, width, height, tile_size, tw, th,
+                               _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects), float(alpha_cutoff),
+                               float(alpha_clamp), _p(_c(render_alphas, np.float32)), _p(_c(last_ids, np.int32)),
+                               _p(_c(grad_colors, np.float32)), _p(_c(grad_alphas, np.float32)),
+                               *[_p(x) for x in g], *[_p(x) for x in a])
+    if rc != 0:
+        raise ValueError("invalid rasterize backward arguments")
+    return RasterGrad(*g, *a)
 
 
 def scene_pipeline(scene, sort=True):

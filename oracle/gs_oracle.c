@@ -14,6 +14,7 @@
  *            front-to-back inverse of that backward.
  *   [rlx-metal] rlx-metal 0.2.9 splat_training.rs, training_forward_metal_traced: names alpha_cutoff and
  *            transmittance_threshold as forward parameters, and a cutoff default of 1/255.
+ *   The composite's backward (orc_rasterize_bwd) follows [gsplat-bwd] gs_raster_backward_pixel directly.
  *
  * Arithmetic: float32 wherever the pages compute in float (all of the above do), evaluated in the pages'
  * expression order with no contraction (build with -ffp-contract=off, never -ffast-math); fmaf appears only
@@ -370,6 +371,119 @@ int64_t orc_rasterize_tile(const float *means2d, const float *conics, const floa
         }
     }
     return n_eval;
+}
+
+/* Backward of the composite ([gsplat-bwd] gs_raster_backward_pixel and gs_raster_backward_without_gvl), for the
+ * loss L = sum over pixels of <grad_colors_px, colour> + grad_alphas_px * alpha.
+ *
+ * Per pixel, from the forward's outputs: T = 1 - render_alpha (the final transmittance), after = 1 (the
+ * transmittance behind the splat being visited), rest[k] = background[k] (the colour seen behind it). The
+ * background term is grad_colour[k] * T. Then the tile's range is walked back to front; position i with splat
+ * g counts when render_alpha > 0, sigma >= 0, alpha >= cutoff, i <= last_id, T < 1 and alpha < 1, with sigma,
+ * the response E(sigma) (orc_exp_neg, the same as the forward's), raw = opacity * E and alpha = min(clamp, raw)
+ * recomputed as in the forward. For a counted splat, in float32 and this order:
+ *   before = T / (1 - alpha);  vis = before * alpha;
+ *   colour term k: grad_colour[k] * vis;  dot = sum_k grad_colour[k] * (colour[k] - rest[k]);
+ *   g_alpha = before * (dot + grad_alpha * after);  g_raw = raw < clamp ? g_alpha : 0;
+ *   opacity term: g_raw * E;  g_sigma = -g_raw * raw;
+ *   mean terms: g_sigma * (a dx + b dy), g_sigma * (c dy + b dx);  conic terms: g_sigma * 0.5 * dx * dx,
+ *   g_sigma * dx * dy, g_sigma * 0.5 * dy * dy;  then rest[k] = alpha * colour[k] + (1 - alpha) * rest[k],
+ *   after *= 1 - alpha, T = before.
+ * The pages add the terms into float arrays in an order their threads leave open; here each float term is added
+ * into double accumulators (the sum of the terms up to double rounding), and abs_* (nullable) receive the sums of
+ * the terms' magnitudes, which bound what any float summation order can change. g_means_abs (nullable) receives
+ * |mean term| per axis. g_bg and abs_bg may be NULL (no background gradient). Masks are not supported.
+ * Returns 0, or -1 for a bad argument. */
+int orc_rasterize_bwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
+                      const float *backgrounds, int64_t C, int64_t N, int K, int width, int height, int tile_size,
+                      int tile_width, int tile_height, const int32_t *offsets, const int32_t *flatten_ids,
+                      int64_t n_isects, float alpha_cutoff, float alpha_clamp, const float *render_alphas,
+                      const int32_t *last_ids, const float *grad_colors_px, const float *grad_alphas_px,
+                      double *g_means, double *g_conics, double *g_colors, double *g_opacities, double *g_bg,
+                      double *g_means_abs, double *abs_means, double *abs_conics, double *abs_colors,
+                      double *abs_opacities, double *abs_bg)
+{
+    int64_t per_camera = (int64_t)tile_width * tile_height;
+    int64_t total_tiles = C * per_camera;
+    float rest[64];
+    if (K < 1 || K > 64 || N < 0 || C < 1) return -1;
+    (void)N;
+    for (int64_t t = 0; t < total_tiles; ++t) {
+        int64_t camera = t / per_camera;
+        int64_t local = t % per_camera;
+        int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
+        int64_t start = offsets[t];
+        int64_t end = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
+        for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
+            for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
+                int64_t pixel = (camera * height + y) * (int64_t)width + x;
+                const float *gc = grad_colors_px + pixel * K;
+                float ga = grad_alphas_px[pixel];
+                float T = 1.0f - render_alphas[pixel];
+                float after = 1.0f;
+                for (int k = 0; k < K; ++k) {
+                    rest[k] = backgrounds ? backgrounds[camera * K + k] : 0.0f;
+                    if (g_bg) {
+                        float term = gc[k] * T;
+                        g_bg[camera * K + k] += (double)term;
+                        if (abs_bg) abs_bg[camera * K + k] += fabs((double)term);
+                    }
+                }
+                float px = (float)x + 0.5f, py = (float)y + 0.5f;
+                for (int64_t i = end - 1; i >= start; --i) {
+                    int64_t g = flatten_ids[i];
+                    float dx = means2d[g * 2] - px;
+                    float dy = means2d[g * 2 + 1] - py;
+                    float a = conics[g * 3], b = conics[g * 3 + 1], c = conics[g * 3 + 2];
+                    float sigma = 0.5f * (a * dx * dx + c * dy * dy) + b * dx * dy;
+                    float response = orc_exp_neg(sigma);
+                    float raw = opacities[g] * response;
+                    float alpha = raw;
+                    if (alpha > alpha_clamp) alpha = alpha_clamp;
+                    if (!(render_alphas[pixel] > 0.0f && sigma >= 0.0f && alpha >= alpha_cutoff &&
+                          (int64_t)last_ids[pixel] >= i && T < 1.0f && alpha < 1.0f))
+                        continue;
+                    float before = T / (1.0f - alpha);
+                    float vis = before * alpha;
+                    const float *col = colors + g * K;
+                    float dot = 0.0f;
+                    for (int k = 0; k < K; ++k) {
+                        float term = gc[k] * vis;
+                        g_colors[g * K + k] += (double)term;
+                        if (abs_colors) abs_colors[g * K + k] += fabs((double)term);
+                        dot += gc[k] * (col[k] - rest[k]);
+                    }
+                    float g_alpha = before * (dot + ga * after);
+                    float g_raw = raw < alpha_clamp ? g_alpha : 0.0f;
+                    float t_opacity = g_raw * response;
+                    g_opacities[g] += (double)t_opacity;
+                    if (abs_opacities) abs_opacities[g] += fabs((double)t_opacity);
+                    float g_sigma = -g_raw * raw;
+                    float mx = g_sigma * (a * dx + b * dy);
+                    float my = g_sigma * (c * dy + b * dx);
+                    float t_conic[3] = {g_sigma * 0.5f * dx * dx, g_sigma * dx * dy, g_sigma * 0.5f * dy * dy};
+                    g_means[g * 2] += (double)mx;
+                    g_means[g * 2 + 1] += (double)my;
+                    if (abs_means) {
+                        abs_means[g * 2] += fabs((double)mx);
+                        abs_means[g * 2 + 1] += fabs((double)my);
+                    }
+                    if (g_means_abs) {
+                        g_means_abs[g * 2] += fabs((double)mx);
+                        g_means_abs[g * 2 + 1] += fabs((double)my);
+                    }
+                    for (int q = 0; q < 3; ++q) {
+                        g_conics[g * 3 + q] += (double)t_conic[q];
+                        if (abs_conics) abs_conics[g * 3 + q] += fabs((double)t_conic[q]);
+                    }
+                    for (int k = 0; k < K; ++k) rest[k] = alpha * col[k] + (1.0f - alpha) * rest[k];
+                    after *= 1.0f - alpha;
+                    T = before;
+                }
+            }
+        }
+    }
+    return 0;
 }
 
 /* Tile rectangles [x0, y0, x1, y1] of every (camera, splat), for vectorised membership checks. */
