@@ -165,6 +165,38 @@ gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const floa
                            float *render_T, int32_t *last_ids, uint64_t *eval_counts, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------------------------------------------
+ * Backward of the composite ([gsplat-bwd] gs_raster_backward_pixel and gs_raster_backward_without_gvl).
+ *
+ * For L = sum(grad_render_colors * render_colors) + sum(grad_render_alphas * render_alphas) of the forward above
+ * (same splats, ranges, cutoff and clamp; render_alphas and last_ids as the forward wrote them), writes the
+ * gradients of means2d [C, N, 2], conics [C, N, 3], colors [C, N, K] and opacities [C, N], and of backgrounds
+ * [C, K] when grad_backgrounds is not NULL (backgrounds may be NULL: a zero background). grad_means2d_abs
+ * (nullable) receives per splat the sum of |d L / d mean| over its pixels, per axis.
+ * Per pixel, T = 1 - render_alpha, after = 1 and rest = background; the background term is
+ * grad_colour * T; then the tile's range is walked back to front and position i with splat g counts when
+ * render_alpha > 0, sigma >= 0, alpha >= alpha_cutoff, i <= last_id, T < 1 and alpha < 1 (sigma, E(sigma),
+ * raw = opacity * E and alpha = min(clamp, raw) exactly as in the forward). A counted splat adds, in float32:
+ *   before = T / (1 - alpha), vis = before * alpha; colour: grad_colour[k] * vis;
+ *   dot = sum_k grad_colour[k] * (colour[k] - rest[k]); g_alpha = before * (dot + grad_alpha * after);
+ *   g_raw = raw < clamp ? g_alpha : 0; opacity: g_raw * E; g_sigma = -g_raw * raw;
+ *   mean: g_sigma * (a dx + b dy), g_sigma * (c dy + b dx); conic: g_sigma * 0.5 * dx * dx, g_sigma * dx * dy,
+ *   g_sigma * 0.5 * dy * dy;
+ * then rest = alpha * colour + (1 - alpha) * rest, after *= 1 - alpha, T = before.
+ * Every term is computed in that order; the terms of one splat are summed in an order the hardware picks (a sum
+ * per wavefront, then float atomics), so results agree with any other summation order to within float rounding
+ * of the sum of the terms' magnitudes, and may differ in the last bits from run to run.
+ * The gradient arrays are overwritten (cleared, then summed into). Limits as gs_rasterize_fwd. Asynchronous.
+ */
+gs_status gs_rasterize_bwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
+                           const float *backgrounds, int64_t C, int64_t N, int K, int width, int height,
+                           int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
+                           const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
+                           const float *render_alphas, const int32_t *last_ids, const float *grad_render_colors,
+                           const float *grad_render_alphas, float *grad_means2d, float *grad_conics,
+                           float *grad_colors, float *grad_opacities, float *grad_backgrounds,
+                           float *grad_means2d_abs, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

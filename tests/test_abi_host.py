@@ -127,3 +127,25 @@ def test_rasterize_argument_errors(lib):
     assert call(ptr=None) == GS_ERR_INVALID_ARG
     assert call(cut=float("nan")) == GS_ERR_INVALID_ARG
     assert b"gs_rasterize_fwd" in lib.gs_last_error()
+
+
+def test_rasterize_bwd_argument_errors(lib):
+    from tile_binned_gaussian_amd.binding import GS_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails on the host first
+
+    def bwd(C=1, N=4, K=3, W=32, H=32, ts=16, tw=2, th=2, n=10, cut=1 / 255, clamp=0.99, means=fake,
+            ra=fake, last=fake, gc=fake, ga=fake, gm=fake):
+        return lib.gs_rasterize_bwd(means, fake, fake, fake, None, C, N, K, W, H, ts, tw, th, fake, fake, n, cut,
+                                    clamp, ra, last, gc, ga, gm, fake, fake, fake, None, None, None)
+
+    assert bwd(K=5) == GS_ERR_INVALID_ARG
+    assert b"K = 5" in lib.gs_last_error()
+    assert bwd(ts=33, tw=1, th=1) == GS_ERR_INVALID_ARG
+    assert bwd(tw=3) == GS_ERR_INVALID_ARG
+    assert b"tile grid" in lib.gs_last_error()
+    assert bwd(C=0) == GS_ERR_INVALID_ARG
+    assert bwd(n=-1) == GS_ERR_INVALID_ARG
+    assert bwd(ra=None) == GS_ERR_INVALID_ARG
+    assert bwd(gm=None) == GS_ERR_INVALID_ARG
+    assert b"NULL" in lib.gs_last_error()
+    assert bwd(clamp=0.0) == GS_ERR_INVALID_ARG

@@ -20,7 +20,7 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
-           "gs_rasterize_fwd")
+           "gs_rasterize_fwd", "gs_rasterize_bwd")
 
 
 class GsError(RuntimeError):
@@ -56,6 +56,9 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F, F,
                                      P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd.restype = I32
+    lib.gs_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F,
+                                     P, P, P, P, P, P, P, P, P, P, P]
+    lib.gs_rasterize_bwd.restype = I32
     _lib = lib
     return lib
 
@@ -216,4 +219,55 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
                                 float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
                                 _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
                                 _ptr(out.last_ids), _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+@dataclass
+class RasterGrad:
+    means2d: torch.Tensor  # [C, N, 2]
+    conics: torch.Tensor  # [C, N, 3]
+    colors: torch.Tensor  # [C, N, K]
+    opacities: torch.Tensor  # [C, N]
+    backgrounds: torch.Tensor | None  # [C, K]
+    means2d_abs: torch.Tensor | None  # [C, N, 2]
+
+
+def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
+                     flatten_ids, render_alphas, last_ids, grad_render_colors, grad_render_alphas, n_isects=None,
+                     alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, grad_backgrounds=None, absgrad=False, out=None,
+                     stream=None) -> RasterGrad:
+    """Gradients of sum(grad_render_colors * colours) + sum(grad_render_alphas * alphas) of gs_rasterize_fwd.
+
+    grad_backgrounds: None -> computed when backgrounds is given; False -> not computed."""
+    lib = load_library()
+    dev = means2d.device
+    _req(means2d, "means2d", torch.float32, dev)
+    C, N = means2d.shape[0], means2d.shape[1]
+    _req(conics, "conics", torch.float32, dev, (C, N, 3))
+    _req(colors, "colors", torch.float32, dev)
+    if colors.dim() != 3 or tuple(colors.shape[:2]) != (C, N):
+        raise ValueError("colors must be [C, N, K]")
+    K = colors.shape[2]
+    _req(opacities, "opacities", torch.float32, dev, (C, N))
+    if backgrounds is not None:
+        _req(backgrounds, "backgrounds", torch.float32, dev, (C, K))
+    _req(isect_offsets, "isect_offsets", torch.int32, dev)
+    th, tw = isect_offsets.shape[1], isect_offsets.shape[2]
+    _req(flatten_ids, "flatten_ids", torch.int32, dev)
+    _req(render_alphas, "render_alphas", torch.float32, dev, (C, height, width))
+    _req(last_ids, "last_ids", torch.int32, dev, (C, height, width))
+    _req(grad_render_colors, "grad_render_colors", torch.float32, dev, (C, height, width, K))
+    _req(grad_render_alphas, "grad_render_alphas", torch.float32, dev, (C, height, width))
+    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    want_bg = backgrounds is not None if grad_backgrounds is None else bool(grad_backgrounds)
+    if out is None:
+        e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
+        out = RasterGrad(e(C, N, 2), e(C, N, 3), e(C, N, K), e(C, N), e(C, K) if want_bg else None,
+                         e(C, N, 2) if absgrad else None)
+    _check(lib.gs_rasterize_bwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
+                                K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
+                                float(alpha_cutoff), float(alpha_clamp), _ptr(render_alphas), _ptr(last_ids),
+                                _ptr(grad_render_colors), _ptr(grad_render_alphas), _ptr(out.means2d),
+                                _ptr(out.conics), _ptr(out.colors), _ptr(out.opacities), _ptr(out.backgrounds),
+                                _ptr(out.means2d_abs), _stream(stream)))
     return out

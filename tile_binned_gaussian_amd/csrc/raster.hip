@@ -8,7 +8,7 @@
 // centre, delta, quadratic form, alpha clamp, skip test, render alpha = 1 - T; gs_raster_backward_without_gvl:
 // tile walk and range end), with alpha_cutoff and transmittance_threshold from rlx-metal 0.2.9
 // splat_training.rs (training_forward_metal_traced).
-#include "gs_internal.hpp"
+#include "raster_common.hpp"
 
 #include <cmath>
 
@@ -16,47 +16,6 @@ namespace gs {
 namespace {
 
 constexpr int kMaxThreads = 256;
-
-// e^-sigma in float32: Cody and Waite's range reduction (k = rint(-sigma / ln 2), r = -sigma - k ln 2 with ln 2
-// split into a 15-bit high part and a low correction, both by fma) and the degree-7 Taylor polynomial of e^r
-// evaluated by fma, scaled by 2^k. sigma > 80 (or NaN) gives 0, which also keeps 2^k a normal scale.
-__device__ __forceinline__ float exp_neg(float sigma) {
-    if (!(sigma <= 80.0f)) return 0.0f;
-    const float t = -sigma;
-    const float k = __builtin_rintf(t * 0x1.715476p+0f);  // 1 / ln 2
-    float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);         // ln 2, high 15 bits
-    r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);             // ln 2 - high part
-    float q = 0x1.a01a02p-13f;                              // 1/7!
-    q = __builtin_fmaf(q, r, 0x1.6c16c2p-10f);              // 1/6!
-    q = __builtin_fmaf(q, r, 0x1.111112p-7f);               // 1/5!
-    q = __builtin_fmaf(q, r, 0x1.555556p-5f);               // 1/4!
-    q = __builtin_fmaf(q, r, 0x1.555556p-3f);               // 1/3!
-    q = __builtin_fmaf(q, r, 0.5f);
-    q = __builtin_fmaf(q, r, 1.0f);
-    q = __builtin_fmaf(q, r, 1.0f);
-    return __builtin_ldexpf(q, static_cast<int>(k));
-}
-
-// The same function without branches (a select replaces the early return), for lock-step loops where every lane
-// evaluates it anyway. Identical bits: the polynomial path is the one above, and any sigma that is not <= 80
-// (including NaN) selects 0.
-__device__ __forceinline__ float exp_neg_select(float sigma) {
-    const float t = -sigma;
-    const float k = __builtin_rintf(t * 0x1.715476p+0f);
-    float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);
-    r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);
-    float q = 0x1.a01a02p-13f;
-    q = __builtin_fmaf(q, r, 0x1.6c16c2p-10f);
-    q = __builtin_fmaf(q, r, 0x1.111112p-7f);
-    q = __builtin_fmaf(q, r, 0x1.555556p-5f);
-    q = __builtin_fmaf(q, r, 0x1.555556p-3f);
-    q = __builtin_fmaf(q, r, 0.5f);
-    q = __builtin_fmaf(q, r, 1.0f);
-    q = __builtin_fmaf(q, r, 1.0f);
-    const int ki = (sigma <= 80.0f) ? static_cast<int>(k) : 0;
-    const float e = __builtin_ldexpf(q, ki);
-    return (sigma <= 80.0f) ? e : 0.0f;
-}
 
 struct RasterArgs {
     const float2 *means;
@@ -189,76 +148,6 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         atomicAdd(&a.eval_counts[3], n_exec);
         atomicAdd(&a.eval_counts[4], n_staged);
     }
-}
-
-// Conservative cull of one splat against a wave's pixel region (pixel-centre box [x0, x1] x [y0, y1]). The splat
-// is dropped for the region only when alpha < cutoff at every pixel of the box, so skipping it there leaves every
-// output bit unchanged:
-//  - opacity < cutoff: alpha = opacity * E(sigma) <= opacity since E(sigma) <= 1 for sigma >= 0;
-//  - otherwise alpha >= cutoff needs sigma_exact <= L = ln(opacity / cutoff) + 0.05. The set {sigma <= L} lies
-//    inside |dx| <= sqrt(2 L S_xx), |dy| <= sqrt(2 L S_yy) with S = inverse of the conic (the marginal bound of a
-//    quadratic form): a box test first; then the minimum of sigma over the region's continuous box (no smaller
-//    than over its pixel centres) must not exceed thr = 1.004 L + 1e-3. The 5% alpha margin in L and the 0.4% in
-//    thr cover float32 rounding: with trace^2 <= 1000 det a computed sigma is within 24 * 2^-24 * trace^2 / det
-//    < 0.15% of the exact one, E is within one ulp of e^-sigma, the minimiser along an edge is found to within
-//    rounding (the quadratic is flat there, so the value moves by a second-order amount the 1e-3 covers), and
-//    0.9985 (ln(o / cutoff) + 0.05) > ln(o / cutoff) for every opacity up to 1e6; the box is padded for the
-//    rounding of its own arithmetic;
-//  - non-positive-definite, badly conditioned or non-finite conics, opacities above 1e6 or NaN, and means beyond
-//    1e6 pixels are never culled.
-struct CullBox {
-    float x0, x1, y0, y1;  // bounding box of the alpha >= cutoff footprint, or +-inf when not culled
-    float thr, ra, rc;     // sigma bound for the region test and 1/a, 1/c (finite only when culled)
-    bool never;            // the splat can reach the cutoff nowhere
-    bool exact;            // the region test applies
-};
-
-__device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c, float o, float alpha_cutoff,
-                                           float log_cutoff) {
-    CullBox box{-INFINITY, INFINITY, -INFINITY, INFINITY, 0.0f, 0.0f, 0.0f, false, false};
-    if (o < alpha_cutoff) {
-        box.never = true;
-        return box;
-    }
-    const float det = a * c - b * b;
-    const float tr = a + c;
-    if (!(o >= alpha_cutoff) || !(o <= 1.0e6f) || !(det > 0.0f) || !(a > 0.0f) || !(c > 0.0f) ||
-        !(tr * tr <= 1.0e3f * det) || !(fabsf(m.x) < 1.0e6f) || !(fabsf(m.y) < 1.0e6f))
-        return box;
-    const float L = logf(o) - log_cutoff + 0.05f;
-    float rx = sqrtf(2.0f * L * (c / det)) * 1.0001f;
-    float ry = sqrtf(2.0f * L * (a / det)) * 1.0001f;
-    if (!(rx < 1.0e6f) || !(ry < 1.0e6f)) return box;
-    rx += 2.0e-3f + 1.0e-6f * (fabsf(m.x) + rx);
-    ry += 2.0e-3f + 1.0e-6f * (fabsf(m.y) + ry);
-    box.x0 = m.x - rx;
-    box.x1 = m.x + rx;
-    box.y0 = m.y - ry;
-    box.y1 = m.y + ry;
-    box.thr = 1.004f * L + 1.0e-3f;
-    box.ra = 1.0f / a;
-    box.rc = 1.0f / c;
-    box.exact = true;
-    return box;
-}
-
-// sigma = 0.5 (a dx^2 + c dy^2) + b dx dy at an offset from the mean
-__device__ __forceinline__ float quad_form(float a, float b, float c, float dx, float dy) {
-    return 0.5f * (a * dx * dx + c * dy * dy) + b * dx * dy;
-}
-
-// Whether sigma can be <= thr somewhere in the box [x0, x1] x [y0, y1]: yes if the mean is inside; otherwise the
-// minimum of the convex quadratic lies on an edge, where it is a one-dimensional quadratic minimised at the
-// clamped stationary point.
-__device__ __forceinline__ bool region_reach(float2 m, float a, float b, float c, float ra, float rc, float thr,
-                                             float x0, float x1, float y0, float y1) {
-    if (m.x >= x0 && m.x <= x1 && m.y >= y0 && m.y <= y1) return true;
-    const float lx = x0 - m.x, hx = x1 - m.x, ly = y0 - m.y, hy = y1 - m.y;
-    float best = quad_form(a, b, c, lx, fminf(fmaxf(-b * lx * rc, ly), hy));
-    best = fminf(best, quad_form(a, b, c, hx, fminf(fmaxf(-b * hx * rc, ly), hy)));
-    best = fminf(best, quad_form(a, b, c, fminf(fmaxf(-b * ly * ra, lx), hx), ly));
-    best = fminf(best, quad_form(a, b, c, fminf(fmaxf(-b * hy * ra, lx), hx), hy));
-    return best <= thr;
 }
 
 // Tiles up to 16x16, one pixel per thread. With 16x16 tiles each wave owns an 8x8 quadrant; otherwise pixels are
