@@ -166,6 +166,17 @@ def main():
     stage_ms = {nm: statistics.median(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
                 for i, nm in enumerate(names)}
     ms_per_step = wall * 1e3 / args.steps
+    # outside the frame: the composite's backward on the last frame (seeded output gradients)
+    bwd = frame.BackwardPlan(plan, seed=0)
+    for _ in range(2):
+        bwd.run()
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(5, args.steps // 2))]
+    for a_ev, b_ev in bev:
+        a_ev.record(plan.stream)
+        bwd.run()
+        b_ev.record(plan.stream)
+    torch.cuda.synchronize()
+    backward_ms = statistics.median(a_ev.elapsed_time(b_ev) for a_ev, b_ev in bev)
     # outside the frame: the stand-alone stable sort of the same intersections over all populated key bits
     stage_ms["generic_sort"], _ = plan.run_generic_sort(max(5, args.steps // 2))
     pixels = scene.C * scene.width * scene.height
@@ -216,6 +227,9 @@ def main():
         "isect_keys_sorted_per_s_generic_sort": round(n / (stage_ms["generic_sort"] * 1e-3), 1),
         "isect_keys_sorted_per_s_frame": round(n / (ms_per_step * 1e-3), 1),
         "rasterized_mpix_per_s_composite_only": round(pixels / (stage_ms["composite"] * 1e-3) / 1e6, 2),
+        "backward": {"ms": round(backward_ms, 4), "Mpix/s": round(pixels / (backward_ms * 1e-3) / 1e6, 2),
+                     "note": "gs_rasterize_bwd on the last frame with seeded standard-normal output gradients; "
+                             "clears the gradients, then sums them"},
         "composite_work": {"evaluations_definition": n_eval, "evaluations_executed": n_exec,
                            "alpha_ge_cutoff": n_pass, "composited": n_comp, "splats_staged": n_staged},
         "stages": stages,

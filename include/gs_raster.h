@@ -183,9 +183,10 @@ gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const floa
  *   mean: g_sigma * (a dx + b dy), g_sigma * (c dy + b dx); conic: g_sigma * 0.5 * dx * dx, g_sigma * dx * dy,
  *   g_sigma * 0.5 * dy * dy;
  * then rest = alpha * colour + (1 - alpha) * rest, after *= 1 - alpha, T = before.
- * Every term is computed in that order; the terms of one splat are summed in an order the hardware picks (a sum
- * per wavefront, then float atomics), so results agree with any other summation order to within float rounding
- * of the sum of the terms' magnitudes, and may differ in the last bits from run to run.
+ * Every term is computed in that order; the terms of one splat are summed in an order the hardware picks (sums
+ * over 16-lane rows, LDS atomics per tile, then one float atomic per splat and tile), so results agree with any
+ * other summation order to within float rounding of the sum of the terms' magnitudes, and may differ in the last
+ * bits from run to run.
  * The gradient arrays are overwritten (cleared, then summed into). Limits as gs_rasterize_fwd. Asynchronous.
  */
 gs_status gs_rasterize_bwd(const float *means2d, const float *conics, const float *colors, const float *opacities,

@@ -2,11 +2,12 @@
 seeded inputs and the same forward outputs.
 
 Each gradient term is computed by both sides with the same float32 operations in the same order; only the order in
-which a splat's terms are summed differs (the oracle sums them exactly in double; the GPU sums each wavefront's
-terms with a 6-level tree, then adds one partial sum per (tile, wavefront) with float atomics). Float summation of
-terms t_i in any order with at most L additions on any path errs by at most L * 2^-24 * sum|t_i|, so each entry is
-checked against |gpu - oracle| <= (6 + A + 2) * 2^-24 * sum|t_i|, with A the number of (tile, wavefront) partial
-sums that can reach the entry (the splat's tile count times the wavefronts per tile) and sum|t_i| from the oracle."""
+which a splat's terms are summed differs (the oracle sums them exactly in double; the GPU sums each 16-lane row of a
+wavefront with a 4-level tree, adds the row sums into a per-tile LDS accumulator, then adds one partial sum per
+(splat, tile) with float atomics). Float summation of terms t_i with at most L additions on any path errs by at
+most L * 2^-24 * sum|t_i|, so each entry is checked against |gpu - oracle| <= (6 + A + 2) * 2^-24 * sum|t_i|, with
+A = 4 x (wavefronts per tile) x (the splat's tile count) partial sums that can reach the entry, and sum|t_i| from
+the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -61,7 +62,7 @@ def run_and_compare(scene, seed=0, absgrad=True):
                                  alpha_clamp=scene.alpha_clamp, absgrad=absgrad)
     torch.cuda.synchronize()
     tiles = host(fr.isect.tiles_per_gauss).astype(np.float64)
-    adds = tiles * _waves_per_tile(scene.tile_size)
+    adds = tiles * 4 * _waves_per_tile(scene.tile_size)
     _assert_close(host(g.means2d), o.means2d, o.abs_means2d, adds[..., None], "means2d")
     _assert_close(host(g.conics), o.conics, o.abs_conics, adds[..., None], "conics")
     _assert_close(host(g.colors), o.colors, o.abs_colors, adds[..., None], "colors")

@@ -5,8 +5,9 @@
 // forward's outputs (final transmittance 1 - render_alpha, last composited index) and walks the tile's range back
 // to front; batches of splats are staged through LDS from the back, with the same exact per-wave cull as the
 // forward (a splat whose alpha stays below the cutoff over a wave's pixels contributes nothing there). For every
-// staged splat that at least one lane of a wave uses, each gradient term is summed over the wave by DPP adds and
-// one lane adds the sum to the splat's gradient with a float atomic.
+// staged splat that at least one lane of a wave uses, each gradient term is summed over each 16-lane row by DPP
+// adds and the row sums are added into the splat's LDS accumulators; after the batch, one thread per splat adds
+// them to the splat's gradient with float atomics (one set per splat and tile).
 //
 // Definition: gsplat 1.0.0 raster_backward.c, gs_raster_backward_pixel (the per-pixel back-to-front recurrence
 // and its gradient terms) and gs_raster_backward_without_gvl (the tile walk), with the forward's exponential.
@@ -42,23 +43,35 @@ __device__ __forceinline__ float dpp_read(float v) {
                                                                  0xf, true));
 }
 
-// Sum of v over the 64 lanes, valid in lane 63. Every lane must be active. Steps: swap neighbours and pairs within
-// quads (every lane holds its quad's sum), shift rows right by 4 and 8 (lane 15 of each row holds the row's sum),
-// then broadcast lane 15 into the next row (lane 31 holds rows 0-1, lane 63 rows 2-3) and lane 31 into rows 2-3.
-__device__ __forceinline__ float wave_sum_last(float v) {
+// Sum of v over each row of 16 lanes, valid in lanes 15, 31, 47 and 63. Every lane must be active. Steps: swap
+// neighbours and pairs within quads (every lane holds its quad's sum), then shift rows right by 4 and by 8.
+__device__ __forceinline__ float row_sum(float v) {
     v += dpp_read<0xb1, 0xf>(v);   // quad_perm [1, 0, 3, 2]
     v += dpp_read<0x4e, 0xf>(v);   // quad_perm [2, 3, 0, 1]
     v += dpp_read<0x114, 0xf>(v);  // row_shr:4
     v += dpp_read<0x118, 0xf>(v);  // row_shr:8
+    return v;
+}
+
+// Sum of v over the 64 lanes, valid in lane 63: the row sums, then lane 15 broadcast into the next row (lane 31
+// holds rows 0-1, lane 63 rows 2-3) and lane 31 into rows 2-3.
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v = row_sum(v);
     v += dpp_read<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
     v += dpp_read<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
-// Adds the wave's sum of v to *dst (one lane, one atomic), skipping exact zeros.
+// Adds the wave's sum of v to *dst in device memory (one lane, one hardware float atomic), skipping exact zeros.
 __device__ __forceinline__ void wave_add(float v, float *dst, int lane) {
     const float s = wave_sum_last(v);
-    if (lane == kWave - 1 && s != 0.0f) unsafeAtomicAdd(dst, s);  // device memory: the hardware float add
+    if (lane == kWave - 1 && s != 0.0f) unsafeAtomicAdd(dst, s);
+}
+
+// Adds the four row sums of v to *acc in LDS (four lanes, LDS float atomics), skipping exact zeros.
+__device__ __forceinline__ void rows_add_lds(float v, float *acc, int lane) {
+    const float s = row_sum(v);
+    if ((lane & 15) == 15 && s != 0.0f) atomicAdd(acc, s);
 }
 
 template <int K, int kThreads>
@@ -69,6 +82,8 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
     __shared__ uint32_t s_mask[kBatch];
     __shared__ uint16_t s_list[kWaves][kBatch];
     __shared__ int s_top[kWaves];
+    constexpr int kAcc = K + 6 + 2;  // colour[K], opacity, mean x y, conic a b c, |mean| x y
+    __shared__ float s_acc[kBatch][kAcc];
 
     const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
@@ -185,6 +200,8 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
                 }
             }
             s_mask[slot] = bits;
+#pragma unroll
+            for (int v = 0; v < kAcc; ++v) s_acc[slot][v] = 0.0f;
         }
         __syncthreads();
         // this wave's splats of the batch from the back, as byte offsets of their records
@@ -229,24 +246,43 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
             const float t_ca = g_sigma * 0.5f * dx * dx;
             const float t_cb = g_sigma * dx * dy;
             const float t_cc = g_sigma * 0.5f * dy * dy;
-            const int64_t g = __float_as_int(r1.w);
+            float *acc = s_acc[s_list[wave][jj] / (kRec * 4)];
 #pragma unroll
-            for (int k = 0; k < K; ++k) wave_add(valid ? t_col[k] : 0.0f, &a.g_colors[g * K + k], lane);
-            wave_add(valid ? t_op : 0.0f, &a.g_opacities[g], lane);
-            wave_add(valid ? t_mx : 0.0f, &a.g_means[g * 2], lane);
-            wave_add(valid ? t_my : 0.0f, &a.g_means[g * 2 + 1], lane);
-            wave_add(valid ? t_ca : 0.0f, &a.g_conics[g * 3], lane);
-            wave_add(valid ? t_cb : 0.0f, &a.g_conics[g * 3 + 1], lane);
-            wave_add(valid ? t_cc : 0.0f, &a.g_conics[g * 3 + 2], lane);
+            for (int k = 0; k < K; ++k) rows_add_lds(valid ? t_col[k] : 0.0f, &acc[k], lane);
+            rows_add_lds(valid ? t_op : 0.0f, &acc[K], lane);
+            rows_add_lds(valid ? t_mx : 0.0f, &acc[K + 1], lane);
+            rows_add_lds(valid ? t_my : 0.0f, &acc[K + 2], lane);
+            rows_add_lds(valid ? t_ca : 0.0f, &acc[K + 3], lane);
+            rows_add_lds(valid ? t_cb : 0.0f, &acc[K + 4], lane);
+            rows_add_lds(valid ? t_cc : 0.0f, &acc[K + 5], lane);
             if (a.g_means_abs) {
-                wave_add(valid ? fabsf(t_mx) : 0.0f, &a.g_means_abs[g * 2], lane);
-                wave_add(valid ? fabsf(t_my) : 0.0f, &a.g_means_abs[g * 2 + 1], lane);
+                rows_add_lds(valid ? fabsf(t_mx) : 0.0f, &acc[K + 6], lane);
+                rows_add_lds(valid ? fabsf(t_my) : 0.0f, &acc[K + 7], lane);
             }
             if (valid) {
 #pragma unroll
                 for (int k = 0; k < K; ++k) rest[k] = alpha * cv[k] + (1.0f - alpha) * rest[k];
                 after *= 1.0f - alpha;
                 T = before;
+            }
+        }
+        // the batch's sums per splat (over this tile's pixels) into the splats' gradients
+        __syncthreads();
+        for (int slot = static_cast<int>(threadIdx.x); slot < count; slot += static_cast<int>(blockDim.x)) {
+            const float *acc = s_acc[slot];
+            const int64_t g = __float_as_int(s_rec[slot * 3 + 1].w);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (acc[k] != 0.0f) unsafeAtomicAdd(&a.g_colors[g * K + k], acc[k]);
+            if (acc[K] != 0.0f) unsafeAtomicAdd(&a.g_opacities[g], acc[K]);
+            if (acc[K + 1] != 0.0f) unsafeAtomicAdd(&a.g_means[g * 2], acc[K + 1]);
+            if (acc[K + 2] != 0.0f) unsafeAtomicAdd(&a.g_means[g * 2 + 1], acc[K + 2]);
+            if (acc[K + 3] != 0.0f) unsafeAtomicAdd(&a.g_conics[g * 3], acc[K + 3]);
+            if (acc[K + 4] != 0.0f) unsafeAtomicAdd(&a.g_conics[g * 3 + 1], acc[K + 4]);
+            if (acc[K + 5] != 0.0f) unsafeAtomicAdd(&a.g_conics[g * 3 + 2], acc[K + 5]);
+            if (a.g_means_abs) {
+                if (acc[K + 6] != 0.0f) unsafeAtomicAdd(&a.g_means_abs[g * 2], acc[K + 6]);
+                if (acc[K + 7] != 0.0f) unsafeAtomicAdd(&a.g_means_abs[g * 2 + 1], acc[K + 7]);
             }
         }
     }

@@ -177,6 +177,31 @@ class FramePlan:
         return times[len(times) // 2], n
 
 
+class BackwardPlan:
+    """The composite's backward on a FramePlan's last frame, with preallocated gradients and fixed seeded output
+    gradients (standard normal), for timing."""
+
+    def __init__(self, plan: FramePlan, seed=0, absgrad=False):
+        self.plan = plan
+        ds = plan.ds
+        g = torch.Generator(device=ds.means2d.device).manual_seed(seed)
+        C, H, W, K = ds.C, ds.height, ds.width, ds.colors.shape[2]
+        self.gc = torch.randn((C, H, W, K), generator=g, device=ds.means2d.device)
+        self.ga = torch.randn((C, H, W), generator=g, device=ds.means2d.device)
+        e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=ds.means2d.device)  # noqa: E731
+        self.out = binding.RasterGrad(e(C, ds.N, 2), e(C, ds.N, 3), e(C, ds.N, K), e(C, ds.N),
+                                      None if ds.backgrounds is None else e(C, K),
+                                      e(C, ds.N, 2) if absgrad else None)
+
+    def run(self):
+        plan, ds = self.plan, self.plan.ds
+        return binding.gs_rasterize_bwd(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, ds.width,
+                                        ds.height, ds.tile_size, plan.offsets, plan.ids, plan.render.render_alphas,
+                                        plan.render.last_ids, self.gc, self.ga, n_isects=plan.n_isects,
+                                        alpha_cutoff=ds.alpha_cutoff, alpha_clamp=ds.alpha_clamp, out=self.out,
+                                        stream=plan.stream)
+
+
 def _bits_for(count: int) -> int:
     bits = 0
     while (1 << bits) < count:
