@@ -36,7 +36,8 @@ OPS_EVAL, OPS_PASS = 29, 3
 # HBM bytes the composite kernel moved per launch on the 1M-splat frame, from two profiler counter runs; valid only
 # while the kernel source is the one the counters were taken on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "raster_cull_kernel_config3_hbm_traffic.txt")
-RASTER_SOURCE = os.path.join(ROOT, "tile_binned_gaussian_amd", "csrc", "raster.hip")
+RASTER_SOURCES = [os.path.join(ROOT, "tile_binned_gaussian_amd", "csrc", f)
+                  for f in ("raster.hip", "raster_common.hpp")]
 
 WORKLOADS = {
     "tiny": "tiny: 1 camera, 256 splats, 64x64, tile 16",
@@ -91,8 +92,11 @@ def measured_traffic(config):
     try:
         with open(TRAFFIC_FILE) as f:
             rec = dict(line.split(":", 1) for line in f.read().splitlines() if ":" in line and not line.startswith(" "))
-        with open(RASTER_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in RASTER_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
     except OSError:
         return None
     rec = {k.strip(): v.strip() for k, v in rec.items()}
