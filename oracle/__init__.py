@@ -66,6 +66,8 @@ def _load():
         lib.orc_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F,
                                           P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_rasterize_bwd.restype = I32
+        lib.orc_project.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P]
+        lib.orc_project.restype = None
         _lib = lib
     return _lib
 
@@ -301,6 +303,34 @@ def rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height
     if rc != 0:
         raise ValueError("invalid rasterize backward arguments")
     return RasterGrad(*g, *a)
+
+
+@dataclass
+class Projection:
+    radii: np.ndarray  # [C, N, 2] int32
+    means2d: np.ndarray  # [C, N, 2]
+    depths: np.ndarray  # [C, N]
+    conics: np.ndarray  # [C, N, 3]
+    compensations: np.ndarray | None  # [C, N]
+
+
+def project(means, covars, viewmats, Ks, width, height, eps2d=0.3, near_plane=0.01, far_plane=1e10,
+            radius_clip=0.0, compensation=False, orthographic=False) -> Projection:
+    """EWA projection of [N, 3] means and [N, 3, 3] covariances into C cameras ([C, 4, 4] views, [C, 3, 3] K)."""
+    lib = _load()
+    means = _c(means, np.float32)
+    N = means.shape[0]
+    views = _c(viewmats, np.float32)
+    C = views.shape[0]
+    radii = np.zeros((C, N, 2), np.int32)
+    m2 = np.zeros((C, N, 2), np.float32)
+    dep = np.zeros((C, N), np.float32)
+    con = np.zeros((C, N, 3), np.float32)
+    comp = np.zeros((C, N), np.float32) if compensation else None
+    lib.orc_project(_p(means), _p(_c(covars, np.float32)), _p(views), _p(_c(Ks, np.float32)), C, N, int(width),
+                    int(height), float(eps2d), float(near_plane), float(far_plane), float(radius_clip),
+                    int(bool(orthographic)), _p(radii), _p(m2), _p(dep), _p(con), _p(comp))
+    return Projection(radii, m2, dep, con, comp)
 
 
 def scene_pipeline(scene, sort=True):

@@ -15,6 +15,8 @@
  *   [rlx-metal] rlx-metal 0.2.9 splat_training.rs, training_forward_metal_traced: names alpha_cutoff and
  *            transmittance_threshold as forward parameters, and a cutoff default of 1/255.
  *   The composite's backward (orc_rasterize_bwd) follows [gsplat-bwd] gs_raster_backward_pixel directly.
+ *   [gsplat-proj] the same gem's projection.c (gs_mat3_product, gs_camera_covar, gs_clip, gs_project_one): the
+ *            EWA projection of 3D Gaussians into cameras (orc_project).
  *
  * Arithmetic: float32 wherever the pages compute in float (all of the above do), evaluated in the pages'
  * expression order with no contraction (build with -ffp-contract=off, never -ffast-math); fmaf appears only
@@ -484,6 +486,115 @@ int orc_rasterize_bwd(const float *means2d, const float *conics, const float *co
         }
     }
     return 0;
+}
+
+/* 3x3 product left * right, each entry summed from 0 over the inner index in order ([gsplat-proj] gs_mat3_product). */
+static void orc_mat3_product(const float *left, const float *right, float *out)
+{
+    for (int r = 0; r < 3; ++r)
+        for (int c = 0; c < 3; ++c) {
+            float v = 0.0f;
+            for (int k = 0; k < 3; ++k) v += left[r * 3 + k] * right[k * 3 + c];
+            out[r * 3 + c] = v;
+        }
+}
+
+/* ceil of a float as int32, clamped to [0, 2^31 - 1] first (NaN -> 0) so that the conversion is defined; equal to
+ * (int32_t)ceilf(v) for every v in range. */
+static int32_t orc_ceil_radius(float v)
+{
+    float c = ceilf(v);
+    if (!(c > 0.0f)) return 0;
+    if (c >= 2147483648.0f) return 2147483647;
+    return (int32_t)c;
+}
+
+/* EWA projection of N 3D Gaussians into C cameras ([gsplat-proj] gs_project_one), per (camera c, Gaussian g):
+ *   R = the view's upper-left 3x3, t its last column; mean_c = R mean + t (each row summed left to right, then t);
+ *   cov_c = (R cov) R^T (orc_mat3_product twice); depth = mean_c.z;
+ *   z = depth unless depth <= near or >= far (then 1);
+ *   perspective: the camera-space x/z and y/z are clipped to the image widened by 15% on each side, and
+ *     J = [[fx / z, 0, -fx x_clipped / z^2], [0, fy / z, -fy y_clipped / z^2]], with x_clipped = clip(x / z) z;
+ *     mean2d = ((K00 x + K01 y + K02 z) / z, (K10 x + K11 y + K12 z) / z);
+ *   orthographic: J = [[fx, 0, 0], [0, fy, 0]], mean2d = (x fx + cx, y fy + cy);
+ *   cov2d = J cov_c J^T (each entry summed over (left, right) in order from 0), det0 = its determinant;
+ *   eps2d is added to the diagonal, det = the new determinant, safe = det <= 0 ? 1e-10 : det;
+ *   r = ceil(3.33 sqrt(max(diagonal, 0))) per axis; visible iff det > 0, near < depth < far, some r > radius_clip
+ *   and the box mean2d +- r overlaps the image; radii = visible ? r : 0;
+ *   conic = (cov2d_11 / safe, -(cov2d_01 + cov2d_10) / (2 safe), cov2d_00 / safe);
+ *   compensation (nullable) = sqrt(max(det0 / safe, 0)).
+ * Float32 in the page's operation order. Outputs: radii [C, N, 2] int32, means2d [C, N, 2], depths [C, N],
+ * conics [C, N, 3]. */
+void orc_project(const float *means, const float *covars, const float *views, const float *Ks, int64_t C,
+                 int64_t N, int width, int height, float eps2d, float near_plane, float far_plane, float radius_clip,
+                 int orthographic, int32_t *radii, float *means2d, float *depths, float *conics, float *comps)
+{
+    for (int64_t c = 0; c < C; ++c) {
+        const float *view = views + c * 16;
+        const float *K = Ks + c * 9;
+        float R[9] = {view[0], view[1], view[2], view[4], view[5], view[6], view[8], view[9], view[10]};
+        float Rt[9];
+        for (int r = 0; r < 3; ++r)
+            for (int q = 0; q < 3; ++q) Rt[r * 3 + q] = R[q * 3 + r];
+        for (int64_t g = 0; g < N; ++g) {
+            const float *m = means + g * 3;
+            const float *cov = covars + g * 9;
+            float mc[3];
+            for (int r = 0; r < 3; ++r) mc[r] = R[r * 3] * m[0] + R[r * 3 + 1] * m[1] + R[r * 3 + 2] * m[2] + view[r * 4 + 3];
+            float tmp[9], cc[9];
+            orc_mat3_product(R, cov, tmp);
+            orc_mat3_product(tmp, Rt, cc);
+            float depth = mc[2];
+            float z = (depth <= near_plane || depth >= far_plane) ? 1.0f : depth;
+            float J[6] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+            float p0, p1;
+            if (orthographic) {
+                J[0] = K[0];
+                J[4] = K[4];
+                p0 = mc[0] * K[0] + K[2];
+                p1 = mc[1] * K[4] + K[5];
+            } else {
+                float w = (float)width, h = (float)height;
+                float min_x = -(K[2] / K[0] + 0.15f * w / K[0]);
+                float max_x = (w - K[2]) / K[0] + 0.15f * w / K[0];
+                float min_y = -(K[5] / K[4] + 0.15f * h / K[4]);
+                float max_y = (h - K[5]) / K[4] + 0.15f * h / K[4];
+                float cx = fminf(fmaxf(mc[0] / z, min_x), max_x) * z;
+                float cy = fminf(fmaxf(mc[1] / z, min_y), max_y) * z;
+                J[0] = K[0] / z;
+                J[2] = -K[0] * cx / (z * z);
+                J[4] = K[4] / z;
+                J[5] = -K[4] * cy / (z * z);
+                p0 = (K[0] * mc[0] + K[1] * mc[1] + K[2] * z) / z;
+                p1 = (K[3] * mc[0] + K[4] * mc[1] + K[5] * z) / z;
+            }
+            float c2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int r = 0; r < 2; ++r)
+                for (int q = 0; q < 2; ++q)
+                    for (int a = 0; a < 3; ++a)
+                        for (int b = 0; b < 3; ++b) c2[r * 2 + q] += J[r * 3 + a] * cc[a * 3 + b] * J[q * 3 + b];
+            float det0 = c2[0] * c2[3] - c2[1] * c2[2];
+            c2[0] += eps2d;
+            c2[3] += eps2d;
+            float det = c2[0] * c2[3] - c2[1] * c2[2];
+            float safe = det <= 0.0f ? 1e-10f : det;
+            int32_t rx = orc_ceil_radius(3.33f * sqrtf(fmaxf(c2[0], 0.0f)));
+            int32_t ry = orc_ceil_radius(3.33f * sqrtf(fmaxf(c2[3], 0.0f)));
+            int visible = det > 0.0f && depth > near_plane && depth < far_plane &&
+                          ((float)rx > radius_clip || (float)ry > radius_clip) && p0 + (float)rx > 0.0f &&
+                          p0 - (float)rx < (float)width && p1 + (float)ry > 0.0f && p1 - (float)ry < (float)height;
+            int64_t i = c * N + g;
+            radii[i * 2] = visible ? rx : 0;
+            radii[i * 2 + 1] = visible ? ry : 0;
+            means2d[i * 2] = p0;
+            means2d[i * 2 + 1] = p1;
+            depths[i] = depth;
+            conics[i * 3] = c2[3] / safe;
+            conics[i * 3 + 1] = -(c2[1] + c2[2]) / (2.0f * safe);
+            conics[i * 3 + 2] = c2[0] / safe;
+            if (comps) comps[i] = sqrtf(fmaxf(det0 / safe, 0.0f));
+        }
+    }
 }
 
 /* Tile rectangles [x0, y0, x1, y1] of every (camera, splat), for vectorised membership checks. */

@@ -269,6 +269,78 @@ def lossless_radii(scene: Scene) -> np.ndarray:
     return _f32(np.stack([rx, ry], -1))
 
 
+@dataclass
+class Scene3D:
+    """3D Gaussians and cameras, the inputs of the EWA projection: means [N, 3], covariances [N, 3, 3] (built as
+    R diag(s^2) R^T from a random unit quaternion and log-normal scales, in float64, then cast), world-to-camera
+    views [C, 4, 4] and intrinsics [C, 3, 3]."""
+
+    name: str
+    means: np.ndarray
+    covars: np.ndarray
+    viewmats: np.ndarray
+    Ks: np.ndarray
+    width: int
+    height: int
+
+    @property
+    def C(self) -> int:
+        return self.viewmats.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.means.shape[0]
+
+
+def _quat_rot(q):
+    w, x, y, z = (q[..., i] for i in range(4))
+    return np.stack([np.stack([1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y)], -1),
+                     np.stack([2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x)], -1),
+                     np.stack([2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)], -1)], -2)
+
+
+def scene3d(seed: int, N: int, C: int = 1, width: int = 1920, height: int = 1080, spread: float = 4.0,
+            scale_median: float = 0.02, scale_sigma_ln: float = 1.0, distance: float = 6.0,
+            behind_frac: float = 0.02, name: str | None = None) -> Scene3D:
+    """Gaussians in a ball of radius `spread` around the origin (a `behind_frac` share moved behind the cameras),
+    C cameras at `distance` looking at the origin from random directions, focal length 1.1 * width. Draw order:
+    centres, quaternions, scales, the behind mask, then per camera its direction and roll."""
+    rng = np.random.default_rng(seed)
+    u = rng.normal(size=(N, 3))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    means = u * spread * rng.uniform(0, 1, (N, 1)) ** (1 / 3)
+    q = rng.normal(size=(N, 4))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    scales = scale_median * np.exp(scale_sigma_ln * rng.normal(size=(N, 3)))
+    behind = rng.uniform(size=N) < behind_frac
+    Rg = _quat_rot(q)
+    covars = Rg @ (scales[:, :, None] ** 2 * np.transpose(Rg, (0, 2, 1)))
+    views = np.zeros((C, 4, 4))
+    Ks = np.zeros((C, 3, 3))
+    for c in range(C):
+        d = rng.normal(size=3)
+        d /= np.linalg.norm(d)
+        roll = rng.uniform(-0.3, 0.3)
+        pos = d * distance
+        fwd = -d  # camera z axis looks at the origin
+        up0 = np.array([0.0, 1.0, 0.0]) if abs(fwd[1]) < 0.9 else np.array([1.0, 0.0, 0.0])
+        right = np.cross(up0, fwd)
+        right /= np.linalg.norm(right)
+        down = np.cross(fwd, right)
+        cr, sr = math.cos(roll), math.sin(roll)
+        right, down = cr * right + sr * down, -sr * right + cr * down
+        Rc = np.stack([right, down, fwd])  # rows: camera axes in world coordinates
+        views[c, :3, :3] = Rc
+        views[c, :3, 3] = -Rc @ pos
+        views[c, 3, 3] = 1.0
+        Ks[c] = [[1.1 * width, 0.0, width / 2], [0.0, 1.1 * width, height / 2], [0.0, 0.0, 1.0]]
+    if C > 0:
+        # move the `behind` share behind the first camera
+        pos0 = -views[0, :3, :3].T @ views[0, :3, 3]
+        means[behind] = pos0 + (pos0 - means[behind]) * 0.1
+    return Scene3D(name or f"scene3d-{seed}", _f32(means), _f32(covars), _f32(views), _f32(Ks), width, height)
+
+
 CONFIGS = {
     "tiny": tiny,
     "config2": config2,
