@@ -142,7 +142,7 @@ def main():
     import numpy as np
     import torch
 
-    from tile_binned_gaussian_amd import frame, synth
+    from tile_binned_gaussian_amd import binding, frame, synth
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     scene = synth.CONFIGS[args.config]()
@@ -181,6 +181,19 @@ def main():
         b_ev.record(plan.stream)
     torch.cuda.synchronize()
     backward_ms = statistics.median(a_ev.elapsed_time(b_ev) for a_ev, b_ev in bev)
+    # outside the frame: the EWA projection that produces such splats, 1M 3D Gaussians into one 1920x1080 camera
+    sc3 = synth.scene3d(19, scene.N, C=1, width=scene.width, height=scene.height)
+    d3 = [torch.from_numpy(a).to("cuda:0") for a in (sc3.means, sc3.covars, sc3.viewmats, sc3.Ks)]
+    proj = binding.gs_project_fwd(*d3, sc3.width, sc3.height, compensation=True)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(5, args.steps // 2))]
+    for a_ev, b_ev in pev:
+        a_ev.record(plan.stream)
+        binding.gs_project_fwd(*d3, sc3.width, sc3.height, compensation=True, out=proj, stream=plan.stream)
+        b_ev.record(plan.stream)
+    torch.cuda.synchronize()
+    project_ms = statistics.median(a_ev.elapsed_time(b_ev) for a_ev, b_ev in pev)
+    project_bytes = sc3.N * (12 + 36) + sc3.C * sc3.N * (8 + 8 + 4 + 12 + 4)
+    del d3, proj
     # outside the frame: the stand-alone stable sort of the same intersections over all populated key bits
     stage_ms["generic_sort"], _ = plan.run_generic_sort(max(5, args.steps // 2))
     pixels = scene.C * scene.width * scene.height
@@ -234,6 +247,11 @@ def main():
         "backward": {"ms": round(backward_ms, 4), "Mpix/s": round(pixels / (backward_ms * 1e-3) / 1e6, 2),
                      "note": "gs_rasterize_bwd on the last frame with seeded standard-normal output gradients; "
                              "clears the gradients, then sums them"},
+        "projection": {"ms": round(project_ms, 4), "gaussians": sc3.N, "bytes": project_bytes,
+                       "GB/s": round(project_bytes / (project_ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(project_bytes / (project_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "note": "gs_project_fwd of 1M seeded 3D Gaussians into one camera at the frame's size, "
+                               "with compensation"},
         "composite_work": {"evaluations_definition": n_eval, "evaluations_executed": n_exec,
                            "alpha_ge_cutoff": n_pass, "composited": n_comp, "splats_staged": n_staged},
         "stages": stages,

@@ -14,7 +14,8 @@
  *                whose per-splat terms fix what the forward computes, and raster_backward_bridge.c
  *                (gs_raster_backward), which lists the forward's arguments;
  *   [rlx-metal]  rlx-metal 0.2.9 splat_training.rs (training_forward_metal_traced): alpha_cutoff and
- *                transmittance_threshold as forward parameters.
+ *                transmittance_threshold as forward parameters;
+ *   [gsplat-proj] the gem's projection.c (gs_project_one): the projection of 3D Gaussians into cameras.
  *
  * Conventions for every entry point.
  *   - Device pointers point to memory on the current HIP device; every array is dense and C-ordered.
@@ -164,6 +165,29 @@ gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const floa
                            float transmittance_threshold, float *render_colors, float *render_alphas,
                            float *render_T, int32_t *last_ids, uint64_t *eval_counts, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * EWA projection of 3D Gaussians ([gsplat-proj] gsplat 1.0.0 projection.c: gs_project_one, gs_mat3_product,
+ * gs_camera_covar, gs_clip) - the step that produces the intersection step's inputs.
+ *
+ * For camera c (world-to-camera viewmats [C, 4, 4], intrinsics Ks [C, 3, 3]) and Gaussian g (means [N, 3],
+ * covariances covars [N, 3, 3]): R = the view's upper 3x3, t its last column; mean_c = R mean + t;
+ * cov_c = (R cov) R^T; depth = mean_c.z; z = depth unless depth <= near_plane or >= far_plane (then 1).
+ * Perspective: x/z and y/z clipped to the image widened by 15% per side, J = [[fx/z, 0, -fx x_c/z^2],
+ * [0, fy/z, -fy y_c/z^2]], mean2d = ((K00 x + K01 y + K02 z)/z, (K10 x + K11 y + K12 z)/z); orthographic:
+ * J = [[fx, 0, 0], [0, fy, 0]], mean2d = (x fx + cx, y fy + cy). cov2d = J cov_c J^T; det0 its determinant;
+ * eps2d added to the diagonal; det; safe = det <= 0 ? 1e-10 : det; r = ceil(3.33 sqrt(max(diag, 0))) per
+ * axis (as int32, clamped to [0, 2^31 - 1]); visible iff det > 0, near < depth < far, some r > radius_clip and
+ * mean2d +- r overlaps the image.
+ * Outputs ([C, N, ...], C order): radii [C, N, 2] int32 (0 when not visible), means2d [C, N, 2], depths [C, N],
+ * conics [C, N, 3] = (c11, -(c01 + c10)/2, c00) / safe, compensations [C, N] (nullable) = sqrt(max(det0 / safe,
+ * 0)). Float32 in the page's operation order (no contraction): the same bits as a plain C evaluation.
+ * Limits: 1 <= C <= 65535, C*N < 2^31. Asynchronous.
+ */
+gs_status gs_project_fwd(const float *means, const float *covars, const float *viewmats, const float *Ks, int64_t C,
+                         int64_t N, int width, int height, float eps2d, float near_plane, float far_plane,
+                         float radius_clip, int orthographic, int32_t *radii, float *means2d, float *depths,
+                         float *conics, float *compensations, void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
  * Backward of the composite ([gsplat-bwd] gs_raster_backward_pixel and gs_raster_backward_without_gvl).

@@ -20,7 +20,7 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
-           "gs_rasterize_fwd", "gs_rasterize_bwd")
+           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_fwd")
 
 
 class GsError(RuntimeError):
@@ -59,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F,
                                      P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_rasterize_bwd.restype = I32
+    lib.gs_project_fwd.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P, P]
+    lib.gs_project_fwd.restype = I32
     _lib = lib
     return lib
 
@@ -270,4 +272,41 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, hei
                                 _ptr(grad_render_colors), _ptr(grad_render_alphas), _ptr(out.means2d),
                                 _ptr(out.conics), _ptr(out.colors), _ptr(out.opacities), _ptr(out.backgrounds),
                                 _ptr(out.means2d_abs), _stream(stream)))
+    return out
+
+
+@dataclass
+class Projection:
+    radii: torch.Tensor  # [C, N, 2] int32
+    means2d: torch.Tensor  # [C, N, 2]
+    depths: torch.Tensor  # [C, N]
+    conics: torch.Tensor  # [C, N, 3]
+    compensations: torch.Tensor | None  # [C, N]
+
+
+def gs_project_fwd(means, covars, viewmats, Ks, width, height, eps2d=0.3, near_plane=0.01, far_plane=1e10,
+                   radius_clip=0.0, compensation=False, orthographic=False, out=None, stream=None) -> Projection:
+    """EWA projection of [N, 3] means and [N, 3, 3] covariances into C cameras."""
+    lib = load_library()
+    dev = means.device
+    _req(means, "means", torch.float32, dev)
+    if means.dim() != 2 or means.shape[1] != 3:
+        raise ValueError("means must be [N, 3]")
+    N = means.shape[0]
+    _req(covars, "covars", torch.float32, dev, (N, 3, 3))
+    _req(viewmats, "viewmats", torch.float32, dev)
+    if viewmats.dim() != 3 or tuple(viewmats.shape[1:]) != (4, 4):
+        raise ValueError("viewmats must be [C, 4, 4]")
+    C = viewmats.shape[0]
+    _req(Ks, "Ks", torch.float32, dev, (C, 3, 3))
+    if out is None:
+        out = Projection(torch.empty((C, N, 2), dtype=torch.int32, device=dev),
+                         torch.empty((C, N, 2), dtype=torch.float32, device=dev),
+                         torch.empty((C, N), dtype=torch.float32, device=dev),
+                         torch.empty((C, N, 3), dtype=torch.float32, device=dev),
+                         torch.empty((C, N), dtype=torch.float32, device=dev) if compensation else None)
+    _check(lib.gs_project_fwd(_ptr(means), _ptr(covars), _ptr(viewmats), _ptr(Ks), C, N, int(width), int(height),
+                              float(eps2d), float(near_plane), float(far_plane), float(radius_clip),
+                              int(bool(orthographic)), _ptr(out.radii), _ptr(out.means2d), _ptr(out.depths),
+                              _ptr(out.conics), _ptr(out.compensations), _stream(stream)))
     return out
