@@ -54,7 +54,7 @@ def _load():
         lib.orc_exp_neg_array.argtypes, lib.orc_exp_neg_array.restype = [P, P, I64], None
         lib.orc_composite_pixel.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, P, P, P, P]
         lib.orc_composite_pixel.restype = None
-        lib.orc_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F, F,
+        lib.orc_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
                                           P, I64, P, P, P, P]
         lib.orc_rasterize_fwd.restype = I64
         lib.orc_tile_lists.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, I64, P, P]
@@ -63,8 +63,8 @@ def _load():
                                            P]
         lib.orc_rasterize_tile.restype = I64
         lib.orc_rects.argtypes, lib.orc_rects.restype = [P, P, I32, I64, I32, I32, I32, P], None
-        lib.orc_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F,
-                                          P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.orc_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
+                                          F, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_rasterize_bwd.restype = I32
         lib.orc_project.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P]
         lib.orc_project.restype = None
@@ -185,7 +185,8 @@ class Raster:
 
 
 def rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
-                  flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, tiles=None) -> Raster:
+                  flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, tiles=None,
+                  masks=None) -> Raster:
     """Front-to-back compositing over every tile (or only the listed global tiles; other pixels stay NaN)."""
     lib = _load()
     means2d = _c(means2d, np.float32)
@@ -202,7 +203,8 @@ def rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height
     tl = None if tiles is None else _c(tiles, np.int64)
     n_eval = lib.orc_rasterize_fwd(_p(means2d), _p(_c(conics, np.float32)), _p(colors),
                                    _p(_c(opacities, np.float32)), _p(bg), C, K, width, height, tile_size, tw, th,
-                                   _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects), float(alpha_cutoff),
+                                   _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects),
+                                   _p(None if masks is None else _c(masks, np.int32)), float(alpha_cutoff),
                                    float(alpha_clamp), float(transmittance_threshold), _p(tl),
                                    0 if tl is None else tl.size, _p(out_c), _p(out_a), _p(out_t), _p(out_l))
     if n_eval < 0:
@@ -282,7 +284,7 @@ class RasterGrad:
 
 def rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                   flatten_ids, n_isects, alpha_cutoff, alpha_clamp, render_alphas, last_ids, grad_colors,
-                  grad_alphas) -> RasterGrad:
+                  grad_alphas, masks=None) -> RasterGrad:
     """Backward of the composite over every tile (orc_rasterize_bwd)."""
     lib = _load()
     means2d = _c(means2d, np.float32)
@@ -296,7 +298,8 @@ def rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height
     a = [z(C, N, 2), z(C, N, 3), z(C, N, K), z(C, N), None if bg is None else z(C, K)]
     rc = lib.orc_rasterize_bwd(_p(means2d), _p(_c(conics, np.float32)), _p(_c(colors, np.float32)),
                                _p(_c(opacities, np.float32)), _p(bg), C, N, K, width, height, tile_size, tw, th,
-                               _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects), float(alpha_cutoff),
+                               _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects),
+                               _p(None if masks is None else _c(masks, np.int32)), float(alpha_cutoff),
                                float(alpha_clamp), _p(_c(render_alphas, np.float32)), _p(_c(last_ids, np.int32)),
                                _p(_c(grad_colors, np.float32)), _p(_c(grad_alphas, np.float32)),
                                *[_p(x) for x in g], *[_p(x) for x in a])

@@ -297,12 +297,14 @@ void orc_composite_pixel(const float *means2d, const float *conics, const float 
  * pixels clipped to width x height. Outputs per pixel: colour = acc + T * background (0 without one),
  * alpha = 1 - T, T, and last id (global intersection index, -1 if nothing composited).
  * tiles == NULL processes every tile; otherwise only the n_tiles listed (other pixels are left untouched).
+ * masks (nullable, [C, th, tw] int32): a tile whose mask is 0 composites nothing (its pixels show the background,
+ * T = 1, last id -1); the backward page skips such tiles' splats, which fixes this reading of the forward.
  * Returns the number of sigma evaluations. */
 int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
                           const float *opacities, const float *backgrounds, int64_t C, int K, int width,
                           int height, int tile_size, int tile_width, int tile_height, const int32_t *offsets,
-                          const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
-                          float transmittance_threshold, const int64_t *tiles, int64_t n_tiles,
+                          const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks, float alpha_cutoff,
+                          float alpha_clamp, float transmittance_threshold, const int64_t *tiles, int64_t n_tiles,
                           float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids)
 {
     int64_t per_camera = (int64_t)tile_width * tile_height;
@@ -319,6 +321,7 @@ int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float
         int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
         int64_t start = offsets[t];
         int64_t end = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
+        if (masks && masks[t] == 0) end = start; /* a masked tile composites nothing: background, T = 1 */
         for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
             for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
                 float T;
@@ -394,13 +397,15 @@ int64_t orc_rasterize_tile(const float *means2d, const float *conics, const floa
  * The pages add the terms into float arrays in an order their threads leave open; here each float term is added
  * into double accumulators (the sum of the terms up to double rounding), and abs_* (nullable) receive the sums of
  * the terms' magnitudes, which bound what any float summation order can change. g_means_abs (nullable) receives
- * |mean term| per axis. g_bg and abs_bg may be NULL (no background gradient). Masks are not supported.
+ * |mean term| per axis. g_bg and abs_bg may be NULL (no background gradient). masks (nullable, [C, th, tw]): a tile
+ * whose mask is 0 adds only its pixels' background terms.
  * Returns 0, or -1 for a bad argument. */
 int orc_rasterize_bwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
                       const float *backgrounds, int64_t C, int64_t N, int K, int width, int height, int tile_size,
                       int tile_width, int tile_height, const int32_t *offsets, const int32_t *flatten_ids,
-                      int64_t n_isects, float alpha_cutoff, float alpha_clamp, const float *render_alphas,
-                      const int32_t *last_ids, const float *grad_colors_px, const float *grad_alphas_px,
+                      int64_t n_isects, const int32_t *masks, float alpha_cutoff, float alpha_clamp,
+                      const float *render_alphas, const int32_t *last_ids, const float *grad_colors_px,
+                      const float *grad_alphas_px,
                       double *g_means, double *g_conics, double *g_colors, double *g_opacities, double *g_bg,
                       double *g_means_abs, double *abs_means, double *abs_conics, double *abs_colors,
                       double *abs_opacities, double *abs_bg)
@@ -416,6 +421,7 @@ int orc_rasterize_bwd(const float *means2d, const float *conics, const float *co
         int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
         int64_t start = offsets[t];
         int64_t end = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
+        if (masks && masks[t] == 0) end = start; /* masked: only the background term ([gsplat-bwd]) */
         for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
             for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
                 int64_t pixel = (camera * height + y) * (int64_t)width + x;

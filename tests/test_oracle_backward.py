@@ -238,3 +238,54 @@ def test_clamped_splat_has_no_shape_or_opacity_gradient():
     np.testing.assert_allclose(g.colors[0, 0], gcv * clamp, rtol=1e-6)
     np.testing.assert_allclose(g.backgrounds[0], gcv * float(np.float32(1) - np.float32(clamp)), rtol=1e-5)
     assert np.all(g.opacities == 0) and np.all(g.means2d == 0) and np.all(g.conics == 0)
+
+
+def test_masked_tiles_finite_differences_and_forward():
+    """Per-tile masks: a masked tile composites nothing (background, T = 1, no last id) in the forward, and in the
+    backward adds only its background terms; checked against finite differences of the float64 forward with the
+    same masks applied, and the forward against the unmasked run on the other tiles."""
+    s = _smooth_scene(31, W=24, H=16, ts=8)
+    it, off, ras = oracle.scene_pipeline(s)
+    masks = np.ones_like(off)
+    masks.reshape(-1)[[0, 4]] = 0  # two of the six tiles
+    rm = oracle.rasterize_fwd(s.means2d, s.conics, s.colors, s.opacities, s.backgrounds, s.width, s.height,
+                              s.tile_size, off, it.flatten_ids, it.n_isects, s.alpha_cutoff, s.alpha_clamp,
+                              s.transmittance_threshold, masks=masks)
+    ty, tx = np.divmod(np.arange(s.height * s.width).reshape(s.height, s.width), s.width)
+    tile = (ty // s.tile_size) * s.tile_width + (tx // s.tile_size)
+    masked_px = masks.reshape(-1)[tile] == 0
+    assert masked_px.any() and not masked_px.all()
+    np.testing.assert_array_equal(rm.render_T[0][masked_px], 1.0)
+    np.testing.assert_array_equal(rm.last_ids[0][masked_px], -1)
+    np.testing.assert_array_equal(rm.render_colors[0][masked_px], np.broadcast_to(s.backgrounds[0], (masked_px.sum(), 3)))
+    for a, b in [(rm.render_colors, ras.render_colors), (rm.render_T, ras.render_T), (rm.last_ids, ras.last_ids)]:
+        np.testing.assert_array_equal(a[0][~masked_px], b[0][~masked_px])
+
+    flat = off.reshape(-1).astype(np.int64)
+    ends = np.append(flat[1:], it.n_isects)
+    lists = [it.flatten_ids[flat[t]:ends[t]] if masks.reshape(-1)[t] else it.flatten_ids[:0]
+             for t in range(flat.size)]
+    rng = np.random.default_rng(32)
+    gc = rng.normal(size=rm.render_colors.shape).astype(np.float32)
+    ga = rng.normal(size=rm.render_alphas.shape).astype(np.float32)
+    g = oracle.rasterize_bwd(s.means2d, s.conics, s.colors, s.opacities, s.backgrounds, s.width, s.height,
+                             s.tile_size, off, it.flatten_ids, it.n_isects, s.alpha_cutoff, s.alpha_clamp,
+                             rm.render_alphas, rm.last_ids, gc, ga, masks=masks)
+    base = [s.means2d.astype(np.float64), s.conics.astype(np.float64), s.colors.astype(np.float64),
+            s.opacities.astype(np.float64), s.backgrounds.astype(np.float64)]
+
+    def loss(params):
+        o, a = _forward64(s, lists, params)
+        return float((gc * o).sum() + (ga * a).sum())
+
+    for which, grad in enumerate([g.means2d, g.opacities, g.backgrounds]):
+        idx_group = [0, 3, 4][which]
+        fd = np.zeros_like(base[idx_group])
+        for idx in np.ndindex(base[idx_group].shape):
+            h = 1e-5 * max(1.0, abs(base[idx_group][idx]))
+            up = [p.copy() for p in base]
+            dn = [p.copy() for p in base]
+            up[idx_group][idx] += h
+            dn[idx_group][idx] -= h
+            fd[idx] = (loss(up) - loss(dn)) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=2e-3, atol=2e-4 * np.abs(fd).max())
