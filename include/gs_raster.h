@@ -146,6 +146,8 @@ gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int64_t C, int 
  * render_alphas [C, H, W] = 1 - T, render_T [C, H, W] = T (nullable), last_ids [C, H, W] = last (nullable;
  * a global intersection index, -1 if nothing composited).
  * conics [C, N, 3] = (inv00, inv01, inv11) of the 2D covariance; colors [C, N, K]; opacities [C, N].
+ * masks: nullable [C, th, tw] int32 per-tile mask; a tile whose mask is 0 composites nothing (its pixels get the
+ *   background, render_alphas 0, T 1 and last id -1) - the backward page skips such tiles' splats.
  * eval_counts: nullable device uint64[5]; when set, the launch ADDS work counts: [0] the evaluations of sigma the
  * definition makes (per pixel, each splat of its range up to and including the one that stops it), [1] those
  * with alpha >= alpha_cutoff, [2] the splats composited, [3] the evaluations the kernel actually made (it skips
@@ -161,7 +163,8 @@ size_t gs_rasterize_workspace_bytes(int64_t C, int tile_width, int tile_height);
 gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
                            const float *backgrounds, int64_t C, int64_t N, int K, int width, int height,
                            int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
-                           const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
+                           const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks,
+                           float alpha_cutoff, float alpha_clamp,
                            float transmittance_threshold, float *render_colors, float *render_alphas,
                            float *render_T, int32_t *last_ids, uint64_t *eval_counts, void *workspace,
                            size_t workspace_bytes, void *stream);
@@ -211,12 +214,14 @@ gs_status gs_project_fwd(const float *means, const float *covars, const float *v
  * over 16-lane rows, LDS atomics per tile, then one float atomic per splat and tile), so results agree with any
  * other summation order to within float rounding of the sum of the terms' magnitudes, and may differ in the last
  * bits from run to run.
+ * masks: nullable [C, th, tw]; a tile whose mask is 0 adds only its pixels' background terms.
  * The gradient arrays are overwritten (cleared, then summed into). Limits as gs_rasterize_fwd. Asynchronous.
  */
 gs_status gs_rasterize_bwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
                            const float *backgrounds, int64_t C, int64_t N, int K, int width, int height,
                            int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
-                           const int32_t *flatten_ids, int64_t n_isects, float alpha_cutoff, float alpha_clamp,
+                           const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks,
+                           float alpha_cutoff, float alpha_clamp,
                            const float *render_alphas, const int32_t *last_ids, const float *grad_render_colors,
                            const float *grad_render_alphas, float *grad_means2d, float *grad_conics,
                            float *grad_colors, float *grad_opacities, float *grad_backgrounds,

@@ -116,7 +116,7 @@ def test_rasterize_argument_errors(lib):
     F = ctypes.c_float
 
     def call(C=1, N=4, K=3, W=64, H=64, ts=16, tw=4, th=4, n=10, cut=1 / 255, clamp=0.99, thr=1e-4, ptr=fake):
-        return lib.gs_rasterize_fwd(ptr, ptr, ptr, ptr, None, C, N, K, W, H, ts, tw, th, ptr, ptr, n, F(cut),
+        return lib.gs_rasterize_fwd(ptr, ptr, ptr, ptr, None, C, N, K, W, H, ts, tw, th, ptr, ptr, n, None, F(cut),
                                     F(clamp), F(thr), ptr, ptr, None, None, None, None, 0, None)
     assert call(K=0) == GS_ERR_INVALID_ARG
     assert call(K=5) == GS_ERR_INVALID_ARG
@@ -135,7 +135,7 @@ def test_rasterize_bwd_argument_errors(lib):
 
     def bwd(C=1, N=4, K=3, W=32, H=32, ts=16, tw=2, th=2, n=10, cut=1 / 255, clamp=0.99, means=fake,
             ra=fake, last=fake, gc=fake, ga=fake, gm=fake):
-        return lib.gs_rasterize_bwd(means, fake, fake, fake, None, C, N, K, W, H, ts, tw, th, fake, fake, n, cut,
+        return lib.gs_rasterize_bwd(means, fake, fake, fake, None, C, N, K, W, H, ts, tw, th, fake, fake, n, None, cut,
                                     clamp, ra, last, gc, ga, gm, fake, fake, fake, None, None, None)
 
     assert bwd(K=5) == GS_ERR_INVALID_ARG

@@ -116,3 +116,33 @@ def test_backward_without_background_gradient_or_abs():
                                      out=full)
     torch.cuda.synchronize()
     torch.testing.assert_close(again.means2d, lean.means2d, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["multicam-ragged-elliptical", "ts8-margin", "ts32-ppt4"])
+def test_masked_backward_matches_oracle(name):
+    scene = SCENES[name]()
+    fr = gpu_frame(scene)
+    off, ids, n = fr.isect_offsets, fr.isect.flatten_ids, fr.isect.n_isects
+    masks = (np.random.default_rng(len(name) + 7).uniform(size=tuple(off.shape)) < 0.6).astype(np.int32)
+    m = lambda a: dev(a)  # noqa: E731
+    bg = None if scene.backgrounds is None else m(scene.backgrounds)
+    ren = binding.gs_rasterize_fwd(m(scene.means2d), m(scene.conics), m(scene.colors), m(scene.opacities), bg,
+                                   scene.width, scene.height, scene.tile_size, off, ids, n, scene.alpha_cutoff,
+                                   scene.alpha_clamp, scene.transmittance_threshold, masks=m(masks))
+    gc, ga = _grads_in(scene, 9)
+    o = oracle.rasterize_bwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
+                             scene.width, scene.height, scene.tile_size, host(off), host(ids), n,
+                             scene.alpha_cutoff, scene.alpha_clamp, host(ren.render_alphas), host(ren.last_ids), gc,
+                             ga, masks=masks)
+    g = binding.gs_rasterize_bwd(m(scene.means2d), m(scene.conics), m(scene.colors), m(scene.opacities), bg,
+                                 scene.width, scene.height, scene.tile_size, off, ids, ren.render_alphas,
+                                 ren.last_ids, m(gc), m(ga), n_isects=n, alpha_cutoff=scene.alpha_cutoff,
+                                 alpha_clamp=scene.alpha_clamp, masks=m(masks))
+    torch.cuda.synchronize()
+    adds = host(fr.isect.tiles_per_gauss).astype(np.float64) * 4 * _waves_per_tile(scene.tile_size)
+    _assert_close(host(g.means2d), o.means2d, o.abs_means2d, adds[..., None], "means2d")
+    _assert_close(host(g.conics), o.conics, o.abs_conics, adds[..., None], "conics")
+    _assert_close(host(g.opacities), o.opacities, o.abs_opacities, adds, "opacities")
+    if scene.backgrounds is not None:
+        pixels_adds = scene.tile_width * scene.tile_height * _waves_per_tile(scene.tile_size)
+        _assert_close(host(g.backgrounds), o.backgrounds, o.abs_backgrounds, pixels_adds, "backgrounds")

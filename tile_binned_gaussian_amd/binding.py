@@ -53,10 +53,10 @@ def load_library(path: str = LIB_PATH):
     lib.gs_tile_ranges.restype = I32
     lib.gs_rasterize_workspace_bytes.argtypes = [I64, I32, I32]
     lib.gs_rasterize_workspace_bytes.restype = SZ
-    lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F, F,
+    lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
                                      P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd.restype = I32
-    lib.gs_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, F, F,
+    lib.gs_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F,
                                      P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_rasterize_bwd.restype = I32
     lib.gs_project_fwd.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P, P]
@@ -189,7 +189,8 @@ class Render:
 
 def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
-                     transmittance_threshold=1e-4, out=None, stream=None, workspace=None, eval_counts=None) -> Render:
+                     transmittance_threshold=1e-4, out=None, stream=None, workspace=None, eval_counts=None,
+                     masks=None) -> Render:
     """Front-to-back compositing of every tile; returns colours, 1 - T, T and the last composited index.
 
     eval_counts: optional int64 [5] device tensor that the launch adds to (evaluations by the definition, alpha >=
@@ -216,9 +217,11 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
                      torch.empty((C, height, width), dtype=torch.float32, device=dev),
                      torch.empty((C, height, width), dtype=torch.int32, device=dev))
     ws = workspace if workspace is not None else _workspace(lib.gs_rasterize_workspace_bytes(C, tw, th), dev)
+    if masks is not None:
+        _req(masks, "masks", torch.int32, dev, (C, th, tw))
     _check(lib.gs_rasterize_fwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
                                 K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
-                                float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
+                                _ptr(masks), float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
                                 _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
                                 _ptr(out.last_ids), _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
     return out
@@ -237,7 +240,7 @@ class RasterGrad:
 def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, render_alphas, last_ids, grad_render_colors, grad_render_alphas, n_isects=None,
                      alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, grad_backgrounds=None, absgrad=False, out=None,
-                     stream=None) -> RasterGrad:
+                     stream=None, masks=None) -> RasterGrad:
     """Gradients of sum(grad_render_colors * colours) + sum(grad_render_alphas * alphas) of gs_rasterize_fwd.
 
     grad_backgrounds: None -> computed when backgrounds is given; False -> not computed."""
@@ -266,9 +269,11 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, hei
         e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
         out = RasterGrad(e(C, N, 2), e(C, N, 3), e(C, N, K), e(C, N), e(C, K) if want_bg else None,
                          e(C, N, 2) if absgrad else None)
+    if masks is not None:
+        _req(masks, "masks", torch.int32, dev, (C, th, tw))
     _check(lib.gs_rasterize_bwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
                                 K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
-                                float(alpha_cutoff), float(alpha_clamp), _ptr(render_alphas), _ptr(last_ids),
+                                _ptr(masks), float(alpha_cutoff), float(alpha_clamp), _ptr(render_alphas), _ptr(last_ids),
                                 _ptr(grad_render_colors), _ptr(grad_render_alphas), _ptr(out.means2d),
                                 _ptr(out.conics), _ptr(out.colors), _ptr(out.opacities), _ptr(out.backgrounds),
                                 _ptr(out.means2d_abs), _stream(stream)))

@@ -25,6 +25,7 @@ struct RasterArgs {
     const float *backgrounds;
     const int32_t *offsets;
     const int32_t *ids;
+    const int32_t *masks;  // nullable [C, th, tw]: 0 = composite nothing in this tile
     int64_t n_isects;
     int total_tiles, width, height, tile_size, tile_width, tile_height;
     float alpha_cutoff, alpha_clamp, transmittance_threshold;
@@ -47,7 +48,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
     const int start = a.offsets[tile];
-    const int end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects);
+    // a tile whose mask is 0 composites nothing (its range is taken as empty)
+    const int end = (a.masks && a.masks[tile] == 0) ? start
+                    : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
     const int ts = a.tile_size;
     const int nthreads = blockDim.x;
 
@@ -171,7 +174,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
     const int start = a.offsets[tile];
-    const int end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects);
+    // a tile whose mask is 0 composites nothing (its range is taken as empty)
+    const int end = (a.masks && a.masks[tile] == 0) ? start
+                    : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
     const int ts = a.tile_size;
     const int nthreads = blockDim.x;
     const int wave = threadIdx.x / kWave;
@@ -346,7 +351,8 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
                                       const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
                                       int width, int height, int tile_size, int tile_width, int tile_height,
                                       const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
-                                      float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                                      const int32_t *masks, float alpha_cutoff, float alpha_clamp,
+                                      float transmittance_threshold,
                                       float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
                                       uint64_t *eval_counts, void *workspace, size_t workspace_bytes,
                                       void *stream_handle) {
@@ -384,6 +390,7 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
     args.offsets = isect_offsets;
     args.ids = flatten_ids;
     args.n_isects = n_isects;
+    args.masks = masks;
     args.total_tiles = static_cast<int>(total_tiles);
     args.width = width;
     args.height = height;

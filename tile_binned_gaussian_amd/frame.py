@@ -146,7 +146,7 @@ class FramePlan:
         binding._check(lib.gs_rasterize_fwd(P(ds.means2d), P(ds.conics), P(ds.colors), P(ds.opacities),
                                             P(ds.backgrounds), ds.C, ds.N, ds.colors.shape[2], ds.width, ds.height,
                                             ds.tile_size, ds.tile_width, ds.tile_height, P(self.offsets),
-                                            P(self.ids), n, ctypes.c_float(ds.alpha_cutoff),
+                                            P(self.ids), n, None, ctypes.c_float(ds.alpha_cutoff),
                                             ctypes.c_float(ds.alpha_clamp),
                                             ctypes.c_float(ds.transmittance_threshold), P(r.render_colors),
                                             P(r.render_alphas), P(r.render_T), P(r.last_ids), P(eval_counts),
