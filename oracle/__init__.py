@@ -57,6 +57,12 @@ def _load():
         lib.orc_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
                                           P, I64, P, P, P, P]
         lib.orc_rasterize_fwd.restype = I64
+        lib.orc_rasterize_fwd_traced.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
+                                                 F, F, P, I64, I64, I64, P, P, P, P, P, P]
+        lib.orc_rasterize_fwd_traced.restype = I64
+        lib.orc_composite_pixel_traced.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, I64, P, P, P,
+                                                   P, P, P]
+        lib.orc_composite_pixel_traced.restype = None
         lib.orc_tile_lists.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, I64, P, P]
         lib.orc_tile_lists.restype = I64
         lib.orc_rasterize_tile.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, P, I64, F, F, F, P, P,
@@ -210,6 +216,68 @@ def rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height
     if n_eval < 0:
         raise ValueError("invalid rasterize arguments")
     return Raster(out_c, out_a, out_t, out_l, int(n_eval))
+
+
+@dataclass
+class TracedRaster(Raster):
+    trace_ids: np.ndarray  # [C, H, W, max_splat_steps] int32 flat splat ids; entries past the count hold -2
+    trace_counts: np.ndarray  # [C, H, W] int32
+
+
+def rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
+                         flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, max_splat_steps,
+                         max_list_entries=-1, masks=None, trace=True) -> TracedRaster:
+    """The traced forward: every tile's list cut to its first ``max_list_entries`` entries (negative: whole
+    lists), every pixel capped at ``max_splat_steps`` composited splats (negative: uncapped, only without a
+    trace), and each pixel's composited flat splat ids recorded in order."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    C = means2d.shape[0]
+    K = colors.shape[-1]
+    off = _c(isect_offsets, np.int32)
+    th, tw = off.shape[1], off.shape[2]
+    colors = _c(colors, np.float32)
+    bg = None if backgrounds is None else _c(backgrounds, np.float32)
+    S = int(max_splat_steps)
+    out_c = np.full((C, height, width, K), np.nan, np.float32)
+    out_a = np.full((C, height, width), np.nan, np.float32)
+    out_t = np.full((C, height, width), np.nan, np.float32)
+    out_l = np.full((C, height, width), -2, np.int32)
+    tr = np.full((C, height, width, max(S, 0)), -2, np.int32) if trace else None
+    cnt = np.full((C, height, width), -2, np.int32) if trace else None
+    n_eval = lib.orc_rasterize_fwd_traced(_p(means2d), _p(_c(conics, np.float32)), _p(colors),
+                                          _p(_c(opacities, np.float32)), _p(bg), C, K, width, height, tile_size, tw,
+                                          th, _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects),
+                                          _p(None if masks is None else _c(masks, np.int32)), float(alpha_cutoff),
+                                          float(alpha_clamp), float(transmittance_threshold), None, 0,
+                                          int(max_list_entries), S, _p(out_c), _p(out_a), _p(out_t), _p(out_l),
+                                          _p(tr), _p(cnt))
+    if n_eval < 0:
+        raise ValueError("invalid rasterize arguments")
+    return TracedRaster(out_c, out_a, out_t, out_l, int(n_eval), tr, cnt)
+
+
+def composite_pixel_traced(means2d, conics, colors, opacities, list_ids, x, y, alpha_cutoff, alpha_clamp,
+                           transmittance_threshold, max_steps):
+    """orc_composite_pixel_traced over an explicit list: (acc[K], T, last_position, n_eval, trace of flat ids)."""
+    lib = _load()
+    means2d = _c(means2d, np.float32).reshape(-1, 2)
+    conics = _c(conics, np.float32).reshape(-1, 3)
+    K = colors.shape[-1]
+    colors = _c(colors, np.float32).reshape(-1, K)
+    opacities = _c(opacities, np.float32).reshape(-1)
+    lst = _c(list_ids, np.int32)
+    acc = np.zeros(K, np.float32)
+    T = np.zeros(1, np.float32)
+    last = np.zeros(1, np.int64)
+    ne = np.zeros(1, np.int64)
+    steps = np.zeros(1, np.int64)
+    tr = np.full(max(lst.size, 1), -2, np.int32)
+    lib.orc_composite_pixel_traced(_p(means2d), _p(conics), _p(colors), _p(opacities), K, _p(lst), 0, lst.size,
+                                   int(x), int(y), float(alpha_cutoff), float(alpha_clamp),
+                                   float(transmittance_threshold), int(max_steps), _p(acc), _p(T), _p(last), _p(ne),
+                                   _p(tr), _p(steps))
+    return acc, float(T[0]), int(last[0]), int(ne[0]), tr[:int(steps[0])].copy()
 
 
 def tile_lists(means2d, radii, depths, tile_size, tile_width, tile_height, tiles):

@@ -13,7 +13,9 @@
  *            end) fix what the forward computes; the forward itself is not on the pages and is read as the
  *            front-to-back inverse of that backward.
  *   [rlx-metal] rlx-metal 0.2.9 splat_training.rs, training_forward_metal_traced: names alpha_cutoff and
- *            transmittance_threshold as forward parameters, and a cutoff default of 1/255.
+ *            transmittance_threshold as forward parameters, and a cutoff default of 1/255; names the traced
+ *            forward's max_splat_steps (per-pixel trace of composited splats kept for the backward: counts and
+ *            ids) and the tile-list cap max_list_entries (orc_rasterize_fwd_traced).
  *   The composite's backward (orc_rasterize_bwd) follows [gsplat-bwd] gs_raster_backward_pixel directly.
  *   [gsplat-proj] the same gem's projection.c (gs_mat3_product, gs_camera_covar, gs_clip, gs_project_one): the
  *            EWA projection of 3D Gaussians into cameras (orc_project).
@@ -258,19 +260,25 @@ void orc_exp_neg_array(const float *sigma, float *out, int64_t n)
  *   sigma < 0 -> skip; alpha = min(clamp, opacity * e^-sigma); alpha < cutoff -> skip;
  *   T' = T (1 - alpha); T' <= threshold -> stop before this splat ([rlx-metal] transmittance_threshold);
  *   otherwise colour += colour_g * (alpha T), T = T', last = position.
+ * The traced variant ([rlx-metal] max_splat_steps): a composited splat is one step; with max_steps >= 0 the
+ * pixel stops right after its max_steps-th step (at once when max_steps is 0), and trace (nullable) receives the
+ * flat splat id of each step in order. *steps_out (nullable) receives the number of steps.
  * Writes acc[K], the final transmittance and the last composited position (-1 if none); counts every
  * evaluation of sigma (including the stopping one) into *n_eval. */
-void orc_composite_pixel(const float *means2d, const float *conics, const float *colors,
-                         const float *opacities, int K, const int32_t *list, int64_t start, int64_t end,
-                         int x, int y, float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
-                         float *acc, float *T_out, int64_t *last_out, int64_t *n_eval)
+void orc_composite_pixel_traced(const float *means2d, const float *conics, const float *colors,
+                                const float *opacities, int K, const int32_t *list, int64_t start, int64_t end,
+                                int x, int y, float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                                int64_t max_steps, float *acc, float *T_out, int64_t *last_out, int64_t *n_eval,
+                                int32_t *trace, int64_t *steps_out)
 {
     float px = (float)x + 0.5f;
     float py = (float)y + 0.5f;
     float T = 1.0f;
     int64_t last = -1;
+    int64_t steps = 0;
     for (int k = 0; k < K; ++k) acc[k] = 0.0f;
     for (int64_t i = start; i < end; ++i) {
+        if (max_steps >= 0 && steps >= max_steps) break;
         int64_t g = list[i];
         float dx = means2d[g * 2] - px;
         float dy = means2d[g * 2 + 1] - py;
@@ -287,9 +295,22 @@ void orc_composite_pixel(const float *means2d, const float *conics, const float 
         for (int k = 0; k < K; ++k) acc[k] = acc[k] + colors[g * K + k] * v;
         T = T_next;
         last = i;
+        if (trace) trace[steps] = (int32_t)g;
+        steps += 1;
     }
     *T_out = T;
     *last_out = last;
+    if (steps_out) *steps_out = steps;
+}
+
+/* The untraced composite of one pixel: orc_composite_pixel_traced with no step cap and no trace. */
+void orc_composite_pixel(const float *means2d, const float *conics, const float *colors,
+                         const float *opacities, int K, const int32_t *list, int64_t start, int64_t end,
+                         int x, int y, float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                         float *acc, float *T_out, int64_t *last_out, int64_t *n_eval)
+{
+    orc_composite_pixel_traced(means2d, conics, colors, opacities, K, list, start, end, x, y, alpha_cutoff,
+                               alpha_clamp, transmittance_threshold, -1, acc, T_out, last_out, n_eval, NULL, NULL);
 }
 
 /* Forward rasterization over tiles ([gsplat-bwd] gs_raster_backward_without_gvl for the tile walk): global
@@ -299,13 +320,23 @@ void orc_composite_pixel(const float *means2d, const float *conics, const float 
  * tiles == NULL processes every tile; otherwise only the n_tiles listed (other pixels are left untouched).
  * masks (nullable, [C, th, tw] int32): a tile whose mask is 0 composites nothing (its pixels show the background,
  * T = 1, last id -1); the backward page skips such tiles' splats, which fixes this reading of the forward.
- * Returns the number of sigma evaluations. */
-int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
-                          const float *opacities, const float *backgrounds, int64_t C, int K, int width,
-                          int height, int tile_size, int tile_width, int tile_height, const int32_t *offsets,
-                          const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks, float alpha_cutoff,
-                          float alpha_clamp, float transmittance_threshold, const int64_t *tiles, int64_t n_tiles,
-                          float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids)
+ * Traced variant ([rlx-metal] training_forward_metal_traced):
+ *   max_list_entries >= 0 keeps only the first max_list_entries entries of every tile's list (the nearest
+ *   ones); a negative value keeps whole lists;
+ *   max_splat_steps >= 0 caps every pixel at that many composited splats (orc_composite_pixel_traced); a
+ *   negative value leaves pixels uncapped;
+ *   trace_ids (nullable, [C, H, W, max_splat_steps] int32) receives each pixel's composited flat splat ids in
+ *   front-to-back order, entries past the pixel's count untouched; trace_counts (nullable, [C, H, W] int32)
+ *   receives the count. Tracing needs max_splat_steps >= 0 (the row length).
+ * Returns the number of sigma evaluations, or -1 for a bad argument. */
+int64_t orc_rasterize_fwd_traced(const float *means2d, const float *conics, const float *colors,
+                                 const float *opacities, const float *backgrounds, int64_t C, int K, int width,
+                                 int height, int tile_size, int tile_width, int tile_height, const int32_t *offsets,
+                                 const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks,
+                                 float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                                 const int64_t *tiles, int64_t n_tiles, int64_t max_list_entries,
+                                 int64_t max_splat_steps, float *render_colors, float *render_alphas,
+                                 float *render_T, int32_t *last_ids, int32_t *trace_ids, int32_t *trace_counts)
 {
     int64_t per_camera = (int64_t)tile_width * tile_height;
     int64_t total_tiles = C * per_camera;
@@ -313,6 +344,7 @@ int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float
     int64_t n_eval = 0;
     float acc[64];
     if (K < 1 || K > 64) return -1;
+    if ((trace_ids || trace_counts) && max_splat_steps < 0) return -1;
     for (int64_t j = 0; j < count; ++j) {
         int64_t t = tiles ? tiles[j] : j;
         if (t < 0 || t >= total_tiles) return -1;
@@ -322,13 +354,16 @@ int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float
         int64_t start = offsets[t];
         int64_t end = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
         if (masks && masks[t] == 0) end = start; /* a masked tile composites nothing: background, T = 1 */
+        if (max_list_entries >= 0 && end - start > max_list_entries) end = start + max_list_entries;
         for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
             for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
                 float T;
-                int64_t last;
-                orc_composite_pixel(means2d, conics, colors, opacities, K, flatten_ids, start, end, x, y,
-                                    alpha_cutoff, alpha_clamp, transmittance_threshold, acc, &T, &last, &n_eval);
+                int64_t last, steps;
                 int64_t pixel = (camera * height + y) * (int64_t)width + x;
+                int32_t *trace = trace_ids ? trace_ids + pixel * max_splat_steps : NULL;
+                orc_composite_pixel_traced(means2d, conics, colors, opacities, K, flatten_ids, start, end, x, y,
+                                           alpha_cutoff, alpha_clamp, transmittance_threshold, max_splat_steps,
+                                           acc, &T, &last, &n_eval, trace, &steps);
                 for (int k = 0; k < K; ++k) {
                     float bg = backgrounds ? backgrounds[camera * K + k] : 0.0f;
                     render_colors[pixel * K + k] = acc[k] + T * bg;
@@ -336,10 +371,25 @@ int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float
                 render_alphas[pixel] = 1.0f - T;
                 if (render_T) render_T[pixel] = T;
                 if (last_ids) last_ids[pixel] = (int32_t)last;
+                if (trace_counts) trace_counts[pixel] = (int32_t)steps;
             }
         }
     }
     return n_eval;
+}
+
+/* The untraced forward: orc_rasterize_fwd_traced with whole lists and no step cap. */
+int64_t orc_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
+                          const float *opacities, const float *backgrounds, int64_t C, int K, int width,
+                          int height, int tile_size, int tile_width, int tile_height, const int32_t *offsets,
+                          const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks, float alpha_cutoff,
+                          float alpha_clamp, float transmittance_threshold, const int64_t *tiles, int64_t n_tiles,
+                          float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids)
+{
+    return orc_rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, C, K, width, height, tile_size,
+                                    tile_width, tile_height, offsets, flatten_ids, n_isects, masks, alpha_cutoff,
+                                    alpha_clamp, transmittance_threshold, tiles, n_tiles, -1, -1, render_colors,
+                                    render_alphas, render_T, last_ids, NULL, NULL);
 }
 
 /* Composite the pixels of one global tile over an explicit front-to-back list of flat ids (the same per-pixel

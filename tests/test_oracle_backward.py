@@ -115,8 +115,9 @@ def _smooth_scene(seed, n=6, W=20, H=18, ts=8, K=3):
     return s
 
 
-def _forward64(s, lists, params):
-    """Independent float64 forward over fixed per-tile lists: returns colour [C,H,W,K] and alpha [C,H,W]."""
+def _forward64(s, lists, params, max_steps=None):
+    """Independent float64 forward over fixed per-tile lists: returns colour [C,H,W,K] and alpha [C,H,W].
+    max_steps: stop each pixel after that many composited splats."""
     means, conics, colors, ops, bg = params
     C, H, W, K, ts = s.C, s.height, s.width, s.colors.shape[-1], s.tile_size
     out = np.zeros((C, H, W, K))
@@ -124,8 +125,10 @@ def _forward64(s, lists, params):
     for y in range(H):
         for x in range(W):
             t = (y // ts) * s.tile_width + x // ts
-            T, acc = 1.0, np.zeros(K)
+            T, acc, steps = 1.0, np.zeros(K), 0
             for g in lists[t]:
+                if max_steps is not None and steps >= max_steps:
+                    break
                 dx, dy = means[0, g, 0] - (x + 0.5), means[0, g, 1] - (y + 0.5)
                 a, b, c = conics[0, g]
                 sigma = 0.5 * (a * dx * dx + c * dy * dy) + b * dx * dy
@@ -139,6 +142,7 @@ def _forward64(s, lists, params):
                     break
                 acc += colors[0, g] * al * T
                 T = tn
+                steps += 1
             out[0, y, x] = acc + T * bg[0]
             alp[0, y, x] = 1 - T
     return out, alp
