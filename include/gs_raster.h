@@ -1,11 +1,14 @@
 /*
  * gs_raster.h: C ABI of the MI355X (gfx950) tile-binned splat rasterizer.
  *
- * One frame runs four steps, each an entry point below:
+ * A frame runs the first four entry points in order; the others extend it:
  *   gs_isect_tiles    splat -> tile intersections and their 64-bit keys (optionally sorted),
  *   gs_sort_keys      stable radix sort of (key, id) pairs over the populated low key bits,
  *   gs_tile_ranges    per-tile [start, end) ranges of a sorted key array,
- *   gs_rasterize_fwd  per-tile front-to-back alpha compositing.
+ *   gs_rasterize_fwd  per-tile front-to-back alpha compositing (gs_rasterize_fwd_traced: with a per-pixel
+ *                     trace, a per-pixel step cap and a per-tile list cap),
+ *   gs_rasterize_bwd  its backward,
+ *   gs_project_fwd    the EWA projection of 3D Gaussians that feeds the intersection step.
  *
  * Definitions follow these pages:
  *   [gsplat]     gsplat 1.0.0 Ruby gem, native C extension, intersections.c (gs_tile_bits, gs_bounds,
@@ -156,7 +159,8 @@ gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int64_t C, int 
  * counted.
  * Limits: 1 <= K <= 4; 1 <= tile_size <= 32; tile_width == ceil(width / tile_size) and
  *   tile_height == ceil(height / tile_size); flatten_ids must index [0, C*N) (not checked on the device).
- * workspace: gs_rasterize_workspace_bytes(C, tile_width, tile_height) bytes (tile scheduling order).
+ * workspace: gs_rasterize_workspace_bytes(C, tile_width, tile_height) bytes, or NULL with 0 bytes. Reserved: the
+ *   size is checked when one is given, but the current kernels neither read nor write it.
  */
 size_t gs_rasterize_workspace_bytes(int64_t C, int tile_width, int tile_height);
 
@@ -168,6 +172,34 @@ gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const floa
                            float transmittance_threshold, float *render_colors, float *render_alphas,
                            float *render_T, int32_t *last_ids, uint64_t *eval_counts, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Traced forward compositing ([rlx-metal] training_forward_metal_traced: max_splat_steps, the per-pixel trace of
+ * counts and ids kept for the backward, and the tile-list cap max_list_entries). Everything gs_rasterize_fwd
+ * computes, with:
+ *   max_list_entries >= 0: each tile's range is cut to its first max_list_entries entries (the nearest ones)
+ *     before compositing; a negative value keeps whole ranges;
+ *   max_splat_steps >= 0: a step is a composited splat; a pixel stops right after its max_splat_steps-th step
+ *     (at once when 0), so render_colors, render_alphas, render_T and last_ids describe exactly the traced splats;
+ *   trace_ids: nullable [C, H, W, max_splat_steps] int32 - each pixel's composited flat splat ids (camera * N +
+ *     Gaussian, the values of flatten_ids) in front-to-back order; entries past the pixel's count are left
+ *     unwritten;
+ *   trace_counts: nullable [C, H, W] int32 - the pixel's number of steps (<= max_splat_steps).
+ * A pixel's trace holds every splat that changed it and nothing else: compositing the pixel over its trace alone
+ * gives the same bits. The range backward (gs_rasterize_bwd) on these outputs is the gradient of the capped forward,
+ * since it walks each pixel back from last_ids and recomputes which splats composited.
+ * eval_counts' first entry counts evaluations up to and including the splat that stops the pixel, by the cap too.
+ * Errors: as gs_rasterize_fwd, plus GS_ERR_INVALID_ARG for max_splat_steps < 0.
+ */
+gs_status gs_rasterize_fwd_traced(const float *means2d, const float *conics, const float *colors,
+                                  const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
+                                  int width, int height, int tile_size, int tile_width, int tile_height,
+                                  const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
+                                  const int32_t *masks, float alpha_cutoff, float alpha_clamp,
+                                  float transmittance_threshold, int max_list_entries, int max_splat_steps,
+                                  float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
+                                  int32_t *trace_ids, int32_t *trace_counts, uint64_t *eval_counts, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
  * EWA projection of 3D Gaussians ([gsplat-proj] gsplat 1.0.0 projection.c: gs_project_one, gs_mat3_product,

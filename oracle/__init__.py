@@ -226,10 +226,11 @@ class TracedRaster(Raster):
 
 def rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                          flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, max_splat_steps,
-                         max_list_entries=-1, masks=None, trace=True) -> TracedRaster:
+                         max_list_entries=-1, masks=None, trace=True, tiles=None) -> TracedRaster:
     """The traced forward: every tile's list cut to its first ``max_list_entries`` entries (negative: whole
     lists), every pixel capped at ``max_splat_steps`` composited splats (negative: uncapped, only without a
-    trace), and each pixel's composited flat splat ids recorded in order."""
+    trace), and each pixel's composited flat splat ids recorded in order. tiles: only these global tiles (other
+    pixels keep the fill values)."""
     lib = _load()
     means2d = _c(means2d, np.float32)
     C = means2d.shape[0]
@@ -245,12 +246,13 @@ def rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width,
     out_l = np.full((C, height, width), -2, np.int32)
     tr = np.full((C, height, width, max(S, 0)), -2, np.int32) if trace else None
     cnt = np.full((C, height, width), -2, np.int32) if trace else None
+    tl = None if tiles is None else _c(tiles, np.int64)
     n_eval = lib.orc_rasterize_fwd_traced(_p(means2d), _p(_c(conics, np.float32)), _p(colors),
                                           _p(_c(opacities, np.float32)), _p(bg), C, K, width, height, tile_size, tw,
                                           th, _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects),
                                           _p(None if masks is None else _c(masks, np.int32)), float(alpha_cutoff),
-                                          float(alpha_clamp), float(transmittance_threshold), None, 0,
-                                          int(max_list_entries), S, _p(out_c), _p(out_a), _p(out_t), _p(out_l),
+                                          float(alpha_clamp), float(transmittance_threshold), _p(tl),
+                                          0 if tl is None else tl.size, int(max_list_entries), S, _p(out_c), _p(out_a), _p(out_t), _p(out_l),
                                           _p(tr), _p(cnt))
     if n_eval < 0:
         raise ValueError("invalid rasterize arguments")

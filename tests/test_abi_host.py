@@ -129,6 +129,23 @@ def test_rasterize_argument_errors(lib):
     assert b"gs_rasterize_fwd" in lib.gs_last_error()
 
 
+def test_rasterize_traced_argument_errors(lib):
+    from tile_binned_gaussian_amd.binding import GS_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails on the host first
+    F = ctypes.c_float
+
+    def call(S=4, L=-1, K=3, tw=4, ptr=fake):
+        return lib.gs_rasterize_fwd_traced(ptr, ptr, ptr, ptr, None, 1, 4, K, 64, 64, 16, tw, 4, ptr, ptr, 10, None,
+                                           F(1 / 255), F(0.99), F(1e-4), L, S, ptr, ptr, None, None, ptr, ptr,
+                                           None, None, 0, None)
+    assert call(S=-1) == GS_ERR_INVALID_ARG
+    assert b"max_splat_steps" in lib.gs_last_error()
+    assert call(K=5) == GS_ERR_INVALID_ARG
+    assert b"gs_rasterize_fwd_traced" in lib.gs_last_error()
+    assert call(tw=3) == GS_ERR_INVALID_ARG
+    assert call(ptr=None) == GS_ERR_INVALID_ARG
+
+
 def test_rasterize_bwd_argument_errors(lib):
     from tile_binned_gaussian_amd.binding import GS_ERR_INVALID_ARG
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails on the host first

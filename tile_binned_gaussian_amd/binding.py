@@ -20,7 +20,7 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
-           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_fwd")
+           "gs_rasterize_fwd", "gs_rasterize_fwd_traced", "gs_rasterize_bwd", "gs_project_fwd")
 
 
 class GsError(RuntimeError):
@@ -56,6 +56,9 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
                                      P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd.restype = I32
+    lib.gs_rasterize_fwd_traced.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
+                                            F, F, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gs_rasterize_fwd_traced.restype = I32
     lib.gs_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F,
                                      P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_rasterize_bwd.restype = I32
@@ -187,6 +190,33 @@ class Render:
     last_ids: torch.Tensor  # [C, H, W] int32
 
 
+def _raster_inputs(means2d, conics, colors, opacities, backgrounds, isect_offsets, flatten_ids, masks):
+    dev = means2d.device
+    _req(means2d, "means2d", torch.float32, dev)
+    C, N = means2d.shape[0], means2d.shape[1]
+    _req(conics, "conics", torch.float32, dev, (C, N, 3))
+    _req(colors, "colors", torch.float32, dev)
+    if colors.dim() != 3 or tuple(colors.shape[:2]) != (C, N):
+        raise ValueError("colors must be [C, N, K]")
+    _req(opacities, "opacities", torch.float32, dev, (C, N))
+    if backgrounds is not None:
+        _req(backgrounds, "backgrounds", torch.float32, dev, (C, colors.shape[2]))
+    _req(isect_offsets, "isect_offsets", torch.int32, dev)
+    if isect_offsets.dim() != 3 or isect_offsets.shape[0] != C:
+        raise ValueError("isect_offsets must be [C, th, tw]")
+    _req(flatten_ids, "flatten_ids", torch.int32, dev)
+    if masks is not None:
+        _req(masks, "masks", torch.int32, dev, tuple(isect_offsets.shape))
+    return dev, C, N, colors.shape[2], isect_offsets.shape[1], isect_offsets.shape[2]
+
+
+def _render_out(C, height, width, K, dev):
+    return Render(torch.empty((C, height, width, K), dtype=torch.float32, device=dev),
+                  torch.empty((C, height, width), dtype=torch.float32, device=dev),
+                  torch.empty((C, height, width), dtype=torch.float32, device=dev),
+                  torch.empty((C, height, width), dtype=torch.int32, device=dev))
+
+
 def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
                      transmittance_threshold=1e-4, out=None, stream=None, workspace=None, eval_counts=None,
@@ -196,34 +226,53 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
     eval_counts: optional int64 [5] device tensor that the launch adds to (evaluations by the definition, alpha >=
     cutoff, composited, evaluations executed, splats staged)."""
     lib = load_library()
-    dev = means2d.device
-    _req(means2d, "means2d", torch.float32, dev)
-    C, N = means2d.shape[0], means2d.shape[1]
-    _req(conics, "conics", torch.float32, dev, (C, N, 3))
-    _req(colors, "colors", torch.float32, dev)
-    if colors.dim() != 3 or tuple(colors.shape[:2]) != (C, N):
-        raise ValueError("colors must be [C, N, K]")
-    K = colors.shape[2]
-    _req(opacities, "opacities", torch.float32, dev, (C, N))
-    if backgrounds is not None:
-        _req(backgrounds, "backgrounds", torch.float32, dev, (C, K))
-    _req(isect_offsets, "isect_offsets", torch.int32, dev)
-    th, tw = isect_offsets.shape[1], isect_offsets.shape[2]
-    _req(flatten_ids, "flatten_ids", torch.int32, dev)
+    dev, C, N, K, th, tw = _raster_inputs(means2d, conics, colors, opacities, backgrounds, isect_offsets,
+                                          flatten_ids, masks)
     n = flatten_ids.numel() if n_isects is None else int(n_isects)
     if out is None:
-        out = Render(torch.empty((C, height, width, K), dtype=torch.float32, device=dev),
-                     torch.empty((C, height, width), dtype=torch.float32, device=dev),
-                     torch.empty((C, height, width), dtype=torch.float32, device=dev),
-                     torch.empty((C, height, width), dtype=torch.int32, device=dev))
+        out = _render_out(C, height, width, K, dev)
     ws = workspace if workspace is not None else _workspace(lib.gs_rasterize_workspace_bytes(C, tw, th), dev)
-    if masks is not None:
-        _req(masks, "masks", torch.int32, dev, (C, th, tw))
     _check(lib.gs_rasterize_fwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
                                 K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
                                 _ptr(masks), float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
                                 _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
                                 _ptr(out.last_ids), _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+@dataclass
+class TracedRender(Render):
+    trace_ids: torch.Tensor | None  # [C, H, W, max_splat_steps] int32 flat splat ids (past the count: unwritten)
+    trace_counts: torch.Tensor | None  # [C, H, W] int32
+
+
+def gs_rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width, height, tile_size,
+                            isect_offsets, flatten_ids, max_splat_steps, max_list_entries=-1, n_isects=None,
+                            alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, transmittance_threshold=1e-4, trace=True,
+                            out=None, stream=None, workspace=None, eval_counts=None, masks=None) -> TracedRender:
+    """The traced forward: each tile's list cut to its first max_list_entries entries (negative: whole lists),
+    each pixel stopped after max_splat_steps composited splats, and (trace=True) each pixel's composited flat splat
+    ids recorded in order with their count. Entries of a trace row past its count are left unwritten."""
+    lib = load_library()
+    dev, C, N, K, th, tw = _raster_inputs(means2d, conics, colors, opacities, backgrounds, isect_offsets,
+                                          flatten_ids, masks)
+    S = int(max_splat_steps)
+    if S < 0:
+        raise ValueError("max_splat_steps must be >= 0")
+    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    if out is None:
+        r = _render_out(C, height, width, K, dev)
+        out = TracedRender(r.render_colors, r.render_alphas, r.render_T, r.last_ids,
+                           torch.empty((C, height, width, S), dtype=torch.int32, device=dev) if trace else None,
+                           torch.empty((C, height, width), dtype=torch.int32, device=dev) if trace else None)
+    ws = workspace if workspace is not None else _workspace(lib.gs_rasterize_workspace_bytes(C, tw, th), dev)
+    _check(lib.gs_rasterize_fwd_traced(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds),
+                                       C, N, K, width, height, tile_size, tw, th, _ptr(isect_offsets),
+                                       _ptr(flatten_ids), n, _ptr(masks), float(alpha_cutoff), float(alpha_clamp),
+                                       float(transmittance_threshold), int(max_list_entries), S,
+                                       _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
+                                       _ptr(out.last_ids), _ptr(out.trace_ids), _ptr(out.trace_counts),
+                                       _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

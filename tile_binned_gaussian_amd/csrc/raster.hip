@@ -33,13 +33,27 @@ struct RasterArgs {
     int32_t *out_last;
     unsigned long long *eval_counts;  // nullable: the five work counts of the ABI
     float log_cutoff;                 // ln(alpha_cutoff), for the conservative cull
+    int max_list;                     // >= 0: composite only the first max_list entries of each tile's range
+    int max_steps;                    // traced kernels: a pixel stops after this many composited splats
+    int32_t *trace_ids;               // traced kernels, nullable: [C, H, W, max_steps] flat splat ids
+    int32_t *trace_counts;            // traced kernels, nullable: [C, H, W] composited splats per pixel
 };
 
-template <int K, int PPT, bool COUNT>
+// The range of global tile `tile`: [offsets[tile], next offset or n_isects), empty when the tile's mask is 0,
+// cut to its first max_list entries when max_list >= 0.
+__device__ __forceinline__ int range_end(const RasterArgs &a, int tile, int start) {
+    int end = (a.masks && a.masks[tile] == 0) ? start
+              : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
+    if (a.max_list >= 0 && end - start > a.max_list) end = start + a.max_list;
+    return end;
+}
+
+template <int K, int PPT, bool COUNT, bool TRACE>
 __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float2 s_xy[kMaxThreads];
     __shared__ float4 s_abco[kMaxThreads];
     __shared__ float s_rgb[kMaxThreads * K];
+    __shared__ int32_t s_g[TRACE ? kMaxThreads : 1];
 
     const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
@@ -48,14 +62,12 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
     const int start = a.offsets[tile];
-    // a tile whose mask is 0 composites nothing (its range is taken as empty)
-    const int end = (a.masks && a.masks[tile] == 0) ? start
-                    : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
+    const int end = range_end(a, tile, start);
     const int ts = a.tile_size;
     const int nthreads = blockDim.x;
 
     float px[PPT], py[PPT], T[PPT], acc[PPT][K];
-    int last[PPT], xs[PPT], ys[PPT], stop[PPT];
+    int last[PPT], xs[PPT], ys[PPT], stop[PPT], steps[PPT];
     bool done[PPT];
     unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
 #pragma unroll
@@ -64,7 +76,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         const int lx = pix % ts, ly = pix / ts;
         xs[q] = tx * ts + lx;
         ys[q] = ty * ts + ly;
-        done[q] = !(pix < ts * ts && xs[q] < a.width && ys[q] < a.height);
+        done[q] = !(pix < ts * ts && xs[q] < a.width && ys[q] < a.height) || (TRACE && a.max_steps == 0);
+        steps[q] = 0;
         px[q] = static_cast<float>(xs[q]) + 0.5f;
         py[q] = static_cast<float>(ys[q]) + 0.5f;
         T[q] = 1.0f;
@@ -83,6 +96,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         if (idx < end) {
             if (COUNT) ++n_staged;
             const int g = a.ids[idx];
+            if (TRACE) s_g[threadIdx.x] = g;
             s_xy[threadIdx.x] = a.means[g];
             const float *cg = a.conics + 3 * static_cast<int64_t>(g);
             s_abco[threadIdx.x] = make_float4(cg[0], cg[1], cg[2], a.opacities[g]);
@@ -118,6 +132,17 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
                 for (int k = 0; k < K; ++k) acc[q][k] = acc[q][k] + s_rgb[j * K + k] * v;
                 T[q] = t_next;
                 last[q] = base + j;
+                if (TRACE) {
+                    if (a.trace_ids) {
+                        const int64_t p = (static_cast<int64_t>(camera) * a.height + ys[q]) * a.width + xs[q];
+                        a.trace_ids[p * a.max_steps + steps[q]] = s_g[j];
+                    }
+                    if (++steps[q] == a.max_steps) {
+                        done[q] = true;
+                        if (COUNT) stop[q] = base + j + 1;
+                        break;
+                    }
+                }
             }
         }
     }
@@ -135,6 +160,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         a.out_alphas[p] = 1.0f - T[q];
         if (a.out_T) a.out_T[p] = T[q];
         if (a.out_last) a.out_last[p] = last[q];
+        if (TRACE && a.trace_counts) a.trace_counts[p] = steps[q];
     }
     if (COUNT) {
         // evaluations under the definition: every splat of the range up to and including the one that stops
@@ -160,9 +186,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
 // order, and evaluates only those. Skipped splats would have been skipped by the cutoff test at every pixel of the
 // region, so the result is the same to the bit. The evaluation loop runs in lock step without per-lane exits: a
 // pixel that stops only sets `done`, and the wave leaves the loop once every lane is done.
-template <int K, bool COUNT>
+template <int K, bool COUNT, bool TRACE>
 __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) {
-    constexpr int kRec = 12;  // floats per record: mx my a b | c o index - | colour[4]
+    constexpr int kRec = 12;  // floats per record: mx my a b | c o index id | colour[4]
     __shared__ float4 s_rec[kMaxThreads * kRec / 4];
     __shared__ uint32_t s_mask[kMaxThreads];
     __shared__ uint16_t s_list[kMaxThreads / kWave][kMaxThreads];
@@ -174,9 +200,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
     const int start = a.offsets[tile];
-    // a tile whose mask is 0 composites nothing (its range is taken as empty)
-    const int end = (a.masks && a.masks[tile] == 0) ? start
-                    : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
+    const int end = range_end(a, tile, start);
     const int ts = a.tile_size;
     const int nthreads = blockDim.x;
     const int wave = threadIdx.x / kWave;
@@ -195,6 +219,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     const int x = tx * ts + lx, y = ty * ts + ly;
     const bool inside = static_cast<int>(threadIdx.x) < ts * ts && x < a.width && y < a.height;
     const float px = static_cast<float>(x) + 0.5f, py = static_cast<float>(y) + 0.5f;
+    const int64_t p = (static_cast<int64_t>(camera) * a.height + y) * a.width + x;
 
     // pixel-centre boxes of every wave's region (for the cull bits), in pixel coordinates
     float rx0[kMaxThreads / kWave], rx1[kMaxThreads / kWave], ry0[kMaxThreads / kWave], ry1[kMaxThreads / kWave];
@@ -221,8 +246,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     float T = 1.0f, acc[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) acc[k] = 0.0f;
-    int last = -1, stop = end;
-    bool done = !inside;
+    int last = -1, stop = end, steps = 0;
+    bool done = !inside || (TRACE && a.max_steps == 0);
     unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const char *rec_base = reinterpret_cast<const char *>(s_rec);
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
             if (K > 2) col.z = cs[2];
             if (K > 3) col.w = cs[3];
             s_rec[threadIdx.x * 3 + 0] = make_float4(m.x, m.y, ca, cb);
-            s_rec[threadIdx.x * 3 + 1] = make_float4(cc, o, __int_as_float(idx), 0.0f);
+            s_rec[threadIdx.x * 3 + 1] = make_float4(cc, o, __int_as_float(idx), __int_as_float(g));
             s_rec[threadIdx.x * 3 + 2] = col;
             const CullBox box = cull_box(m, ca, cb, cc, o, a.alpha_cutoff, a.log_cutoff);
             uint32_t bits = 0;
@@ -296,13 +321,21 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
                     if (K > 3) acc[3] = acc[3] + col.w * v;
                     T = t_next;
                     last = __float_as_int(*reinterpret_cast<const float *>(rec + 24));
+                    if (TRACE) {
+                        if (a.trace_ids)
+                            a.trace_ids[p * a.max_steps + steps] =
+                                __float_as_int(*reinterpret_cast<const float *>(rec + 28));
+                        if (++steps == a.max_steps) {
+                            done = true;
+                            if (COUNT) stop = last + 1;
+                        }
+                    }
                 }
             }
         }
     }
 
     if (inside) {
-        const int64_t p = (static_cast<int64_t>(camera) * a.height + y) * a.width + x;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const float bg = a.backgrounds ? a.backgrounds[camera * K + k] : 0.0f;
@@ -311,6 +344,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
         a.out_alphas[p] = 1.0f - T;
         if (a.out_T) a.out_T[p] = T;
         if (a.out_last) a.out_last[p] = last;
+        if (TRACE && a.trace_counts) a.trace_counts[p] = steps;
     }
     if (COUNT) {
         const unsigned long long n_eval = inside ? static_cast<unsigned>(stop - start) : 0u;
@@ -322,19 +356,22 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     }
 }
 
-template <int K, bool COUNT>
-gs_status launch_kc(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
+template <int K, bool COUNT, bool TRACE>
+gs_status launch_kct(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(args.total_tiles)), block(static_cast<unsigned>(threads));
-    if (ppt == 1) hipLaunchKernelGGL((raster_cull_kernel<K, COUNT>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4, COUNT>), grid, block, 0, stream, args);
+    if (ppt == 1) hipLaunchKernelGGL((raster_cull_kernel<K, COUNT, TRACE>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4, COUNT, TRACE>), grid, block, 0, stream, args);
     GS_LAUNCH_TRY("raster_fwd_kernel");
     return ok();
 }
 
 template <int K>
-gs_status launch_k(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
-    return args.eval_counts ? launch_kc<K, true>(args, threads, ppt, stream)
-                            : launch_kc<K, false>(args, threads, ppt, stream);
+gs_status launch_k(const RasterArgs &args, int threads, int ppt, bool trace, hipStream_t stream) {
+    if (trace)
+        return args.eval_counts ? launch_kct<K, true, true>(args, threads, ppt, stream)
+                                : launch_kct<K, false, true>(args, threads, ppt, stream);
+    return args.eval_counts ? launch_kct<K, true, false>(args, threads, ppt, stream)
+                            : launch_kct<K, false, false>(args, threads, ppt, stream);
 }
 
 }  // namespace
@@ -347,39 +384,40 @@ extern "C" size_t gs_rasterize_workspace_bytes(int64_t C, int tile_width, int ti
     return align_up(static_cast<size_t>(C) * tile_width * tile_height * sizeof(int32_t), 256);
 }
 
-extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
-                                      const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
-                                      int width, int height, int tile_size, int tile_width, int tile_height,
-                                      const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
-                                      const int32_t *masks, float alpha_cutoff, float alpha_clamp,
-                                      float transmittance_threshold,
-                                      float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
-                                      uint64_t *eval_counts, void *workspace, size_t workspace_bytes,
-                                      void *stream_handle) {
+namespace {
+
+gs_status rasterize(const char *fn, const float *means2d, const float *conics, const float *colors,
+                    const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K, int width,
+                    int height, int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
+                    const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks, float alpha_cutoff,
+                    float alpha_clamp, float transmittance_threshold, int max_list_entries, int max_splat_steps,
+                    float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
+                    int32_t *trace_ids, int32_t *trace_counts, uint64_t *eval_counts, void *workspace,
+                    size_t workspace_bytes, void *stream_handle) {
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
     if (C < 1 || N < 0 || C * N >= (int64_t(1) << 31))
-        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: need C >= 1, N >= 0 and C*N < 2^31");
-    if (K < 1 || K > 4) return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: K = %d channels outside [1, 4]", K);
+        return fail(GS_ERR_INVALID_ARG, "%s: need C >= 1, N >= 0 and C*N < 2^31", fn);
+    if (K < 1 || K > 4) return fail(GS_ERR_INVALID_ARG, "%s: K = %d channels outside [1, 4]", fn, K);
     if (width < 1 || height < 1 || tile_size < 1 || tile_size > 32)
-        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: need width, height >= 1 and 1 <= tile_size <= 32");
+        return fail(GS_ERR_INVALID_ARG, "%s: need width, height >= 1 and 1 <= tile_size <= 32", fn);
     if (tile_width != (width + tile_size - 1) / tile_size || tile_height != (height + tile_size - 1) / tile_size)
         return fail(GS_ERR_INVALID_ARG,
-                    "gs_rasterize_fwd: tile grid %dx%d does not match ceil(%d/%d) x ceil(%d/%d)", tile_width,
+                    "%s: tile grid %dx%d does not match ceil(%d/%d) x ceil(%d/%d)", fn, tile_width,
                     tile_height, width, tile_size, height, tile_size);
     const int64_t total_tiles = C * tile_width * tile_height;
     if (total_tiles >= (int64_t(1) << 31) || C * height * width * K >= (int64_t(1) << 40))
-        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: image batch too large");
+        return fail(GS_ERR_INVALID_ARG, "%s: image batch too large", fn);
     if (n_isects < 0 || n_isects >= (int64_t(1) << 31))
-        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: n_isects = %lld outside [0, 2^31)", (long long)n_isects);
+        return fail(GS_ERR_INVALID_ARG, "%s: n_isects = %lld outside [0, 2^31)", fn, (long long)n_isects);
     if (!isect_offsets || !render_colors || !render_alphas || (n_isects > 0 && !flatten_ids) ||
         (N > 0 && (!means2d || !conics || !colors || !opacities)))
-        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: a required pointer is NULL");
+        return fail(GS_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
     if (!(alpha_cutoff >= 0.0f) || !(alpha_clamp > 0.0f) || !(transmittance_threshold >= 0.0f))
-        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: alpha_cutoff >= 0, alpha_clamp > 0 and "
-                                        "transmittance_threshold >= 0 are required");
+        return fail(GS_ERR_INVALID_ARG, "%s: alpha_cutoff >= 0, alpha_clamp > 0 and "
+                                        "transmittance_threshold >= 0 are required", fn);
     const size_t need = gs_rasterize_workspace_bytes(C, tile_width, tile_height);
     if (workspace_bytes > 0 && workspace_bytes < need)
-        return fail(GS_ERR_WORKSPACE, "gs_rasterize_fwd: needs %zu workspace bytes (got %zu)", need, workspace_bytes);
+        return fail(GS_ERR_WORKSPACE, "%s: needs %zu workspace bytes (got %zu)", fn, need, workspace_bytes);
 
     RasterArgs args{};
     args.means = reinterpret_cast<const float2 *>(means2d);
@@ -406,6 +444,11 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
     args.out_last = last_ids;
     args.eval_counts = reinterpret_cast<unsigned long long *>(eval_counts);
     args.log_cutoff = alpha_cutoff > 0.0f ? static_cast<float>(std::log(static_cast<double>(alpha_cutoff))) : -INFINITY;
+    args.max_list = max_list_entries < 0 ? -1 : max_list_entries;
+    args.max_steps = max_splat_steps;
+    args.trace_ids = trace_ids;
+    args.trace_counts = trace_counts;
+    const bool trace = max_splat_steps >= 0;
 
     const int pixels = tile_size * tile_size;
     int threads, ppt;
@@ -417,9 +460,45 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
         ppt = 4;
     }
     switch (K) {
-        case 1: return launch_k<1>(args, threads, ppt, stream);
-        case 2: return launch_k<2>(args, threads, ppt, stream);
-        case 3: return launch_k<3>(args, threads, ppt, stream);
-        default: return launch_k<4>(args, threads, ppt, stream);
+        case 1: return launch_k<1>(args, threads, ppt, trace, stream);
+        case 2: return launch_k<2>(args, threads, ppt, trace, stream);
+        case 3: return launch_k<3>(args, threads, ppt, trace, stream);
+        default: return launch_k<4>(args, threads, ppt, trace, stream);
     }
+}
+
+}  // namespace
+
+extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const float *colors,
+                                      const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
+                                      int width, int height, int tile_size, int tile_width, int tile_height,
+                                      const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
+                                      const int32_t *masks, float alpha_cutoff, float alpha_clamp,
+                                      float transmittance_threshold,
+                                      float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
+                                      uint64_t *eval_counts, void *workspace, size_t workspace_bytes,
+                                      void *stream_handle) {
+    return rasterize("gs_rasterize_fwd", means2d, conics, colors, opacities, backgrounds, C, N, K, width, height,
+                     tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, masks, alpha_cutoff,
+                     alpha_clamp, transmittance_threshold, -1, -1, render_colors, render_alphas, render_T, last_ids,
+                     nullptr, nullptr, eval_counts, workspace, workspace_bytes, stream_handle);
+}
+
+extern "C" gs_status gs_rasterize_fwd_traced(const float *means2d, const float *conics, const float *colors,
+                                             const float *opacities, const float *backgrounds, int64_t C, int64_t N,
+                                             int K, int width, int height, int tile_size, int tile_width,
+                                             int tile_height, const int32_t *isect_offsets,
+                                             const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks,
+                                             float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                                             int max_list_entries, int max_splat_steps, float *render_colors,
+                                             float *render_alphas, float *render_T, int32_t *last_ids,
+                                             int32_t *trace_ids, int32_t *trace_counts, uint64_t *eval_counts,
+                                             void *workspace, size_t workspace_bytes, void *stream_handle) {
+    if (max_splat_steps < 0)
+        return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd_traced: max_splat_steps = %d must be >= 0", max_splat_steps);
+    return rasterize("gs_rasterize_fwd_traced", means2d, conics, colors, opacities, backgrounds, C, N, K, width,
+                     height, tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, masks,
+                     alpha_cutoff, alpha_clamp, transmittance_threshold, max_list_entries, max_splat_steps,
+                     render_colors, render_alphas, render_T, last_ids, trace_ids, trace_counts, eval_counts,
+                     workspace, workspace_bytes, stream_handle);
 }
