@@ -181,6 +181,32 @@ def main():
         b_ev.record(plan.stream)
     torch.cuda.synchronize()
     backward_ms = statistics.median(a_ev.elapsed_time(b_ev) for a_ev, b_ev in bev)
+    # outside the frame: the traced forward on the last frame (every pixel's composited splat ids, up to 256)
+    S_TRACE = 256
+    C_, H_, W_, K_ = scene.C, scene.height, scene.width, scene.colors.shape[-1]
+    f32, i32 = dict(device="cuda:0"), dict(dtype=torch.int32, device="cuda:0")
+    tr_out = binding.TracedRender(torch.empty((C_, H_, W_, K_), **f32), torch.empty((C_, H_, W_), **f32),
+                                  torch.empty((C_, H_, W_), **f32), torch.empty((C_, H_, W_), **i32),
+                                  torch.empty((C_, H_, W_, S_TRACE), **i32), torch.empty((C_, H_, W_), **i32))
+
+    def traced():
+        binding.gs_rasterize_fwd_traced(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, W_, H_,
+                                        scene.tile_size, plan.offsets, plan.ids, S_TRACE, n_isects=plan.n_isects,
+                                        alpha_cutoff=scene.alpha_cutoff, alpha_clamp=scene.alpha_clamp,
+                                        transmittance_threshold=scene.transmittance_threshold, out=tr_out,
+                                        stream=plan.stream)
+    for _ in range(2):
+        traced()
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(5, args.steps // 2))]
+    for a_ev, b_ev in tev:
+        a_ev.record(plan.stream)
+        traced()
+        b_ev.record(plan.stream)
+    torch.cuda.synchronize()
+    traced_ms = statistics.median(a_ev.elapsed_time(b_ev) for a_ev, b_ev in tev)
+    traced_steps = int(tr_out.trace_counts.sum())
+    traced_capped = int((tr_out.trace_counts == S_TRACE).sum())
+    del tr_out
     # outside the frame: the EWA projection that produces such splats, 1M 3D Gaussians into one 1920x1080 camera
     sc3 = synth.scene3d(19, scene.N, C=1, width=scene.width, height=scene.height)
     d3 = [torch.from_numpy(a).to("cuda:0") for a in (sc3.means, sc3.covars, sc3.viewmats, sc3.Ks)]
@@ -247,6 +273,11 @@ def main():
         "backward": {"ms": round(backward_ms, 4), "Mpix/s": round(pixels / (backward_ms * 1e-3) / 1e6, 2),
                      "note": "gs_rasterize_bwd on the last frame with seeded standard-normal output gradients; "
                              "clears the gradients, then sums them"},
+        "traced_forward": {"ms": round(traced_ms, 4), "max_splat_steps": S_TRACE, "trace_entries": traced_steps,
+                           "pixels_at_cap": traced_capped,
+                           "trace_bytes_written": 4 * traced_steps + 4 * pixels,
+                           "note": "gs_rasterize_fwd_traced on the last frame's lists, no list cap: the composite "
+                                   "plus each pixel's trace row and count"},
         "projection": {"ms": round(project_ms, 4), "gaussians": sc3.N, "bytes": project_bytes,
                        "GB/s": round(project_bytes / (project_ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(project_bytes / (project_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

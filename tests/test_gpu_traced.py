@@ -152,3 +152,29 @@ def test_traced_forward_1m_splats_1080p_sampled_tiles():
         mask[cam, ty * ts:(ty + 1) * ts, tx * ts:(tx + 1) * ts] = True
     _assert_traced_equal(g, o, sel=mask)
     assert (o.trace_counts[mask] == S).any()  # the step cap bites on this frame
+
+
+def test_trace_rows_not_16_byte_aligned():
+    """A trace buffer that starts 4 bytes past a 16-byte boundary takes the 4-byte store path; same results."""
+    scene = SCENES["deep-tiles"]()
+    fr = gpu_frame(scene)
+    S = 8
+    ref = _gpu_traced(scene, fr, S)
+    C, H, W, K = scene.C, scene.height, scene.width, scene.colors.shape[-1]
+    d = torch.device("cuda")
+    flat = torch.full((C * H * W * S + 1,), SENTINEL, dtype=torch.int32, device=d)
+    trace = flat[1:].view(C, H, W, S)
+    assert trace.data_ptr() % 16 == 4
+    out = binding.TracedRender(torch.empty((C, H, W, K), device=d), torch.empty((C, H, W), device=d),
+                               torch.empty((C, H, W), device=d), torch.empty((C, H, W), dtype=torch.int32, device=d),
+                               trace, torch.empty((C, H, W), dtype=torch.int32, device=d))
+    binding.gs_rasterize_fwd_traced(dev(scene.means2d), dev(scene.conics), dev(scene.colors), dev(scene.opacities),
+                                    None, W, H, scene.tile_size, fr.isect_offsets, fr.isect.flatten_ids, S,
+                                    n_isects=fr.isect.n_isects, alpha_cutoff=scene.alpha_cutoff,
+                                    alpha_clamp=scene.alpha_clamp,
+                                    transmittance_threshold=scene.transmittance_threshold, out=out)
+    torch.cuda.synchronize()
+    assert int(flat[0]) == SENTINEL
+    torch.testing.assert_close(out.trace_counts, ref.trace_counts, rtol=0, atol=0)
+    torch.testing.assert_close(out.trace_ids, ref.trace_ids, rtol=0, atol=0)
+    torch.testing.assert_close(out.render_colors, ref.render_colors, rtol=0, atol=0)

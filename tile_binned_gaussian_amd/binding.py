@@ -322,8 +322,8 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, hei
         _req(masks, "masks", torch.int32, dev, (C, th, tw))
     _check(lib.gs_rasterize_bwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
                                 K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
-                                _ptr(masks), float(alpha_cutoff), float(alpha_clamp), _ptr(render_alphas), _ptr(last_ids),
-                                _ptr(grad_render_colors), _ptr(grad_render_alphas), _ptr(out.means2d),
+                                _ptr(masks), float(alpha_cutoff), float(alpha_clamp), _ptr(render_alphas),
+                                _ptr(last_ids), _ptr(grad_render_colors), _ptr(grad_render_alphas), _ptr(out.means2d),
                                 _ptr(out.conics), _ptr(out.colors), _ptr(out.opacities), _ptr(out.backgrounds),
                                 _ptr(out.means2d_abs), _stream(stream)))
     return out

@@ -37,7 +37,30 @@ struct RasterArgs {
     int max_steps;                    // traced kernels: a pixel stops after this many composited splats
     int32_t *trace_ids;               // traced kernels, nullable: [C, H, W, max_steps] flat splat ids
     int32_t *trace_counts;            // traced kernels, nullable: [C, H, W] composited splats per pixel
+    int trace_vec;                    // trace_ids is 16-byte aligned and max_steps a multiple of 4
 };
+
+// Traced kernels stage each pixel's trace in LDS, kTraceChunk ids per thread, and store a full chunk as four
+// contiguous 16-byte non-temporal pieces (one whole 64-byte segment that bypasses the caches the composite's
+// gathers use), so rows reach memory in whole segments rather than as scattered 4-byte writes. The per-thread
+// slots are kTraceChunk + 1 words apart (no LDS bank conflicts when the threads of a wave write different slots).
+// The staging area (17 KB) lowers the traced build's occupancy from 8 to 4 workgroups per CU; the untraced
+// build does not allocate it.
+constexpr int kTraceChunk = 16;
+constexpr int kTraceStride = kTraceChunk + 1;
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Store the n staged ids `buf` as trace entries [j, j + n) of the row `row`.
+__device__ __forceinline__ void flush_trace(int32_t *row, int j, const int32_t *buf, int n, bool vec) {
+    if (vec && n == kTraceChunk) {
+#pragma unroll
+        for (int k = 0; k < kTraceChunk; k += 4)
+            __builtin_nontemporal_store(v4i{buf[k], buf[k + 1], buf[k + 2], buf[k + 3]},
+                                        reinterpret_cast<v4i *>(row + j + k));
+    } else {
+        for (int k = 0; k < n; ++k) row[j + k] = buf[k];
+    }
+}
 
 // The range of global tile `tile`: [offsets[tile], next offset or n_isects), empty when the tile's mask is 0,
 // cut to its first max_list entries when max_list >= 0.
@@ -192,6 +215,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     __shared__ float4 s_rec[kMaxThreads * kRec / 4];
     __shared__ uint32_t s_mask[kMaxThreads];
     __shared__ uint16_t s_list[kMaxThreads / kWave][kMaxThreads];
+    __shared__ int32_t s_trace[TRACE ? kMaxThreads * kTraceStride : 1];
 
     const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
@@ -247,6 +271,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
 #pragma unroll
     for (int k = 0; k < K; ++k) acc[k] = 0.0f;
     int last = -1, stop = end, steps = 0;
+    int32_t *const my_trace = s_trace + (TRACE ? threadIdx.x * kTraceStride : 0);
     bool done = !inside || (TRACE && a.max_steps == 0);
     unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -322,10 +347,12 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
                     T = t_next;
                     last = __float_as_int(*reinterpret_cast<const float *>(rec + 24));
                     if (TRACE) {
-                        if (a.trace_ids)
-                            a.trace_ids[p * a.max_steps + steps] =
-                                __float_as_int(*reinterpret_cast<const float *>(rec + 28));
-                        if (++steps == a.max_steps) {
+                        my_trace[steps & (kTraceChunk - 1)] = __float_as_int(*reinterpret_cast<const float *>(rec + 28));
+                        ++steps;
+                        if (a.trace_ids && (steps & (kTraceChunk - 1)) == 0)
+                            flush_trace(a.trace_ids + p * a.max_steps, steps - kTraceChunk, my_trace, kTraceChunk,
+                                        a.trace_vec);
+                        if (steps == a.max_steps) {
                             done = true;
                             if (COUNT) stop = last + 1;
                         }
@@ -345,6 +372,11 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
         if (a.out_T) a.out_T[p] = T;
         if (a.out_last) a.out_last[p] = last;
         if (TRACE && a.trace_counts) a.trace_counts[p] = steps;
+        if (TRACE && a.trace_ids) {
+            // the steps after the last full chunk
+            const int r = steps & (kTraceChunk - 1);
+            flush_trace(a.trace_ids + p * a.max_steps, steps - r, my_trace, r, false);
+        }
     }
     if (COUNT) {
         const unsigned long long n_eval = inside ? static_cast<unsigned>(stop - start) : 0u;
@@ -448,6 +480,7 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
     args.max_steps = max_splat_steps;
     args.trace_ids = trace_ids;
     args.trace_counts = trace_counts;
+    args.trace_vec = (max_splat_steps % 4 == 0 && (reinterpret_cast<uintptr_t>(trace_ids) & 15) == 0) ? 1 : 0;
     const bool trace = max_splat_steps >= 0;
 
     const int pixels = tile_size * tile_size;
