@@ -74,6 +74,11 @@ def _load():
         lib.orc_rasterize_bwd.restype = I32
         lib.orc_project.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P]
         lib.orc_project.restype = None
+        lib.orc_bin_tiles.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, I64, P, P]
+        lib.orc_bin_tiles.restype = I64
+        lib.orc_rasterize_bins.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, I64, F, F, F, P, P,
+                                           P, P]
+        lib.orc_rasterize_bins.restype = I64
         _lib = lib
     return _lib
 
@@ -252,8 +257,8 @@ def rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width,
                                           th, _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects),
                                           _p(None if masks is None else _c(masks, np.int32)), float(alpha_cutoff),
                                           float(alpha_clamp), float(transmittance_threshold), _p(tl),
-                                          0 if tl is None else tl.size, int(max_list_entries), S, _p(out_c), _p(out_a), _p(out_t), _p(out_l),
-                                          _p(tr), _p(cnt))
+                                          0 if tl is None else tl.size, int(max_list_entries), S, _p(out_c),
+                                          _p(out_a), _p(out_t), _p(out_l), _p(tr), _p(cnt))
     if n_eval < 0:
         raise ValueError("invalid rasterize arguments")
     return TracedRaster(out_c, out_a, out_t, out_l, int(n_eval), tr, cnt)
@@ -302,6 +307,53 @@ def tile_lists(means2d, radii, depths, tile_size, tile_width, tile_height, tiles
         out.append(ids[pos:pos + int(c)])
         pos += int(c)
     return out
+
+
+@dataclass
+class Bins:
+    bin_ids: np.ndarray  # [C, th, tw, capacity] int32 flat ids by (depth bits, id), -1 in empty slots
+    bin_counts: np.ndarray  # [C, th, tw] int32 full count (> capacity when the bin overflowed)
+    largest: int
+
+
+def bin_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, capacity) -> Bins:
+    """Fixed-capacity per-tile bins (orc_bin_tiles)."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    radii = _c(radii, np.float32)
+    C, N = means2d.shape[0], means2d.shape[1]
+    rpg = 2 if radii.ndim == 3 else 1
+    ids = np.full((C, tile_height, tile_width, int(capacity)), -2, np.int32)
+    counts = np.full((C, tile_height, tile_width), -2, np.int32)
+    largest = lib.orc_bin_tiles(_p(means2d), _p(radii), rpg, _p(_c(depths, np.float32)), C, N, tile_size, tile_width,
+                                tile_height, int(capacity), _p(ids), _p(counts))
+    if largest < 0:
+        raise ValueError("invalid bin arguments")
+    return Bins(ids, counts, int(largest))
+
+
+def rasterize_bins(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, bin_ids,
+                   alpha_cutoff, alpha_clamp, transmittance_threshold) -> Raster:
+    """Compositing over fixed-capacity bins [C, th, tw, capacity] (orc_rasterize_bins); last ids are bin
+    positions."""
+    lib = _load()
+    means2d = _c(means2d, np.float32)
+    C = means2d.shape[0]
+    K = colors.shape[-1]
+    bins = _c(bin_ids, np.int32)
+    th, tw, cap = bins.shape[1], bins.shape[2], bins.shape[3]
+    bg = None if backgrounds is None else _c(backgrounds, np.float32)
+    out_c = np.full((C, height, width, K), np.nan, np.float32)
+    out_a = np.full((C, height, width), np.nan, np.float32)
+    out_t = np.full((C, height, width), np.nan, np.float32)
+    out_l = np.full((C, height, width), -2, np.int32)
+    n_eval = lib.orc_rasterize_bins(_p(means2d), _p(_c(conics, np.float32)), _p(_c(colors, np.float32)),
+                                    _p(_c(opacities, np.float32)), _p(bg), C, K, width, height, tile_size, tw, th,
+                                    _p(bins), cap, float(alpha_cutoff), float(alpha_clamp),
+                                    float(transmittance_threshold), _p(out_c), _p(out_a), _p(out_t), _p(out_l))
+    if n_eval < 0:
+        raise ValueError("invalid rasterize arguments")
+    return Raster(out_c, out_a, out_t, out_l, int(n_eval))
 
 
 def rasterize_tile(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, tile_width,

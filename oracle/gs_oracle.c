@@ -19,6 +19,9 @@
  *   The composite's backward (orc_rasterize_bwd) follows [gsplat-bwd] gs_raster_backward_pixel directly.
  *   [gsplat-proj] the same gem's projection.c (gs_mat3_product, gs_camera_covar, gs_clip, gs_project_one): the
  *            EWA projection of 3D Gaussians into cameras (orc_project).
+ *   [pytorch3d-fine] PyTorch3D rasterize_meshes.cu, RasterizeMeshesFineCudaKernel: reads per-bin lists of fixed
+ *            capacity with -1 in empty slots (orc_bin_tiles, orc_rasterize_bins: the fixed-capacity alternative to
+ *            sort-based binning).
  *
  * Arithmetic: float32 wherever the pages compute in float (all of the above do), evaluated in the pages'
  * expression order with no contraction (build with -ffp-contract=off, never -ffast-math); fmaf appears only
@@ -721,4 +724,141 @@ int64_t orc_tile_lists(const float *means2d, const float *radii, int radii_per_g
     }
     free(cursor);
     return total;
+}
+
+/* Fixed-capacity per-tile bins, the alternative to sort-based binning (the bin list layout of [pytorch3d-fine]
+ * RasterizeMeshesFineCudaKernel: bins [C, th, tw, capacity] int32 with -1 marking empty slots; the step that fills
+ * them is not on the page). Definition used here: bin t holds the (camera, splat) flat ids whose rectangle
+ * ([gsplat] gs_bounds) contains tile t, ordered by (depth bit pattern, flat id) - the order of the sorted
+ * intersection list - the first min(count, capacity) of them, then -1 in every remaining slot; bin_counts[t] is
+ * the full count (greater than capacity when the bin overflowed). Returns the largest count, or -1 on a bad
+ * argument or allocation failure. */
+int64_t orc_bin_tiles(const float *means2d, const float *radii, int radii_per_gauss, const float *depths,
+                      int64_t C, int64_t N, int tile_size, int tile_width, int tile_height, int64_t capacity,
+                      int32_t *bin_ids, int32_t *bin_counts)
+{
+    int64_t per_camera = (int64_t)tile_width * tile_height;
+    int64_t total_tiles = C * per_camera;
+    if (capacity < 1 || C < 1 || N < 0) return -1;
+    int64_t *count = (int64_t *)calloc((size_t)total_tiles + 1, sizeof(int64_t));
+    if (!count) return -1;
+    /* pass 1: every (camera, splat) rectangle, counted per tile */
+    for (int64_t index = 0; index < C * N; ++index) {
+        int64_t camera = index / N;
+        int32_t b[4];
+        orc_bounds_of(means2d, radii, radii_per_gauss, index, tile_size, tile_width, tile_height, b);
+        for (int ty = b[1]; ty < b[3]; ++ty)
+            for (int tx = b[0]; tx < b[2]; ++tx) count[camera * per_camera + (int64_t)ty * tile_width + tx] += 1;
+    }
+    int64_t *start = (int64_t *)malloc(((size_t)total_tiles + 1) * sizeof(int64_t));
+    if (!start) {
+        free(count);
+        return -1;
+    }
+    start[0] = 0;
+    for (int64_t t = 0; t < total_tiles; ++t) start[t + 1] = start[t] + count[t];
+    int32_t *all = (int32_t *)malloc(((size_t)start[total_tiles] + 1) * sizeof(int32_t));
+    int64_t *cursor = (int64_t *)malloc(((size_t)total_tiles + 1) * sizeof(int64_t));
+    if (!all || !cursor) {
+        free(count);
+        free(start);
+        free(all);
+        free(cursor);
+        return -1;
+    }
+    memcpy(cursor, start, (size_t)total_tiles * sizeof(int64_t));
+    /* pass 2: the same rectangles, ids appended per tile in ascending order */
+    for (int64_t index = 0; index < C * N; ++index) {
+        int64_t camera = index / N;
+        int32_t b[4];
+        orc_bounds_of(means2d, radii, radii_per_gauss, index, tile_size, tile_width, tile_height, b);
+        for (int ty = b[1]; ty < b[3]; ++ty)
+            for (int tx = b[0]; tx < b[2]; ++tx)
+                all[cursor[camera * per_camera + (int64_t)ty * tile_width + tx]++] = (int32_t)index;
+    }
+    int64_t largest = 0;
+    for (int64_t t = 0; t < total_tiles; ++t) {
+        int32_t *list = all + start[t];
+        int64_t n = count[t];
+        /* stable insertion sort by depth bits: ids arrived ascending, so equal depths keep ascending id */
+        for (int64_t i = 1; i < n; ++i) {
+            int32_t v = list[i];
+            uint32_t dv;
+            memcpy(&dv, &depths[v], sizeof dv);
+            int64_t p = i;
+            while (p > 0) {
+                uint32_t du;
+                memcpy(&du, &depths[list[p - 1]], sizeof du);
+                if (du <= dv) break;
+                list[p] = list[p - 1];
+                --p;
+            }
+            list[p] = v;
+        }
+        for (int64_t m = 0; m < capacity; ++m) bin_ids[t * capacity + m] = m < n ? list[m] : -1;
+        bin_counts[t] = (int32_t)n;
+        if (n > largest) largest = n;
+    }
+    free(count);
+    free(start);
+    free(all);
+    free(cursor);
+    return largest;
+}
+
+/* Compositing over fixed-capacity bins, following [pytorch3d-fine] RasterizeMeshesFineCudaKernel's walk: every
+ * slot m in [0, capacity) of the pixel's bin in order, a negative entry (the -1 sentinel) skipped wherever it
+ * stands; every other entry composited by the rule of orc_composite_pixel. last_ids holds the bin position
+ * t * capacity + m of the last composited entry (-1 if none). Returns the number of sigma evaluations, or -1. */
+int64_t orc_rasterize_bins(const float *means2d, const float *conics, const float *colors, const float *opacities,
+                           const float *backgrounds, int64_t C, int K, int width, int height, int tile_size,
+                           int tile_width, int tile_height, const int32_t *bin_ids, int64_t capacity,
+                           float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                           float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids)
+{
+    int64_t per_camera = (int64_t)tile_width * tile_height;
+    int64_t total_tiles = C * per_camera;
+    int64_t n_eval = 0;
+    float acc[64];
+    if (K < 1 || K > 64 || capacity < 1) return -1;
+    int32_t *list = (int32_t *)malloc((size_t)capacity * sizeof(int32_t));
+    int64_t *where = (int64_t *)malloc((size_t)capacity * sizeof(int64_t));
+    if (!list || !where) {
+        free(list);
+        free(where);
+        return -1;
+    }
+    for (int64_t t = 0; t < total_tiles; ++t) {
+        int64_t camera = t / per_camera;
+        int64_t local = t % per_camera;
+        int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
+        /* the bin's entries with the sentinels taken out, and where each one stood */
+        int64_t n = 0;
+        for (int64_t m = 0; m < capacity; ++m) {
+            int32_t g = bin_ids[t * capacity + m];
+            if (g < 0) continue;
+            list[n] = g;
+            where[n] = t * capacity + m;
+            ++n;
+        }
+        for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
+            for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
+                float T;
+                int64_t last;
+                orc_composite_pixel(means2d, conics, colors, opacities, K, list, 0, n, x, y, alpha_cutoff,
+                                    alpha_clamp, transmittance_threshold, acc, &T, &last, &n_eval);
+                int64_t pixel = (camera * height + y) * (int64_t)width + x;
+                for (int k = 0; k < K; ++k) {
+                    float bg = backgrounds ? backgrounds[camera * K + k] : 0.0f;
+                    render_colors[pixel * K + k] = acc[k] + T * bg;
+                }
+                render_alphas[pixel] = 1.0f - T;
+                if (render_T) render_T[pixel] = T;
+                if (last_ids) last_ids[pixel] = last >= 0 ? (int32_t)where[last] : -1;
+            }
+        }
+    }
+    free(list);
+    free(where);
+    return n_eval;
 }
