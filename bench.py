@@ -207,6 +207,34 @@ def main():
     traced_steps = int(tr_out.trace_counts.sum())
     traced_capped = int((tr_out.trace_counts == S_TRACE).sum())
     del tr_out
+    # outside the frame: fixed-capacity per-tile bins as the alternative to the sort path, and the composite
+    # over them (capacity 8192 holds the frame's largest tile)
+    CAP = 8192
+    radii_d = ds.radii
+
+    def build_bins(out=None):
+        return binding.gs_bin_tiles(ds.means2d, radii_d, ds.depths, scene.tile_size, scene.tile_width,
+                                    scene.tile_height, CAP, out=out, stream=plan.stream)
+    bins = build_bins()
+    bin_render = binding.gs_rasterize_fwd_bins(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, W_,
+                                               H_, scene.tile_size, bins.bin_ids, bins.bin_counts,
+                                               scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold,
+                                               stream=plan.stream)
+    bev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(5, args.steps // 2))]
+    for e0, e1, e2 in bev_b:
+        e0.record(plan.stream)
+        build_bins(out=bins)
+        e1.record(plan.stream)
+        binding.gs_rasterize_fwd_bins(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, W_, H_,
+                                      scene.tile_size, bins.bin_ids, bins.bin_counts, scene.alpha_cutoff,
+                                      scene.alpha_clamp, scene.transmittance_threshold, out=bin_render,
+                                      stream=plan.stream)
+        e2.record(plan.stream)
+    torch.cuda.synchronize()
+    bins_build_ms = statistics.median(e0.elapsed_time(e1) for e0, e1, _ in bev_b)
+    bins_comp_ms = statistics.median(e1.elapsed_time(e2) for _, e1, e2 in bev_b)
+    bin_counts = bins.bin_counts.cpu().numpy()
+    del bins, bin_render
     # outside the frame: the EWA projection that produces such splats, 1M 3D Gaussians into one 1920x1080 camera
     sc3 = synth.scene3d(19, scene.N, C=1, width=scene.width, height=scene.height)
     d3 = [torch.from_numpy(a).to("cuda:0") for a in (sc3.means, sc3.covars, sc3.viewmats, sc3.Ks)]
@@ -278,6 +306,13 @@ def main():
                            "trace_bytes_written": 4 * traced_steps + 4 * pixels,
                            "note": "gs_rasterize_fwd_traced on the last frame's lists, no list cap: the composite "
                                    "plus each pixel's trace row and count"},
+        "fixed_capacity_bins": {
+            "capacity": CAP, "build_ms": round(bins_build_ms, 4), "composite_ms": round(bins_comp_ms, 4),
+            "sort_path_ms": round(stage_ms["count_depth_order"] + stage_ms["emit_sort"] + stage_ms["ranges"], 4),
+            "largest_bin": int(bin_counts.max()), "overflowed_bins": int((bin_counts > CAP).sum()),
+            "bin_bytes": int(bin_counts.size) * CAP * 4,
+            "note": "gs_bin_tiles (atomic slot claims, then a bitonic sort of each bin in LDS) against the frame's "
+                    "intersect + sort + ranges stages; composite_ms is gs_rasterize_fwd_bins over the bins"},
         "projection": {"ms": round(project_ms, 4), "gaussians": sc3.N, "bytes": project_bytes,
                        "GB/s": round(project_bytes / (project_ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(project_bytes / (project_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -8,7 +8,9 @@
  *   gs_rasterize_fwd  per-tile front-to-back alpha compositing (gs_rasterize_fwd_traced: with a per-pixel
  *                     trace, a per-pixel step cap and a per-tile list cap),
  *   gs_rasterize_bwd  its backward,
- *   gs_project_fwd    the EWA projection of 3D Gaussians that feeds the intersection step.
+ *   gs_project_fwd    the EWA projection of 3D Gaussians that feeds the intersection step,
+ *   gs_bin_tiles      fixed-capacity per-tile bins (the alternative to the first three steps), composited by
+ *                     gs_rasterize_fwd_bins.
  *
  * Definitions follow these pages:
  *   [gsplat]     gsplat 1.0.0 Ruby gem, native C extension, intersections.c (gs_tile_bits, gs_bounds,
@@ -18,7 +20,8 @@
  *                (gs_raster_backward), which lists the forward's arguments;
  *   [rlx-metal]  rlx-metal 0.2.9 splat_training.rs (training_forward_metal_traced): alpha_cutoff and
  *                transmittance_threshold as forward parameters;
- *   [gsplat-proj] the gem's projection.c (gs_project_one): the projection of 3D Gaussians into cameras.
+ *   [gsplat-proj] the gem's projection.c (gs_project_one): the projection of 3D Gaussians into cameras;
+ *   [pytorch3d-fine] PyTorch3D rasterize_meshes.cu (RasterizeMeshesFineCudaKernel): the -1-sentinel bin layout.
  *
  * Conventions for every entry point.
  *   - Device pointers point to memory on the current HIP device; every array is dense and C-ordered.
@@ -200,6 +203,36 @@ gs_status gs_rasterize_fwd_traced(const float *means2d, const float *conics, con
                                   float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
                                   int32_t *trace_ids, int32_t *trace_counts, uint64_t *eval_counts, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Fixed-capacity per-tile bins, an alternative to sort-based binning ([pytorch3d-fine] PyTorch3D
+ * rasterize_meshes.cu, RasterizeMeshesFineCudaKernel, reads bins [N, BH, BW, M] int32 with -1 in empty slots;
+ * the step that fills them is not on the page).
+ *
+ * gs_bin_tiles: for each global tile t = (c * th + ty) * tw + tx, bin_counts[t] (int32 [C, th, tw]) receives the
+ * number of (camera, splat) pairs whose rectangle ([gsplat] gs_bounds, as in gs_isect_tiles) contains the tile, and
+ * bin_ids[t] (int32 [C, th, tw, capacity]) their flat ids camera * N + splat ordered by (depth bit pattern, flat
+ * id) - the tile's list of the sorted intersection path - in slots [0, min(count, capacity)), then -1.
+ * When a bin overflows (count > capacity) it keeps `capacity` of its splats, in that order; which ones is not
+ * specified (they are claimed concurrently), and the caller detects it from bin_counts.
+ * Limits: 1 <= capacity <= 16384; C * th * tw * capacity < 2^31; C*N < 2^31; radii as in gs_isect_tiles.
+ * Asynchronous; needs no workspace.
+ *
+ * gs_rasterize_fwd_bins: gs_rasterize_fwd over such bins: tile t composites slots [0, min(bin_counts[t],
+ * capacity)) of its bin in order, skipping negative entries (the sentinel); last_ids holds bin positions
+ * t * capacity + m. Same outputs, limits and errors as gs_rasterize_fwd otherwise (no masks, no workspace).
+ */
+gs_status gs_bin_tiles(const float *means2d, const float *radii, int radii_per_gauss, const float *depths, int64_t C,
+                       int64_t N, int tile_size, int tile_width, int tile_height, int capacity, int32_t *bin_ids,
+                       int32_t *bin_counts, void *stream);
+
+gs_status gs_rasterize_fwd_bins(const float *means2d, const float *conics, const float *colors,
+                                const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
+                                int width, int height, int tile_size, int tile_width, int tile_height,
+                                const int32_t *bin_ids, const int32_t *bin_counts, int capacity, float alpha_cutoff,
+                                float alpha_clamp, float transmittance_threshold, float *render_colors,
+                                float *render_alphas, float *render_T, int32_t *last_ids, uint64_t *eval_counts,
+                                void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
  * EWA projection of 3D Gaussians ([gsplat-proj] gsplat 1.0.0 projection.c: gs_project_one, gs_mat3_product,

@@ -166,3 +166,28 @@ def test_rasterize_bwd_argument_errors(lib):
     assert bwd(gm=None) == GS_ERR_INVALID_ARG
     assert b"NULL" in lib.gs_last_error()
     assert bwd(clamp=0.0) == GS_ERR_INVALID_ARG
+
+
+def test_bins_argument_errors(lib):
+    from tile_binned_gaussian_amd.binding import GS_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails on the host first
+    F = ctypes.c_float
+
+    def bins(C=1, N=4, rpg=1, ts=16, tw=4, th=4, cap=64, ids=fake, counts=fake):
+        return lib.gs_bin_tiles(fake, fake, rpg, fake, C, N, ts, tw, th, cap, ids, counts, None)
+    assert bins(cap=0) == GS_ERR_INVALID_ARG
+    assert bins(cap=16385) == GS_ERR_INVALID_ARG
+    assert b"capacity" in lib.gs_last_error()
+    assert bins(tw=1 << 12, th=1 << 12, cap=256) == GS_ERR_INVALID_ARG  # slots beyond 2^31
+    assert bins(rpg=3) == GS_ERR_INVALID_ARG
+    assert bins(ids=None) == GS_ERR_INVALID_ARG
+    assert bins(C=0) == GS_ERR_INVALID_ARG
+
+    def comp(cap=64, counts=fake, K=3, tw=4):
+        return lib.gs_rasterize_fwd_bins(fake, fake, fake, fake, None, 1, 4, K, 64, 64, 16, tw, 4, fake, counts, cap,
+                                         F(1 / 255), F(0.99), F(1e-4), fake, fake, None, None, None, None)
+    assert comp(counts=None) == GS_ERR_INVALID_ARG
+    assert comp(cap=0) == GS_ERR_INVALID_ARG
+    assert comp(K=5) == GS_ERR_INVALID_ARG
+    assert comp(tw=3) == GS_ERR_INVALID_ARG
+    assert b"gs_rasterize_fwd_bins" in lib.gs_last_error()

@@ -20,7 +20,8 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
-           "gs_rasterize_fwd", "gs_rasterize_fwd_traced", "gs_rasterize_bwd", "gs_project_fwd")
+           "gs_rasterize_fwd", "gs_rasterize_fwd_traced", "gs_rasterize_bwd", "gs_project_fwd", "gs_bin_tiles",
+           "gs_rasterize_fwd_bins")
 
 
 class GsError(RuntimeError):
@@ -59,6 +60,11 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_fwd_traced.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
                                             F, F, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd_traced.restype = I32
+    lib.gs_bin_tiles.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, I32, P, P, P]
+    lib.gs_bin_tiles.restype = I32
+    lib.gs_rasterize_fwd_bins.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I32, F, F, F,
+                                          P, P, P, P, P, P]
+    lib.gs_rasterize_fwd_bins.restype = I32
     lib.gs_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F,
                                      P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_rasterize_bwd.restype = I32
@@ -273,6 +279,62 @@ def gs_rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, wid
                                        _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
                                        _ptr(out.last_ids), _ptr(out.trace_ids), _ptr(out.trace_counts),
                                        _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+@dataclass
+class Bins:
+    bin_ids: torch.Tensor  # [C, th, tw, capacity] int32, -1 in empty slots
+    bin_counts: torch.Tensor  # [C, th, tw] int32 full counts (> capacity: the bin overflowed)
+
+
+def gs_bin_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, capacity, out=None,
+                 stream=None) -> Bins:
+    """Fixed-capacity per-tile bins: each tile's splats in (depth, id) order, -1 after them, and full counts."""
+    lib = load_library()
+    dev = means2d.device
+    _req(means2d, "means2d", torch.float32, dev)
+    if means2d.dim() != 3 or means2d.shape[2] != 2:
+        raise ValueError("means2d must be [C, N, 2]")
+    C, N = means2d.shape[0], means2d.shape[1]
+    _req(radii, "radii", torch.float32, dev)
+    if tuple(radii.shape) == (C, N):
+        rpg = 1
+    elif tuple(radii.shape) == (C, N, 2):
+        rpg = 2
+    else:
+        raise ValueError(f"radii must be [C, N] or [C, N, 2] (got {tuple(radii.shape)})")
+    _req(depths, "depths", torch.float32, dev, (C, N))
+    if out is None:
+        out = Bins(torch.empty((C, tile_height, tile_width, int(capacity)), dtype=torch.int32, device=dev),
+                   torch.empty((C, tile_height, tile_width), dtype=torch.int32, device=dev))
+    _req(out.bin_ids, "bin_ids", torch.int32, dev, (C, tile_height, tile_width, int(capacity)))
+    _req(out.bin_counts, "bin_counts", torch.int32, dev, (C, tile_height, tile_width))
+    _check(lib.gs_bin_tiles(_ptr(means2d), _ptr(radii), rpg, _ptr(depths), C, N, tile_size, tile_width, tile_height,
+                            int(capacity), _ptr(out.bin_ids), _ptr(out.bin_counts), _stream(stream)))
+    return out
+
+
+def gs_rasterize_fwd_bins(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, bin_ids,
+                          bin_counts, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, transmittance_threshold=1e-4,
+                          out=None, stream=None, eval_counts=None) -> Render:
+    """Front-to-back compositing over fixed-capacity bins; last ids are bin positions t * capacity + m."""
+    lib = load_library()
+    dev = means2d.device
+    _req(bin_ids, "bin_ids", torch.int32, dev)
+    if bin_ids.dim() != 4:
+        raise ValueError("bin_ids must be [C, th, tw, capacity]")
+    _, C, N, K, th, tw = _raster_inputs(means2d, conics, colors, opacities, backgrounds, bin_counts,
+                                        bin_ids, None)
+    if tuple(bin_ids.shape[:3]) != (C, th, tw):
+        raise ValueError("bin_ids and bin_counts disagree on [C, th, tw]")
+    if out is None:
+        out = _render_out(C, height, width, K, dev)
+    _check(lib.gs_rasterize_fwd_bins(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds),
+                                     C, N, K, width, height, tile_size, tw, th, _ptr(bin_ids), _ptr(bin_counts),
+                                     bin_ids.shape[3], float(alpha_cutoff), float(alpha_clamp),
+                                     float(transmittance_threshold), _ptr(out.render_colors), _ptr(out.render_alphas),
+                                     _ptr(out.render_T), _ptr(out.last_ids), _ptr(eval_counts), _stream(stream)))
     return out
 
 

@@ -38,6 +38,8 @@ struct RasterArgs {
     int32_t *trace_ids;               // traced kernels, nullable: [C, H, W, max_steps] flat splat ids
     int32_t *trace_counts;            // traced kernels, nullable: [C, H, W] composited splats per pixel
     int trace_vec;                    // trace_ids is 16-byte aligned and max_steps a multiple of 4
+    const int32_t *bin_counts;        // nullable: ranges from fixed-capacity bins instead of offsets
+    int capacity;                     // bin capacity (bin t occupies ids[t * capacity, (t + 1) * capacity))
 };
 
 // Traced kernels stage each pixel's trace in LDS, kTraceChunk ids per thread, and store a full chunk as four
@@ -62,13 +64,21 @@ __device__ __forceinline__ void flush_trace(int32_t *row, int j, const int32_t *
     }
 }
 
-// The range of global tile `tile`: [offsets[tile], next offset or n_isects), empty when the tile's mask is 0,
-// cut to its first max_list entries when max_list >= 0.
-__device__ __forceinline__ int range_end(const RasterArgs &a, int tile, int start) {
-    int end = (a.masks && a.masks[tile] == 0) ? start
-              : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
+// The range [start, end) of global tile `tile` in `ids`: [offsets[tile], next offset or n_isects), or with
+// bins the first min(count, capacity) slots of the tile's bin; empty when the tile's mask is 0, cut to its first
+// max_list entries when max_list >= 0.
+__device__ __forceinline__ void tile_range(const RasterArgs &a, int tile, int &start, int &end) {
+    if (a.bin_counts) {
+        start = tile * a.capacity;
+        int c = a.bin_counts[tile];
+        c = c < 0 ? 0 : (c < a.capacity ? c : a.capacity);
+        end = start + c;
+    } else {
+        start = a.offsets[tile];
+        end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects);
+    }
+    if (a.masks && a.masks[tile] == 0) end = start;
     if (a.max_list >= 0 && end - start > a.max_list) end = start + a.max_list;
-    return end;
 }
 
 template <int K, int PPT, bool COUNT, bool TRACE>
@@ -76,7 +86,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float2 s_xy[kMaxThreads];
     __shared__ float4 s_abco[kMaxThreads];
     __shared__ float s_rgb[kMaxThreads * K];
-    __shared__ int32_t s_g[TRACE ? kMaxThreads : 1];
+    __shared__ int32_t s_g[kMaxThreads];  // the staged ids (negative: an empty bin slot, skipped)
 
     const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
@@ -84,8 +94,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     const int local = tile - camera * per_camera;
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
-    const int start = a.offsets[tile];
-    const int end = range_end(a, tile, start);
+    int start, end;
+    tile_range(a, tile, start, end);
     const int ts = a.tile_size;
     const int nthreads = blockDim.x;
 
@@ -119,12 +129,14 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         if (idx < end) {
             if (COUNT) ++n_staged;
             const int g = a.ids[idx];
-            if (TRACE) s_g[threadIdx.x] = g;
-            s_xy[threadIdx.x] = a.means[g];
-            const float *cg = a.conics + 3 * static_cast<int64_t>(g);
-            s_abco[threadIdx.x] = make_float4(cg[0], cg[1], cg[2], a.opacities[g]);
+            s_g[threadIdx.x] = g;
+            if (g >= 0) {
+                s_xy[threadIdx.x] = a.means[g];
+                const float *cg = a.conics + 3 * static_cast<int64_t>(g);
+                s_abco[threadIdx.x] = make_float4(cg[0], cg[1], cg[2], a.opacities[g]);
 #pragma unroll
-            for (int k = 0; k < K; ++k) s_rgb[threadIdx.x * K + k] = a.colors[static_cast<int64_t>(g) * K + k];
+                for (int k = 0; k < K; ++k) s_rgb[threadIdx.x * K + k] = a.colors[static_cast<int64_t>(g) * K + k];
+            }
         }
         __syncthreads();
         const int count = end - base < nthreads ? end - base : nthreads;
@@ -132,6 +144,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         for (int q = 0; q < PPT; ++q) {
             if (done[q]) continue;
             for (int j = 0; j < count; ++j) {
+                if (a.bin_counts && s_g[j] < 0) continue;
                 if (COUNT) ++n_exec;
                 const float2 m = s_xy[j];
                 const float4 c = s_abco[j];
@@ -223,8 +236,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     const int local = tile - camera * per_camera;
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
-    const int start = a.offsets[tile];
-    const int end = range_end(a, tile, start);
+    int start, end;
+    tile_range(a, tile, start, end);
     const int ts = a.tile_size;
     const int nthreads = blockDim.x;
     const int wave = threadIdx.x / kWave;
@@ -280,9 +293,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     for (int base = start; base < end; base += nthreads) {
         if (__syncthreads_and(done)) break;  // also orders the previous batch's LDS reads before refilling
         const int idx = base + static_cast<int>(threadIdx.x);
-        if (idx < end) {
+        const int g = idx < end ? a.ids[idx] : -1;  // negative: an empty bin slot, never listed
+        if (g >= 0) {
             if (COUNT) ++n_staged;
-            const int g = a.ids[idx];
             const float2 m = a.means[g];
             const float *cg = a.conics + 3 * static_cast<int64_t>(g);
             const float ca = cg[0], cb = cg[1], cc = cg[2], o = a.opacities[g];
@@ -307,6 +320,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
                 }
             }
             s_mask[threadIdx.x] = bits;
+        } else if (idx < end) {
+            s_mask[threadIdx.x] = 0u;
         }
         __syncthreads();
         const int count = end - base < nthreads ? end - base : nthreads;
@@ -421,7 +436,8 @@ namespace {
 gs_status rasterize(const char *fn, const float *means2d, const float *conics, const float *colors,
                     const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K, int width,
                     int height, int tile_size, int tile_width, int tile_height, const int32_t *isect_offsets,
-                    const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks, float alpha_cutoff,
+                    const int32_t *flatten_ids, int64_t n_isects, const int32_t *bin_counts, int capacity,
+                    const int32_t *masks, float alpha_cutoff,
                     float alpha_clamp, float transmittance_threshold, int max_list_entries, int max_splat_steps,
                     float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
                     int32_t *trace_ids, int32_t *trace_counts, uint64_t *eval_counts, void *workspace,
@@ -439,9 +455,17 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
     const int64_t total_tiles = C * tile_width * tile_height;
     if (total_tiles >= (int64_t(1) << 31) || C * height * width * K >= (int64_t(1) << 40))
         return fail(GS_ERR_INVALID_ARG, "%s: image batch too large", fn);
+    if (bin_counts) {
+        // fixed-capacity bins: the ids array is [C, th, tw, capacity]
+        if (capacity < 1 || total_tiles * capacity >= (int64_t(1) << 31))
+            return fail(GS_ERR_INVALID_ARG, "%s: need capacity >= 1 and C*th*tw*capacity < 2^31", fn);
+        n_isects = total_tiles * capacity;
+    } else if (!isect_offsets) {
+        return fail(GS_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    }
     if (n_isects < 0 || n_isects >= (int64_t(1) << 31))
         return fail(GS_ERR_INVALID_ARG, "%s: n_isects = %lld outside [0, 2^31)", fn, (long long)n_isects);
-    if (!isect_offsets || !render_colors || !render_alphas || (n_isects > 0 && !flatten_ids) ||
+    if (!render_colors || !render_alphas || (n_isects > 0 && !flatten_ids) ||
         (N > 0 && (!means2d || !conics || !colors || !opacities)))
         return fail(GS_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
     if (!(alpha_cutoff >= 0.0f) || !(alpha_clamp > 0.0f) || !(transmittance_threshold >= 0.0f))
@@ -481,6 +505,8 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
     args.trace_ids = trace_ids;
     args.trace_counts = trace_counts;
     args.trace_vec = (max_splat_steps % 4 == 0 && (reinterpret_cast<uintptr_t>(trace_ids) & 15) == 0) ? 1 : 0;
+    args.bin_counts = bin_counts;
+    args.capacity = capacity;
     const bool trace = max_splat_steps >= 0;
 
     const int pixels = tile_size * tile_size;
@@ -512,9 +538,9 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
                                       uint64_t *eval_counts, void *workspace, size_t workspace_bytes,
                                       void *stream_handle) {
     return rasterize("gs_rasterize_fwd", means2d, conics, colors, opacities, backgrounds, C, N, K, width, height,
-                     tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, masks, alpha_cutoff,
-                     alpha_clamp, transmittance_threshold, -1, -1, render_colors, render_alphas, render_T, last_ids,
-                     nullptr, nullptr, eval_counts, workspace, workspace_bytes, stream_handle);
+                     tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, nullptr, 0, masks,
+                     alpha_cutoff, alpha_clamp, transmittance_threshold, -1, -1, render_colors, render_alphas,
+                     render_T, last_ids, nullptr, nullptr, eval_counts, workspace, workspace_bytes, stream_handle);
 }
 
 extern "C" gs_status gs_rasterize_fwd_traced(const float *means2d, const float *conics, const float *colors,
@@ -530,8 +556,23 @@ extern "C" gs_status gs_rasterize_fwd_traced(const float *means2d, const float *
     if (max_splat_steps < 0)
         return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd_traced: max_splat_steps = %d must be >= 0", max_splat_steps);
     return rasterize("gs_rasterize_fwd_traced", means2d, conics, colors, opacities, backgrounds, C, N, K, width,
-                     height, tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, masks,
-                     alpha_cutoff, alpha_clamp, transmittance_threshold, max_list_entries, max_splat_steps,
+                     height, tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, nullptr, 0,
+                     masks, alpha_cutoff, alpha_clamp, transmittance_threshold, max_list_entries, max_splat_steps,
                      render_colors, render_alphas, render_T, last_ids, trace_ids, trace_counts, eval_counts,
                      workspace, workspace_bytes, stream_handle);
+}
+
+extern "C" gs_status gs_rasterize_fwd_bins(const float *means2d, const float *conics, const float *colors,
+                                           const float *opacities, const float *backgrounds, int64_t C, int64_t N,
+                                           int K, int width, int height, int tile_size, int tile_width,
+                                           int tile_height, const int32_t *bin_ids, const int32_t *bin_counts,
+                                           int capacity, float alpha_cutoff, float alpha_clamp,
+                                           float transmittance_threshold, float *render_colors, float *render_alphas,
+                                           float *render_T, int32_t *last_ids, uint64_t *eval_counts,
+                                           void *stream_handle) {
+    if (!bin_counts) return fail(GS_ERR_INVALID_ARG, "gs_rasterize_fwd_bins: bin_counts is NULL");
+    return rasterize("gs_rasterize_fwd_bins", means2d, conics, colors, opacities, backgrounds, C, N, K, width,
+                     height, tile_size, tile_width, tile_height, nullptr, bin_ids, 0, bin_counts, capacity, nullptr,
+                     alpha_cutoff, alpha_clamp, transmittance_threshold, -1, -1, render_colors, render_alphas,
+                     render_T, last_ids, nullptr, nullptr, eval_counts, nullptr, 0, stream_handle);
 }
