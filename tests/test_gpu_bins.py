@@ -134,3 +134,15 @@ def test_bins_1m_splats_1080p_match_the_sorted_path():
     t = np.maximum(lb, 0) // cap
     mapped = np.where(lb >= 0, off[t] + lb % cap, -1)
     np.testing.assert_array_equal(mapped, host(fr.render.last_ids))
+
+
+def test_bins_with_more_tiles_than_the_lds_counters():
+    """Above 32768 tiles the fill takes one global atomic per (splat, tile) instead of the LDS-aggregated path."""
+    scene = synth.random_scene(72, 1, 400, 256, 160, 1, r_range=(0.3, 4.0))
+    assert scene.tile_width * scene.tile_height > 32768
+    cap = _largest(scene) + 1
+    g = _gpu_bins(scene, cap)
+    o = _oracle_bins(scene, cap)
+    np.testing.assert_array_equal(host(g.bin_counts), o.bin_counts)
+    np.testing.assert_array_equal(host(g.bin_ids), o.bin_ids)
+    _assert_render_equal(_gpu_composite(scene, g), _oracle_composite(scene, o.bin_ids))
