@@ -161,7 +161,9 @@ gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int64_t C, int 
  * output), [4] the splats staged per tile. The counting variant is a separate kernel build; with NULL nothing is
  * counted.
  * Limits: 1 <= K <= 4; 1 <= tile_size <= 32; tile_width == ceil(width / tile_size) and
- *   tile_height == ceil(height / tile_size); flatten_ids must index [0, C*N) (not checked on the device).
+ *   tile_height == ceil(height / tile_size). An entry of flatten_ids outside [0, C*N) is skipped (never read
+ *   through; the -1 of an empty bin slot is one), so malformed ids cannot make the kernels address outside their
+ *   inputs. gs_rasterize_bwd skips such entries the same way.
  * workspace: gs_rasterize_workspace_bytes(C, tile_width, tile_height) bytes, or NULL with 0 bytes. Reserved: the
  *   size is checked when one is given, but the current kernels neither read nor write it.
  */

@@ -7,6 +7,8 @@ device) and the stream (torch's current stream unless one is passed). The librar
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from dataclasses import dataclass
 
@@ -83,6 +85,23 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _stream_scoped(fn):
+    """Runs fn with its `stream` argument (when one is given) as torch's current stream, so that every buffer the
+    call allocates - workspaces, outputs, a grown workspace and the copy into it - belongs to the stream its
+    kernels run on: torch's caching allocator then never hands such a buffer to another stream while work queued
+    on this one may still use it, and the copy is ordered after the work that produced its source."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -118,6 +137,7 @@ class Intersections:
     n_isects: int
 
 
+@_stream_scoped
 def gs_isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True, stream=None,
                    workspace=None) -> Intersections:
     """Both phases of gs_isect_tiles: count (synchronises once for the size), then emit (and sort)."""
@@ -162,6 +182,7 @@ def gs_isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, s
     return Intersections(tiles_per, goff, keys, ids, n)
 
 
+@_stream_scoped
 def gs_sort_keys(keys, flatten_ids, end_bit=64, stream=None, workspace=None):
     """Stable in-place sort of (keys, flatten_ids) by bits [0, end_bit) of the keys."""
     lib = load_library()
@@ -173,6 +194,7 @@ def gs_sort_keys(keys, flatten_ids, end_bit=64, stream=None, workspace=None):
     return keys, flatten_ids
 
 
+@_stream_scoped
 def gs_tile_ranges(sorted_keys, C, tile_width, tile_height, validate=False, out=None, stream=None,
                    workspace=None):
     """Per-tile offsets [C, th, tw] int32 of sorted keys (boundary detection)."""
@@ -223,6 +245,7 @@ def _render_out(C, height, width, K, dev):
                   torch.empty((C, height, width), dtype=torch.int32, device=dev))
 
 
+@_stream_scoped
 def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
                      transmittance_threshold=1e-4, out=None, stream=None, workspace=None, eval_counts=None,
@@ -252,6 +275,7 @@ class TracedRender(Render):
     trace_counts: torch.Tensor | None  # [C, H, W] int32
 
 
+@_stream_scoped
 def gs_rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width, height, tile_size,
                             isect_offsets, flatten_ids, max_splat_steps, max_list_entries=-1, n_isects=None,
                             alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, transmittance_threshold=1e-4, trace=True,
@@ -288,6 +312,7 @@ class Bins:
     bin_counts: torch.Tensor  # [C, th, tw] int32 full counts (> capacity: the bin overflowed)
 
 
+@_stream_scoped
 def gs_bin_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, capacity, out=None,
                  stream=None) -> Bins:
     """Fixed-capacity per-tile bins: each tile's splats in (depth, id) order, -1 after them, and full counts."""
@@ -315,6 +340,7 @@ def gs_bin_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, cap
     return out
 
 
+@_stream_scoped
 def gs_rasterize_fwd_bins(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, bin_ids,
                           bin_counts, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, transmittance_threshold=1e-4,
                           out=None, stream=None, eval_counts=None) -> Render:
@@ -348,6 +374,7 @@ class RasterGrad:
     means2d_abs: torch.Tensor | None  # [C, N, 2]
 
 
+@_stream_scoped
 def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, render_alphas, last_ids, grad_render_colors, grad_render_alphas, n_isects=None,
                      alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99, grad_backgrounds=None, absgrad=False, out=None,
@@ -400,6 +427,7 @@ class Projection:
     compensations: torch.Tensor | None  # [C, N]
 
 
+@_stream_scoped
 def gs_project_fwd(means, covars, viewmats, Ks, width, height, eps2d=0.3, near_plane=0.01, far_plane=1e10,
                    radius_clip=0.0, compensation=False, orthographic=False, out=None, stream=None) -> Projection:
     """EWA projection of [N, 3] means and [N, 3, 3] covariances into C cameras."""

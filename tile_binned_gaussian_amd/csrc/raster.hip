@@ -27,6 +27,7 @@ struct RasterArgs {
     const int32_t *ids;
     const int32_t *masks;  // nullable [C, th, tw]: 0 = composite nothing in this tile
     int64_t n_isects;
+    int n_splats;  // C * N: ids outside [0, n_splats) (the -1 of an empty bin slot) are skipped, never gathered
     int total_tiles, width, height, tile_size, tile_width, tile_height;
     float alpha_cutoff, alpha_clamp, transmittance_threshold;
     float *out_colors, *out_alphas, *out_T;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float2 s_xy[kMaxThreads];
     __shared__ float4 s_abco[kMaxThreads];
     __shared__ float s_rgb[kMaxThreads * K];
-    __shared__ int32_t s_g[kMaxThreads];  // the staged ids (negative: an empty bin slot, skipped)
+    __shared__ int32_t s_g[kMaxThreads];  // the staged ids (-1: outside [0, n_splats), e.g. an empty bin slot)
 
     const int tile = static_cast<int>(blockIdx.x);
     const int per_camera = a.tile_width * a.tile_height;
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         const int idx = base + static_cast<int>(threadIdx.x);
         if (idx < end) {
             if (COUNT) ++n_staged;
-            const int g = a.ids[idx];
+            const int g0 = a.ids[idx];
+            const int g = static_cast<unsigned>(g0) < static_cast<unsigned>(a.n_splats) ? g0 : -1;
             s_g[threadIdx.x] = g;
             if (g >= 0) {
                 s_xy[threadIdx.x] = a.means[g];
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
         for (int q = 0; q < PPT; ++q) {
             if (done[q]) continue;
             for (int j = 0; j < count; ++j) {
-                if (a.bin_counts && s_g[j] < 0) continue;
+                if (s_g[j] < 0) continue;
                 if (COUNT) ++n_exec;
                 const float2 m = s_xy[j];
                 const float4 c = s_abco[j];
@@ -293,7 +295,9 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     for (int base = start; base < end; base += nthreads) {
         if (__syncthreads_and(done)) break;  // also orders the previous batch's LDS reads before refilling
         const int idx = base + static_cast<int>(threadIdx.x);
-        const int g = idx < end ? a.ids[idx] : -1;  // negative: an empty bin slot, never listed
+        const int g0 = idx < end ? a.ids[idx] : -1;
+        // outside [0, n_splats) (an empty bin slot): never listed
+        const int g = static_cast<unsigned>(g0) < static_cast<unsigned>(a.n_splats) ? g0 : -1;
         if (g >= 0) {
             if (COUNT) ++n_staged;
             const float2 m = a.means[g];
@@ -484,6 +488,7 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
     args.offsets = isect_offsets;
     args.ids = flatten_ids;
     args.n_isects = n_isects;
+    args.n_splats = static_cast<int>(C * N);
     args.masks = masks;
     args.total_tiles = static_cast<int>(total_tiles);
     args.width = width;

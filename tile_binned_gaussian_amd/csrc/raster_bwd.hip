@@ -28,6 +28,7 @@ struct BwdArgs {
     const int32_t *ids;
     const int32_t *masks;  // nullable [C, th, tw]: 0 = no splat gradients from this tile
     int64_t n_isects;
+    int n_splats;  // C * N: ids outside [0, n_splats) are skipped (never gathered, never given gradients)
     int total_tiles, width, height, tile_size, tile_width, tile_height;
     float alpha_cutoff, alpha_clamp, log_cutoff;
     const float *render_alphas;
@@ -178,6 +179,12 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
         for (int slot = static_cast<int>(threadIdx.x); slot < count; slot += static_cast<int>(blockDim.x)) {
             const int idx = lo + slot;
             const int g = a.ids[idx];
+#pragma unroll
+            for (int v = 0; v < kAcc; ++v) s_acc[slot][v] = 0.0f;
+            if (static_cast<unsigned>(g) >= static_cast<unsigned>(a.n_splats)) {
+                s_mask[slot] = 0u;  // never listed, so its accumulators stay zero and nothing is added for it
+                continue;
+            }
             const float2 m = a.means[g];
             const float *cg = a.conics + 3 * static_cast<int64_t>(g);
             const float ca = cg[0], cb = cg[1], cc = cg[2], o = a.opacities[g];
@@ -203,8 +210,6 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
                 }
             }
             s_mask[slot] = bits;
-#pragma unroll
-            for (int v = 0; v < kAcc; ++v) s_acc[slot][v] = 0.0f;
         }
         __syncthreads();
         // this wave's splats of the batch from the back, as byte offsets of their records
@@ -357,6 +362,7 @@ extern "C" gs_status gs_rasterize_bwd(const float *means2d, const float *conics,
     args.opacities = opacities;
     args.backgrounds = backgrounds;
     args.offsets = isect_offsets;
+    args.n_splats = static_cast<int>(C * N);
     args.ids = flatten_ids;
     args.n_isects = n_isects;
     args.masks = masks;

@@ -156,6 +156,9 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     for (int w = 0; w < kWaves; ++w) s_wave_hist[w][tid] = 0;
     __syncthreads();
     const uint32_t part = s_part;
+    // the host launches exactly one workgroup per partition; a counter left inconsistent by a corrupted workspace
+    // must not address past the arrays (the result is then wrong, but every access stays in bounds)
+    if (static_cast<int64_t>(part) * kTile >= n) return;
     if (status_next) status_next[static_cast<size_t>(part) * kRadix + tid] = 0;
 
     // global start of each digit bucket for this pass (exclusive scan of the histogram)
@@ -283,7 +286,8 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         const KeyT key = s_buf.keys[q];
         const uint32_t dd = digit_of(key, shift, digit_mask);
         dst[i] = s_global_base[dd] + (static_cast<uint32_t>(q) - s_local_start[dd]);
-        if (full || q < valid) keys_out[dst[i]] = key;
+        // dst < n always holds when the histogram matches the keys; the test keeps a corrupted one in bounds
+        if ((full || q < valid) && dst[i] < n) keys_out[dst[i]] = key;
     }
     // the ids follow through the same LDS bytes
     __syncthreads();
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const int q = i * kThreads + tid;
-        if (full || q < valid) ids_out[dst[i]] = s_buf.ids[q];
+        if ((full || q < valid) && dst[i] < n) ids_out[dst[i]] = s_buf.ids[q];
     }
 }
 

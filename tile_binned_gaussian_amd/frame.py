@@ -72,6 +72,14 @@ class FramePlan:
         self.ds = ds
         self.lib = binding.load_library()
         self.stream = stream if stream is not None else torch.cuda.current_stream()
+        # every buffer belongs to the plan's stream (torch's caching allocator then reuses a freed one only in
+        # that stream's order), and the workspace growth below copies on that stream too
+        with torch.cuda.stream(self.stream):
+            self._allocate(ds)
+        self.capacity = -1
+        self.n_isects = 0
+
+    def _allocate(self, ds):
         dev = ds.means2d.device
         C, N = ds.C, ds.N
         self.rpg = 2 if ds.radii.dim() == 3 else 1
@@ -93,12 +101,14 @@ class FramePlan:
                                      dtype=torch.uint8, device=dev)
         # page-locked host word for the intersection count (the device writes it without blocking the host)
         self.n_host = torch.zeros(1, dtype=torch.int64, pin_memory=True)
-        self.capacity = -1
-        self.n_isects = 0
 
     def _ensure(self, n):
         if n <= self.capacity:
             return
+        with torch.cuda.stream(self.stream):
+            self._grow(n)
+
+    def _grow(self, n):
         dev = self.ds.means2d.device
         self.keys = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
         self.ids = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
@@ -160,8 +170,9 @@ class FramePlan:
         s = binding._stream(self.stream)
         n = self._count(s)
         self._ensure(n)
-        ws = torch.empty(max(self.lib.gs_sort_workspace_bytes(n, self.end_bit), 1), dtype=torch.uint8,
-                         device=self.ds.means2d.device)
+        with torch.cuda.stream(self.stream):
+            ws = torch.empty(max(self.lib.gs_sort_workspace_bytes(n, self.end_bit), 1), dtype=torch.uint8,
+                             device=self.ds.means2d.device)
         times = []
         for r in range(warmup + repeats):
             self._emit(s, n, sort=False)
@@ -184,14 +195,15 @@ class BackwardPlan:
     def __init__(self, plan: FramePlan, seed=0, absgrad=False):
         self.plan = plan
         ds = plan.ds
-        g = torch.Generator(device=ds.means2d.device).manual_seed(seed)
-        C, H, W, K = ds.C, ds.height, ds.width, ds.colors.shape[2]
-        self.gc = torch.randn((C, H, W, K), generator=g, device=ds.means2d.device)
-        self.ga = torch.randn((C, H, W), generator=g, device=ds.means2d.device)
-        e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=ds.means2d.device)  # noqa: E731
-        self.out = binding.RasterGrad(e(C, ds.N, 2), e(C, ds.N, 3), e(C, ds.N, K), e(C, ds.N),
-                                      None if ds.backgrounds is None else e(C, K),
-                                      e(C, ds.N, 2) if absgrad else None)
+        with torch.cuda.stream(plan.stream):  # buffers belong to the stream the backward runs on
+            g = torch.Generator(device=ds.means2d.device).manual_seed(seed)
+            C, H, W, K = ds.C, ds.height, ds.width, ds.colors.shape[2]
+            self.gc = torch.randn((C, H, W, K), generator=g, device=ds.means2d.device)
+            self.ga = torch.randn((C, H, W), generator=g, device=ds.means2d.device)
+            e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=ds.means2d.device)  # noqa: E731
+            self.out = binding.RasterGrad(e(C, ds.N, 2), e(C, ds.N, 3), e(C, ds.N, K), e(C, ds.N),
+                                          None if ds.backgrounds is None else e(C, K),
+                                          e(C, ds.N, 2) if absgrad else None)
 
     def run(self):
         plan, ds = self.plan, self.plan.ds
