@@ -6,7 +6,12 @@ A step is the whole hot path on one batch of synthetic input already resident in
 of the tile bits, tile ranges and compositing. The default workload is
 the 1M-splat 1920x1080 frame (64-component clustered mixture, tile 16). Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config config3] [--no-cpu-baseline]
+Frames are independent, so the timed steps keep --frames-in-flight frames queued on as many streams (each frame
+whole, on its own buffers): one frame's latency-bound intersection chain overlaps another's compositing. The
+per-frame latency with one frame at a time is measured first and reported beside the throughput, with the
+per-stage times.
+
+    python bench.py [--steps K] [--warmup W] [--config config3] [--frames-in-flight F] [--no-cpu-baseline]
 
 Only one GPU is supported: --gpus above 1 (or a multi-rank launch) exits with a message.
 """
@@ -52,9 +57,11 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="config3", choices=sorted(WORKLOADS))
+    ap.add_argument("--frames-in-flight", type=int, default=3,
+                    help="frames queued at once on separate streams in the timed steps (1 = one at a time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tile-stride", type=int, default=4,
                     help="CPU baseline composites every k-th tile (then scales to the frame)")
@@ -169,7 +176,23 @@ def main():
     names = ["count_depth_order", "emit_sort", "ranges", "composite"]
     stage_ms = {nm: statistics.median(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
                 for i, nm in enumerate(names)}
-    ms_per_step = wall * 1e3 / args.steps
+    latency_ms = wall * 1e3 / args.steps
+    # the timed steps: frames-in-flight frames queued at once, each on its own stream and buffers
+    F = max(1, args.frames_in_flight)
+    if F == 1:
+        ms_per_step = latency_ms
+    else:
+        flight = [frame.FramePlan(ds, stream=torch.cuda.Stream()) for _ in range(F)]
+        for k in range(max(args.warmup, F)):
+            flight[k % F].run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            flight[k % F].run()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        assert all(p.n_isects == plan.n_isects for p in flight)
+        del flight
     # outside the frame: the composite's backward on the last frame (seeded output gradients)
     bwd = frame.BackwardPlan(plan, seed=0)
     for _ in range(2):
@@ -283,6 +306,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "frames_in_flight": F,
+        "latency_ms_per_frame": round(latency_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
