@@ -230,6 +230,30 @@ def main():
     traced_steps = int(tr_out.trace_counts.sum())
     traced_capped = int((tr_out.trace_counts == S_TRACE).sum())
     del tr_out
+    # outside the frame: the composite with the hardware exponential on the last frame, and how far it lands from
+    # the specified one
+    hw_out = binding.Render(torch.empty((C_, H_, W_, K_), **f32), torch.empty((C_, H_, W_), **f32),
+                            torch.empty((C_, H_, W_), **f32), torch.empty((C_, H_, W_), **i32))
+
+    def hw_composite():
+        binding.gs_rasterize_fwd_hwexp(ds.means2d, ds.conics, ds.colors, ds.opacities, ds.backgrounds, W_, H_,
+                                       scene.tile_size, plan.offsets, plan.ids, plan.n_isects, scene.alpha_cutoff,
+                                       scene.alpha_clamp, scene.transmittance_threshold, out=hw_out,
+                                       stream=plan.stream)
+    for _ in range(2):
+        hw_composite()
+    hev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(5, args.steps // 2))]
+    for a_ev, b_ev in hev:
+        a_ev.record(plan.stream)
+        hw_composite()
+        b_ev.record(plan.stream)
+    torch.cuda.synchronize()
+    hw_ms = statistics.median(a_ev.elapsed_time(b_ev) for a_ev, b_ev in hev)
+    hw_dc = (hw_out.render_colors - plan.render.render_colors).abs().amax(-1)
+    hw_dT = (hw_out.render_T - plan.render.render_T).abs()
+    hw_bad = int(((hw_dc > 1e-4) | (hw_dT > 1e-4)).sum())
+    hw_max = max(float(hw_dc.max()), float(hw_dT.max()))
+    del hw_out, hw_dc, hw_dT
     # outside the frame: fixed-capacity per-tile bins as the alternative to the sort path, and the composite
     # over them (capacity 8192 holds the frame's largest tile)
     CAP = 8192
@@ -331,6 +355,10 @@ def main():
                            "trace_bytes_written": 4 * traced_steps + 4 * pixels,
                            "note": "gs_rasterize_fwd_traced on the last frame's lists, no list cap: the composite "
                                    "plus each pixel's trace row and count"},
+        "hw_exp_composite": {"ms": round(hw_ms, 4), "Mpix/s": round(pixels / (hw_ms * 1e-3) / 1e6, 2),
+                             "pixels_over_1e-4_vs_specified": hw_bad, "max_abs_diff_vs_specified": hw_max,
+                             "note": "gs_rasterize_fwd_hwexp (v_exp_f32) on the last frame's lists; the difference "
+                                     "is to the specified-exponential composite of the same frame"},
         "fixed_capacity_bins": {
             "capacity": CAP, "build_ms": round(bins_build_ms, 4), "composite_ms": round(bins_comp_ms, 4),
             "sort_path_ms": round(stage_ms["count_depth_order"] + stage_ms["emit_sort"] + stage_ms["ranges"], 4),

@@ -179,6 +179,22 @@ gs_status gs_rasterize_fwd(const float *means2d, const float *conics, const floa
                            size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
+ * gs_rasterize_fwd_hwexp: gs_rasterize_fwd with e^-sigma taken from the hardware base-2 exponential
+ * (v_exp_f32 of -sigma log2 e, about one ulp; 0 for sigma > 80 or NaN) instead of the specified E(sigma). Faster,
+ * and not bit-identical: an alpha within about an ulp of alpha_cutoff or alpha_clamp, or a transmittance product
+ * within rounding of transmittance_threshold, can fall on the other side, which moves that pixel by up to about
+ * alpha * T (reported separately from the specified mode; the backward always recomputes with E(sigma)).
+ * Same arguments, outputs, limits and errors as gs_rasterize_fwd, without the workspace.
+ */
+gs_status gs_rasterize_fwd_hwexp(const float *means2d, const float *conics, const float *colors,
+                                 const float *opacities, const float *backgrounds, int64_t C, int64_t N, int K,
+                                 int width, int height, int tile_size, int tile_width, int tile_height,
+                                 const int32_t *isect_offsets, const int32_t *flatten_ids, int64_t n_isects,
+                                 const int32_t *masks, float alpha_cutoff, float alpha_clamp,
+                                 float transmittance_threshold, float *render_colors, float *render_alphas,
+                                 float *render_T, int32_t *last_ids, uint64_t *eval_counts, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
  * Traced forward compositing ([rlx-metal] training_forward_metal_traced: max_splat_steps, the per-pixel trace of
  * counts and ids kept for the backward, and the tile-list cap max_list_entries). Everything gs_rasterize_fwd
  * computes, with:

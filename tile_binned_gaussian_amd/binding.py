@@ -22,7 +22,7 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
-           "gs_rasterize_fwd", "gs_rasterize_fwd_traced", "gs_rasterize_bwd", "gs_project_fwd", "gs_bin_tiles",
+           "gs_rasterize_fwd", "gs_rasterize_fwd_hwexp", "gs_rasterize_fwd_traced", "gs_rasterize_bwd", "gs_project_fwd", "gs_bin_tiles",
            "gs_rasterize_fwd_bins")
 
 
@@ -59,6 +59,9 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
                                      P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd.restype = I32
+    lib.gs_rasterize_fwd_hwexp.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F,
+                                           F, P, P, P, P, P, P]
+    lib.gs_rasterize_fwd_hwexp.restype = I32
     lib.gs_rasterize_fwd_traced.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
                                             F, F, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
     lib.gs_rasterize_fwd_traced.restype = I32
@@ -266,6 +269,27 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
                                 _ptr(masks), float(alpha_cutoff), float(alpha_clamp), float(transmittance_threshold),
                                 _ptr(out.render_colors), _ptr(out.render_alphas), _ptr(out.render_T),
                                 _ptr(out.last_ids), _ptr(eval_counts), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+@_stream_scoped
+def gs_rasterize_fwd_hwexp(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
+                           flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
+                           transmittance_threshold=1e-4, out=None, stream=None, eval_counts=None,
+                           masks=None) -> Render:
+    """gs_rasterize_fwd with the hardware exponential (faster; not bit-identical to the specified one)."""
+    lib = load_library()
+    dev, C, N, K, th, tw = _raster_inputs(means2d, conics, colors, opacities, backgrounds, isect_offsets,
+                                          flatten_ids, masks)
+    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    if out is None:
+        out = _render_out(C, height, width, K, dev)
+    _check(lib.gs_rasterize_fwd_hwexp(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds),
+                                      C, N, K, width, height, tile_size, tw, th, _ptr(isect_offsets),
+                                      _ptr(flatten_ids), n, _ptr(masks), float(alpha_cutoff), float(alpha_clamp),
+                                      float(transmittance_threshold), _ptr(out.render_colors),
+                                      _ptr(out.render_alphas), _ptr(out.render_T), _ptr(out.last_ids),
+                                      _ptr(eval_counts), _stream(stream)))
     return out
 
 

@@ -82,7 +82,7 @@ __device__ __forceinline__ void tile_range(const RasterArgs &a, int tile, int &s
     if (a.max_list >= 0 && end - start > a.max_list) end = start + a.max_list;
 }
 
-template <int K, int PPT, bool COUNT, bool TRACE>
+template <int K, int PPT, bool COUNT, bool TRACE, bool HWEXP>
 __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float2 s_xy[kMaxThreads];
     __shared__ float4 s_abco[kMaxThreads];
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
                 const float dy = m.y - py[q];
                 const float sigma = 0.5f * (c.x * dx * dx + c.z * dy * dy) + c.y * dx * dy;
                 if (sigma < 0.0f) continue;
-                float alpha = c.w * exp_neg(sigma);
+                float alpha = c.w * (HWEXP ? exp_neg_hw(sigma) : exp_neg(sigma));
                 if (alpha > a.alpha_clamp) alpha = a.alpha_clamp;
                 if (alpha < a.alpha_cutoff) continue;
                 if (COUNT) ++n_pass;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
 // order, and evaluates only those. Skipped splats would have been skipped by the cutoff test at every pixel of the
 // region, so the result is the same to the bit. The evaluation loop runs in lock step without per-lane exits: a
 // pixel that stops only sets `done`, and the wave leaves the loop once every lane is done.
-template <int K, bool COUNT, bool TRACE>
+template <int K, bool COUNT, bool TRACE, bool HWEXP>
 __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) {
     constexpr int kRec = 12;  // floats per record: mx my a b | c o index id | colour[4]
     __shared__ float4 s_rec[kMaxThreads * kRec / 4];
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
             const float dx = r0.x - px;
             const float dy = r0.y - py;
             const float sigma = 0.5f * (r0.z * dx * dx + r1.x * dy * dy) + r0.w * dx * dy;
-            float alpha = r1.y * exp_neg_select(sigma);
+            float alpha = r1.y * (HWEXP ? exp_neg_hw(sigma) : exp_neg_select(sigma));
             alpha = alpha > a.alpha_clamp ? a.alpha_clamp : alpha;
             if (COUNT && !done) ++n_exec;
             if (!done && !(sigma < 0.0f) && !(alpha < a.alpha_cutoff)) {
@@ -407,22 +407,27 @@ __global__ __launch_bounds__(kMaxThreads) void raster_cull_kernel(RasterArgs a) 
     }
 }
 
-template <int K, bool COUNT, bool TRACE>
+template <int K, bool COUNT, bool TRACE, bool HWEXP>
 gs_status launch_kct(const RasterArgs &args, int threads, int ppt, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(args.total_tiles)), block(static_cast<unsigned>(threads));
-    if (ppt == 1) hipLaunchKernelGGL((raster_cull_kernel<K, COUNT, TRACE>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4, COUNT, TRACE>), grid, block, 0, stream, args);
+    if (ppt == 1) hipLaunchKernelGGL((raster_cull_kernel<K, COUNT, TRACE, HWEXP>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((raster_fwd_kernel<K, 4, COUNT, TRACE, HWEXP>), grid, block, 0, stream, args);
     GS_LAUNCH_TRY("raster_fwd_kernel");
     return ok();
 }
 
+// builds: the specified exponential with or without a trace, and the hardware exponential without one
 template <int K>
-gs_status launch_k(const RasterArgs &args, int threads, int ppt, bool trace, hipStream_t stream) {
+gs_status launch_k(const RasterArgs &args, int threads, int ppt, bool trace, bool hw_exp, hipStream_t stream) {
+    const bool count = args.eval_counts != nullptr;
+    if (hw_exp)
+        return count ? launch_kct<K, true, false, true>(args, threads, ppt, stream)
+                     : launch_kct<K, false, false, true>(args, threads, ppt, stream);
     if (trace)
-        return args.eval_counts ? launch_kct<K, true, true>(args, threads, ppt, stream)
-                                : launch_kct<K, false, true>(args, threads, ppt, stream);
-    return args.eval_counts ? launch_kct<K, true, false>(args, threads, ppt, stream)
-                            : launch_kct<K, false, false>(args, threads, ppt, stream);
+        return count ? launch_kct<K, true, true, false>(args, threads, ppt, stream)
+                     : launch_kct<K, false, true, false>(args, threads, ppt, stream);
+    return count ? launch_kct<K, true, false, false>(args, threads, ppt, stream)
+                 : launch_kct<K, false, false, false>(args, threads, ppt, stream);
 }
 
 }  // namespace
@@ -444,8 +449,8 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
                     const int32_t *masks, float alpha_cutoff,
                     float alpha_clamp, float transmittance_threshold, int max_list_entries, int max_splat_steps,
                     float *render_colors, float *render_alphas, float *render_T, int32_t *last_ids,
-                    int32_t *trace_ids, int32_t *trace_counts, uint64_t *eval_counts, void *workspace,
-                    size_t workspace_bytes, void *stream_handle) {
+                    int32_t *trace_ids, int32_t *trace_counts, int exp_mode, uint64_t *eval_counts,
+                    void *workspace, size_t workspace_bytes, void *stream_handle) {
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
     if (C < 1 || N < 0 || C * N >= (int64_t(1) << 31))
         return fail(GS_ERR_INVALID_ARG, "%s: need C >= 1, N >= 0 and C*N < 2^31", fn);
@@ -513,6 +518,8 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
     args.bin_counts = bin_counts;
     args.capacity = capacity;
     const bool trace = max_splat_steps >= 0;
+    if (exp_mode != 0 && exp_mode != 1) return fail(GS_ERR_INVALID_ARG, "%s: exp_mode %d is not 0 or 1", fn, exp_mode);
+    if (exp_mode == 1 && trace) return fail(GS_ERR_INVALID_ARG, "%s: the hardware exponential has no traced build", fn);
 
     const int pixels = tile_size * tile_size;
     int threads, ppt;
@@ -524,10 +531,10 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
         ppt = 4;
     }
     switch (K) {
-        case 1: return launch_k<1>(args, threads, ppt, trace, stream);
-        case 2: return launch_k<2>(args, threads, ppt, trace, stream);
-        case 3: return launch_k<3>(args, threads, ppt, trace, stream);
-        default: return launch_k<4>(args, threads, ppt, trace, stream);
+        case 1: return launch_k<1>(args, threads, ppt, trace, exp_mode == 1, stream);
+        case 2: return launch_k<2>(args, threads, ppt, trace, exp_mode == 1, stream);
+        case 3: return launch_k<3>(args, threads, ppt, trace, exp_mode == 1, stream);
+        default: return launch_k<4>(args, threads, ppt, trace, exp_mode == 1, stream);
     }
 }
 
@@ -545,7 +552,7 @@ extern "C" gs_status gs_rasterize_fwd(const float *means2d, const float *conics,
     return rasterize("gs_rasterize_fwd", means2d, conics, colors, opacities, backgrounds, C, N, K, width, height,
                      tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, nullptr, 0, masks,
                      alpha_cutoff, alpha_clamp, transmittance_threshold, -1, -1, render_colors, render_alphas,
-                     render_T, last_ids, nullptr, nullptr, eval_counts, workspace, workspace_bytes, stream_handle);
+                     render_T, last_ids, nullptr, nullptr, 0, eval_counts, workspace, workspace_bytes, stream_handle);
 }
 
 extern "C" gs_status gs_rasterize_fwd_traced(const float *means2d, const float *conics, const float *colors,
@@ -563,7 +570,7 @@ extern "C" gs_status gs_rasterize_fwd_traced(const float *means2d, const float *
     return rasterize("gs_rasterize_fwd_traced", means2d, conics, colors, opacities, backgrounds, C, N, K, width,
                      height, tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, nullptr, 0,
                      masks, alpha_cutoff, alpha_clamp, transmittance_threshold, max_list_entries, max_splat_steps,
-                     render_colors, render_alphas, render_T, last_ids, trace_ids, trace_counts, eval_counts,
+                     render_colors, render_alphas, render_T, last_ids, trace_ids, trace_counts, 0, eval_counts,
                      workspace, workspace_bytes, stream_handle);
 }
 
@@ -579,5 +586,19 @@ extern "C" gs_status gs_rasterize_fwd_bins(const float *means2d, const float *co
     return rasterize("gs_rasterize_fwd_bins", means2d, conics, colors, opacities, backgrounds, C, N, K, width,
                      height, tile_size, tile_width, tile_height, nullptr, bin_ids, 0, bin_counts, capacity, nullptr,
                      alpha_cutoff, alpha_clamp, transmittance_threshold, -1, -1, render_colors, render_alphas,
-                     render_T, last_ids, nullptr, nullptr, eval_counts, nullptr, 0, stream_handle);
+                     render_T, last_ids, nullptr, nullptr, 0, eval_counts, nullptr, 0, stream_handle);
+}
+
+extern "C" gs_status gs_rasterize_fwd_hwexp(const float *means2d, const float *conics, const float *colors,
+                                            const float *opacities, const float *backgrounds, int64_t C, int64_t N,
+                                            int K, int width, int height, int tile_size, int tile_width,
+                                            int tile_height, const int32_t *isect_offsets,
+                                            const int32_t *flatten_ids, int64_t n_isects, const int32_t *masks,
+                                            float alpha_cutoff, float alpha_clamp, float transmittance_threshold,
+                                            float *render_colors, float *render_alphas, float *render_T,
+                                            int32_t *last_ids, uint64_t *eval_counts, void *stream_handle) {
+    return rasterize("gs_rasterize_fwd_hwexp", means2d, conics, colors, opacities, backgrounds, C, N, K, width,
+                     height, tile_size, tile_width, tile_height, isect_offsets, flatten_ids, n_isects, nullptr, 0,
+                     masks, alpha_cutoff, alpha_clamp, transmittance_threshold, -1, -1, render_colors,
+                     render_alphas, render_T, last_ids, nullptr, nullptr, 1, eval_counts, nullptr, 0, stream_handle);
 }
