@@ -14,6 +14,8 @@
 // of keys with their ids). Stability makes the result unique, so it is compared bit for bit.
 #include "gs_sort.hpp"
 
+#include <algorithm>
+
 namespace gs {
 namespace {
 
@@ -72,7 +74,9 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_
     return before + inc - v;
 }
 
-constexpr int64_t kHistBlocks = 1024;
+// histogram workgroups: 1024 up to 8192 tiles of keys, then one per 8 tiles up to 4096 (measured: 4096 workgroups
+// read 157M keys 19% faster than 1024; on 13M keys more than 1024 only add flushes)
+constexpr int64_t kHistBlocksMin = 1024, kHistBlocksMax = 4096, kHistTilesPerBlock = 8;
 
 // Digit histograms of every pass. Each thread holds 16 keys read lane-contiguous (consecutive lanes hold
 // consecutive keys). Per pass, a lane whose digit differs from the previous lane's starts a run, and only run
@@ -358,7 +362,8 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     // a few workgroups per CU, each striding over many tiles, so that few per-workgroup flushes hit the 256 x
     // passes global counters (contended device-scope atomics dominate when every tile flushes its own)
     const int64_t hist_tiles = (n + kHistTile - 1) / kHistTile;
-    const unsigned hist_blocks = static_cast<unsigned>(hist_tiles < kHistBlocks ? hist_tiles : kHistBlocks);
+    const int64_t want = std::min(kHistBlocksMax, std::max(kHistBlocksMin, hist_tiles / kHistTilesPerBlock));
+    const unsigned hist_blocks = static_cast<unsigned>(hist_tiles < want ? hist_tiles : want);
     hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(hist_blocks), dim3(kThreads), 0, stream,
                        keys_in, n, plan, radix_histograms(scratch, n));
     GS_LAUNCH_TRY("histogram_kernel");
