@@ -70,10 +70,23 @@ __device__ __forceinline__ void wave_add(float v, float *dst, int lane) {
     if (lane == kWave - 1 && s != 0.0f) unsafeAtomicAdd(dst, s);
 }
 
-// Adds the four row sums of v to *acc in LDS (four lanes, LDS float atomics), skipping exact zeros.
-__device__ __forceinline__ void rows_add_lds(float v, float *acc, int lane) {
-    const float s = row_sum(v);
-    if ((lane & 15) == 15 && s != 0.0f) atomicAdd(acc, s);
+// Adds the four row sums of each of the N values to acc[0..N) in LDS (lanes 15, 31, 47 and 63, LDS float atomics,
+// exact zeros skipped). The DPP steps of the N sums are interleaved, so no step waits on the one just before it.
+template <int N>
+__device__ __forceinline__ void rows_add_lds(float (&v)[N], float *acc, int lane) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_read<0xb1, 0xf>(v[i]);   // quad_perm [1, 0, 3, 2]
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_read<0x4e, 0xf>(v[i]);   // quad_perm [2, 3, 0, 1]
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_read<0x114, 0xf>(v[i]);  // row_shr:4
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_read<0x118, 0xf>(v[i]);  // row_shr:8
+    if ((lane & 15) == 15) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (v[i] != 0.0f) atomicAdd(&acc[i], v[i]);
+    }
 }
 
 template <int K, int kThreads>
@@ -255,17 +268,19 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
             const float t_cb = g_sigma * dx * dy;
             const float t_cc = g_sigma * 0.5f * dy * dy;
             float *acc = s_acc[s_list[wave][jj] / (kRec * 4)];
+            float terms[K + 6];
 #pragma unroll
-            for (int k = 0; k < K; ++k) rows_add_lds(valid ? t_col[k] : 0.0f, &acc[k], lane);
-            rows_add_lds(valid ? t_op : 0.0f, &acc[K], lane);
-            rows_add_lds(valid ? t_mx : 0.0f, &acc[K + 1], lane);
-            rows_add_lds(valid ? t_my : 0.0f, &acc[K + 2], lane);
-            rows_add_lds(valid ? t_ca : 0.0f, &acc[K + 3], lane);
-            rows_add_lds(valid ? t_cb : 0.0f, &acc[K + 4], lane);
-            rows_add_lds(valid ? t_cc : 0.0f, &acc[K + 5], lane);
+            for (int k = 0; k < K; ++k) terms[k] = valid ? t_col[k] : 0.0f;
+            terms[K] = valid ? t_op : 0.0f;
+            terms[K + 1] = valid ? t_mx : 0.0f;
+            terms[K + 2] = valid ? t_my : 0.0f;
+            terms[K + 3] = valid ? t_ca : 0.0f;
+            terms[K + 4] = valid ? t_cb : 0.0f;
+            terms[K + 5] = valid ? t_cc : 0.0f;
+            rows_add_lds(terms, acc, lane);
             if (a.g_means_abs) {
-                rows_add_lds(valid ? fabsf(t_mx) : 0.0f, &acc[K + 6], lane);
-                rows_add_lds(valid ? fabsf(t_my) : 0.0f, &acc[K + 7], lane);
+                float mag[2] = {valid ? fabsf(t_mx) : 0.0f, valid ? fabsf(t_my) : 0.0f};
+                rows_add_lds(mag, acc + K + 6, lane);
             }
             if (valid) {
 #pragma unroll
