@@ -6,8 +6,9 @@ A step is the whole hot path on one batch of synthetic input already resident in
 of the tile bits, tile ranges and compositing. The default workload is
 the 1M-splat 1920x1080 frame (64-component clustered mixture, tile 16). Prints one JSON line.
 
-Frames are independent, so the timed steps keep --frames-in-flight frames queued on as many streams (each frame
-whole, on its own buffers): one frame's latency-bound intersection chain overlaps another's compositing. The
+Frames are independent, so the timed steps keep --frames-in-flight frames in flight on as many streams, each fed
+by its own host thread (each frame whole, on its own buffers): one frame's latency-bound intersection chain
+overlaps another's compositing. The
 per-frame latency with one frame at a time is measured first and reported beside the throughput, with the
 per-stage times.
 
@@ -22,6 +23,7 @@ import json
 import os
 import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -57,11 +59,12 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="config3", choices=sorted(WORKLOADS))
     ap.add_argument("--frames-in-flight", type=int, default=3,
-                    help="frames queued at once on separate streams in the timed steps (1 = one at a time)")
+                    help="frames in flight at once on separate streams and host threads in the timed steps "
+                         "(1 = one at a time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tile-stride", type=int, default=4,
                     help="CPU baseline composites every k-th tile (then scales to the frame)")
@@ -177,7 +180,8 @@ def main():
     stage_ms = {nm: statistics.median(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
                 for i, nm in enumerate(names)}
     latency_ms = wall * 1e3 / args.steps
-    # the timed steps: frames-in-flight frames queued at once, each on its own stream and buffers
+    # the timed steps: frames-in-flight frames at once, each on its own stream and buffers, each stream fed by its
+    # own host thread (a frame's host thread waits for its intersection count; the others keep queueing work)
     F = max(1, args.frames_in_flight)
     if F == 1:
         ms_per_step = latency_ms
@@ -186,11 +190,30 @@ def main():
         for k in range(max(args.warmup, F)):
             flight[k % F].run()
         torch.cuda.synchronize()
+        share = [args.steps // F + (1 if i < args.steps % F else 0) for i in range(F)]  # exactly K steps in all
+        gate = threading.Barrier(F + 1)
+
+        errors = []
+
+        def feed(p, count):
+            gate.wait()
+            try:
+                for _ in range(count):
+                    p.run()
+            except Exception as e:  # re-raised on the main thread below
+                errors.append(e)
+        workers = [threading.Thread(target=feed, args=(p, c)) for p, c in zip(flight, share)]
+        for w in workers:
+            w.start()
+        torch.cuda.synchronize()
+        gate.wait()
         t0 = time.perf_counter()
-        for k in range(args.steps):
-            flight[k % F].run()
+        for w in workers:
+            w.join()
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        if errors:
+            raise errors[0]
         assert all(p.n_isects == plan.n_isects for p in flight)
         del flight
     # outside the frame: the composite's backward on the last frame (seeded output gradients)
