@@ -181,8 +181,9 @@ def test_frame_is_deterministic():
 
 
 @pytest.mark.parametrize("n,end_bit,distinct", [(2, 64, 2), (100, 64, 7), (4095, 36, 50), (4096, 45, 4096),
-                                                (4097, 64, 3), (70001, 17, 1000), (70001, 1, 2), (300000, 47, 20000),
-                                                (1 << 20, 64, 1 << 20), (1000, 0, 5)])
+                                                (4097, 64, 3), (14335, 40, 14335), (14336, 45, 14336),
+                                                (14337, 64, 5), (28673, 47, 300), (70001, 17, 1000), (70001, 1, 2),
+                                                (300000, 47, 20000), (1 << 20, 64, 1 << 20), (1000, 0, 5)])
 def test_sort_keys_random(n, end_bit, distinct):
     rng = np.random.default_rng(n + end_bit)
     pool = rng.integers(0, 2 ** 63, size=distinct, dtype=np.uint64) * np.uint64(2) + \

@@ -2,8 +2,8 @@
 //   1. one read of the keys builds every pass's digit histogram (lanes holding consecutive keys compare digits
 //      with their neighbour and only the first lane of a run of equal digits adds to the LDS histogram, so keys
 //      that share digits - e.g. one splat's intersections - cost one LDS atomic per run);
-//   2. one kernel per digit pass: a workgroup takes the next partition (7168 pairs for 8-byte keys, 4096 for
-//      4-byte keys; dynamic index, so every predecessor is already running), ranks its keys stably with wave64
+//   2. one kernel per digit pass: a 16-wave workgroup takes the next partition (14336 pairs for 8-byte keys, 4096
+//      for 4-byte keys; dynamic index, so every predecessor is already running), ranks its keys stably with wave64
 //      ballot matching, publishes its per-digit counts, resolves its global per-digit offsets by a decoupled
 //      look-back (a window of predecessors per load round) that overlaps the LDS reorder and the id loads,
 //      reorders the pairs through LDS by digit (keys first, then ids in the same LDS bytes) and writes runs of
@@ -19,31 +19,35 @@
 namespace gs {
 namespace {
 
-constexpr int kThreads = 256;                 // 4 waves
-constexpr int kWaves = kThreads / kWave;
 constexpr int kRadix = 256;
+constexpr int kThreads = 1024;                // digit-pass workgroup: 16 waves; threads [0, kRadix) own a digit each
+constexpr int kWaves = kThreads / kWave;
+constexpr int kHistThreads = kRadix;          // histogram workgroup: one thread per digit
+static_assert(kThreads % kRadix == 0 && kThreads / kWave * kWave == kThreads, "digit threads are whole waves");
 constexpr uint32_t kFlagAggregate = 1u << 30; // partition's own count published
 constexpr uint32_t kFlagInclusive = 2u << 30; // count including every earlier partition published
 constexpr uint32_t kValueMask = (1u << 30) - 1;
 
-// Partition shape of a digit pass per key type. 8-byte keys take larger partitions and a shorter look-back
-// window: fewer partitions in flight shorten the look-back walks, whose loads (device-coherent, ~1 us each under
-// load) dominate a partition's life. Measured on 13M frame keys: 28 items and window 4 beat 16 and 8 by ~10%.
-// 4-byte keys sort the splats' depths (about a million, every partition in flight at once): 16 items and window 4
-// measured best there (windows 8, 16 and 32 and 24 or 32 items were 2-25% slower).
+// Partition shape of a digit pass per key type. Large partitions keep the look-back walks short: their loads
+// (device-coherent, ~1 us each under load) dominate a partition's life. One 1024-thread workgroup per CU with 14
+// pairs per thread (128 VGPRs, 130 KB of LDS) holds 14336 pairs; measured on 13M and 157M random 45/47-bit keys it
+// beat 256 threads x 28 pairs (two workgroups per CU) by 12% and 16%, 512 x 14 by 3% and 13%, 768 x 18-20 by 1-4%,
+// and 1024 x 12 by 5%; more than 14 pairs per thread spill past 128 VGPRs. Look-back windows of 2, 3 and 4 were
+// within 1% (2 best). 4-byte keys sort the splats' depths (about a million, every partition in flight at once):
+// 4 or 8 pairs per thread measured the same there.
 template <typename KeyT>
 struct Tiling {
-    static constexpr int items = sizeof(KeyT) == 8 ? 28 : 16;  // pairs per thread
+    static constexpr int items = sizeof(KeyT) == 8 ? 14 : 4;   // pairs per thread
     static constexpr int tile = kThreads * items;              // pairs per partition
     static constexpr int wave_span = kWave * items;            // contiguous pairs owned by one wave
-    static constexpr int window = 4;                            // predecessors inspected per look-back round
+    static constexpr int window = sizeof(KeyT) == 8 ? 2 : 4;   // predecessors inspected per look-back round
 };
 // the smallest partition of any key type sizes the look-back arrays (one status word per digit and partition)
 constexpr int kMinTile = Tiling<uint32_t>::tile < Tiling<uint64_t>::tile ? Tiling<uint32_t>::tile
                                                                           : Tiling<uint64_t>::tile;
 // histogram kernel: keys per thread and per workgroup step
 constexpr int kHistItems = 16;
-constexpr int kHistTile = kThreads * kHistItems;
+constexpr int kHistTile = kHistThreads * kHistItems;
 
 __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -57,7 +61,7 @@ __device__ __forceinline__ uint32_t digit_of(KeyT k, int shift, uint32_t mask) {
     return static_cast<uint32_t>(k >> shift) & mask;
 }
 
-// Exclusive prefix over the 256 threads of the workgroup (one value each); *total = sum.
+// Exclusive prefix over the threads of the workgroup (one value each); *total = sum.
 __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_tmp, uint32_t *total) {
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const uint32_t inc = wave_inclusive_sum(v);
@@ -83,7 +87,7 @@ constexpr int64_t kHistBlocksMin = 1024, kHistBlocksMax = 4096, kHistTilesPerBlo
 // starts add to the LDS histogram (the run length), so keys that share digits - one splat's intersections share
 // their depth bits - cost one LDS atomic per run.
 template <typename KeyT>
-__global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restrict__ keys, int64_t n,
+__global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__restrict__ keys, int64_t n,
                                                              PassPlan plan, uint32_t *__restrict__ hist) {
     __shared__ uint32_t s_hist[kMaxPasses][kRadix];
     for (int p = 0; p < plan.passes; ++p) s_hist[p][threadIdx.x] = 0;
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restr
         KeyT k[kHistItems];
 #pragma unroll
         for (int i = 0; i < kHistItems; ++i) {
-            const int q = i * kThreads + threadIdx.x;
+            const int q = i * kHistThreads + threadIdx.x;
             k[i] = q < valid ? keys[base + q] : KeyT(0);
         }
         for (int p = 0; p < plan.passes; ++p) {
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const KeyT *__restr
             const uint32_t mask = (1u << plan.bits[p]) - 1u;
 #pragma unroll
             for (int i = 0; i < kHistItems; ++i) {
-                const bool in = i * kThreads + static_cast<int>(threadIdx.x) < valid;
+                const bool in = i * kHistThreads + static_cast<int>(threadIdx.x) < valid;
                 const uint32_t d = in ? digit_of(k[i], shift, mask) : 0xffffffffu;
                 // the previous lane's digit (a whole-wave shift right by one lane; lane 0 keeps the all-ones value)
                 const uint32_t prev = __builtin_amdgcn_update_dpp(0xffffffffu, d, 0x138, 0xf, 0xf, false);
@@ -156,18 +160,20 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const uint32_t digit_mask = (1u << digit_bits) - 1u;
 
     if (tid == 0) s_part = atomicAdd(part_counter, 1u);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s_wave_hist[w][tid] = 0;
+    for (int i = tid; i < kWaves * kRadix; i += kThreads) (&s_wave_hist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t part = s_part;
     // the host launches exactly one workgroup per partition; a counter left inconsistent by a corrupted workspace
     // must not address past the arrays (the result is then wrong, but every access stays in bounds)
     if (static_cast<int64_t>(part) * kTile >= n) return;
-    if (status_next) status_next[static_cast<size_t>(part) * kRadix + tid] = 0;
+    // threads [0, kRadix) own digit d = tid for the per-digit steps; the other waves only rank and move pairs
+    const bool digit_thread = tid < kRadix;
+    const int d = digit_thread ? tid : 0;
+    if (status_next && digit_thread) status_next[static_cast<size_t>(part) * kRadix + d] = 0;
 
     // global start of each digit bucket for this pass (exclusive scan of the histogram)
     uint32_t unused_total;
-    const uint32_t digit_global_start = block_exclusive_u32(hist[tid], s_tmp, &unused_total);
+    const uint32_t digit_global_start = block_exclusive_u32(digit_thread ? hist[d] : 0u, s_tmp, &unused_total);
 
     // load this wave's span of keys (ids are loaded after the keys are written, to keep registers free)
     const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan + lane;
@@ -209,29 +215,31 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     }
     __syncthreads();
 
-    // per digit (thread d): counts of the 4 waves -> exclusive prefix over waves, and the partition total
-    const int d = tid;
+    // per digit (thread d): counts of the waves -> exclusive prefix over waves, and the partition total
     uint32_t running = 0;
+    if (digit_thread) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const uint32_t c = s_wave_hist[w][d];
-        s_wave_hist[w][d] = running;
-        running += c;
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t c = s_wave_hist[w][d];
+            s_wave_hist[w][d] = running;
+            running += c;
+        }
     }
     const uint32_t part_count = running;
     uint32_t *my_status = status + static_cast<size_t>(part) * kRadix + d;
-    atomic_store_agent(my_status, (part == 0 ? kFlagInclusive : kFlagAggregate) | part_count);
+    if (digit_thread) atomic_store_agent(my_status, (part == 0 ? kFlagInclusive : kFlagAggregate) | part_count);
 
     // issue the first look-back window now; its round trip overlaps the local reorder and the id loads below
     uint32_t s[kLookWindow];
     int64_t j = static_cast<int64_t>(part) - 1;
 #pragma unroll
     for (int w = 0; w < kLookWindow; ++w)
-        s[w] = (j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d) : kFlagInclusive;
+        s[w] = (digit_thread && j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d)
+                                            : kFlagInclusive;
 
     uint32_t local_total;
     const uint32_t local_start = block_exclusive_u32(part_count, s_tmp, &local_total);
-    s_local_start[d] = local_start;
+    if (digit_thread) s_local_start[d] = local_start;
     __syncthreads();
 
     // reorder the partition's keys by digit through LDS (local positions need no global offsets)
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     // decoupled look-back for digit d: walk back over the predecessors' published counts, a window of kLookWindow
     // at a time, until one carries an inclusive count (partition 0 always does)
     uint32_t before = 0;
-    if (part > 0) {
+    if (part > 0 && digit_thread) {
         while (true) {
             int used = 0;
             bool found = false;
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         }
         atomic_store_agent(my_status, kFlagInclusive | (before + part_count));
     }
-    s_global_base[d] = digit_global_start + before;
+    if (digit_thread) s_global_base[d] = digit_global_start + before;
     __syncthreads();
 
     // write keys: consecutive local positions of one digit go to consecutive global positions
@@ -364,7 +372,7 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     const int64_t hist_tiles = (n + kHistTile - 1) / kHistTile;
     const int64_t want = std::min(kHistBlocksMax, std::max(kHistBlocksMin, hist_tiles / kHistTilesPerBlock));
     const unsigned hist_blocks = static_cast<unsigned>(hist_tiles < want ? hist_tiles : want);
-    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(hist_blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(histogram_kernel<KeyT>, dim3(hist_blocks), dim3(kHistThreads), 0, stream,
                        keys_in, n, plan, radix_histograms(scratch, n));
     GS_LAUNCH_TRY("histogram_kernel");
     return radix_passes<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, scratch, stream,
