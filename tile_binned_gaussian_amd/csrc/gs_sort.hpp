@@ -7,6 +7,15 @@ namespace gs {
 
 constexpr int kMaxPasses = 8;
 
+// The digit histograms (kMaxPasses x 256 counts) are kept in kHistCopies copies: producer workgroup b adds its
+// counts into copy b % kHistCopies and the digit passes sum the copies. Device-scope atomics to one word serialize
+// at the memory side, so thousands of workgroups flushing into a single copy queue up behind each other.
+constexpr int kHistCopies = 16;
+constexpr int kHistCopyWords = kMaxPasses * 256;
+__device__ __forceinline__ uint32_t *hist_copy(uint32_t *hist, unsigned block) {
+    return hist + static_cast<size_t>(block % kHistCopies) * kHistCopyWords;
+}
+
 // Digit passes over bits [begin_bit, end_bit): pass p sorts `bits[p]` bits starting at `shift[p]`.
 struct PassPlan {
     int passes;
@@ -26,7 +35,7 @@ SortScratchLayout sort_scratch_layout(int64_t n);
 
 // Clears the scratch's histograms, partition counters and first look-back array for a sort of n pairs.
 gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream);
-// The scratch's per-pass digit histograms (kMaxPasses x 256 counts) for a sort of n pairs.
+// The scratch's per-pass digit histograms (kHistCopies copies of kMaxPasses x 256 counts) for a sort of n pairs.
 uint32_t *radix_histograms(void *scratch, int64_t n);
 
 // The digit passes alone, after radix_prepare and with the histograms already accumulated by the caller.

@@ -45,6 +45,7 @@ struct Tiling {
 // the smallest partition of any key type sizes the look-back arrays (one status word per digit and partition)
 constexpr int kMinTile = Tiling<uint32_t>::tile < Tiling<uint64_t>::tile ? Tiling<uint32_t>::tile
                                                                           : Tiling<uint64_t>::tile;
+static_assert(kHistCopyWords == kMaxPasses * kRadix, "one histogram copy holds every pass's digits");
 // histogram kernel: keys per thread and per workgroup step
 constexpr int kHistItems = 16;
 constexpr int kHistTile = kHistThreads * kHistItems;
@@ -78,9 +79,10 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_
     return before + inc - v;
 }
 
-// histogram workgroups: 1024 up to 8192 tiles of keys, then one per 8 tiles up to 4096 (measured: 4096 workgroups
-// read 157M keys 19% faster than 1024; on 13M keys more than 1024 only add flushes)
-constexpr int64_t kHistBlocksMin = 1024, kHistBlocksMax = 4096, kHistTilesPerBlock = 8;
+// histogram workgroups: 2048 up to 16384 tiles of keys, then one per 8 tiles up to 4096 (measured with the
+// flushes spread over the histogram copies: 2048 read 13M keys 15% faster than 1024, and 4096 read 157M keys 19%
+// faster than 1024)
+constexpr int64_t kHistBlocksMin = 2048, kHistBlocksMax = 4096, kHistTilesPerBlock = 8;
 
 // Digit histograms of every pass. Each thread holds 16 keys read lane-contiguous (consecutive lanes hold
 // consecutive keys). Per pass, a lane whose digit differs from the previous lane's starts a run, and only run
@@ -125,9 +127,10 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
         }
     }
     __syncthreads();
+    uint32_t *copy = hist_copy(hist, blockIdx.x);
     for (int p = 0; p < plan.passes; ++p) {
         const uint32_t c = s_hist[p][threadIdx.x];
-        if (c) atomicAdd(&hist[p * kRadix + threadIdx.x], c);
+        if (c) atomicAdd(&copy[p * kRadix + threadIdx.x], c);
     }
 }
 
@@ -171,9 +174,15 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const int d = digit_thread ? tid : 0;
     if (status_next && digit_thread) status_next[static_cast<size_t>(part) * kRadix + d] = 0;
 
-    // global start of each digit bucket for this pass (exclusive scan of the histogram)
+    // global start of each digit bucket for this pass (exclusive scan of the histogram, summed over its copies;
+    // before the key loads, whose latency the scan's barrier would otherwise wait out)
+    uint32_t digit_count = 0;
+    if (digit_thread) {
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) digit_count += hist[c * kHistCopyWords + d];
+    }
     uint32_t unused_total;
-    const uint32_t digit_global_start = block_exclusive_u32(digit_thread ? hist[d] : 0u, s_tmp, &unused_total);
+    const uint32_t digit_global_start = block_exclusive_u32(digit_count, s_tmp, &unused_total);
 
     // load this wave's span of keys (ids are loaded after the keys are written, to keep registers free)
     const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan + lane;
@@ -189,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
             k[i] = pos < n ? keys_in[pos] : ~KeyT(0);  // past the end: largest digit, ranked after every real pair
         }
     }
+
 
     // stable rank within the wave: lanes holding the same digit found by ballots over the digit's bits
     uint32_t rank[kItems];
@@ -335,7 +345,7 @@ SortScratchLayout sort_scratch_layout(int64_t n) {
     L.parts = (n + kMinTile - 1) / kMinTile;
     Carver c(nullptr);
     L.hist = 0;
-    c.take<uint32_t>(kMaxPasses * kRadix);
+    c.take<uint32_t>(static_cast<size_t>(kHistCopies) * kHistCopyWords);
     L.counters = align_up(c.used, 256);
     c.take<uint32_t>(kMaxPasses);
     const size_t status_words = static_cast<size_t>(L.parts > 0 ? L.parts : 1) * kRadix;
@@ -367,8 +377,8 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     if (plan.passes == 0 || n < 1) return ok();
     gs_status st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
-    // a few workgroups per CU, each striding over many tiles, so that few per-workgroup flushes hit the 256 x
-    // passes global counters (contended device-scope atomics dominate when every tile flushes its own)
+    // a few workgroups per CU, each striding over several tiles, so that the per-workgroup flushes into the
+    // histogram copies stay few (contended device-scope atomics dominate when every tile flushes its own)
     const int64_t hist_tiles = (n + kHistTile - 1) / kHistTile;
     const int64_t want = std::min(kHistBlocksMax, std::max(kHistBlocksMin, hist_tiles / kHistTilesPerBlock));
     const unsigned hist_blocks = static_cast<unsigned>(hist_tiles < want ? hist_tiles : want);
