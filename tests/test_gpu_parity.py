@@ -103,6 +103,19 @@ def test_isect_unsorted_and_sorted(name):
         assert_isect_equal(scene, it_g, it_o, sort)
 
 
+def test_isect_rectangle_past_2_pow_22_tiles():
+    # one splat whose rectangle covers a 2300 x 2000 grid of one-pixel tiles (4.6M > 2^22 tiles) among small ones:
+    # the emission splits a slot's index in the rectangle into row and column with a float reciprocal below 2^22
+    # and with the integer division from 2^22 on, so both ways meet in one rectangle
+    s = synth.random_scene(45, 1, 40, 2300, 2000, 1, r_range=(0.5, 6.0))
+    s.means2d[0, 0] = np.float32([1150.0, 1000.0])
+    s.radii[0, 0] = np.float32(5000.0)
+    for sort in (False, True):
+        it_o = oracle.isect_tiles(s.means2d, s.radii, s.depths, s.tile_size, s.tile_width, s.tile_height, sort=sort)
+        assert it_o.tiles_per_gauss[0, 0] == 2300 * 2000 > (1 << 22)
+        assert_isect_equal(s, gpu_isect(s, sort), it_o, sort)
+
+
 @pytest.mark.parametrize("name", list(SCENES))
 def test_ranges_on_oracle_keys(name):
     scene = SCENES[name]()
