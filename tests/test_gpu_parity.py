@@ -128,6 +128,21 @@ def test_ranges_on_oracle_keys(name):
         np.testing.assert_array_equal(host(off_g), off_o)
 
 
+@pytest.mark.parametrize("name", ["multicam-ragged-elliptical", "ts8-margin", "one-isect", "deep-tiles"])
+def test_ranges_on_keys_not_16_byte_aligned(name):
+    # keys one element into an allocation: 8-byte but not 16-byte aligned, which takes the scalar-load path
+    scene = SCENES[name]()
+    it_o = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                              scene.tile_height, sort=True)
+    off_o = oracle.tile_offsets(it_o.keys, scene.C, scene.tile_width, scene.tile_height)
+    padded = dev(np.concatenate([np.zeros(1, np.int64), it_o.keys.view(np.int64)]))
+    keys = padded[1:]
+    assert keys.data_ptr() % 16 == 8
+    for validate in (False, True):
+        off_g = binding.gs_tile_ranges(keys, scene.C, scene.tile_width, scene.tile_height, validate=validate)
+        np.testing.assert_array_equal(host(off_g), off_o)
+
+
 @pytest.mark.parametrize("name", list(SCENES))
 def test_frame_end_to_end(name):
     scene = SCENES[name]()

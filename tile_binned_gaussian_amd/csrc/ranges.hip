@@ -1,6 +1,7 @@
-// Per-tile ranges of a sorted intersection array by boundary detection: thread i compares the global tile of
+// Per-tile ranges of a sorted intersection array by boundary detection: position i compares the global tile of
 // key i with that of key i - 1 and, when they differ, writes i as the start offset of every tile in between
-// (empty tiles included). Output format and the out-of-grid error: gsplat 1.0.0 native extension,
+// (empty tiles included). Each thread walks kPer consecutive positions (16-byte loads when the keys are 16-byte
+// aligned), so it reads one key before its run and its own kPer keys. Output format and the out-of-grid error: gsplat 1.0.0 native extension,
 // intersections.c, gs_offset_encode; range reading: raster_backward.c, gs_raster_backward_without_gvl.
 #include "gs_internal.hpp"
 
@@ -8,6 +9,7 @@ namespace gs {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPer = 8;  // positions per thread
 constexpr uint32_t kErrOutOfGrid = 1u;
 constexpr uint32_t kErrUnsorted = 2u;
 
@@ -31,19 +33,39 @@ __device__ __forceinline__ int64_t global_tile(uint64_t key, const Grid &g, uint
     return static_cast<int64_t>(camera) * g.per_camera + static_cast<int64_t>(tile);
 }
 
+template <bool kVec>
 __global__ __launch_bounds__(kThreads) void ranges_kernel(const uint64_t *__restrict__ keys, int64_t n, Grid g,
                                                           int32_t *__restrict__ offsets, uint32_t *__restrict__ flag) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (i >= n) return;
+    const int64_t base = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * kPer;
+    if (base >= n) return;
+    uint64_t k[kPer];
+    if (kVec && base + kPer <= n) {
+        const ulonglong2 *v = reinterpret_cast<const ulonglong2 *>(keys + base);
+#pragma unroll
+        for (int j = 0; j < kPer / 2; ++j) {
+            const ulonglong2 x = v[j];
+            k[2 * j] = x.x;
+            k[2 * j + 1] = x.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) k[j] = base + j < n ? keys[base + j] : 0ull;
+    }
     uint32_t err = 0;
-    const int64_t cur = global_tile(keys[i], g, &err);
-    const int64_t prev = (i == 0) ? -1 : global_tile(keys[i - 1], g, &err);
-    if (prev > cur) err |= kErrUnsorted;
-    // tiles (prev, cur] start at i
-    const int64_t hi = cur < g.total ? cur : g.total - 1;
-    for (int64_t t = prev + 1; t <= hi; ++t) offsets[t] = static_cast<int32_t>(i);
-    if (i == n - 1)
-        for (int64_t t = (cur > prev ? cur : prev) + 1; t < g.total; ++t) offsets[t] = static_cast<int32_t>(n);
+    int64_t prev = (base == 0) ? -1 : global_tile(keys[base - 1], g, &err);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t i = base + j;
+        if (i >= n) break;
+        const int64_t cur = global_tile(k[j], g, &err);
+        if (prev > cur) err |= kErrUnsorted;
+        // tiles (prev, cur] start at i
+        const int64_t hi = cur < g.total ? cur : g.total - 1;
+        for (int64_t t = prev + 1; t <= hi; ++t) offsets[t] = static_cast<int32_t>(i);
+        if (i == n - 1)
+            for (int64_t t = (cur > prev ? cur : prev) + 1; t < g.total; ++t) offsets[t] = static_cast<int32_t>(n);
+        prev = cur;
+    }
     if (err && flag) atomicOr(flag, err);
 }
 
@@ -78,9 +100,14 @@ extern "C" gs_status gs_tile_ranges(const uint64_t *sorted_keys, int64_t n, int6
         return ok();
     }
     if (validate) GS_HIP_TRY(fill_u32(flag, 0, 1, stream));
-    const int64_t blocks = (n + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(ranges_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sorted_keys, n,
-                       g, isect_offsets, validate ? flag : nullptr);
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kPer;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    if (reinterpret_cast<uintptr_t>(sorted_keys) % 16 == 0)
+        hipLaunchKernelGGL(ranges_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                           sorted_keys, n, g, isect_offsets, validate ? flag : nullptr);
+    else
+        hipLaunchKernelGGL(ranges_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                           sorted_keys, n, g, isect_offsets, validate ? flag : nullptr);
     GS_LAUNCH_TRY("ranges_kernel");
     if (validate) {
         uint32_t host_flag = 0;
