@@ -70,22 +70,67 @@ __device__ __forceinline__ void wave_add(float v, float *dst, int lane) {
     if (lane == kWave - 1 && s != 0.0f) unsafeAtomicAdd(dst, s);
 }
 
-// Adds the four row sums of each of the N values to acc[0..N) in LDS (lanes 15, 31, 47 and 63, LDS float atomics,
-// exact zeros skipped). The DPP steps of the N sums are interleaved, so no step waits on the one just before it.
+// Adds the four row sums of each of the N values to acc[0..N) in LDS (LDS float atomics, exact zeros skipped).
+// For N >= 8 the first 8 values are reduced scatter-wise: in the two quad steps each lane keeps one half of every
+// pair of values and adds its partner's copy of that half (value 2i + bit 0 of the lane after the first step, and
+// q or q + 4, q = lane & 3, after the second), so each lane carries 2 of the 8 values through the row shifts by 4
+// and by 8, and lanes 12-15 of a row end with the row sums of values q and q + 4. Values 8.. and all values when
+// N < 8 take the plain steps (every lane of a quad keeps every sum; lane 15 of the row ends with the row sum).
+// Every sum still has 4 levels of additions. The DPP steps of independent sums are interleaved.
 template <int N>
 __device__ __forceinline__ void rows_add_lds(float (&v)[N], float *acc, int lane) {
+    if constexpr (N >= 8) {
+        const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+        float w[4];
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_read<0xb1, 0xf>(v[i]);   // quad_perm [1, 0, 3, 2]
+        for (int i = 0; i < 4; ++i) {
+            const float send = b0 ? v[2 * i] : v[2 * i + 1];
+            const float keep = b0 ? v[2 * i + 1] : v[2 * i];
+            w[i] = keep + dpp_read<0xb1, 0xf>(send);  // quad_perm [1, 0, 3, 2]
+        }
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_read<0x4e, 0xf>(v[i]);   // quad_perm [2, 3, 0, 1]
+        for (int i = 8; i < N; ++i) v[i] += dpp_read<0xb1, 0xf>(v[i]);
+        float u[2];
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_read<0x114, 0xf>(v[i]);  // row_shr:4
+        for (int i = 0; i < 2; ++i) {
+            const float send = b1 ? w[2 * i] : w[2 * i + 1];
+            const float keep = b1 ? w[2 * i + 1] : w[2 * i];
+            u[i] = keep + dpp_read<0x4e, 0xf>(send);  // quad_perm [2, 3, 0, 1]
+        }
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_read<0x118, 0xf>(v[i]);  // row_shr:8
-    if ((lane & 15) == 15) {
+        for (int i = 8; i < N; ++i) v[i] += dpp_read<0x4e, 0xf>(v[i]);
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            if (v[i] != 0.0f) atomicAdd(&acc[i], v[i]);
+        for (int i = 0; i < 2; ++i) u[i] += dpp_read<0x114, 0xf>(u[i]);  // row_shr:4
+#pragma unroll
+        for (int i = 8; i < N; ++i) v[i] += dpp_read<0x114, 0xf>(v[i]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) u[i] += dpp_read<0x118, 0xf>(u[i]);  // row_shr:8
+#pragma unroll
+        for (int i = 8; i < N; ++i) v[i] += dpp_read<0x118, 0xf>(v[i]);
+        if ((lane & 15) >= 12) {
+            const int q = lane & 3;
+            if (u[0] != 0.0f) atomicAdd(&acc[q], u[0]);
+            if (u[1] != 0.0f) atomicAdd(&acc[q + 4], u[1]);
+        }
+        if ((lane & 15) == 15) {
+#pragma unroll
+            for (int i = 8; i < N; ++i)
+                if (v[i] != 0.0f) atomicAdd(&acc[i], v[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp_read<0xb1, 0xf>(v[i]);   // quad_perm [1, 0, 3, 2]
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp_read<0x4e, 0xf>(v[i]);   // quad_perm [2, 3, 0, 1]
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp_read<0x114, 0xf>(v[i]);  // row_shr:4
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp_read<0x118, 0xf>(v[i]);  // row_shr:8
+        if ((lane & 15) == 15) {
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if (v[i] != 0.0f) atomicAdd(&acc[i], v[i]);
+        }
     }
 }
 
