@@ -261,7 +261,8 @@ def test_masked_tiles_finite_differences_and_forward():
     assert masked_px.any() and not masked_px.all()
     np.testing.assert_array_equal(rm.render_T[0][masked_px], 1.0)
     np.testing.assert_array_equal(rm.last_ids[0][masked_px], -1)
-    np.testing.assert_array_equal(rm.render_colors[0][masked_px], np.broadcast_to(s.backgrounds[0], (masked_px.sum(), 3)))
+    np.testing.assert_array_equal(rm.render_colors[0][masked_px],
+                                  np.broadcast_to(s.backgrounds[0], (masked_px.sum(), 3)))
     for a, b in [(rm.render_colors, ras.render_colors), (rm.render_T, ras.render_T), (rm.last_ids, ras.last_ids)]:
         np.testing.assert_array_equal(a[0][~masked_px], b[0][~masked_px])
 

@@ -14,7 +14,8 @@ from tile_binned_gaussian_amd import synth
 @pytest.mark.parametrize("n,distinct", [(0, 1), (1, 1), (2, 1), (7, 3), (1000, 5), (4097, 4097), (30000, 100)])
 def test_sort_matches_numpy_stable(orc, n, distinct):
     rng = np.random.default_rng(n + distinct)
-    base = rng.integers(0, 2 ** 63, size=distinct, dtype=np.uint64) | np.uint64(1 << 63) * rng.integers(0, 2, distinct).astype(np.uint64)
+    base = (rng.integers(0, 2 ** 63, size=distinct, dtype=np.uint64)
+            | np.uint64(1 << 63) * rng.integers(0, 2, distinct).astype(np.uint64))
     keys = base[rng.integers(0, distinct, size=n)]
     ids = rng.integers(-2 ** 31, 2 ** 31 - 1, size=n).astype(np.int32)
     k, i = orc.sort_pairs(keys, ids)

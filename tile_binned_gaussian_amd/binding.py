@@ -22,8 +22,8 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
-           "gs_rasterize_fwd", "gs_rasterize_fwd_hwexp", "gs_rasterize_fwd_traced", "gs_rasterize_bwd", "gs_project_fwd", "gs_bin_tiles",
-           "gs_rasterize_fwd_bins")
+           "gs_rasterize_fwd", "gs_rasterize_fwd_hwexp", "gs_rasterize_fwd_traced", "gs_rasterize_bwd",
+           "gs_project_fwd", "gs_bin_tiles", "gs_rasterize_fwd_bins")
 
 
 class GsError(RuntimeError):

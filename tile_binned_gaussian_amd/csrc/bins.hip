@@ -1,7 +1,8 @@
 // Fixed-capacity per-tile bins on gfx950, the alternative to sort-based binning: every (camera, splat) claims a
 // slot in each bin its rectangle covers by atomic adds on the bin's counter (no global sort, no prefix sums;
-// aggregated per workgroup in LDS when the tile counters fit there), then one workgroup per bin orders the bin's entries in LDS by (depth bit pattern, flat id) with a
-// bitonic network and writes them back followed by -1 sentinels. The result holds, bin by bin, the same list
+// aggregated per workgroup in LDS when the tile counters fit there), then one workgroup per bin orders the bin's
+// entries in LDS by (depth bit pattern, flat id) with a bitonic network and writes them back followed by -1
+// sentinels. The result holds, bin by bin, the same list
 // as the sorted intersection path (when no bin overflows).
 //
 // Layout: the -1-sentinel bins [C, th, tw, capacity] int32 read by PyTorch3D rasterize_meshes.cu

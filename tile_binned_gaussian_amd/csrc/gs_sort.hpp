@@ -44,9 +44,10 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
                        KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
                        hipStream_t stream, int *result_in_b);
 
-// Stable LSD sort of n (key, id) pairs (prepare + histograms + passes). Pass 0 reads (keys_in, ids_in) (ids_in == nullptr: ids are the input
-// positions); pass p writes buffer A when p is even and B when odd, so the result is in B after an even number of
-// passes (*result_in_b = 1) and in A after an odd number. keys_in may alias B but never A.
+// Stable LSD sort of n (key, id) pairs (prepare + histograms + passes). Pass 0 reads (keys_in, ids_in)
+// (ids_in == nullptr: ids are the input positions); pass p writes buffer A when p is even and B when odd, so the
+// result is in B after an even number of passes (*result_in_b = 1) and in A after an odd number. keys_in may alias
+// B but never A.
 template <typename KeyT>
 gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                            KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,

@@ -211,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                 s_y0[threadIdx.x] = r.y0;
                 s_w[threadIdx.x] = r.x1 - r.x0;
             }
-            // a slot never maps to an empty rectangle unless the offsets are corrupt; width 1 keeps the division defined
+            // a slot never maps to an empty rectangle unless the offsets are corrupt; width 1 keeps the division
+            // defined
             const int w = max(s_w[threadIdx.x], 1);
             s_w[threadIdx.x] = w;
             s_rcp_w[threadIdx.x] = 1.0f / static_cast<float>(w);

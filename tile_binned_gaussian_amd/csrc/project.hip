@@ -105,10 +105,11 @@ __global__ __launch_bounds__(kThreads) void project_kernel(ProjectArgs a) {
     const float safe = det <= 0.0f ? 1e-10f : det;
     const int32_t rx = ceil_radius(3.33f * sqrtf(fmaxf(c2[0], 0.0f)));
     const int32_t ry = ceil_radius(3.33f * sqrtf(fmaxf(c2[3], 0.0f)));
+    const float frx = static_cast<float>(rx), fry = static_cast<float>(ry);
     const bool visible = det > 0.0f && depth > a.near_plane && depth < a.far_plane &&
-                         (static_cast<float>(rx) > a.radius_clip || static_cast<float>(ry) > a.radius_clip) &&
-                         p0 + static_cast<float>(rx) > 0.0f && p0 - static_cast<float>(rx) < static_cast<float>(a.width) &&
-                         p1 + static_cast<float>(ry) > 0.0f && p1 - static_cast<float>(ry) < static_cast<float>(a.height);
+                         (frx > a.radius_clip || fry > a.radius_clip) && p0 + frx > 0.0f &&
+                         p0 - frx < static_cast<float>(a.width) && p1 + fry > 0.0f &&
+                         p1 - fry < static_cast<float>(a.height);
     const int64_t i = static_cast<int64_t>(c) * a.N + g;
     reinterpret_cast<int2 *>(a.radii)[i] = visible ? make_int2(rx, ry) : make_int2(0, 0);
     reinterpret_cast<float2 *>(a.means2d)[i] = make_float2(p0, p1);

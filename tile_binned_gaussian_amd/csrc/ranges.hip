@@ -1,8 +1,9 @@
 // Per-tile ranges of a sorted intersection array by boundary detection: position i compares the global tile of
 // key i with that of key i - 1 and, when they differ, writes i as the start offset of every tile in between
 // (empty tiles included). Each thread walks kPer consecutive positions (16-byte loads when the keys are 16-byte
-// aligned), so it reads one key before its run and its own kPer keys. Output format and the out-of-grid error: gsplat 1.0.0 native extension,
-// intersections.c, gs_offset_encode; range reading: raster_backward.c, gs_raster_backward_without_gvl.
+// aligned), so it reads one key before its run and its own kPer keys. Output format and the out-of-grid error:
+// gsplat 1.0.0 native extension, intersections.c, gs_offset_encode; range reading: raster_backward.c,
+// gs_raster_backward_without_gvl.
 #include "gs_internal.hpp"
 
 namespace gs {

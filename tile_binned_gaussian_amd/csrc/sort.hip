@@ -28,8 +28,8 @@ constexpr uint32_t kFlagAggregate = 1u << 30; // partition's own count published
 constexpr uint32_t kFlagInclusive = 2u << 30; // count including every earlier partition published
 constexpr uint32_t kValueMask = (1u << 30) - 1;
 
-// Partition shape of a digit pass per key type. Large partitions keep the look-back walks short: their loads
-// (device-coherent, ~1 us each under load) dominate a partition's life. One 1024-thread workgroup per CU with 14
+// Partition shape of a digit pass per key type. Large partitions shorten the look-back walks (device-coherent
+// loads, ~1 us each under load) as long as the CU keeps 16 waves: one 1024-thread workgroup per CU with 14
 // pairs per thread (128 VGPRs, 130 KB of LDS) holds 14336 pairs; measured on 13M and 157M random 45/47-bit keys it
 // beat 256 threads x 28 pairs (two workgroups per CU) by 12% and 16%, 512 x 14 by 3% and 13%, 768 x 18-20 by 1-4%,
 // and 1024 x 12 by 5%; more than 14 pairs per thread spill past 128 VGPRs. Look-back windows of 2, 3 and 4 were
@@ -135,8 +135,9 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
 }
 
 // One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling<KeyT>);
-// wave w owns the contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at w*kWaveSpan + i*64 + l,
-// so (wave, item, lane) order is input order and the per-wave running counts give a stable rank.
+// wave w owns the contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at
+// w * kWaveSpan + i * 64 + l, so (wave, item, lane) order is input order and the per-wave running counts give a
+// stable rank.
 // ids_in == nullptr means the identity (id = input position). status[part][d] holds this pass's look-back
 // words; status_next[part][d] is cleared for the next pass.
 template <typename KeyT, int kDigitBits>
