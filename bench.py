@@ -138,6 +138,27 @@ def cpu_baseline(scene, stride):
                   f"tile ({tiles.size} of {off.size}, {t2 - t1:.2f} s) scaled to all tiles; single thread",
         "frame_s_estimate": round(frame_s, 3), "isect_sort_offsets_s": round(t1 - t0, 3),
         "keys_sorted_per_s": it.n_isects / (t1 - t0),
+    }, (it, off, tiles, t1 - t0)
+
+
+def cpu_baseline_openmp(scene, sample):
+    """The same oracle built with OpenMP over the composite's tiles (the pages' CPU parallelisation) on the same
+    tile sample; intersections, sort and offsets stay single-threaded (the single-thread time above is reused)."""
+    import oracle
+    it, off, tiles, isect_s = sample
+    t0 = time.perf_counter()
+    oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds, scene.width,
+                         scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects, scene.alpha_cutoff,
+                         scene.alpha_clamp, scene.transmittance_threshold, tiles=tiles, openmp=True)
+    comp_s = time.perf_counter() - t0
+    frame_s = isect_s + comp_s * off.size / tiles.size
+    threads = oracle.threads(openmp=True)
+    return {
+        "value": scene.C * scene.width * scene.height / frame_s / 1e6, "unit": "Mpix/s", "cores": threads,
+        "kind": "oracle (OpenMP build)",
+        "sample": f"composite on the same {tiles.size} tiles with {threads} threads ({comp_s:.2f} s) scaled to all "
+                  f"tiles, plus the single-thread intersections+sort+offsets ({isect_s:.2f} s)",
+        "frame_s_estimate": round(frame_s, 3),
     }
 
 
@@ -410,7 +431,8 @@ def main():
         result["copy_calibration"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "copies": 3}
         del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(scene, args.cpu_tile_stride)
+        result["cpu_baseline"], sample = cpu_baseline(scene, args.cpu_tile_stride)
+        result["cpu_baseline_openmp"] = cpu_baseline_openmp(scene, sample)
     print(json.dumps(result), flush=True)
 
 

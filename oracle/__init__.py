@@ -19,29 +19,35 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gs_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")  # the same source built with OpenMP (the composite's tile loop)
 _lib = None
+_lib_omp = None
 
 OK, ERR_INVALID_ARG, ERR_OUT_OF_GRID, ERR_NOMEM = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (no contraction, no fast-math: float32 results are reproducible)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
-                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
+    """Compile the oracle with gcc (no contraction, no fast-math: float32 results are reproducible), once as is and
+    once with OpenMP; the tests use the first."""
+    flags = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-fPIC", "-shared"]
+    for out, extra in ((_LIB, ["-Wno-unknown-pragmas"]), (_LIB_OMP, ["-fopenmp"])):
+        if force or not os.path.exists(out):
+            tmp = out + ".tmp"
+            subprocess.check_call(["gcc", *flags, *extra, _SRC, "-o", tmp, "-lm"])
+            os.replace(tmp, out)
     return _LIB
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+def _load(openmp: bool = False):
+    global _lib, _lib_omp
+    if (_lib_omp if openmp else _lib) is None:
+        path = _LIB_OMP if openmp else _LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
             build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
         lib.orc_bits_for.argtypes, lib.orc_bits_for.restype = [I64], I32
+        lib.orc_threads.argtypes, lib.orc_threads.restype = [], I32
         lib.orc_bounds.argtypes = [F, F, F, F, I32, I32, I32, P]
         lib.orc_bounds.restype = None
         lib.orc_isect_count.argtypes = [P, P, I32, I64, I64, I32, I32, I32, P, P]
@@ -79,8 +85,11 @@ def _load():
         lib.orc_rasterize_bins.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, I64, F, F, F, P, P,
                                            P, P]
         lib.orc_rasterize_bins.restype = I64
-        _lib = lib
-    return _lib
+        if openmp:
+            _lib_omp = lib
+        else:
+            _lib = lib
+    return _lib_omp if openmp else _lib
 
 
 def _p(a):
@@ -89,6 +98,11 @@ def _p(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads(openmp: bool = False) -> int:
+    """Threads the compositing loop uses in the plain (1) or the OpenMP build."""
+    return int(_load(openmp).orc_threads())
 
 
 def bits_for(count: int) -> int:
@@ -197,9 +211,10 @@ class Raster:
 
 def rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                   flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, tiles=None,
-                  masks=None) -> Raster:
-    """Front-to-back compositing over every tile (or only the listed global tiles; other pixels stay NaN)."""
-    lib = _load()
+                  masks=None, openmp=False) -> Raster:
+    """Front-to-back compositing over every tile (or only the listed global tiles; other pixels stay NaN).
+    openmp: use the OpenMP build (tiles over the host's threads; the same results)."""
+    lib = _load(openmp)
     means2d = _c(means2d, np.float32)
     C = means2d.shape[0]
     K = colors.shape[-1]

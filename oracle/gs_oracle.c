@@ -2,7 +2,8 @@
  * Plain, slow CPU oracle for the tile-binned splat rasterizer.
  *
  * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU-baseline leg use
- * this file. It shares no code, header, table or constant with the HIP library; the two meet only at the
+ * this file (built plain for the tests, and once more with OpenMP for the multi-core baseline, where only the
+ * composite's tile loop runs in parallel). It shares no code, header, table or constant with the HIP library; the two meet only at the
  * seeded synthetic inputs.
  *
  * Sources (the pages the method is defined on):
@@ -42,6 +43,15 @@
 
 /* Smallest b >= 0 with 2^b >= count: [gsplat] gs_tile_bits (ceil(log2(w*h)); 0 for one tile).
  * The same rule gives the camera field width from C. */
+/* Threads the compositing loop may use: the OpenMP maximum in the OpenMP build, 1 otherwise (not part of the
+ * method; reported beside the CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_threads(void) { return 1; }
+#endif
+
 int orc_bits_for(int64_t count)
 {
     int bits = 0;
@@ -345,12 +355,17 @@ int64_t orc_rasterize_fwd_traced(const float *means2d, const float *conics, cons
     int64_t total_tiles = C * per_camera;
     int64_t count = tiles ? n_tiles : total_tiles;
     int64_t n_eval = 0;
-    float acc[64];
     if (K < 1 || K > 64) return -1;
     if ((trace_ids || trace_counts) && max_splat_steps < 0) return -1;
+    for (int64_t j = 0; tiles && j < count; ++j)
+        if (tiles[j] < 0 || tiles[j] >= total_tiles) return -1;
+    /* Tiles are independent (each writes only its own pixels and trace rows). Built with OpenMP, the tiles are
+     * handed out one at a time to the host's threads - the pages' CPU parallelisation of compositing - with the
+     * same per-pixel arithmetic; without OpenMP the pragma is ignored and the loop runs in order. */
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : n_eval)
     for (int64_t j = 0; j < count; ++j) {
+        float acc[64];
         int64_t t = tiles ? tiles[j] : j;
-        if (t < 0 || t >= total_tiles) return -1;
         int64_t camera = t / per_camera;
         int64_t local = t % per_camera;
         int ty = (int)(local / tile_width), tx = (int)(local % tile_width);

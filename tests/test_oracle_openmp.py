@@ -1,0 +1,22 @@
+"""The oracle's OpenMP build (used only for the benchmark's multi-core CPU baseline) composites the same tiles with
+the same per-pixel arithmetic as the plain build the tests use: every output must be equal bit for bit."""
+import numpy as np
+
+import oracle
+from tile_binned_gaussian_amd import synth
+
+
+def test_openmp_build_matches_plain_build():
+    s = synth.random_scene(47, 2, 900, 90, 70, 16, elliptical=True, background=True)
+    it = oracle.isect_tiles(s.means2d, s.radii, s.depths, s.tile_size, s.tile_width, s.tile_height, sort=True)
+    off = oracle.tile_offsets(it.keys, s.C, s.tile_width, s.tile_height)
+    args = (s.means2d, s.conics, s.colors, s.opacities, s.backgrounds, s.width, s.height, s.tile_size, off,
+            it.flatten_ids, it.n_isects, s.alpha_cutoff, s.alpha_clamp, s.transmittance_threshold)
+    for tiles in (None, np.arange(1, off.size, 3, dtype=np.int64)):
+        a = oracle.rasterize_fwd(*args, tiles=tiles)
+        b = oracle.rasterize_fwd(*args, tiles=tiles, openmp=True)
+        for x, y in [(a.render_colors, b.render_colors), (a.render_alphas, b.render_alphas),
+                     (a.render_T, b.render_T), (a.last_ids, b.last_ids)]:
+            np.testing.assert_array_equal(x, y)
+        assert a.n_eval == b.n_eval
+    assert oracle.threads() == 1 and oracle.threads(openmp=True) >= 1
