@@ -59,7 +59,7 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="config3", choices=sorted(WORKLOADS))
     ap.add_argument("--frames-in-flight", type=int, default=3,
