@@ -167,7 +167,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the frame is "
-              f"not sharded across GPUs in this build.", file=sys.stderr)
+              f"rasterized on one GPU and is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
