@@ -71,7 +71,67 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 device-to-device copies of exactly 1 GiB (a known-size reference for the HBM "
                          "byte counters of a profiler run)")
+    ap.add_argument("--valu-calibration", action="store_true",
+                    help="also run the VALU calibration kernels (a known vector-instruction count per wave, for the "
+                         "instruction counter of a profiler run, and the measured issue rate and shader clock)")
     return ap.parse_args()
+
+
+CALIB_KINDS = ["v_fmac_f32", "v_mul_f32", "v_cndmask_b32", "v_mov_b32_dpp", "v_exp_f32", "v_cmp_gt_f32",
+               "mix(4 fmac,2 mul,1 cndmask,1 exp)"]
+
+
+def valu_calibration(stream):
+    """Each calibration kernel 3 times at 1024 rounds, then 3 times at 2048 rounds (16 vector instructions per
+    round and wave, every lane active, 8 waves per SIMD). The difference between the two round counts cancels the
+    kernels' fixed prologue and epilogue: 16 x 1024 x waves wave-instructions, which is what a profiler's VALU
+    instruction counter must read between the two dispatch groups. Returns per kind the lane-instruction rate, the
+    wave-instructions issued per SIMD per shader cycle, and the shader clock read from s_memtime against the
+    constant-rate s_memrealtime."""
+    import ctypes
+    import numpy as np
+    import torch
+    from tile_binned_gaussian_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.CALIB_LIB)
+    lib.gs_calib_valu_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.gs_calib_valu_launch.restype = ctypes.c_int
+    lib.gs_calib_wall_clock_khz.restype = ctypes.c_int
+    blocks = 256 * 8
+    waves = blocks * 4
+    simds = 256 * 4
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    clocks = torch.zeros(waves * 4, dtype=torch.int64, device="cuda:0")
+    s = ctypes.c_void_p(stream.cuda_stream)
+    wall_hz = lib.gs_calib_wall_clock_khz() * 1e3
+    res = {"blocks": blocks, "waves": waves, "rounds": [1024, 2048], "instructions_per_round": 16,
+           "counter_delta_expected": 16 * 1024 * waves, "wall_clock_hz": wall_hz, "kinds": {}}
+    for kind, name in enumerate(CALIB_KINDS):
+        ms = {}
+        for iters in (1024, 2048):
+            t = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                rc = lib.gs_calib_valu_launch(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                              ctypes.c_void_p(clocks.data_ptr()), s)
+                b.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"calibration launch failed: {rc}")
+                b.synchronize()
+                t.append(a.elapsed_time(b))
+            ms[iters] = statistics.median(t)
+        c = clocks.view(waves, 4).cpu().numpy().astype(np.float64)
+        shader_hz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1.0))) * wall_hz
+        dt = (ms[2048] - ms[1024]) * 1e-3
+        lane_instr = 16 * 1024 * waves * 64
+        rate = lane_instr / dt
+        res["kinds"][name] = {
+            "ms_1024": round(ms[1024], 4), "ms_2048": round(ms[2048], 4),
+            "T_lane_instructions_per_s": round(rate / 1e12, 3),
+            "wave_instructions_per_simd_cycle": round(16 * 1024 * waves / simds / (dt * shader_hz), 4),
+            "shader_clock_GHz": round(shader_hz / 1e9, 4)}
+    return res
 
 
 def stage_bytes(scene, n, tile_passes, generic_passes):
@@ -430,6 +490,8 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "copies": 3}
         del src, dst
+    if args.valu_calibration:
+        result["valu_calibration"] = valu_calibration(plan.stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"], sample = cpu_baseline(scene, args.cpu_tile_stride)
         result["cpu_baseline_openmp"] = cpu_baseline_openmp(scene, sample)

@@ -26,7 +26,8 @@
  * Conventions for every entry point.
  *   - Device pointers point to memory on the current HIP device; every array is dense and C-ordered.
  *     The caller allocates and owns every buffer, workspace included; the library never allocates or frees
- *     device memory and keeps no state between calls except a thread-local error message.
+ *     device memory. State kept between calls: a thread-local error message, the sort's process-wide spin limit
+ *     and one 4-byte device error word per GPU (gs_set_spin_limit, gs_device_check).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls are asynchronous on it unless
  *     stated otherwise; inputs must stay valid until the stream has run the work.
  *   - On any error nothing is launched (argument checks run on the host first), the return value says why,
@@ -114,6 +115,25 @@ size_t gs_sort_workspace_bytes(int64_t n, int end_bit);
 
 gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_bit, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Device-side failure of the sort ([gsplat] gs_isect_tiles turns a failure of its sort into an error status,
+ * NoMemError; here the sort's only device-side failure is a wait that does not end).
+ *
+ * Each digit pass of the sort (gs_sort_keys, and gs_isect_tiles with sort != 0) lets a partition wait for the
+ * counts of the partitions before it. The wait is bounded: after `limit` rounds (one round is one
+ * device-coherent load plus a short sleep; the default, 2^20, is about a second) the partition gives up, sets the
+ * library's device error word of the current GPU and finishes, so the pass always completes; that sort's output
+ * is then invalid (every access still stays inside the caller's buffers).
+ * gs_set_spin_limit: sets the limit used by passes launched after the call (process-wide) and returns the
+ *   previous one. 0 makes every partition that does not find its predecessors' counts at the first look give up
+ *   (for testing the failure path).
+ * gs_device_check: SYNCHRONISES `stream`, then reads and clears the device error word of the current GPU;
+ *   GS_ERR_DEVICE if a wait gave up since the last check (on any stream of that GPU), GS_OK otherwise.
+ */
+uint32_t gs_set_spin_limit(uint32_t limit);
+
+gs_status gs_device_check(void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
  * Tile ranges ([gsplat] gs_offset_encode for the output, [gsplat-bwd] gs_raster_backward_without_gvl for how

@@ -191,3 +191,52 @@ def test_bins_argument_errors(lib):
     assert comp(K=5) == GS_ERR_INVALID_ARG
     assert comp(tw=3) == GS_ERR_INVALID_ARG
     assert b"gs_rasterize_fwd_bins" in lib.gs_last_error()
+
+
+def test_binding_rejects_counts_past_the_ids():
+    """n_isects may not exceed flatten_ids' length (the kernels index ids up to n_isects); checked before any
+    device work, so CPU tensors reach the check."""
+    import torch
+    from tile_binned_gaussian_amd import binding
+    ids = torch.zeros(5, dtype=torch.int32)
+    assert binding._n_isects(ids, None) == 5
+    assert binding._n_isects(ids, 3) == 3
+    for bad in (6, -1):
+        with pytest.raises(ValueError, match="n_isects"):
+            binding._n_isects(ids, bad)
+
+
+def test_binding_rejects_misshapen_outputs():
+    """Caller-supplied outputs must match the image batch; a wrong shape or dtype is rejected before the device
+    check (the kernels would write every pixel of the declared batch)."""
+    import torch
+    from tile_binned_gaussian_amd import binding
+    C, H, W, K = 2, 5, 7, 3
+    good = binding.Render(torch.zeros((C, H, W, K)), torch.zeros((C, H, W)), torch.zeros((C, H, W)),
+                          torch.zeros((C, H, W), dtype=torch.int32))
+    bad_sets = [
+        binding.Render(torch.zeros((C, H, W, K + 1)), good.render_alphas, good.render_T, good.last_ids),
+        binding.Render(good.render_colors, torch.zeros((C, H + 1, W)), good.render_T, good.last_ids),
+        binding.Render(good.render_colors, good.render_alphas, torch.zeros((C, H, W - 1)), good.last_ids),
+        binding.Render(good.render_colors, good.render_alphas, good.render_T, torch.zeros((C, H, W))),
+    ]
+    for out in bad_sets:
+        with pytest.raises((ValueError, TypeError), match="shape|must be torch"):
+            binding._check_render_out(out, C, H, W, K, None)
+    # the right shapes pass every shape check and stop only at the device check
+    with pytest.raises(ValueError, match="GPU device"):
+        binding._check_render_out(good, C, H, W, K, None)
+    with pytest.raises(ValueError, match="shape"):
+        binding._check_eval_counts(torch.zeros(4, dtype=torch.int64), None)
+    with pytest.raises(TypeError):
+        binding._check_eval_counts(torch.zeros(5, dtype=torch.int32), None)
+
+
+def test_spin_limit_setter_round_trips(lib):
+    """gs_set_spin_limit is host state only (no device call): it returns the previous limit."""
+    prev = lib.gs_set_spin_limit(7)
+    try:
+        assert prev == 1 << 20
+        assert lib.gs_set_spin_limit(0) == 7
+    finally:
+        lib.gs_set_spin_limit(prev)

@@ -23,7 +23,7 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
            "gs_rasterize_fwd", "gs_rasterize_fwd_hwexp", "gs_rasterize_fwd_traced", "gs_rasterize_bwd",
-           "gs_project_fwd", "gs_bin_tiles", "gs_rasterize_fwd_bins")
+           "gs_project_fwd", "gs_bin_tiles", "gs_rasterize_fwd_bins", "gs_set_spin_limit", "gs_device_check")
 
 
 class GsError(RuntimeError):
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_bwd.restype = I32
     lib.gs_project_fwd.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P, P]
     lib.gs_project_fwd.restype = I32
+    lib.gs_set_spin_limit.argtypes, lib.gs_set_spin_limit.restype = [ctypes.c_uint32], ctypes.c_uint32
+    lib.gs_device_check.argtypes, lib.gs_device_check.restype = [P], I32
     _lib = lib
     return lib
 
@@ -111,19 +113,25 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _req(t, name, dtype, device=None, shape=None):
+def _req_layout(t, name, dtype, shape=None):
+    """Type, dtype, shape and contiguity of one argument (no device check)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _req(t, name, dtype, device=None, shape=None):
+    _req_layout(t, name, dtype, shape)
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     return t
 
 
@@ -197,6 +205,18 @@ def gs_sort_keys(keys, flatten_ids, end_bit=64, stream=None, workspace=None):
     return keys, flatten_ids
 
 
+def gs_set_spin_limit(limit: int) -> int:
+    """Look-back rounds a sort partition may wait before it gives up (passes launched afterwards); returns the
+    previous limit."""
+    return int(load_library().gs_set_spin_limit(int(limit)))
+
+
+def gs_device_check(stream=None):
+    """Synchronises the stream, then raises GsError (GS_ERR_DEVICE) if a sort's bounded wait gave up on this GPU
+    since the last check (the device error word is cleared either way)."""
+    _check(load_library().gs_device_check(_stream(stream)))
+
+
 @_stream_scoped
 def gs_tile_ranges(sorted_keys, C, tile_width, tile_height, validate=False, out=None, stream=None,
                    workspace=None):
@@ -248,6 +268,33 @@ def _render_out(C, height, width, K, dev):
                   torch.empty((C, height, width), dtype=torch.int32, device=dev))
 
 
+def _check_render_out(out, C, height, width, K, dev):
+    """A caller-supplied output set must match the image batch (the kernels write every pixel of it): every
+    field's layout is checked first, then its device."""
+    fields = [(out.render_colors, "render_colors", torch.float32, (C, height, width, K)),
+              (out.render_alphas, "render_alphas", torch.float32, (C, height, width)),
+              (out.render_T, "render_T", torch.float32, (C, height, width)),
+              (out.last_ids, "last_ids", torch.int32, (C, height, width))]
+    fields = [f for i, f in enumerate(fields) if i < 2 or f[0] is not None]
+    for t, name, dtype, shape in fields:
+        _req_layout(t, name, dtype, shape)
+    for t, name, dtype, shape in fields:
+        _req(t, name, dtype, dev, shape)
+
+
+def _n_isects(flatten_ids, n_isects):
+    """The intersection count the kernels may index: flatten_ids' length, or a given count that fits in it."""
+    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    if n < 0 or n > flatten_ids.numel():
+        raise ValueError(f"n_isects = {n} outside [0, flatten_ids.numel() = {flatten_ids.numel()}]")
+    return n
+
+
+def _check_eval_counts(eval_counts, dev):
+    if eval_counts is not None:
+        _req(eval_counts, "eval_counts", torch.int64, dev, (5,))
+
+
 @_stream_scoped
 def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                      flatten_ids, n_isects=None, alpha_cutoff=1.0 / 255.0, alpha_clamp=0.99,
@@ -260,9 +307,11 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, backgrounds, width, hei
     lib = load_library()
     dev, C, N, K, th, tw = _raster_inputs(means2d, conics, colors, opacities, backgrounds, isect_offsets,
                                           flatten_ids, masks)
-    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    n = _n_isects(flatten_ids, n_isects)
+    _check_eval_counts(eval_counts, dev)
     if out is None:
         out = _render_out(C, height, width, K, dev)
+    _check_render_out(out, C, height, width, K, dev)
     ws = workspace if workspace is not None else _workspace(lib.gs_rasterize_workspace_bytes(C, tw, th), dev)
     _check(lib.gs_rasterize_fwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,
                                 K, width, height, tile_size, tw, th, _ptr(isect_offsets), _ptr(flatten_ids), n,
@@ -281,9 +330,11 @@ def gs_rasterize_fwd_hwexp(means2d, conics, colors, opacities, backgrounds, widt
     lib = load_library()
     dev, C, N, K, th, tw = _raster_inputs(means2d, conics, colors, opacities, backgrounds, isect_offsets,
                                           flatten_ids, masks)
-    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    n = _n_isects(flatten_ids, n_isects)
+    _check_eval_counts(eval_counts, dev)
     if out is None:
         out = _render_out(C, height, width, K, dev)
+    _check_render_out(out, C, height, width, K, dev)
     _check(lib.gs_rasterize_fwd_hwexp(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds),
                                       C, N, K, width, height, tile_size, tw, th, _ptr(isect_offsets),
                                       _ptr(flatten_ids), n, _ptr(masks), float(alpha_cutoff), float(alpha_clamp),
@@ -313,12 +364,18 @@ def gs_rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, wid
     S = int(max_splat_steps)
     if S < 0:
         raise ValueError("max_splat_steps must be >= 0")
-    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    n = _n_isects(flatten_ids, n_isects)
+    _check_eval_counts(eval_counts, dev)
     if out is None:
         r = _render_out(C, height, width, K, dev)
         out = TracedRender(r.render_colors, r.render_alphas, r.render_T, r.last_ids,
                            torch.empty((C, height, width, S), dtype=torch.int32, device=dev) if trace else None,
                            torch.empty((C, height, width), dtype=torch.int32, device=dev) if trace else None)
+    _check_render_out(out, C, height, width, K, dev)
+    if out.trace_ids is not None:
+        _req(out.trace_ids, "trace_ids", torch.int32, dev, (C, height, width, S))
+    if out.trace_counts is not None:
+        _req(out.trace_counts, "trace_counts", torch.int32, dev, (C, height, width))
     ws = workspace if workspace is not None else _workspace(lib.gs_rasterize_workspace_bytes(C, tw, th), dev)
     _check(lib.gs_rasterize_fwd_traced(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds),
                                        C, N, K, width, height, tile_size, tw, th, _ptr(isect_offsets),
@@ -378,8 +435,10 @@ def gs_rasterize_fwd_bins(means2d, conics, colors, opacities, backgrounds, width
                                         bin_ids, None)
     if tuple(bin_ids.shape[:3]) != (C, th, tw):
         raise ValueError("bin_ids and bin_counts disagree on [C, th, tw]")
+    _check_eval_counts(eval_counts, dev)
     if out is None:
         out = _render_out(C, height, width, K, dev)
+    _check_render_out(out, C, height, width, K, dev)
     _check(lib.gs_rasterize_fwd_bins(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds),
                                      C, N, K, width, height, tile_size, tw, th, _ptr(bin_ids), _ptr(bin_counts),
                                      bin_ids.shape[3], float(alpha_cutoff), float(alpha_clamp),
@@ -425,12 +484,22 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, hei
     _req(last_ids, "last_ids", torch.int32, dev, (C, height, width))
     _req(grad_render_colors, "grad_render_colors", torch.float32, dev, (C, height, width, K))
     _req(grad_render_alphas, "grad_render_alphas", torch.float32, dev, (C, height, width))
-    n = flatten_ids.numel() if n_isects is None else int(n_isects)
+    n = _n_isects(flatten_ids, n_isects)
+    if isect_offsets.dim() != 3 or isect_offsets.shape[0] != C:
+        raise ValueError("isect_offsets must be [C, th, tw]")
     want_bg = backgrounds is not None if grad_backgrounds is None else bool(grad_backgrounds)
     if out is None:
         e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
         out = RasterGrad(e(C, N, 2), e(C, N, 3), e(C, N, K), e(C, N), e(C, K) if want_bg else None,
                          e(C, N, 2) if absgrad else None)
+    _req(out.means2d, "grad_means2d", torch.float32, dev, (C, N, 2))
+    _req(out.conics, "grad_conics", torch.float32, dev, (C, N, 3))
+    _req(out.colors, "grad_colors", torch.float32, dev, (C, N, K))
+    _req(out.opacities, "grad_opacities", torch.float32, dev, (C, N))
+    if out.backgrounds is not None:
+        _req(out.backgrounds, "grad_backgrounds", torch.float32, dev, (C, K))
+    if out.means2d_abs is not None:
+        _req(out.means2d_abs, "grad_means2d_abs", torch.float32, dev, (C, N, 2))
     if masks is not None:
         _req(masks, "masks", torch.int32, dev, (C, th, tw))
     _check(lib.gs_rasterize_bwd(_ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(backgrounds), C, N,

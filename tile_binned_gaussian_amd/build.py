@@ -10,6 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgs_raster.so")
 SOURCES = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+# calibration kernels for the benchmark's counter and issue-rate checks (a separate library, not the ABI)
+CALIB_LIB = os.path.join(HERE, "libgs_calib.so")
+CALIB_SOURCES = [os.path.join(HERE, "csrc", "calib", "valu_calib.hip")]
 HEADERS = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hpp"))) + [os.path.join(ROOT, "include", "gs_raster.h")]
 
 # -ffp-contract=off: the composite's float32 operation order is part of its definition (no fused multiply-adds
@@ -28,15 +31,15 @@ def hipcc() -> str:
 
 
 def stale() -> bool:
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(CALIB_LIB):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(f) > t for f in SOURCES + HEADERS)
+    t = min(os.path.getmtime(LIB), os.path.getmtime(CALIB_LIB))
+    return any(os.path.getmtime(f) > t for f in SOURCES + CALIB_SOURCES + HEADERS)
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,7 +49,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SOURCES, LIB, verbose)
+    _compile(CALIB_SOURCES, CALIB_LIB, verbose)
     return LIB
 
 

@@ -72,7 +72,8 @@ __device__ __forceinline__ void flush_trace(int32_t *row, int j, const int32_t *
 
 // The range [start, end) of global tile `tile` in `ids`: [offsets[tile], next offset or n_isects), or with
 // bins the first min(count, capacity) slots of the tile's bin; empty when the tile's mask is 0, cut to its first
-// max_list entries when max_list >= 0.
+// max_list entries when max_list >= 0. Caller-supplied offsets are clamped to 0 <= start <= end <= n_isects, so
+// offsets that disagree with n_isects never address outside the ids.
 __device__ __forceinline__ void tile_range(const RasterArgs &a, int tile, int &start, int &end) {
     if (a.bin_counts) {
         start = tile * a.capacity;
@@ -80,8 +81,10 @@ __device__ __forceinline__ void tile_range(const RasterArgs &a, int tile, int &s
         c = c < 0 ? 0 : (c < a.capacity ? c : a.capacity);
         end = start + c;
     } else {
-        start = a.offsets[tile];
-        end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects);
+        const int n = static_cast<int>(a.n_isects);
+        start = min(max(a.offsets[tile], 0), n);
+        end = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : n;
+        end = min(max(end, start), n);
     }
     if (a.masks && a.masks[tile] == 0) end = start;
     if (a.max_list >= 0 && end - start > a.max_list) end = start + a.max_list;

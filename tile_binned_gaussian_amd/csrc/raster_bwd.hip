@@ -153,10 +153,12 @@ __global__ __launch_bounds__(kThreads) void raster_bwd_kernel(BwdArgs a) {
     const int local = tile - camera * per_camera;
     const int ty = local / a.tile_width;
     const int tx = local - ty * a.tile_width;
-    const int start = a.offsets[tile];
-    // a tile whose mask is 0 composites nothing (its range is taken as empty)
-    const int end = (a.masks && a.masks[tile] == 0) ? start
-                    : (tile + 1 < a.total_tiles ? a.offsets[tile + 1] : static_cast<int>(a.n_isects));
+    // caller-supplied offsets clamped to 0 <= start <= end <= n_isects (never an access outside the ids); a tile
+    // whose mask is 0 composites nothing (its range is taken as empty)
+    const int n_all = static_cast<int>(a.n_isects);
+    const int start = min(max(a.offsets[tile], 0), n_all);
+    const int end_raw = tile + 1 < a.total_tiles ? a.offsets[tile + 1] : n_all;
+    const int end = (a.masks && a.masks[tile] == 0) ? start : min(max(end_raw, start), n_all);
     const int ts = a.tile_size;
     const int nwaves = static_cast<int>(blockDim.x) / kWave;
     const int wave = threadIdx.x / kWave;

@@ -15,6 +15,7 @@
 #include "gs_sort.hpp"
 
 #include <algorithm>
+#include <atomic>
 
 namespace gs {
 namespace {
@@ -49,6 +50,22 @@ static_assert(kHistCopyWords == kMaxPasses * kRadix, "one histogram copy holds e
 // histogram kernel: keys per thread and per workgroup step
 constexpr int kHistItems = 16;
 constexpr int kHistTile = kHistThreads * kHistItems;
+
+}  // namespace
+
+// Device-wide error word of the library (one per GPU): bit kDeviceErrLookBack is set by a digit pass whose
+// look-back wait for a predecessor partition ran past the spin limit. Read and cleared by gs_device_check.
+__device__ uint32_t g_device_error = 0;
+constexpr uint32_t kDeviceErrLookBack = 1u;
+
+namespace {
+
+// Spin limit handed to every digit pass launched after it is set (gs_set_spin_limit): look-back rounds a
+// partition may wait for its predecessors before it gives up. A round is one device-coherent load of the window
+// (about a microsecond under load) plus a short sleep, so the default bounds a wait by about a second, far past
+// any legitimate one (a predecessor took its partition index first and is already running).
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;
+std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
 
 __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -144,7 +161,8 @@ template <typename KeyT, int kDigitBits>
 __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const KeyT *__restrict__ keys_in, const int32_t *__restrict__ ids_in, KeyT *__restrict__ keys_out,
     int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ hist,
-    uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next) {
+    uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next,
+    uint32_t spin_limit) {
     constexpr int digit_bits = kDigitBits;
     constexpr int kItems = Tiling<KeyT>::items, kTile = Tiling<KeyT>::tile, kWaveSpan = Tiling<KeyT>::wave_span;
     constexpr int kLookWindow = Tiling<KeyT>::window;
@@ -271,9 +289,13 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     }
 
     // decoupled look-back for digit d: walk back over the predecessors' published counts, a window of kLookWindow
-    // at a time, until one carries an inclusive count (partition 0 always does)
+    // at a time, until one carries an inclusive count (partition 0 always does). The wait is bounded: after
+    // spin_limit rounds without finding one the partition gives up, flags the device error word and publishes
+    // what it has, so that every later partition also finishes (the pass's output is then invalid, and every
+    // write still stays inside the arrays).
     uint32_t before = 0;
     if (part > 0 && digit_thread) {
+        uint32_t rounds = 0;
         while (true) {
             int used = 0;
             bool found = false;
@@ -287,6 +309,10 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
                 if (flag == kFlagInclusive) found = true;
             }
             if (found) break;
+            if (rounds++ >= spin_limit) {
+                atomicOr(&g_device_error, kDeviceErrLookBack);
+                break;
+            }
             j -= used;
             if (used < kLookWindow) __builtin_amdgcn_s_sleep(1);
 #pragma unroll
@@ -404,6 +430,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
 
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
+    const uint32_t spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     for (int p = 0; p < plan.passes; ++p) {
         const bool to_a = (p % 2) == 0;
         KeyT *dk = to_a ? buf_a_keys : buf_b_keys;
@@ -420,7 +447,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
 #define GS_PASS(B)                                                                                                  \
     case B:                                                                                                         \
         hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B>), grid, block, 0, stream, src_k, src_i, dk, di, n,       \
-                           plan.shift[p], h, counters + p, st, st_next);                                            \
+                           plan.shift[p], h, counters + p, st, st_next, spin_limit);                                \
         break;
             GS_PASS(1) GS_PASS(2) GS_PASS(3) GS_PASS(4) GS_PASS(5) GS_PASS(6) GS_PASS(7) GS_PASS(8)
 #undef GS_PASS
@@ -509,4 +536,23 @@ extern "C" gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t 
     if (!workspace || workspace_bytes < need)
         return fail(GS_ERR_WORKSPACE, "gs_sort_keys: needs %zu workspace bytes (got %zu)", need, workspace_bytes);
     return sort_pairs_u64(keys, flatten_ids, n, end_bit, workspace, static_cast<hipStream_t>(stream));
+}
+
+extern "C" uint32_t gs_set_spin_limit(uint32_t limit) { return g_spin_limit.exchange(limit); }
+
+extern "C" gs_status gs_device_check(void *stream_handle) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+    uint32_t word = 0;
+    const uint32_t zero = 0;
+    GS_HIP_TRY(hipMemcpyFromSymbolAsync(&word, HIP_SYMBOL(g_device_error), sizeof word, 0, hipMemcpyDeviceToHost,
+                                        stream));
+    GS_HIP_TRY(hipStreamSynchronize(stream));
+    if (word == 0) return ok();
+    GS_HIP_TRY(hipMemcpyToSymbolAsync(HIP_SYMBOL(g_device_error), &zero, sizeof zero, 0, hipMemcpyHostToDevice,
+                                      stream));
+    GS_HIP_TRY(hipStreamSynchronize(stream));
+    if (word & kDeviceErrLookBack)
+        return fail(GS_ERR_DEVICE, "gs_device_check: a radix sort partition stopped waiting for its predecessors "
+                                   "(spin limit reached); that sort's output is invalid");
+    return fail(GS_ERR_DEVICE, "gs_device_check: device error word 0x%x", word);
 }
