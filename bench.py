@@ -32,8 +32,17 @@ if ROOT not in sys.path:
 
 METRIC = "isect keys sorted/s; rasterized Mpix/s (1M splats, 1920x1080, 1 GPU)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-# non-packed FP32 VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T lane-operations per second
-PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# VALU issue limit: each of the 256 x 4 SIMDs issues at most 2 wave64 VALU instructions per 4 cycles (dual issue:
+# FP32 add/mul/fma, v_mov and v_add_u32 pair with each other and with compares, selects and conversions, which never
+# pair among themselves; measured by the calibration kernels), 64 lanes each, at 2.4 GHz: 78.64 T lane-instructions
+# per second, the 157.3 TFLOP/s FP32 figure at 2 flops per fma. Reachable when at least half of a kernel's VALU
+# instructions can pair and none is transcendental (the composite: 62% FP32 add/mul/fma, 0.2% transcendental).
+PEAK_VALU_TOPS = 256 * 4 * 64 * 2 / 4 * 2.4e9 / 1e12
+# VALU wave-instructions per launch of the composite and its backward on the 1M-splat frame, from the profiler's
+# instruction counter (exact: calibrated against kernels of known count); valid only while the kernel sources are
+# the ones the counters were taken on
+VALU_FILE = os.path.join(ROOT, "profiles", "raster_valu_instructions_config3.txt")
+BWD_SOURCES = [os.path.join(ROOT, "tile_binned_gaussian_amd", "csrc", f) for f in ("raster_bwd.hip", "raster_common.hpp")]
 # lane-operations per evaluation of the composite's definition:
 #   every evaluation: 2 (delta) + 9 (quadratic form) + 1 (sign test) + 14 (exponential incl. the >80 test)
 #                     + 1 (opacity product) + 1 (clamp) + 1 (cutoff test) = 29
@@ -78,7 +87,9 @@ def parse():
 
 
 CALIB_KINDS = ["v_fmac_f32", "v_mul_f32", "v_cndmask_b32", "v_mov_b32_dpp", "v_exp_f32", "v_cmp_gt_f32",
-               "mix(4 fmac,2 mul,1 cndmask,1 exp)"]
+               "mix(4 fmac,2 mul,1 cndmask,1 exp)", "v_add_f32", "v_sub_f32", "v_fma_f32", "v_fmaak_f32",
+               "v_mov_b32", "v_add_u32", "v_rndne_f32", "v_ldexp_f32", "v_cvt_i32_f32", "v_max_f32",
+               "composite mix(5 mul,2 add,1 sub,2 fma,2 cndmask,2 cmp,1 rndne,1 ldexp)"]
 
 
 def valu_calibration(stream):
@@ -153,6 +164,34 @@ def stage_bytes(scene, n, tile_passes, generic_passes):
         "composite": n * (4 + 8 + 12 + 4 + 4 * K) + pixels * (4 * K + 4 + 4 + 4),
         "generic_sort": n * 8 + generic_passes * n * 24 + (n * 24 if generic_passes % 2 else 0),
     }
+
+
+def _record(path):
+    with open(path) as f:
+        return {k.strip(): v.strip() for k, v in (line.split(":", 1) for line in f.read().splitlines()
+                                                  if ":" in line and not line.startswith(" "))}
+
+
+def _sha(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_valu(config, which):
+    """Profiler-counted VALU wave-instructions per launch of the composite ("composite") or its backward
+    ("backward") on this workload, or None if there is no record or the kernel source changed since."""
+    try:
+        rec = _record(VALU_FILE)
+        sha = _sha(RASTER_SOURCES if which == "composite" else BWD_SOURCES)
+    except OSError:
+        return None
+    if rec.get("workload") != config or rec.get(f"{which}_kernel_source_sha256") != sha:
+        return None
+    return int(rec[f"{which}_valu_wave_instructions_per_launch"])
 
 
 def measured_traffic(config):
@@ -402,6 +441,12 @@ def main():
     # outside the frame: the stand-alone stable sort of the same intersections over all populated key bits
     stage_ms["generic_sort"], _ = plan.run_generic_sort(max(5, args.steps // 2))
     pixels = scene.C * scene.width * scene.height
+    bwd_valu = measured_valu(args.config, "backward")
+    bwd_issued = None if bwd_valu is None else bwd_valu * 64 / (backward_ms * 1e-3) / 1e12
+    bwd_roofline = {"bound": "alu", "achieved": None if bwd_issued is None else round(bwd_issued, 3),
+                    "peak": round(PEAK_VALU_TOPS, 2), "unit": "T VALU lane-instructions/s (as roofline)",
+                    "frac": None if bwd_issued is None else round(bwd_issued / PEAK_VALU_TOPS, 4),
+                    "valu_wave_instructions_per_launch": bwd_valu}
     tile_passes = (plan.end_bit - 32 + 7) // 8
     generic_passes = (plan.end_bit + 7) // 8
     nbytes = stage_bytes(scene, n, tile_passes, generic_passes)
@@ -414,16 +459,27 @@ def main():
         gbs = nbytes[nm] / (stage_ms[nm] * 1e-3) / 1e9
         stages[nm] = {"ms": round(stage_ms[nm], 4), "bytes": nbytes[nm], "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
-    comp_tops = ops / (stage_ms["composite"] * 1e-3) / 1e12
+    comp_s = stage_ms["composite"] * 1e-3
+    comp_tops = ops / comp_s / 1e12
     stages["composite"].update({"lane_ops_executed": ops, "lane_ops_definition": ops_def,
-                                "Tops/s": round(comp_tops, 3), "valu_frac": round(comp_tops / PEAK_VALU_TOPS, 4),
-                                "definition_Tops/s_equivalent": round(ops_def / (stage_ms["composite"] * 1e-3) / 1e12,
-                                                                      3)})
+                                "spec_Tops/s_executed": round(comp_tops, 3),
+                                "definition_Tops/s_equivalent": round(ops_def / comp_s / 1e12, 3)})
     # the roofline object is for the longest single kernel, the composite (one launch bracketed by one event
-    # pair); the other stages, several kernels each, are reported against HBM in "stages"
-    roofline = {"bound": "alu", "kernel": "raster_cull_kernel", "achieved": round(comp_tops, 3),
-                "peak": round(PEAK_VALU_TOPS, 2), "unit": "Tops/s (FP32 VALU lane-ops)",
-                "frac": round(comp_tops / PEAK_VALU_TOPS, 4), "traffic": measured_traffic(args.config),
+    # pair); the other stages, several kernels each, are reported against HBM in "stages". achieved = the VALU
+    # instructions the kernel issues (profiler count x 64 lanes) per second of its live duration
+    valu = measured_valu(args.config, "composite")
+    issued = None if valu is None else valu * 64 / comp_s / 1e12
+    roofline = {"bound": "alu", "kernel": "raster_cull_kernel",
+                "achieved": None if issued is None else round(issued, 3), "peak": round(PEAK_VALU_TOPS, 2),
+                "unit": "T VALU lane-instructions/s (profiler VALU count x 64 / live duration; peak = 2 wave64 "
+                        "instructions per SIMD per 4 cycles x 1024 SIMDs x 2.4 GHz, the measured dual-issue rate)",
+                "frac": None if issued is None else round(issued / PEAK_VALU_TOPS, 4),
+                "valu_wave_instructions_per_launch": valu,
+                "definition_equivalent_Tops": round(ops_def / comp_s / 1e12, 3),
+                "definition_equivalent_note": "the definition's lane-operations (every evaluation the tile walk "
+                                              "makes, 29 per evaluation + 3 per alpha >= cutoff + 7 per composited "
+                                              "splat) per second: what the kernel's exact cull saves",
+                "traffic": measured_traffic(args.config),
                 "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": nbytes["composite"]}
 
     result = {
@@ -451,9 +507,9 @@ def main():
         "isect_keys_sorted_per_s_generic_sort": round(n / (stage_ms["generic_sort"] * 1e-3), 1),
         "isect_keys_sorted_per_s_frame": round(n / (ms_per_step * 1e-3), 1),
         "rasterized_mpix_per_s_composite_only": round(pixels / (stage_ms["composite"] * 1e-3) / 1e6, 2),
-        "backward": {"ms": round(backward_ms, 4), "Mpix/s": round(pixels / (backward_ms * 1e-3) / 1e6, 2),
-                     "note": "gs_rasterize_bwd on the last frame with seeded standard-normal output gradients; "
-                             "clears the gradients, then sums them"},
+        "backward": dict({"ms": round(backward_ms, 4), "Mpix/s": round(pixels / (backward_ms * 1e-3) / 1e6, 2),
+                          "note": "gs_rasterize_bwd on the last frame with seeded standard-normal output gradients; "
+                                  "clears the gradients, then sums them"}, **bwd_roofline),
         "traced_forward": {"ms": round(traced_ms, 4), "max_splat_steps": S_TRACE, "trace_entries": traced_steps,
                            "pixels_at_cap": traced_capped,
                            "trace_bytes_written": 4 * traced_steps + 4 * pixels,
