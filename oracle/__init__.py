@@ -9,6 +9,7 @@ this module marshals numpy arrays into it. Definitions are cited in the C file.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -44,52 +45,70 @@ def _load(openmp: bool = False):
         path = _LIB_OMP if openmp else _LIB
         if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
             build()
-        lib = ctypes.CDLL(path)
-        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
-        lib.orc_bits_for.argtypes, lib.orc_bits_for.restype = [I64], I32
-        lib.orc_threads.argtypes, lib.orc_threads.restype = [], I32
-        lib.orc_bounds.argtypes = [F, F, F, F, I32, I32, I32, P]
-        lib.orc_bounds.restype = None
-        lib.orc_isect_count.argtypes = [P, P, I32, I64, I64, I32, I32, I32, P, P]
-        lib.orc_isect_count.restype = I64
-        lib.orc_isect_emit.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, P]
-        lib.orc_isect_emit.restype = I32
-        lib.orc_sort_pairs.argtypes, lib.orc_sort_pairs.restype = [P, P, I64], I32
-        lib.orc_tile_offsets.argtypes, lib.orc_tile_offsets.restype = [P, I64, I64, I32, I32, P], I32
-        lib.orc_exp_neg.argtypes, lib.orc_exp_neg.restype = [F], F
-        lib.orc_exp_neg_array.argtypes, lib.orc_exp_neg_array.restype = [P, P, I64], None
-        lib.orc_composite_pixel.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, P, P, P, P]
-        lib.orc_composite_pixel.restype = None
-        lib.orc_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
-                                          P, I64, P, P, P, P]
-        lib.orc_rasterize_fwd.restype = I64
-        lib.orc_rasterize_fwd_traced.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
-                                                 F, F, P, I64, I64, I64, P, P, P, P, P, P]
-        lib.orc_rasterize_fwd_traced.restype = I64
-        lib.orc_composite_pixel_traced.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, I64, P, P, P,
-                                                   P, P, P]
-        lib.orc_composite_pixel_traced.restype = None
-        lib.orc_tile_lists.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, I64, P, P]
-        lib.orc_tile_lists.restype = I64
-        lib.orc_rasterize_tile.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, P, I64, F, F, F, P, P,
-                                           P]
-        lib.orc_rasterize_tile.restype = I64
-        lib.orc_rects.argtypes, lib.orc_rects.restype = [P, P, I32, I64, I32, I32, I32, P], None
-        lib.orc_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
-                                          F, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
-        lib.orc_rasterize_bwd.restype = I32
-        lib.orc_project.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P]
-        lib.orc_project.restype = None
-        lib.orc_bin_tiles.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, I64, P, P]
-        lib.orc_bin_tiles.restype = I64
-        lib.orc_rasterize_bins.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, I64, F, F, F, P, P,
-                                           P, P]
-        lib.orc_rasterize_bins.restype = I64
+        lib = _declare(ctypes.CDLL(path))
         if openmp:
             _lib_omp = lib
         else:
             _lib = lib
     return _lib_omp if openmp else _lib
+
+
+@contextlib.contextmanager
+def variant(path):
+    """Runs the wrappers of this module against another build of the oracle's source (the tests' mutated copies,
+    each with one planted mistake) instead of liboracle.so, for the duration of the block."""
+    global _lib
+    saved = _load()
+    _lib = _declare(ctypes.CDLL(path))
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _declare(lib):
+    """Declares every exported signature on a loaded build of gs_oracle.c."""
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.orc_bits_for.argtypes, lib.orc_bits_for.restype = [I64], I32
+    lib.orc_threads.argtypes, lib.orc_threads.restype = [], I32
+    lib.orc_bounds.argtypes = [F, F, F, F, I32, I32, I32, P]
+    lib.orc_bounds.restype = None
+    lib.orc_isect_count.argtypes = [P, P, I32, I64, I64, I32, I32, I32, P, P]
+    lib.orc_isect_count.restype = I64
+    lib.orc_isect_emit.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, P]
+    lib.orc_isect_emit.restype = I32
+    lib.orc_sort_pairs.argtypes, lib.orc_sort_pairs.restype = [P, P, I64], I32
+    lib.orc_tile_offsets.argtypes, lib.orc_tile_offsets.restype = [P, I64, I64, I32, I32, P], I32
+    lib.orc_exp_neg.argtypes, lib.orc_exp_neg.restype = [F], F
+    lib.orc_exp_neg_array.argtypes, lib.orc_exp_neg_array.restype = [P, P, I64], None
+    lib.orc_composite_pixel.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, P, P, P, P]
+    lib.orc_composite_pixel.restype = None
+    lib.orc_rasterize_fwd.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F, F, F,
+                                      P, I64, P, P, P, P]
+    lib.orc_rasterize_fwd.restype = I64
+    lib.orc_rasterize_fwd_traced.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
+                                             F, F, P, I64, I64, I64, P, P, P, P, P, P]
+    lib.orc_rasterize_fwd_traced.restype = I64
+    lib.orc_composite_pixel_traced.argtypes = [P, P, P, P, I32, P, I64, I64, I32, I32, F, F, F, I64, P, P, P,
+                                               P, P, P]
+    lib.orc_composite_pixel_traced.restype = None
+    lib.orc_tile_lists.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, P, I64, P, P]
+    lib.orc_tile_lists.restype = I64
+    lib.orc_rasterize_tile.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, P, I64, F, F, F, P, P,
+                                       P]
+    lib.orc_rasterize_tile.restype = I64
+    lib.orc_rects.argtypes, lib.orc_rects.restype = [P, P, I32, I64, I32, I32, I32, P], None
+    lib.orc_rasterize_bwd.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, I64, P, F,
+                                      F, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_rasterize_bwd.restype = I32
+    lib.orc_project.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P]
+    lib.orc_project.restype = None
+    lib.orc_bin_tiles.argtypes = [P, P, I32, P, I64, I64, I32, I32, I32, I64, P, P]
+    lib.orc_bin_tiles.restype = I64
+    lib.orc_rasterize_bins.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, P, I64, F, F, F, P, P,
+                                       P, P]
+    lib.orc_rasterize_bins.restype = I64
+    return lib
 
 
 def _p(a):
@@ -126,9 +145,10 @@ class Isect:
     n_isects: int
 
 
-def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True) -> Isect:
-    """Intersections of every (camera, splat) with the tile grid, as the pages' isect_tiles returns them."""
-    lib = _load()
+def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True, openmp=False) -> Isect:
+    """Intersections of every (camera, splat) with the tile grid, as the pages' isect_tiles returns them.
+    openmp: the OpenMP build (emission and the sort's merges on the host's threads; the same result)."""
+    lib = _load(openmp)
     means2d = _c(means2d, np.float32)
     radii = _c(radii, np.float32)
     depths = _c(depths, np.float32)
@@ -140,8 +160,9 @@ def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort
                                 _p(tiles_per), _p(goff)))
     keys = np.zeros(n, np.uint64)
     ids = np.zeros(n, np.int32)
-    lib.orc_isect_emit(_p(means2d), _p(radii), rpg, _p(depths), C, N, tile_size, tile_width, tile_height,
-                       _p(keys), _p(ids))
+    if lib.orc_isect_emit(_p(means2d), _p(radii), rpg, _p(depths), C, N, tile_size, tile_width, tile_height,
+                          _p(keys), _p(ids)) != OK:
+        raise MemoryError("oracle emission allocation failed")
     if sort and n > 1:
         rc = lib.orc_sort_pairs(_p(keys), _p(ids), n)
         if rc != OK:
@@ -246,12 +267,12 @@ class TracedRaster(Raster):
 
 def rasterize_fwd_traced(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                          flatten_ids, n_isects, alpha_cutoff, alpha_clamp, transmittance_threshold, max_splat_steps,
-                         max_list_entries=-1, masks=None, trace=True, tiles=None) -> TracedRaster:
+                         max_list_entries=-1, masks=None, trace=True, tiles=None, openmp=False) -> TracedRaster:
     """The traced forward: every tile's list cut to its first ``max_list_entries`` entries (negative: whole
     lists), every pixel capped at ``max_splat_steps`` composited splats (negative: uncapped, only without a
     trace), and each pixel's composited flat splat ids recorded in order. tiles: only these global tiles (other
-    pixels keep the fill values)."""
-    lib = _load()
+    pixels keep the fill values). openmp: the OpenMP build (tiles on the host's threads; the same results)."""
+    lib = _load(openmp)
     means2d = _c(means2d, np.float32)
     C = means2d.shape[0]
     K = colors.shape[-1]
@@ -404,8 +425,10 @@ def rects(means2d, radii, tile_size, tile_width, tile_height):
 
 @dataclass
 class RasterGrad:
-    """Gradients of L = sum(grad_colors * render_colors) + sum(grad_alphas * render_alphas) (float64 sums of the
-    float32 terms) and, per entry, the sum of the terms' magnitudes (abs_*)."""
+    """Exact gradients (float64) of L = sum(grad_colors * render_colors) + sum(grad_alphas * render_alphas); per entry
+    the sum of the terms' magnitudes (abs_*) and the derived bound on how far a float32 evaluation of each term by
+    the pages' recurrence may lie from it (err_*, summed over the entry's terms). A float32 result summed in any order
+    with at most D additions on a path lies within err + D * 2^-24 * abs of the exact gradient (to first order)."""
     means2d: np.ndarray  # [C, N, 2]
     conics: np.ndarray  # [C, N, 3]
     colors: np.ndarray  # [C, N, K]
@@ -417,12 +440,24 @@ class RasterGrad:
     abs_colors: np.ndarray
     abs_opacities: np.ndarray
     abs_backgrounds: np.ndarray | None
+    err_means2d: np.ndarray
+    err_conics: np.ndarray
+    err_colors: np.ndarray
+    err_opacities: np.ndarray
+    err_backgrounds: np.ndarray | None
+
+    def bound(self, field, adds):
+        """|float result - exact| bound of one output: err + (adds + 2) * 2^-24 * abs, widened by 2% for the
+        first-order analysis (adds: the summation depth, an array broadcast against the field)."""
+        u = 2.0 ** -24
+        return 1.02 * (getattr(self, "err_" + field) + (np.asarray(adds, np.float64) + 2.0) * u *
+                       getattr(self, "abs_" + field)) + 1e-30
 
 
 def rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height, tile_size, isect_offsets,
                   flatten_ids, n_isects, alpha_cutoff, alpha_clamp, render_alphas, last_ids, grad_colors,
                   grad_alphas, masks=None) -> RasterGrad:
-    """Backward of the composite over every tile (orc_rasterize_bwd)."""
+    """Exact backward of the composite over every tile (orc_rasterize_bwd), with magnitudes and error bounds."""
     lib = _load()
     means2d = _c(means2d, np.float32)
     C, N = means2d.shape[0], means2d.shape[1]
@@ -433,16 +468,19 @@ def rasterize_bwd(means2d, conics, colors, opacities, backgrounds, width, height
     z = lambda *shape: np.zeros(shape, np.float64)  # noqa: E731
     g = [z(C, N, 2), z(C, N, 3), z(C, N, K), z(C, N), None if bg is None else z(C, K), z(C, N, 2)]
     a = [z(C, N, 2), z(C, N, 3), z(C, N, K), z(C, N), None if bg is None else z(C, K)]
+    e = [z(C, N, 2), z(C, N, 3), z(C, N, K), z(C, N), None if bg is None else z(C, K)]
     rc = lib.orc_rasterize_bwd(_p(means2d), _p(_c(conics, np.float32)), _p(_c(colors, np.float32)),
                                _p(_c(opacities, np.float32)), _p(bg), C, N, K, width, height, tile_size, tw, th,
                                _p(off), _p(_c(flatten_ids, np.int32)), int(n_isects),
                                _p(None if masks is None else _c(masks, np.int32)), float(alpha_cutoff),
                                float(alpha_clamp), _p(_c(render_alphas, np.float32)), _p(_c(last_ids, np.int32)),
                                _p(_c(grad_colors, np.float32)), _p(_c(grad_alphas, np.float32)),
-                               *[_p(x) for x in g], *[_p(x) for x in a])
+                               *[_p(x) for x in g], *[_p(x) for x in a], *[_p(x) for x in e])
+    if rc == -2:
+        raise MemoryError("oracle backward allocation failed")
     if rc != 0:
         raise ValueError("invalid rasterize backward arguments")
-    return RasterGrad(*g, *a)
+    return RasterGrad(*g, *a, *e)
 
 
 @dataclass

@@ -2,8 +2,9 @@
  * Plain, slow CPU oracle for the tile-binned splat rasterizer.
  *
  * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU-baseline leg use
- * this file (built plain for the tests, and once more with OpenMP for the multi-core baseline, where only the
- * composite's tile loop runs in parallel). It shares no code, header, table or constant with the HIP library; the two meet only at the
+ * this file (built plain, and once more with OpenMP for the multi-core baseline and the largest test frames, where
+ * the emission's splats, the merge sort's merges and the composite's tiles run in parallel with the same
+ * per-element arithmetic). It shares no code, header, table or constant with the HIP library; the two meet only at the
  * seeded synthetic inputs.
  *
  * Sources (the pages the method is defined on):
@@ -17,7 +18,9 @@
  *            transmittance_threshold as forward parameters, and a cutoff default of 1/255; names the traced
  *            forward's max_splat_steps (per-pixel trace of composited splats kept for the backward: counts and
  *            ids) and the tile-list cap max_list_entries (orc_rasterize_fwd_traced).
- *   The composite's backward (orc_rasterize_bwd) follows [gsplat-bwd] gs_raster_backward_pixel directly.
+ *   The composite's backward (orc_rasterize_bwd) is the exact gradient of the forward, the quantity whose
+ *            back-to-front recurrence [gsplat-bwd] gs_raster_backward_pixel evaluates, computed here from
+ *            front-to-back transmittances and suffix sums in double, with a derived bound for float32 evaluations.
  *   [gsplat-proj] the same gem's projection.c (gs_mat3_product, gs_camera_covar, gs_clip, gs_project_one): the
  *            EWA projection of 3D Gaussians into cameras (orc_project).
  *   [pytorch3d-fine] PyTorch3D rasterize_meshes.cu, RasterizeMeshesFineCudaKernel: reads per-bin lists of fixed
@@ -28,8 +31,10 @@
  * expression order with no contraction (build with -ffp-contract=off, never -ffast-math); fmaf appears only
  * where the exponential below names it. Integer work is exact.
  *
- * Parity pins: every function here is checked by the CPU test suite against closed forms, brute-force
- * enumerations, library routines and invariants; none is "parity unpinned".
+ * Parity pins: every exported function here is checked by the CPU test suite (tests/test_oracle_*.py) against
+ * closed forms, brute-force enumerations, library routines, invariants or another pinned oracle function, and each
+ * pin is shown to catch a planted mistake in a mutated copy of this file (tests/oracle_mutants.py); none is
+ * "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -116,34 +121,50 @@ int64_t orc_isect_count(const float *means2d, const float *radii, int radii_per_
     return total;
 }
 
-/* Step 2 of [gsplat] gs_isect_tiles: in (camera, splat, tile row, tile column) order write
- *   key = ((camera << tile_bits) | (ty * tile_width + tx)) << 32 | bit pattern of the depth,
- *   id  = camera * N + splat.
+/* The 64-bit intersection key of [gsplat] gs_isect_tiles: the camera index above the tile index in the upper 32 bits
+ * (the tile taking the low tile_bits of them), the depth's IEEE bit pattern in the lower 32. */
+static uint64_t orc_pack_key(uint64_t camera, int tile_bits, uint64_t tile, uint32_t depth_bits)
+{
+    uint64_t upper = (camera << tile_bits) | tile;
+    return (upper << 32) | (uint64_t)depth_bits;
+}
+
+/* Step 2 of [gsplat] gs_isect_tiles, stated per output slot: splat i (flat index camera * N + splat) owns the
+ * slots [start_i, start_i + count_i), start_i being the exclusive prefix of the counts in flat order; its k-th
+ * slot holds the k-th tile of its rectangle in row-major order, i.e. row y0 + k / w and column x0 + k % w with
+ * w = x1 - x0, as key orc_pack_key(camera, tile_bits, row * tile_width + column, depth bits) and id i.
  * Writes exactly n_isects entries; returns 0. */
 int orc_isect_emit(const float *means2d, const float *radii, int radii_per_gauss, const float *depths,
                    int64_t C, int64_t N, int tile_size, int tile_width, int tile_height, uint64_t *keys,
                    int32_t *flatten_ids)
 {
-    int tile_bits = orc_bits_for((int64_t)tile_width * tile_height);
-    int64_t write_index = 0;
-    for (int64_t camera = 0; camera < C; ++camera) {
-        for (int64_t splat = 0; splat < N; ++splat) {
-            int64_t index = camera * N + splat;
-            int32_t b[4];
-            orc_bounds_of(means2d, radii, radii_per_gauss, index, tile_size, tile_width, tile_height, b);
-            uint32_t depth_bits;
-            memcpy(&depth_bits, &depths[index], sizeof depth_bits);
-            uint64_t upper_camera = (uint64_t)camera << tile_bits;
-            for (int ty = b[1]; ty < b[3]; ++ty) {
-                for (int tx = b[0]; tx < b[2]; ++tx) {
-                    uint64_t tile = (uint64_t)ty * (uint64_t)tile_width + (uint64_t)tx;
-                    keys[write_index] = ((upper_camera | tile) << 32) | (uint64_t)depth_bits;
-                    flatten_ids[write_index] = (int32_t)index;
-                    write_index += 1;
-                }
-            }
+    const int tile_bits = orc_bits_for((int64_t)tile_width * tile_height);
+    const int64_t M = C * N;
+    int64_t *start = (int64_t *)malloc((size_t)(M > 0 ? M : 1) * sizeof(int64_t));
+    if (!start) return ORC_ERR_NOMEM;
+    int64_t running = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int32_t r[4];
+        orc_bounds_of(means2d, radii, radii_per_gauss, i, tile_size, tile_width, tile_height, r);
+        start[i] = running;
+        running += (int64_t)(r[2] - r[0]) * (int64_t)(r[3] - r[1]);
+    }
+    /* every splat writes only its own slots; the OpenMP build hands splats to the host's threads */
+#pragma omp parallel for schedule(dynamic, 4096)
+    for (int64_t i = 0; i < M; ++i) {
+        int32_t r[4];
+        orc_bounds_of(means2d, radii, radii_per_gauss, i, tile_size, tile_width, tile_height, r);
+        const int64_t w = r[2] - r[0], count = w * (int64_t)(r[3] - r[1]);
+        uint32_t depth_bits;
+        memcpy(&depth_bits, &depths[i], sizeof depth_bits);
+        for (int64_t k = 0; k < count; ++k) {
+            const int64_t row = r[1] + k / w, column = r[0] + k % w;
+            keys[start[i] + k] = orc_pack_key((uint64_t)(i / N), tile_bits,
+                                              (uint64_t)(row * tile_width + column), depth_bits);
+            flatten_ids[start[i] + k] = (int32_t)i;
         }
     }
+    free(start);
     return ORC_OK;
 }
 
@@ -163,6 +184,8 @@ int orc_sort_pairs(uint64_t *keys, int32_t *ids, int64_t n)
     uint64_t *sk = keys, *dk = tk;
     int32_t *si = ids, *di = ti;
     for (int64_t width = 1; width < n; width *= 2) {
+        /* the merges of one pass are independent (the OpenMP build runs them on the host's threads) */
+#pragma omp parallel for schedule(dynamic, 1)
         for (int64_t lo = 0; lo < n; lo += 2 * width) {
             int64_t mid = lo + width < n ? lo + width : n;
             int64_t hi = lo + 2 * width < n ? lo + 2 * width : n;
@@ -201,34 +224,39 @@ int orc_sort_pairs(uint64_t *keys, int32_t *ids, int64_t n)
     return ORC_OK;
 }
 
-/* [gsplat] gs_offset_encode: histogram of intersections per global tile camera * (w*h) + (upper & mask), with
- * upper = key >> 32 and camera = upper >> tile_bits, then an exclusive prefix into offsets[C, h, w].
- * A key whose camera or tile falls outside the grid is an error (the pages raise ArgError). */
+/* The global tile camera * (w * h) + tile of a key, whose upper 32 bits hold camera << tile_bits | tile; -1 when
+ * the camera or the tile lies outside the grid ([gsplat] gs_offset_encode rejects such a key). */
+static int64_t orc_key_tile(uint64_t key, int tile_bits, int64_t C, int64_t per_camera)
+{
+    const uint64_t upper = key >> 32;
+    const uint64_t camera = upper >> tile_bits;
+    const uint64_t tile = upper - (camera << tile_bits);
+    if (camera >= (uint64_t)C || tile >= (uint64_t)per_camera) return -1;
+    return (int64_t)camera * per_camera + (int64_t)tile;
+}
+
+/* [gsplat] gs_offset_encode's output: offsets[t] = the number of keys whose global tile is below t, for every global
+ * tile t of the [C, h, w] grid, so that tile t's keys are [offsets[t], offsets[t + 1]) (the last ending at n) in a
+ * sorted key array. Counted here as the number of keys per tile, each tile's offset the previous tile's plus the
+ * previous tile's count. A key outside the grid is an error (the pages raise ArgError). */
 int orc_tile_offsets(const uint64_t *keys, int64_t n, int64_t C, int tile_width, int tile_height,
                      int32_t *offsets)
 {
-    int tile_bits = orc_bits_for((int64_t)tile_width * tile_height);
-    uint64_t mask = tile_bits == 0 ? 0 : ((1ULL << tile_bits) - 1);
-    uint64_t per_camera = (uint64_t)tile_width * (uint64_t)tile_height;
-    int64_t tiles = C * (int64_t)per_camera;
-    int64_t *counts = (int64_t *)calloc((size_t)(tiles > 0 ? tiles : 1), sizeof(int64_t));
-    if (!counts) return ORC_ERR_NOMEM;
+    const int tile_bits = orc_bits_for((int64_t)tile_width * tile_height);
+    const int64_t per_camera = (int64_t)tile_width * tile_height;
+    const int64_t tiles = C * per_camera;
+    int64_t *per_tile = (int64_t *)calloc((size_t)(tiles > 0 ? tiles : 1), sizeof(int64_t));
+    if (!per_tile) return ORC_ERR_NOMEM;
     for (int64_t i = 0; i < n; ++i) {
-        uint64_t upper = keys[i] >> 32;
-        uint64_t camera = upper >> tile_bits;
-        uint64_t tile = upper & mask;
-        if (camera >= (uint64_t)C || tile >= per_camera) {
-            free(counts);
+        const int64_t t = orc_key_tile(keys[i], tile_bits, C, per_camera);
+        if (t < 0) {
+            free(per_tile);
             return ORC_ERR_OUT_OF_GRID;
         }
-        counts[camera * per_camera + tile] += 1;
+        per_tile[t] += 1;
     }
-    int64_t running = 0;
-    for (int64_t t = 0; t < tiles; ++t) {
-        offsets[t] = (int32_t)running;
-        running += counts[t];
-    }
-    free(counts);
+    for (int64_t t = 0; t < tiles; ++t) offsets[t] = t == 0 ? 0 : (int32_t)(offsets[t - 1] + per_tile[t - 1]);
+    free(per_tile);
     return ORC_OK;
 }
 
@@ -267,6 +295,27 @@ void orc_exp_neg_array(const float *sigma, float *out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = orc_exp_neg(sigma[i]);
 }
 
+/* The forward's per-splat quantities at the pixel centre (px, py), float32 in the expression order of [gsplat-bwd]
+ * gs_raster_backward_pixel: d = mean - centre; sigma = 0.5 (a dx dx + c dy dy) + b dx dy with the conic (a, b, c);
+ * E = orc_exp_neg(sigma); raw = opacity E; alpha = min(clamp, raw) (a NaN raw stays NaN). */
+typedef struct {
+    float dx, dy, sigma, E, raw, alpha;
+} orc_eval;
+
+static orc_eval orc_evaluate(const float *means2d, const float *conics, const float *opacities, int64_t g, float px,
+                             float py, float alpha_clamp)
+{
+    orc_eval e;
+    float a = conics[g * 3], b = conics[g * 3 + 1], c = conics[g * 3 + 2];
+    e.dx = means2d[g * 2] - px;
+    e.dy = means2d[g * 2 + 1] - py;
+    e.sigma = 0.5f * (a * e.dx * e.dx + c * e.dy * e.dy) + b * e.dx * e.dy;
+    e.E = orc_exp_neg(e.sigma);
+    e.raw = opacities[g] * e.E;
+    e.alpha = e.raw > alpha_clamp ? alpha_clamp : e.raw;
+    return e;
+}
+
 /* Front-to-back compositing of one pixel over list[start, end) (the forward read from [gsplat-bwd]):
  *   centre (x + 0.5, y + 0.5); d = mean - centre;
  *   sigma = 0.5 * (a dx dx + c dy dy) + b dx dy with the conic (a, b, c), each product and sum rounded to float;
@@ -293,14 +342,10 @@ void orc_composite_pixel_traced(const float *means2d, const float *conics, const
     for (int64_t i = start; i < end; ++i) {
         if (max_steps >= 0 && steps >= max_steps) break;
         int64_t g = list[i];
-        float dx = means2d[g * 2] - px;
-        float dy = means2d[g * 2 + 1] - py;
-        float a = conics[g * 3], b = conics[g * 3 + 1], c = conics[g * 3 + 2];
-        float sigma = 0.5f * (a * dx * dx + c * dy * dy) + b * dx * dy;
+        orc_eval e = orc_evaluate(means2d, conics, opacities, g, px, py, alpha_clamp);
         if (n_eval) *n_eval += 1;
-        if (sigma < 0.0f) continue;
-        float alpha = opacities[g] * orc_exp_neg(sigma);
-        if (alpha > alpha_clamp) alpha = alpha_clamp;
+        if (e.sigma < 0.0f) continue;
+        float alpha = e.alpha;
         if (alpha < alpha_cutoff) continue;
         float T_next = T * (1.0f - alpha);
         if (T_next <= transmittance_threshold) break;
@@ -446,28 +491,51 @@ int64_t orc_rasterize_tile(const float *means2d, const float *conics, const floa
     return n_eval;
 }
 
-/* Backward of the composite ([gsplat-bwd] gs_raster_backward_pixel and gs_raster_backward_without_gvl), for the
- * loss L = sum over pixels of <grad_colors_px, colour> + grad_alphas_px * alpha.
+/* Backward of the composite: the gradient of L = sum over pixels of <grad_colors_px, colour> + grad_alphas_px * alpha
+ * with respect to every splat's colour, opacity, mean and conic (and the background), for the forward above ([gsplat-bwd]
+ * gs_raster_backward_pixel and gs_raster_backward_without_gvl state the same gradient as a back-to-front recurrence).
  *
- * Per pixel, from the forward's outputs: T = 1 - render_alpha (the final transmittance), after = 1 (the
- * transmittance behind the splat being visited), rest[k] = background[k] (the colour seen behind it). The
- * background term is grad_colour[k] * T. Then the tile's range is walked back to front; position i with splat
- * g counts when render_alpha > 0, sigma >= 0, alpha >= cutoff, i <= last_id, T < 1 and alpha < 1, with sigma,
- * the response E(sigma) (orc_exp_neg, the same as the forward's), raw = opacity * E and alpha = min(clamp, raw)
- * recomputed as in the forward. For a counted splat, in float32 and this order:
- *   before = T / (1 - alpha);  vis = before * alpha;
- *   colour term k: grad_colour[k] * vis;  dot = sum_k grad_colour[k] * (colour[k] - rest[k]);
- *   g_alpha = before * (dot + grad_alpha * after);  g_raw = raw < clamp ? g_alpha : 0;
- *   opacity term: g_raw * E;  g_sigma = -g_raw * raw;
- *   mean terms: g_sigma * (a dx + b dy), g_sigma * (c dy + b dx);  conic terms: g_sigma * 0.5 * dx * dx,
- *   g_sigma * dx * dy, g_sigma * 0.5 * dy * dy;  then rest[k] = alpha * colour[k] + (1 - alpha) * rest[k],
- *   after *= 1 - alpha, T = before.
- * The pages add the terms into float arrays in an order their threads leave open; here each float term is added
- * into double accumulators (the sum of the terms up to double rounding), and abs_* (nullable) receive the sums of
- * the terms' magnitudes, which bound what any float summation order can change. g_means_abs (nullable) receives
- * |mean term| per axis. g_bg and abs_bg may be NULL (no background gradient). masks (nullable, [C, th, tw]): a tile
- * whose mask is 0 adds only its pixels' background terms.
- * Returns 0, or -1 for a bad argument. */
+ * Definition used here, per pixel. The composited splats j = 1..L are the positions i of the tile's range with
+ * i <= last_id, sigma >= 0, alpha >= cutoff and alpha < 1 (none when render_alpha is 0 or the tile's mask is 0), each with
+ * the forward's float32 alpha_j, raw_j = opacity E_j and E_j (orc_evaluate). In exact arithmetic on those values:
+ *   T_1 = 1, T_{j+1} = T_j (1 - alpha_j) (front-to-back transmittance), T_f = T_{L+1};
+ *   colour C_k = sum_j c_jk alpha_j T_j + T_f bg_k,  alpha = 1 - T_f;
+ *   S_jk = sum_{l > j} c_lk alpha_l T_l + T_f bg_k (the suffix sum behind splat j), so that
+ *   dC_k / d alpha_j = c_jk T_j - S_jk / (1 - alpha_j),  d alpha / d alpha_j = T_f / (1 - alpha_j);
+ *   dL/d alpha_j = sum_k g_k dC_k/d alpha_j + g_a T_f / (1 - alpha_j); dL/d raw_j = that, or 0 where the clamp holds
+ *   (raw_j >= clamp); dL/d opacity_j += dL/d raw_j E_j; d raw / d sigma = -raw, and with d = mean - centre (exact,
+ *   from the float inputs) d sigma / d mean = (a dx + b dy, c dy + b dx), d sigma / d(a, b, c) = (dx^2/2, dx dy, dy^2/2);
+ *   dL/d c_jk = g_k alpha_j T_j;  dL/d bg_k = g_k T_f.
+ * Evaluated in double: T by products from the front, S by sums from the back (so no division rebuilds a
+ * transmittance). g_means_abs (nullable) receives per splat and axis the sum over pixels of |dL/d mean|.
+ *
+ * Error bound for a float32 evaluation of the same gradient by the pages' recurrence (transmittance rebuilt back to
+ * front from 1 - render_alpha by divisions, the colour behind a splat and the transmittance behind it updated step by
+ * step, the pages' operation order for each term). With u = 2^-24 and, per pixel, phi = (8 L + K + 12) u + u / T_f:
+ * every term t of that pixel is within phi * M(t) of its exact value, where M(t) is t with every sum replaced by the
+ * sum of magnitudes (|g_k| (|c_jk| T_j + |S|_jk / (1 - alpha_j)) + |g_a| T_f / (1 - alpha_j) in place of dL/d alpha_j,
+ * |a dx| + |b dy| in place of a dx + b dy, and so on). The u / T_f part is the rounding of render_alpha = 1 - T_f,
+ * which every rebuilt transmittance of the pixel inherits; 2L + 1 rounding steps come from the forward's and the
+ * backward's transmittance chains each, 4L from the colour-behind recurrence, K + 12 from the term's own operations.
+ * abs_* receive the sums of |t| over the terms of each entry and err_* the sums of phi * M(t) (all nullable); a float
+ * sum of the terms in any order with at most D additions on a path then lies within err + D u abs (to first order).
+ * g_bg, abs_bg and err_bg may be NULL (no background gradient). masks (nullable, [C, th, tw]): a tile whose mask is 0
+ * contributes only its pixels' background terms.
+ * Returns 0, -1 for a bad argument, -2 if an allocation failed. */
+typedef struct {
+    int64_t g;
+    double alpha, raw, E, T, dx, dy;
+    int unclamped;
+} orc_bwd_step;
+
+static void orc_acc(double *g, double *abs_sum, double *err, int64_t at, double term, double magnitude,
+                    double phi)
+{
+    g[at] += term;
+    if (abs_sum) abs_sum[at] += fabs(term);
+    if (err) err[at] += phi * magnitude;
+}
+
 int orc_rasterize_bwd(const float *means2d, const float *conics, const float *colors, const float *opacities,
                       const float *backgrounds, int64_t C, int64_t N, int K, int width, int height, int tile_size,
                       int tile_width, int tile_height, const int32_t *offsets, const int32_t *flatten_ids,
@@ -476,89 +544,106 @@ int orc_rasterize_bwd(const float *means2d, const float *conics, const float *co
                       const float *grad_alphas_px,
                       double *g_means, double *g_conics, double *g_colors, double *g_opacities, double *g_bg,
                       double *g_means_abs, double *abs_means, double *abs_conics, double *abs_colors,
-                      double *abs_opacities, double *abs_bg)
+                      double *abs_opacities, double *abs_bg, double *err_means, double *err_conics,
+                      double *err_colors, double *err_opacities, double *err_bg)
 {
+    const double u = ldexp(1.0, -24);
     int64_t per_camera = (int64_t)tile_width * tile_height;
     int64_t total_tiles = C * per_camera;
-    float rest[64];
     if (K < 1 || K > 64 || N < 0 || C < 1) return -1;
-    (void)N;
+    int64_t longest = 1;
+    for (int64_t t = 0; t < total_tiles; ++t) {
+        int64_t e = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
+        if (e - offsets[t] > longest) longest = e - offsets[t];
+    }
+    orc_bwd_step *steps = (orc_bwd_step *)malloc((size_t)longest * sizeof(orc_bwd_step));
+    if (!steps) return -2;
+    double S[64], S_abs[64];
     for (int64_t t = 0; t < total_tiles; ++t) {
         int64_t camera = t / per_camera;
         int64_t local = t % per_camera;
         int ty = (int)(local / tile_width), tx = (int)(local % tile_width);
         int64_t start = offsets[t];
         int64_t end = t + 1 < total_tiles ? offsets[t + 1] : n_isects;
-        if (masks && masks[t] == 0) end = start; /* masked: only the background term ([gsplat-bwd]) */
+        if (masks && masks[t] == 0) end = start;
         for (int y = ty * tile_size; y < (ty + 1) * tile_size && y < height; ++y) {
             for (int x = tx * tile_size; x < (tx + 1) * tile_size && x < width; ++x) {
                 int64_t pixel = (camera * height + y) * (int64_t)width + x;
-                const float *gc = grad_colors_px + pixel * K;
-                float ga = grad_alphas_px[pixel];
-                float T = 1.0f - render_alphas[pixel];
-                float after = 1.0f;
-                for (int k = 0; k < K; ++k) {
-                    rest[k] = backgrounds ? backgrounds[camera * K + k] : 0.0f;
-                    if (g_bg) {
-                        float term = gc[k] * T;
-                        g_bg[camera * K + k] += (double)term;
-                        if (abs_bg) abs_bg[camera * K + k] += fabs((double)term);
-                    }
-                }
+                const float *gk = grad_colors_px + pixel * K;
+                double ga = grad_alphas_px[pixel];
                 float px = (float)x + 0.5f, py = (float)y + 0.5f;
-                for (int64_t i = end - 1; i >= start; --i) {
+                /* the composited splats, front to back, with the transmittance in front of each */
+                int64_t stop = (int64_t)last_ids[pixel] + 1;
+                if (!(render_alphas[pixel] > 0.0f)) stop = start;
+                if (stop > end) stop = end;
+                int64_t L = 0;
+                double T = 1.0;
+                for (int64_t i = start; i < stop; ++i) {
                     int64_t g = flatten_ids[i];
-                    float dx = means2d[g * 2] - px;
-                    float dy = means2d[g * 2 + 1] - py;
-                    float a = conics[g * 3], b = conics[g * 3 + 1], c = conics[g * 3 + 2];
-                    float sigma = 0.5f * (a * dx * dx + c * dy * dy) + b * dx * dy;
-                    float response = orc_exp_neg(sigma);
-                    float raw = opacities[g] * response;
-                    float alpha = raw;
-                    if (alpha > alpha_clamp) alpha = alpha_clamp;
-                    if (!(render_alphas[pixel] > 0.0f && sigma >= 0.0f && alpha >= alpha_cutoff &&
-                          (int64_t)last_ids[pixel] >= i && T < 1.0f && alpha < 1.0f))
-                        continue;
-                    float before = T / (1.0f - alpha);
-                    float vis = before * alpha;
+                    orc_eval e = orc_evaluate(means2d, conics, opacities, g, px, py, alpha_clamp);
+                    if (!(e.sigma >= 0.0f) || !(e.alpha >= alpha_cutoff) || !(e.alpha < 1.0f)) continue;
+                    orc_bwd_step *st = &steps[L++];
+                    st->g = g;
+                    st->alpha = e.alpha;
+                    st->raw = e.raw;
+                    st->E = e.E;
+                    st->T = T;
+                    st->dx = (double)means2d[g * 2] - (double)px;
+                    st->dy = (double)means2d[g * 2 + 1] - (double)py;
+                    st->unclamped = e.raw < alpha_clamp;
+                    T *= 1.0 - (double)e.alpha;
+                }
+                const double T_f = T;
+                const double phi = (8.0 * (double)L + (double)K + 12.0) * u + u / T_f;
+                for (int k = 0; k < K; ++k) {
+                    double bg = backgrounds ? backgrounds[camera * K + k] : 0.0;
+                    S[k] = T_f * bg;
+                    S_abs[k] = T_f * fabs(bg);
+                    if (g_bg) orc_acc(g_bg, abs_bg, err_bg, camera * K + k, gk[k] * T_f, fabs(gk[k]) * T_f, phi);
+                }
+                /* back to front: each splat's gradient from the suffix sums behind it */
+                for (int64_t j = L - 1; j >= 0; --j) {
+                    const orc_bwd_step *st = &steps[j];
+                    const int64_t g = st->g;
                     const float *col = colors + g * K;
-                    float dot = 0.0f;
+                    const double one_minus = 1.0 - st->alpha, w = st->alpha * st->T;
+                    double d_alpha = ga * T_f / one_minus;
+                    double m_alpha = fabs(ga) * T_f / one_minus;
                     for (int k = 0; k < K; ++k) {
-                        float term = gc[k] * vis;
-                        g_colors[g * K + k] += (double)term;
-                        if (abs_colors) abs_colors[g * K + k] += fabs((double)term);
-                        dot += gc[k] * (col[k] - rest[k]);
+                        d_alpha += gk[k] * (col[k] * st->T - S[k] / one_minus);
+                        m_alpha += fabs(gk[k]) * (fabs(col[k]) * st->T + S_abs[k] / one_minus);
+                        orc_acc(g_colors, abs_colors, err_colors, g * K + k, gk[k] * w, fabs(gk[k]) * w, phi);
                     }
-                    float g_alpha = before * (dot + ga * after);
-                    float g_raw = raw < alpha_clamp ? g_alpha : 0.0f;
-                    float t_opacity = g_raw * response;
-                    g_opacities[g] += (double)t_opacity;
-                    if (abs_opacities) abs_opacities[g] += fabs((double)t_opacity);
-                    float g_sigma = -g_raw * raw;
-                    float mx = g_sigma * (a * dx + b * dy);
-                    float my = g_sigma * (c * dy + b * dx);
-                    float t_conic[3] = {g_sigma * 0.5f * dx * dx, g_sigma * dx * dy, g_sigma * 0.5f * dy * dy};
-                    g_means[g * 2] += (double)mx;
-                    g_means[g * 2 + 1] += (double)my;
-                    if (abs_means) {
-                        abs_means[g * 2] += fabs((double)mx);
-                        abs_means[g * 2 + 1] += fabs((double)my);
-                    }
+                    const double d_raw = st->unclamped ? d_alpha : 0.0;
+                    const double m_raw = st->unclamped ? m_alpha : 0.0;
+                    orc_acc(g_opacities, abs_opacities, err_opacities, g, d_raw * st->E, m_raw * st->E, phi);
+                    const double d_sigma = -d_raw * st->raw, m_sigma = m_raw * st->raw;
+                    const double a = conics[g * 3], b = conics[g * 3 + 1], c = conics[g * 3 + 2];
+                    const double dx = st->dx, dy = st->dy;
+                    const double mean_x = d_sigma * (a * dx + b * dy), mean_y = d_sigma * (c * dy + b * dx);
+                    orc_acc(g_means, abs_means, err_means, g * 2, mean_x, m_sigma * (fabs(a * dx) + fabs(b * dy)), phi);
+                    orc_acc(g_means, abs_means, err_means, g * 2 + 1, mean_y,
+                            m_sigma * (fabs(c * dy) + fabs(b * dx)), phi);
                     if (g_means_abs) {
-                        g_means_abs[g * 2] += fabs((double)mx);
-                        g_means_abs[g * 2 + 1] += fabs((double)my);
+                        g_means_abs[g * 2] += fabs(mean_x);
+                        g_means_abs[g * 2 + 1] += fabs(mean_y);
                     }
-                    for (int q = 0; q < 3; ++q) {
-                        g_conics[g * 3 + q] += (double)t_conic[q];
-                        if (abs_conics) abs_conics[g * 3 + q] += fabs((double)t_conic[q]);
+                    orc_acc(g_conics, abs_conics, err_conics, g * 3, d_sigma * 0.5 * dx * dx, m_sigma * 0.5 * dx * dx,
+                            phi);
+                    orc_acc(g_conics, abs_conics, err_conics, g * 3 + 1, d_sigma * dx * dy, m_sigma * fabs(dx * dy),
+                            phi);
+                    orc_acc(g_conics, abs_conics, err_conics, g * 3 + 2, d_sigma * 0.5 * dy * dy,
+                            m_sigma * 0.5 * dy * dy, phi);
+                    /* splat j now lies behind the splats in front of it */
+                    for (int k = 0; k < K; ++k) {
+                        S[k] += col[k] * w;
+                        S_abs[k] += fabs(col[k]) * w;
                     }
-                    for (int k = 0; k < K; ++k) rest[k] = alpha * col[k] + (1.0f - alpha) * rest[k];
-                    after *= 1.0f - alpha;
-                    T = before;
                 }
             }
         }
     }
+    free(steps);
     return 0;
 }
 

@@ -39,6 +39,26 @@ def assert_isect_equal(scene, it_gpu, it_orc, sorted_):
     np.testing.assert_array_equal(host(it_gpu.flatten_ids), it_orc.flatten_ids)
 
 
+def oracle_lists(scene, openmp=False):
+    """The oracle's sorted intersections and tile offsets of a scene: the only lists any oracle call in the GPU tests
+    is given (never the GPU's). openmp: the oracle's OpenMP build (the same result)."""
+    it = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                            scene.tile_height, sort=True, openmp=openmp)
+    off = oracle.tile_offsets(it.keys, scene.C, scene.tile_width, scene.tile_height)
+    return it, off
+
+
+def oracle_frame(scene, masks=None, openmp=False):
+    """The oracle's whole frame: sorted intersections, tile offsets and the composite over them (openmp: the
+    OpenMP build, the same bits)."""
+    it, off = oracle_lists(scene, openmp=openmp)
+    ras = oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
+                               scene.width, scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects,
+                               scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold, masks=masks,
+                               openmp=openmp)
+    return it, off, ras
+
+
 def gpu_frame(scene):
     ds = frame.to_device(scene)
     fr = frame.render_frame(ds)
@@ -66,43 +86,3 @@ def assert_raster_equal(scene, fr_gpu, ras_orc, orc_ids):
     np.testing.assert_array_equal(last_splat(g_last, g_ids), last_splat(o_last, orc_ids))
     # within tolerance too (the bar stated for colour and transmittance)
     np.testing.assert_allclose(host(fr_gpu.render.render_colors), ras_orc.render_colors, atol=1e-4, rtol=0)
-
-
-def sampled_tiles(offsets, n_isects, count, seed):
-    """The heaviest tiles plus a seeded random sample (global tile indices)."""
-    flat = offsets.reshape(-1).astype(np.int64)
-    lengths = np.diff(np.append(flat, n_isects))
-    heavy = np.argsort(-lengths, kind="stable")[: count // 4]
-    rng = np.random.default_rng(seed)
-    rand = rng.choice(flat.size, size=min(flat.size, count - heavy.size), replace=False)
-    return np.unique(np.concatenate([heavy, rand]))
-
-
-def check_tiles_against_oracle(scene, fr_gpu, tiles):
-    """Composite the sampled tiles in the oracle from its own per-tile lists and compare to the GPU frame."""
-    off_g = host(fr_gpu.isect_offsets).reshape(-1).astype(np.int64)
-    ids_g = host(fr_gpu.isect.flatten_ids)
-    n = fr_gpu.isect.n_isects
-    lists = oracle.tile_lists(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
-                              scene.tile_height, tiles)
-    col_g = host(fr_gpu.render.render_colors)
-    T_g = host(fr_gpu.render.render_T)
-    last_g = host(fr_gpu.render.last_ids)
-    ts, tw, th = scene.tile_size, scene.tile_width, scene.tile_height
-    for t, lst in zip(tiles, lists):
-        s = off_g[t]
-        e = off_g[t + 1] if t + 1 < off_g.size else n
-        np.testing.assert_array_equal(ids_g[s:e], lst, err_msg=f"tile {t} list")
-        oc, oT, ol, _ = oracle.rasterize_tile(scene.means2d, scene.conics, scene.colors, scene.opacities,
-                                              scene.backgrounds, scene.width, scene.height, ts, tw, th, t, lst,
-                                              scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold)
-        cam, local = divmod(int(t), tw * th)
-        ty, tx = divmod(local, tw)
-        y0, x0 = ty * ts, tx * ts
-        y1, x1 = min(y0 + ts, scene.height), min(x0 + ts, scene.width)
-        np.testing.assert_array_equal(col_g[cam, y0:y1, x0:x1], oc[: y1 - y0, : x1 - x0], err_msg=f"tile {t}")
-        np.testing.assert_array_equal(T_g[cam, y0:y1, x0:x1], oT[: y1 - y0, : x1 - x0], err_msg=f"tile {t}")
-        gl = last_g[cam, y0:y1, x0:x1].astype(np.int64)
-        olp = ol[: y1 - y0, : x1 - x0]
-        np.testing.assert_array_equal(last_splat(gl, ids_g), last_splat(olp, lst), err_msg=f"tile {t} last ids")
-        assert ((gl == -1) | ((gl >= s) & (gl < e))).all()

@@ -26,7 +26,8 @@ int64_t orc_rasterize_tile(const float *, const float *, const float *, const fl
 int orc_rasterize_bwd(const float *, const float *, const float *, const float *, const float *, int64_t, int64_t,
                       int, int, int, int, int, int, const int32_t *, const int32_t *, int64_t, const int32_t *, float,
                       float, const float *, const int32_t *, const float *, const float *, double *, double *,
-                      double *, double *, double *, double *, double *, double *, double *, double *, double *);
+                      double *, double *, double *, double *, double *, double *, double *, double *, double *,
+                      double *, double *, double *, double *, double *);
 void orc_project(const float *, const float *, const float *, const float *, int64_t, int64_t, int, int, float,
                  float, float, float, int, int32_t *, float *, float *, float *, float *);
 int64_t orc_tile_lists(const float *, const float *, int, const float *, int64_t, int64_t, int, int, int,
@@ -86,12 +87,13 @@ static int run_scene(int64_t C, int64_t N, int W, int H, int ts, int K, int rpg)
     float *gc = NEW(float, P * K), *ga = NEW(float, P);
     for (int64_t i = 0; i < P * K; ++i) gc[i] = uniform(-1.0f, 1.0f);
     for (int64_t i = 0; i < P; ++i) ga[i] = uniform(-1.0f, 1.0f);
-    double *g = NEW(double, M * (2 + 3 + K + 1 + 2) * 2 + C * K * 2);
+    double *g = NEW(double, M * ((2 + 3 + K + 1) * 3 + 2) + C * K * 3);
     double *gm = g, *gq = gm + 2 * M, *gcol = gq + 3 * M, *go = gcol + K * M, *gabs = go + M, *am = gabs + 2 * M;
-    double *aq = am + 2 * M, *acol = aq + 3 * M, *ao = acol + K * M, *gbg = ao + M, *abg = gbg + C * K;
+    double *aq = am + 2 * M, *acol = aq + 3 * M, *ao = acol + K * M, *em = ao + M, *eq = em + 2 * M;
+    double *ecol = eq + 3 * M, *eo = ecol + K * M, *gbg = eo + M, *abg = gbg + C * K, *ebg = abg + C * K;
     if (orc_rasterize_bwd(means, conics, colors, ops, bg, C, N, K, W, H, ts, tw, th, off, ids, n, masks,
                           1.0f / 255.0f, 0.99f, alp, last, gc, ga, gm, gq, gcol, go, gbg, gabs, am, aq, acol, ao,
-                          abg) != 0)
+                          abg, em, eq, ecol, eo, ebg) != 0)
         return 1;
     /* one tile over an explicit list, the brute-force lists and the bins */
     float *tc = NEW(float, ts * ts * K), *tT = NEW(float, ts * ts);

@@ -10,7 +10,7 @@ import torch
 import oracle
 from tile_binned_gaussian_amd import binding, synth
 
-from gpu_util import dev, gpu_frame, host, require_gpu
+from gpu_util import dev, gpu_frame, host, oracle_frame, require_gpu
 from test_gpu_parity import SCENES
 
 pytestmark = pytest.mark.gpu
@@ -113,13 +113,14 @@ def test_sentinels_anywhere_in_a_bin_are_skipped():
 
 
 def test_bins_1m_splats_1080p_match_the_sorted_path():
+    """At 1M splats the bins equal the oracle's sorted tile lists and their composite the oracle's frame."""
     scene = synth.config3()
-    fr = gpu_frame(scene)
+    it_o, off_o, ras_o = oracle_frame(scene, openmp=True)
     cap = 8192
     g = _gpu_bins(scene, cap)
-    off = host(fr.isect_offsets).reshape(-1).astype(np.int64)
-    ids = host(fr.isect.flatten_ids)
-    ends = np.append(off[1:], fr.isect.n_isects)
+    off = off_o.reshape(-1).astype(np.int64)
+    ids = it_o.flatten_ids
+    ends = np.append(off[1:], it_o.n_isects)
     counts = host(g.bin_counts).reshape(-1)
     np.testing.assert_array_equal(counts, ends - off)
     assert counts.max() <= cap
@@ -128,12 +129,12 @@ def test_bins_1m_splats_1080p_match_the_sorted_path():
         np.testing.assert_array_equal(gb[t, :counts[t]], ids[off[t]:ends[t]], err_msg=f"tile {t}")
     assert (gb[np.arange(cap)[None, :] >= counts[:, None]] == -1).all()
     r = _gpu_composite(scene, g)
-    np.testing.assert_array_equal(host(r.render_colors), host(fr.render.render_colors))
-    np.testing.assert_array_equal(host(r.render_T), host(fr.render.render_T))
+    np.testing.assert_array_equal(host(r.render_colors), ras_o.render_colors)
+    np.testing.assert_array_equal(host(r.render_T), ras_o.render_T)
     lb = host(r.last_ids).astype(np.int64)
     t = np.maximum(lb, 0) // cap
     mapped = np.where(lb >= 0, off[t] + lb % cap, -1)
-    np.testing.assert_array_equal(mapped, host(fr.render.last_ids))
+    np.testing.assert_array_equal(mapped, ras_o.last_ids)
 
 
 def test_bins_with_more_tiles_than_the_lds_counters():

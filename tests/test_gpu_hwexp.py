@@ -11,7 +11,7 @@ import torch
 import oracle
 from tile_binned_gaussian_amd import binding, synth
 
-from gpu_util import dev, gpu_frame, host, require_gpu
+from gpu_util import dev, gpu_frame, host, oracle_lists, require_gpu
 from test_gpu_parity import SCENES
 
 pytestmark = pytest.mark.gpu
@@ -57,12 +57,14 @@ def _near_boundary(scene, lst, c, x, y):
 def test_hwexp_matches_the_specified_composite_except_boundary_flips(name):
     scene = SCENES[name]()
     fr = gpu_frame(scene)
-    off = host(fr.isect_offsets).reshape(-1).astype(np.int64)
-    ids = host(fr.isect.flatten_ids)
-    n = fr.isect.n_isects
+    it_o, off_o = oracle_lists(scene)
+    np.testing.assert_array_equal(host(fr.isect.flatten_ids), it_o.flatten_ids)  # the GPU's lists are the oracle's
+    off = off_o.reshape(-1).astype(np.int64)
+    ids = it_o.flatten_ids
+    n = it_o.n_isects
     ref = oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
-                               scene.width, scene.height, scene.tile_size, host(fr.isect_offsets), ids, n,
-                               scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold)
+                               scene.width, scene.height, scene.tile_size, off_o, ids, n, scene.alpha_cutoff,
+                               scene.alpha_clamp, scene.transmittance_threshold)
     bg = None if scene.backgrounds is None else dev(scene.backgrounds)
     g = binding.gs_rasterize_fwd_hwexp(dev(scene.means2d), dev(scene.conics), dev(scene.colors),
                                        dev(scene.opacities), bg, scene.width, scene.height, scene.tile_size,

@@ -9,7 +9,7 @@ import torch
 import oracle
 from tile_binned_gaussian_amd import binding, frame, synth
 
-from gpu_util import dev, host, last_splat, require_gpu
+from gpu_util import dev, host, last_splat, oracle_lists, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -71,9 +71,11 @@ def test_out_of_range_ids_are_skipped():
     scene = synth.random_scene(81, 2, 500, 70, 45, 16, background=True)
     fr = frame.render_frame(frame.to_device(scene, "cuda:0"))
     torch.cuda.synchronize()
-    off = host(fr.isect_offsets).reshape(-1).astype(np.int64)
-    ids = host(fr.isect.flatten_ids).copy()
-    n = fr.isect.n_isects
+    it_o, off_o = oracle_lists(scene)
+    np.testing.assert_array_equal(host(fr.isect.flatten_ids), it_o.flatten_ids)
+    off = off_o.reshape(-1).astype(np.int64)
+    ids = it_o.flatten_ids.copy()
+    n = it_o.n_isects
     rng = np.random.default_rng(82)
     bad = rng.choice(n, size=n // 7, replace=False)
     M = scene.C * scene.N
@@ -108,8 +110,6 @@ def test_out_of_range_ids_are_skipped():
                                   fr.isect_offsets, dev(ids), g.render_alphas, g.last_ids, dev(gc), dev(ga),
                                   n_isects=n, alpha_cutoff=scene.alpha_cutoff, alpha_clamp=scene.alpha_clamp)
     torch.cuda.synchronize()
-    tiles = host(fr.isect.tiles_per_gauss).astype(np.float64)
-    bound = (8.0 + tiles[..., None] * 16) * 2.0 ** -24 * ob.abs_means2d + 1e-30
-    assert (np.abs(host(gb.means2d) - ob.means2d) <= bound).all()
-    bound_o = (8.0 + tiles * 16) * 2.0 ** -24 * ob.abs_opacities + 1e-30
-    assert (np.abs(host(gb.opacities) - ob.opacities) <= bound_o).all()
+    from test_gpu_backward import assert_within, summation_depth
+    for field in ("means2d", "opacities", "colors", "conics"):
+        assert_within(gb, ob, field, summation_depth(scene, it_o))

@@ -10,7 +10,7 @@ import torch
 import oracle
 from tile_binned_gaussian_amd import binding, synth
 
-from gpu_util import dev, gpu_frame, host, require_gpu, sampled_tiles
+from gpu_util import dev, gpu_frame, host, oracle_lists, require_gpu
 from test_gpu_parity import SCENES
 
 pytestmark = pytest.mark.gpu
@@ -43,12 +43,15 @@ def _gpu_traced(scene, fr, S, L=-1, masks=None, eval_counts=None):
     return out
 
 
-def _oracle_traced(scene, fr, S, L=-1, masks=None, tiles=None):
+def _oracle_traced(scene, fr, S, L=-1, masks=None, tiles=None, lists=None, openmp=False):
+    """The oracle's traced forward over the oracle's own lists (fr is the GPU frame, unused here: kept so both
+    sides of a comparison read alike)."""
+    it_o, off_o = lists if lists is not None else oracle_lists(scene)
     return oracle.rasterize_fwd_traced(scene.means2d, scene.conics, scene.colors, scene.opacities,
-                                       scene.backgrounds, scene.width, scene.height, scene.tile_size,
-                                       host(fr.isect_offsets), host(fr.isect.flatten_ids), fr.isect.n_isects,
-                                       scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold, S,
-                                       max_list_entries=L, masks=masks, tiles=tiles)
+                                       scene.backgrounds, scene.width, scene.height, scene.tile_size, off_o,
+                                       it_o.flatten_ids, it_o.n_isects, scene.alpha_cutoff, scene.alpha_clamp,
+                                       scene.transmittance_threshold, S, max_list_entries=L, masks=masks,
+                                       tiles=tiles, openmp=openmp)
 
 
 def _assert_traced_equal(g, o, sel=(...,)):
@@ -112,46 +115,41 @@ def test_work_counter_under_the_caps(name, S, L):
 def test_backward_on_a_capped_forward_matches_oracle():
     """The range backward walks each pixel back from its last id, so on a step-capped forward's outputs it gives
     the capped forward's gradient; compared with the oracle's backward on the oracle's capped outputs."""
-    from test_gpu_backward import _assert_close, _grads_in, _waves_per_tile
+    from test_gpu_backward import assert_within, grads_in, summation_depth
     scene = SCENES["multicam-ragged-elliptical"]()
     fr = gpu_frame(scene)
     S = 4
+    it_o, off_o = oracle_lists(scene)
     g = _gpu_traced(scene, fr, S)
-    o = _oracle_traced(scene, fr, S)
+    o = _oracle_traced(scene, fr, S, lists=(it_o, off_o))
     _assert_traced_equal(g, o)
-    gc, ga = _grads_in(scene, 21)
+    gc, ga = grads_in(scene, 21)
     ob = oracle.rasterize_bwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
-                              scene.width, scene.height, scene.tile_size, host(fr.isect_offsets),
-                              host(fr.isect.flatten_ids), fr.isect.n_isects, scene.alpha_cutoff, scene.alpha_clamp,
-                              o.render_alphas, o.last_ids, gc, ga)
+                              scene.width, scene.height, scene.tile_size, off_o, it_o.flatten_ids, it_o.n_isects,
+                              scene.alpha_cutoff, scene.alpha_clamp, o.render_alphas, o.last_ids, gc, ga)
     gb = binding.gs_rasterize_bwd(dev(scene.means2d), dev(scene.conics), dev(scene.colors), dev(scene.opacities),
                                   dev(scene.backgrounds), scene.width, scene.height, scene.tile_size,
                                   fr.isect_offsets, fr.isect.flatten_ids, g.render_alphas, g.last_ids, dev(gc),
                                   dev(ga), n_isects=fr.isect.n_isects, alpha_cutoff=scene.alpha_cutoff,
                                   alpha_clamp=scene.alpha_clamp)
     torch.cuda.synchronize()
-    adds = host(fr.isect.tiles_per_gauss).astype(np.float64) * 4 * _waves_per_tile(scene.tile_size)
-    _assert_close(host(gb.means2d), ob.means2d, ob.abs_means2d, adds[..., None], "means2d")
-    _assert_close(host(gb.conics), ob.conics, ob.abs_conics, adds[..., None], "conics")
-    _assert_close(host(gb.colors), ob.colors, ob.abs_colors, adds[..., None], "colors")
-    _assert_close(host(gb.opacities), ob.opacities, ob.abs_opacities, adds, "opacities")
+    adds = summation_depth(scene, it_o)
+    for field in ("means2d", "conics", "colors", "opacities"):
+        assert_within(gb, ob, field, adds)
 
 
-def test_traced_forward_1m_splats_1080p_sampled_tiles():
+def test_traced_forward_1m_splats_1080p_full_frame():
+    """Every pixel of the 1M-splat frame with a 48-step cap and a 2000-entry list cap, against the oracle's traced
+    forward (OpenMP build) over its own lists."""
     scene = synth.config3()
     fr = gpu_frame(scene)
     S, L = 48, 2000
     g = _gpu_traced(scene, fr, S, L)
-    tiles = sampled_tiles(host(fr.isect_offsets), fr.isect.n_isects, 96, seed=3)
-    o = _oracle_traced(scene, fr, S, L, tiles=tiles)
-    ts, tw = scene.tile_size, scene.tile_width
-    mask = np.zeros((scene.C, scene.height, scene.width), bool)
-    for t in tiles:
-        cam, local = divmod(int(t), tw * scene.tile_height)
-        ty, tx = divmod(local, tw)
-        mask[cam, ty * ts:(ty + 1) * ts, tx * ts:(tx + 1) * ts] = True
-    _assert_traced_equal(g, o, sel=mask)
-    assert (o.trace_counts[mask] == S).any()  # the step cap bites on this frame
+    it_o, off_o = oracle_lists(scene, openmp=True)
+    o = _oracle_traced(scene, fr, S, L, lists=(it_o, off_o), openmp=True)
+    _assert_traced_equal(g, o)
+    assert (o.trace_counts == S).any()  # the step cap bites on this frame
+    assert (np.diff(np.append(off_o.reshape(-1), it_o.n_isects)) > L).any()  # and so does the list cap
 
 
 def test_trace_rows_not_16_byte_aligned():
@@ -175,6 +173,8 @@ def test_trace_rows_not_16_byte_aligned():
                                     transmittance_threshold=scene.transmittance_threshold, out=out)
     torch.cuda.synchronize()
     assert int(flat[0]) == SENTINEL
+    # the aligned run is itself checked against the oracle, then the unaligned one against it
+    _assert_traced_equal(ref, _oracle_traced(scene, fr, S))
     torch.testing.assert_close(out.trace_counts, ref.trace_counts, rtol=0, atol=0)
     torch.testing.assert_close(out.trace_ids, ref.trace_ids, rtol=0, atol=0)
     torch.testing.assert_close(out.render_colors, ref.render_colors, rtol=0, atol=0)

@@ -1,5 +1,6 @@
-"""The oracle's OpenMP build (used only for the benchmark's multi-core CPU baseline) composites the same tiles with
-the same per-pixel arithmetic as the plain build the tests use: every output must be equal bit for bit."""
+"""The oracle's OpenMP build (the benchmark's multi-core CPU baseline, and the largest frames of the GPU tests) runs
+the emission's splats, the sort's merges and the composite's tiles on several threads with the same per-element
+arithmetic as the plain build: every output must be equal bit for bit."""
 import numpy as np
 
 import oracle
@@ -20,3 +21,14 @@ def test_openmp_build_matches_plain_build():
             np.testing.assert_array_equal(x, y)
         assert a.n_eval == b.n_eval
     assert oracle.threads() == 1 and oracle.threads(openmp=True) >= 1
+
+
+def test_openmp_intersections_match_plain_build():
+    s = synth.random_scene(48, 3, 4000, 300, 200, 8, elliptical=True, dup_depth_frac=0.3, zero_radius_frac=0.05)
+    for sort in (False, True):
+        a = oracle.isect_tiles(s.means2d, s.radii, s.depths, s.tile_size, s.tile_width, s.tile_height, sort=sort)
+        b = oracle.isect_tiles(s.means2d, s.radii, s.depths, s.tile_size, s.tile_width, s.tile_height, sort=sort,
+                               openmp=True)
+        assert a.n_isects == b.n_isects > 20_000
+        np.testing.assert_array_equal(a.keys, b.keys)
+        np.testing.assert_array_equal(a.flatten_ids, b.flatten_ids)
