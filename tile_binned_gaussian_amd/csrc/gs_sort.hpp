@@ -28,7 +28,7 @@ PassPlan make_pass_plan(int begin_bit, int end_bit);
 
 // Per-sort scratch: digit histograms, partition counters and two look-back arrays sized for n pairs.
 struct SortScratchLayout {
-    size_t hist, counters, status0, status1, bytes;
+    size_t hist, counters, status0, status1, starts, bytes;
     int64_t parts;
 };
 SortScratchLayout sort_scratch_layout(int64_t n);

@@ -151,6 +151,29 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
     }
 }
 
+// Global start of every digit bucket of every pass: for pass p and digit d, the number of keys whose digit p is
+// below d, summed over the histogram copies. One workgroup, one thread per digit; computed once per sort, so a
+// digit pass's partitions only load their digit's start (off their critical path) instead of each summing the
+// copies and scanning them.
+__global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__restrict__ hist, int passes,
+                                                          uint32_t *__restrict__ starts) {
+    __shared__ uint32_t s_w[kRadix / kWave];
+    const int d = threadIdx.x, wave = d / kWave, lane = __lane_id();
+    for (int p = 0; p < passes; ++p) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < kHistCopies; ++k) c += hist[k * kHistCopyWords + p * kRadix + d];
+        const uint32_t inc = wave_inclusive_sum(c);
+        __syncthreads();  // the previous pass's reads of s_w are done
+        if (lane == kWave - 1) s_w[wave] = inc;
+        __syncthreads();
+        uint32_t before = 0;
+#pragma unroll
+        for (int w = 0; w < kRadix / kWave; ++w) before += w < wave ? s_w[w] : 0u;
+        starts[p * kRadix + d] = before + inc - c;
+    }
+}
+
 // One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling<KeyT>);
 // wave w owns the contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at
 // w * kWaveSpan + i * 64 + l, so (wave, item, lane) order is input order and the per-wave running counts give a
@@ -160,7 +183,7 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
 template <typename KeyT, int kDigitBits>
 __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const KeyT *__restrict__ keys_in, const int32_t *__restrict__ ids_in, KeyT *__restrict__ keys_out,
-    int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ hist,
+    int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ digit_starts,
     uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next,
     uint32_t spin_limit) {
     constexpr int digit_bits = kDigitBits;
@@ -193,15 +216,9 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const int d = digit_thread ? tid : 0;
     if (status_next && digit_thread) status_next[static_cast<size_t>(part) * kRadix + d] = 0;
 
-    // global start of each digit bucket for this pass (exclusive scan of the histogram, summed over its copies;
-    // before the key loads, whose latency the scan's barrier would otherwise wait out)
-    uint32_t digit_count = 0;
-    if (digit_thread) {
-#pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) digit_count += hist[c * kHistCopyWords + d];
-    }
-    uint32_t unused_total;
-    const uint32_t digit_global_start = block_exclusive_u32(digit_count, s_tmp, &unused_total);
+    // global start of this thread's digit bucket for the pass (precomputed once per sort); used only when the
+    // pairs are written, so its load is in flight with the key loads
+    const uint32_t digit_global_start = digit_thread ? digit_starts[d] : 0u;
 
     // load this wave's span of keys (ids are loaded after the keys are written, to keep registers free)
     const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan + lane;
@@ -219,22 +236,25 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     }
 
 
-    // stable rank within the wave: lanes holding the same digit found by ballots over the digit's bits
+    // stable rank within the wave: the lanes holding the same digit, from one ballot per digit bit. A lane's
+    // mismatch set gathers, for every bit, the lanes whose bit differs from its own (ballot XOR the lane's bit spread
+    // over 32 bits, ORed in by one three-input bit operation per half of the 64-lane mask); its complement is the set
+    // of lanes with the same digit.
     uint32_t rank[kItems];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const uint32_t d = digit_of(k[i], shift, digit_mask);
-        // lanes whose digit equals this lane's: for every bit, keep the lanes whose bit matches (ballot XNOR the
-        // lane's own bit spread over 32 bits), on both halves of the 64-lane mask
-        uint32_t same_lo = ~0u, same_hi = ~0u;
+        uint32_t miss_lo = 0u, miss_hi = 0u;
 #pragma unroll
         for (int b = 0; b < digit_bits; ++b) {
-            const uint32_t spread = static_cast<uint32_t>(static_cast<int32_t>(d << (31 - b)) >> 31);
+            const uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), b, 1));
             const uint64_t ballot = __ballot(spread != 0u);
-            same_lo &= ~(static_cast<uint32_t>(ballot) ^ spread);
-            same_hi &= ~(static_cast<uint32_t>(ballot >> 32) ^ spread);
+            // truth table 0xF6: first | (second ^ third), the first operand being the table's high index bit
+            miss_lo = __builtin_amdgcn_bitop3_b32(miss_lo, static_cast<uint32_t>(ballot), spread, 0xF6);
+            miss_hi = __builtin_amdgcn_bitop3_b32(miss_hi, static_cast<uint32_t>(ballot >> 32), spread, 0xF6);
         }
+        const uint32_t same_lo = ~miss_lo, same_hi = ~miss_hi;
         const uint64_t same = (static_cast<uint64_t>(same_hi) << 32) | same_lo;
         const uint32_t below = static_cast<uint32_t>(__popcll(same & lt_mask));
         const uint32_t run = s_wave_hist[wave][d];
@@ -380,6 +400,8 @@ SortScratchLayout sort_scratch_layout(int64_t n) {
     c.take<uint32_t>(status_words);
     L.status1 = align_up(c.used, 256);
     c.take<uint32_t>(status_words);
+    L.starts = align_up(c.used, 256);
+    c.take<uint32_t>(static_cast<size_t>(kMaxPasses) * kRadix);
     L.bytes = align_up(c.used, 256);
     return L;
 }
@@ -427,6 +449,9 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
     uint32_t *status[2] = {reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1)};
+    uint32_t *starts = reinterpret_cast<uint32_t *>(ws + L.starts);
+    hipLaunchKernelGGL(digit_starts_kernel, dim3(1), dim3(kRadix), 0, stream, hist, plan.passes, starts);
+    GS_LAUNCH_TRY("digit_starts_kernel");
 
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
@@ -442,7 +467,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
             return fail(GS_ERR_INVALID_ARG, "radix pass: %lld partitions exceed the look-back arrays (%lld)",
                         (long long)parts, (long long)L.parts);
         const dim3 grid(static_cast<unsigned>(parts)), block(kThreads);
-        const uint32_t *h = hist + p * kRadix;
+        const uint32_t *h = starts + p * kRadix;
         switch (plan.bits[p]) {
 #define GS_PASS(B)                                                                                                  \
     case B:                                                                                                         \
