@@ -117,6 +117,18 @@ gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_
                        size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
+ * gs_sort_keys without a workspace, for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * The same stable sort as gs_sort_keys (same arguments and result), with its alternate buffers, digit histograms and
+ * look-back words in a file-scope device array of the library (about 52 MB per GPU, held until the process ends)
+ * instead of a caller workspace. n is limited to 2^22 pairs (GS_ERR_INVALID_ARG above that, before any launch). The
+ * call allocates nothing. Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and give wrong orders; serialize them. Errors as gs_sort_keys.
+ */
+gs_status gs_sort_keys_static(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_bit, void *stream);
+
+/* ------------------------------------------------------------------------------------------------------------
  * Device-side failure of the sort ([gsplat] gs_isect_tiles turns a failure of its sort into an error status,
  * NoMemError; here the sort's only device-side failure is a wait that does not end).
  *

@@ -23,7 +23,8 @@ _STATUS = {1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_OUT_OF_GRID", 3: "GS_ERR_WORKSPAC
 EXPORTS = ("gs_last_error", "gs_isect_workspace_bytes", "gs_isect_tiles", "gs_sort_workspace_bytes",
            "gs_sort_keys", "gs_tile_ranges_workspace_bytes", "gs_tile_ranges", "gs_rasterize_workspace_bytes",
            "gs_rasterize_fwd", "gs_rasterize_fwd_hwexp", "gs_rasterize_fwd_traced", "gs_rasterize_bwd",
-           "gs_project_fwd", "gs_bin_tiles", "gs_rasterize_fwd_bins", "gs_set_spin_limit", "gs_device_check")
+           "gs_project_fwd", "gs_bin_tiles", "gs_rasterize_fwd_bins", "gs_set_spin_limit", "gs_device_check",
+           "gs_sort_keys_static")
 
 
 class GsError(RuntimeError):
@@ -75,6 +76,7 @@ def load_library(path: str = LIB_PATH):
     lib.gs_rasterize_bwd.restype = I32
     lib.gs_project_fwd.argtypes = [P, P, P, P, I64, I64, I32, I32, F, F, F, F, I32, P, P, P, P, P, P]
     lib.gs_project_fwd.restype = I32
+    lib.gs_sort_keys_static.argtypes, lib.gs_sort_keys_static.restype = [P, P, I64, I32, P], I32
     lib.gs_set_spin_limit.argtypes, lib.gs_set_spin_limit.restype = [ctypes.c_uint32], ctypes.c_uint32
     lib.gs_device_check.argtypes, lib.gs_device_check.restype = [P], I32
     _lib = lib
@@ -202,6 +204,16 @@ def gs_sort_keys(keys, flatten_ids, end_bit=64, stream=None, workspace=None):
     n = keys.numel()
     ws = workspace if workspace is not None else _workspace(lib.gs_sort_workspace_bytes(n, end_bit), keys.device)
     _check(lib.gs_sort_keys(_ptr(keys), _ptr(flatten_ids), n, end_bit, _ptr(ws), ws.numel(), _stream(stream)))
+    return keys, flatten_ids
+
+
+def gs_sort_keys_static(keys, flatten_ids, end_bit=64, stream=None):
+    """gs_sort_keys without a workspace (the library's static scratch; at most 2^22 pairs; allocates nothing).
+    Calls that overlap on one GPU race."""
+    lib = load_library()
+    _req(keys, "keys", torch.int64)
+    _req(flatten_ids, "flatten_ids", torch.int32, keys.device, (keys.numel(),))
+    _check(lib.gs_sort_keys_static(_ptr(keys), _ptr(flatten_ids), keys.numel(), end_bit, _stream(stream)))
     return keys, flatten_ids
 
 

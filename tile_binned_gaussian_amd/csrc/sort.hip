@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 namespace gs {
 namespace {
@@ -561,6 +562,64 @@ extern "C" gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t 
     if (!workspace || workspace_bytes < need)
         return fail(GS_ERR_WORKSPACE, "gs_sort_keys: needs %zu workspace bytes (got %zu)", need, workspace_bytes);
     return sort_pairs_u64(keys, flatten_ids, n, end_bit, workspace, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// The sort without a caller workspace: its alternate buffers, histograms and look-back words live in a file-scope
+// device array (one per GPU, held until the process ends), for callers that cannot allocate.
+namespace gs {
+namespace {
+
+constexpr int64_t kStaticSortMaxPairs = int64_t(1) << 22;
+constexpr size_t kStaticScratchBytes = size_t(52) << 20;  // >= sort_layout(kStaticSortMaxPairs).bytes (checked)
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace gs
+
+__device__ __align__(256) unsigned char scratch[gs::kStaticScratchBytes];
+
+namespace gs {
+namespace {
+
+// The device address of this GPU's `scratch` array (the host-side name is only a stand-in for the symbol), looked up
+// once per device with that device current.
+gs_status static_scratch(void **out) {
+    int dev = 0;
+    GS_HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GS_ERR_DEVICE, "gs_sort_keys_static: device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        GS_HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return fail(GS_ERR_DEVICE, "gs_sort_keys_static: no address for the scratch array");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+
+}  // namespace
+}  // namespace gs
+
+extern "C" gs_status gs_sort_keys_static(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_bit, void *stream) {
+    if (n < 0 || n > gs::kStaticSortMaxPairs)
+        return fail(GS_ERR_INVALID_ARG, "gs_sort_keys_static: n = %lld outside [0, 2^22] (the static scratch holds at "
+                                        "most 2^22 pairs; use gs_sort_keys with a workspace for more)", (long long)n);
+    if (end_bit < 0 || end_bit > 64)
+        return fail(GS_ERR_INVALID_ARG, "gs_sort_keys_static: end_bit = %d outside [0, 64]", end_bit);
+    if (n > 0 && (!keys || !flatten_ids))
+        return fail(GS_ERR_INVALID_ARG, "gs_sort_keys_static: keys and ids are required");
+    if (n < 2 || end_bit == 0) return ok();
+    if (sort_layout(gs::kStaticSortMaxPairs).bytes > gs::kStaticScratchBytes)
+        return fail(GS_ERR_DEVICE, "gs_sort_keys_static: the static scratch is smaller than the sort's layout");
+    void *ws = nullptr;
+    gs_status st = gs::static_scratch(&ws);
+    if (st != GS_OK) return st;
+    return sort_pairs_u64(keys, flatten_ids, n, end_bit, ws, static_cast<hipStream_t>(stream));
 }
 
 extern "C" uint32_t gs_set_spin_limit(uint32_t limit) { return g_spin_limit.exchange(limit); }
