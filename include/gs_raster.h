@@ -88,9 +88,9 @@ const char *gs_last_error(void);
  * workspace: gs_isect_workspace_bytes(C, N, n, tile_width, tile_height, sort) bytes; n = 0 sizes phase 1.
  *   With sort != 0, phase 1 also puts the splats in (depth bits, id) order and computes each one's first output
  *   slot in that order, into the first gs_isect_workspace_bytes(C, N, 0, tile_width, tile_height, 1) bytes of
- *   the workspace; this work is queued behind the count's copy, so it runs while the count reaches the host.
- *   When n_isects_out is page-locked host memory (hipHostMalloc, or a pinned torch tensor) the copy does not
- *   block the host, so that work is queued before the host waits; with pageable memory the copy call waits.
+ *   the workspace. When n_isects_out is page-locked host memory (hipHostMalloc, or a pinned torch tensor) the
+ *   count kernel writes the total there itself and the host waits for that word alone, so this work, queued
+ *   behind the count, runs while the host returns; with pageable memory a copy call waits for the count first.
  *   Phase 2 must then receive a workspace that starts with those bytes unchanged: the same buffer (sized for
  *   phase 2 from the start), or a larger one into which the caller copied them on the same stream. A workspace
  *   without them gives a wrong order (never an access outside the buffers).
@@ -129,13 +129,14 @@ gs_status gs_sort_keys(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_
 gs_status gs_sort_keys_static(uint64_t *keys, int32_t *flatten_ids, int64_t n, int end_bit, void *stream);
 
 /* ------------------------------------------------------------------------------------------------------------
- * Device-side failure of the sort ([gsplat] gs_isect_tiles turns a failure of its sort into an error status,
- * NoMemError; here the sort's only device-side failure is a wait that does not end).
+ * Device-side failure of the sort and the count scans ([gsplat] gs_isect_tiles turns a failure of its sort into
+ * an error status, NoMemError; here the only device-side failure is a wait that does not end).
  *
- * Each digit pass of the sort (gs_sort_keys, and gs_isect_tiles with sort != 0) lets a partition wait for the
- * counts of the partitions before it. The wait is bounded: after `limit` rounds (one round is one
+ * Each digit pass of the sort (gs_sort_keys, and gs_isect_tiles with sort != 0) and the two scans of
+ * gs_isect_tiles' phase 1 (the counts in splat order, and with sort != 0 in depth order) let a partition wait for
+ * the counts of the partitions before it. The wait is bounded: after `limit` rounds (one round is one
  * device-coherent load plus a short sleep; the default, 2^20, is about a second) the partition gives up, sets the
- * library's device error word of the current GPU and finishes, so the pass always completes; that sort's output
+ * library's device error word of the current GPU and finishes, so the kernel always completes; that call's output
  * is then invalid (every access still stays inside the caller's buffers).
  * gs_set_spin_limit: sets the limit used by passes launched after the call (process-wide) and returns the
  *   previous one. 0 makes every partition that does not find its predecessors' counts at the first look give up

@@ -1,7 +1,8 @@
-"""The sort's bounded look-back wait: with a spin limit of zero a partition that does not find its predecessors'
-counts at the first look gives up, flags the device error word and finishes, so every kernel still exits
-normally; gs_device_check then reports GS_ERR_DEVICE. With the default limit the same sort is exact and reports
-nothing. (The limit is set from the host; no workspace is corrupted to provoke the failure.)
+"""The bounded look-back waits of the sort and of the intersection-count scans: with a spin limit of zero a
+partition that does not find its predecessors' counts at the first look gives up, flags the device error word and
+finishes, so every kernel still exits normally; gs_device_check then reports GS_ERR_DEVICE. With the default limit
+the same work is exact and reports nothing. (The limit is set from the host; no workspace is corrupted to provoke
+the failure.)
 
 Semantics being guarded: gsplat 1.0.0 native extension, intersections.c, gs_isect_tiles turns a failure of its
 sort into an error status (NoMemError) rather than returning a wrong order silently."""
@@ -69,3 +70,33 @@ def test_frame_path_reports_no_error_at_the_default_limit():
     gpu_frame(synth.config2())
     binding.gs_device_check()
     torch.cuda.synchronize()
+
+
+def test_zero_spin_limit_in_the_count_scans_is_reported():
+    """Phase 1 (the count scan, the depth sort, the scan of the counts in depth order) and the tile sort of a
+    4M-splat frame at a zero limit: some partition gives up and the check says so; every kernel finishes and every
+    write stays in the buffers (the outputs are then meaningless and not compared). The default limit then gives a
+    frame with nothing to report again."""
+    from tile_binned_gaussian_amd import synth
+    from gpu_util import gpu_frame
+    ds = synth.random_scene(seed=5, C=1, N=4 << 20, width=1920, height=1080, tile_size=16)
+    binding.gs_device_check()
+    prev = binding.gs_set_spin_limit(0)
+    gave_up = False
+    try:
+        for attempt in range(3):
+            print(f"zero-limit frame attempt {attempt}: N={ds.N}", flush=True)
+            gpu_frame(ds)
+            try:
+                binding.gs_device_check()
+            except binding.GsError as e:
+                assert e.status == binding.GS_ERR_DEVICE
+                assert "spin limit" in str(e)
+                gave_up = True
+                break
+    finally:
+        binding.gs_set_spin_limit(prev)
+    assert gave_up, "no partition gave up with a zero spin limit in 3 frames of 4M splats"
+    binding.gs_device_check()
+    gpu_frame(ds)
+    binding.gs_device_check()

@@ -35,6 +35,8 @@ SortScratchLayout sort_scratch_layout(int64_t n);
 
 // Clears the scratch's histograms, partition counters and first look-back array for a sort of n pairs.
 gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream);
+// Bytes at the start of the scratch that radix_prepare clears (a caller may clear them itself instead).
+size_t radix_clear_bytes(int64_t n);
 // The scratch's per-pass digit histograms (kHistCopies copies of kMaxPasses x 256 counts) for a sort of n pairs.
 uint32_t *radix_histograms(void *scratch, int64_t n);
 
@@ -52,5 +54,14 @@ template <typename KeyT>
 gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                            KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
                            hipStream_t stream, int *result_in_b);
+
+// Bits of the library's device error word (one per GPU, read and cleared by gs_device_check): a digit pass, or a
+// single-pass scan of the intersection counts, whose look-back wait ran past the spin limit.
+constexpr uint32_t kDeviceErrSortLookBack = 1u;
+constexpr uint32_t kDeviceErrScanLookBack = 2u;
+// The device address of this GPU's error word (looked up once per device with that device current).
+gs_status device_error_word(uint32_t **out);
+// Look-back rounds a waiting partition may spend before it gives up (gs_set_spin_limit).
+uint32_t spin_limit();
 
 }  // namespace gs

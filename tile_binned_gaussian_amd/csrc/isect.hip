@@ -15,141 +15,224 @@ constexpr int kThreads = 256;
 // than 2048; 8192 were no faster)
 constexpr int kEmitBlocks = 4096;
 
-// Sum of one int64 per thread over a 256-thread workgroup (result valid in thread 0).
-__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t *s_tmp) {
-    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_down(v, d, kWave);
-    const int wave = threadIdx.x / kWave;
-    if (__lane_id() == 0) s_tmp[wave] = v;
-    __syncthreads();
-    int64_t total = 0;
-    if (threadIdx.x == 0)
-        for (int w = 0; w < kThreads / kWave; ++w) total += s_tmp[w];
-    return total;
+// ------------------------------------------------------------------------------------------------------------
+// Phase 1. Two single-pass scans over partitions of kScanTile consecutive positions: the tile counts in splat order
+// (each splat's first output slot, and the total) and, when sorting, the counts in depth order. Item i of thread t
+// is position i * kScanThreads + t of the partition, so every load and store of a wave is contiguous.
+// A partition takes its index from a counter (so every predecessor is already running), publishes its sum in its
+// status word, and finds the sum over all predecessors by a decoupled look-back in which the 64 lanes of the first
+// wave each inspect one predecessor per round. A status word holds a flag in its top two bits (the partition's own
+// sum published, or its inclusive prefix published) and the value below.
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 4;
+constexpr int kScanTile = kScanThreads * kScanItems;
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr uint64_t kStatAggregate = 1ull << 62;
+constexpr uint64_t kStatInclusive = 2ull << 62;
+constexpr uint64_t kStatValue = (1ull << 62) - 1;
+
+__device__ __forceinline__ uint64_t load_status(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_status(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exclusive prefix of one int64 per thread over a 256-thread workgroup; *total gets the sum (all threads).
-__device__ __forceinline__ int64_t block_exclusive(int64_t v, int64_t *s_tmp, int64_t *total) {
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// Exclusive prefix over the partition's positions of one value per item (item i of thread t at i * kScanThreads +
+// t): v[i] is replaced by its prefix and the partition's sum is returned (every thread). The (item row, wave) sums
+// are 64 values in position order, scanned by wave 0 in LDS.
+static_assert(kScanItems * kScanWaves == kWave, "one lane of wave 0 per (item row, wave) sum");
+__device__ __forceinline__ int64_t scan_items_exclusive(int64_t (&v)[kScanItems], int64_t *s_part_sums,
+                                                        int64_t *s_total) {
     const int wave = threadIdx.x / kWave, lane = __lane_id();
-    const int64_t inc = wave_inclusive_sum(v);
-    if (lane == kWave - 1) s_tmp[wave] = inc;
+    int64_t inc[kScanItems];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        inc[i] = wave_inclusive_sum(v[i]);
+        if (lane == kWave - 1) s_part_sums[i * kScanWaves + wave] = inc[i];
+    }
     __syncthreads();
-    int64_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
-        const int64_t t = s_tmp[w];
-        if (w < wave) before += t;
-        all += t;
+    if (wave == 0) {
+        const int64_t x = s_part_sums[lane];
+        const int64_t x_inc = wave_inclusive_sum(x);
+        s_part_sums[lane] = x_inc - x;
+        if (lane == kWave - 1) *s_total = x_inc;
     }
-    *total = all;
-    return before + inc - v;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) v[i] = s_part_sums[i * kScanWaves + wave] + inc[i] - v[i];
+    return *s_total;
 }
 
-// Phase 1a: per-splat tile count, and one partial sum per workgroup. rects (nullable) receives each splat's
-// rectangle as (x0, y0, width, height) in tiles, for the depth-ordered steps.
-template <int RPG>
-__global__ __launch_bounds__(kThreads) void count_kernel(const float2 *__restrict__ means,
-                                                         const float *__restrict__ radii, int M, float ts, int tw,
-                                                         int th, int32_t *__restrict__ tiles_per_gauss,
-                                                         int4 *__restrict__ rects, int64_t *__restrict__ block_sums) {
-    __shared__ int64_t s_tmp[kThreads / kWave];
-    const int j = blockIdx.x * kThreads + threadIdx.x;
-    int64_t count = 0;
-    if (j < M) {
-        const Rect r = rect_of<RPG>(means, radii, j, ts, tw, th);
-        count = static_cast<int64_t>(r.x1 - r.x0) * static_cast<int64_t>(r.y1 - r.y0);
-        tiles_per_gauss[j] = static_cast<int32_t>(count);
-        if (rects) rects[j] = make_int4(r.x0, r.y0, r.x1 - r.x0, r.y1 - r.y0);
-    }
-    const int64_t total = block_sum(count, s_tmp);
-    if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+// The partition index from the counter (thread 0 asks; valid in every thread after the next barrier).
+__device__ __forceinline__ void take_partition(uint32_t *counter, uint32_t *s_part) {
+    if (threadIdx.x == 0) *s_part = atomicAdd(counter, 1u);
 }
 
-// Phase 1b: exclusive scan of the workgroup sums in place (one workgroup), total to *total_out. The sums pass
-// through LDS in chunks of 16 per thread: each thread adds its 16 consecutive values, one workgroup scan spreads
-// the partial sums, and each thread writes its 16 prefixes (LDS rows padded by one word against bank conflicts).
-constexpr int kScanPer = 16;
-constexpr int kScanChunk = kThreads * kScanPer;
-__device__ __forceinline__ int scan_slot(int i) { return i + i / kScanPer; }
-
-__global__ __launch_bounds__(kThreads) void scan_block_sums_kernel(int64_t *__restrict__ sums, int count,
-                                                                   int64_t *__restrict__ total_out) {
-    __shared__ int64_t s_v[kScanChunk + kScanChunk / kScanPer];
-    __shared__ int64_t s_tmp[kThreads / kWave];
-    int64_t carry = 0;
-    for (int base = 0; base < count; base += kScanChunk) {
-        const int len = count - base < kScanChunk ? count - base : kScanChunk;
-        for (int i = threadIdx.x; i < len; i += kThreads) s_v[scan_slot(i)] = sums[base + i];
-        __syncthreads();
-        const int first = static_cast<int>(threadIdx.x) * kScanPer;
-        int64_t local = 0;
-#pragma unroll
-        for (int i = 0; i < kScanPer; ++i)
-            if (first + i < len) local += s_v[scan_slot(first + i)];
-        int64_t chunk_total;
-        int64_t run = carry + block_exclusive(local, s_tmp, &chunk_total);
-#pragma unroll
-        for (int i = 0; i < kScanPer; ++i) {
-            if (first + i < len) {
-                const int64_t v = s_v[scan_slot(first + i)];
-                s_v[scan_slot(first + i)] = run;
-                run += v;
+// Publishes the partition's sum and returns the sum over partitions [0, part) (wave 0 only; the other waves get 0).
+// Each round every lane of wave 0 loads one predecessor's status word, newest first; the round consumes the words up
+// to and including the first inclusive one, or up to the first unpublished one when that comes earlier. After
+// spin_limit rounds that find the newest remaining predecessor unpublished the wait gives up: it sets the scan bit
+// of *err and returns what it has (the offsets are then wrong; every access stays in bounds).
+__device__ int64_t publish_and_look_back(uint64_t *status, uint32_t part, int64_t aggregate, uint32_t spin_limit,
+                                         uint32_t *err) {
+    if (threadIdx.x >= kWave) return 0;
+    const int lane = __lane_id();
+    if (lane == 0)
+        store_status(status + part, (part == 0 ? kStatInclusive : kStatAggregate) | static_cast<uint64_t>(aggregate));
+    if (part == 0) return 0;
+    int64_t prefix = 0;
+    int64_t j = static_cast<int64_t>(part) - 1;  // the newest predecessor not yet added
+    uint32_t idle = 0;
+    while (true) {
+        const int64_t q = j - lane;
+        const uint64_t w = q >= 0 ? load_status(status + q) : kStatInclusive;
+        const uint64_t flag = w & ~kStatValue;
+        const uint64_t pending = __ballot(flag == 0);
+        const uint64_t inclusive = __ballot(flag == kStatInclusive);
+        const int first_pending = pending ? __builtin_ctzll(pending) : kWave;
+        const int first_inclusive = inclusive ? __builtin_ctzll(inclusive) : kWave;
+        const bool done = first_inclusive < first_pending;
+        const int used = done ? first_inclusive + 1 : first_pending;
+        prefix += wave_sum(lane < used ? static_cast<int64_t>(w & kStatValue) : 0);
+        if (done) break;
+        j -= used;
+        if (used == 0) {
+            if (idle++ >= spin_limit) {
+                if (lane == 0) atomicOr(err, kDeviceErrScanLookBack);
+                break;
             }
+            __builtin_amdgcn_s_sleep(1);
         }
-        __syncthreads();
-        for (int i = threadIdx.x; i < len; i += kThreads) sums[base + i] = s_v[scan_slot(i)];
-        carry += chunk_total;
-        __syncthreads();
     }
-    if (threadIdx.x == 0) *total_out = carry;
+    if (lane == 0) store_status(status + part, kStatInclusive | static_cast<uint64_t>(prefix + aggregate));
+    return prefix;
 }
 
-// Phase 1c: per-splat first output slot = workgroup prefix + exclusive scan of the counts within it (the counts
-// are read back from phase 1a, coalesced).
-__global__ __launch_bounds__(kThreads) void offsets_kernel(const int32_t *__restrict__ tiles_per_gauss, int M,
-                                                           const int64_t *__restrict__ block_prefix,
-                                                           int32_t *__restrict__ gauss_offsets) {
-    __shared__ int64_t s_tmp[kThreads / kWave];
-    const int j = blockIdx.x * kThreads + threadIdx.x;
-    const int64_t count = j < M ? static_cast<int64_t>(tiles_per_gauss[j]) : 0;
-    int64_t unused;
-    const int64_t ex = block_exclusive(count, s_tmp, &unused);
-    if (j < M) gauss_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
+// Phase 1a: per-splat tile count (tiles_per_gauss), its exclusive prefix in splat order (gauss_offsets) and the total
+// (*total; also *total_host when non-null, a device-visible address of page-locked host memory). When sorting,
+// rects receives each splat's rectangle as (x0, y0, width, height) in tiles, and the depth sort's digit histograms
+// (hplan's passes over the depth bits) are accumulated, so neither the rectangles nor the depths are read again
+// for them.
+static_assert(kScanThreads == 4 * 256, "one thread per digit of the depth sort's four 8-bit passes");
+template <int RPG>
+__global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
+    const float2 *__restrict__ means, const float *__restrict__ radii, const uint32_t *__restrict__ depth_bits, int M,
+    float ts, int tw, int th, int32_t *__restrict__ tiles_per_gauss, int32_t *__restrict__ gauss_offsets,
+    int4 *__restrict__ rects, int64_t *__restrict__ total, int64_t *total_host, uint64_t *status,
+    uint32_t *__restrict__ counter, uint32_t *__restrict__ hist, PassPlan hplan, uint32_t spin_limit, uint32_t *err) {
+    __shared__ uint32_t s_hist[4][256];
+    __shared__ int64_t s_part_sums[kScanItems * kScanWaves];
+    __shared__ int64_t s_total;
+    __shared__ int64_t s_prefix;
+    __shared__ uint32_t s_part;
+    take_partition(counter, &s_part);
+    if (hist) (&s_hist[0][0])[threadIdx.x] = 0;
+    __syncthreads();
+    const uint32_t part = s_part;
+    if (static_cast<int64_t>(part) * kScanTile >= M) return;  // only with a corrupted counter
+    const int j0 = static_cast<int>(part) * kScanTile + static_cast<int>(threadIdx.x);
+    // every load of the thread's splats is issued before any result is used
+    float2 m[kScanItems];
+    float2 rad[kScanItems];
+    uint32_t bits[kScanItems];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int j = j0 + i * kScanThreads < M ? j0 + i * kScanThreads : M - 1;
+        m[i] = means[j];
+        rad[i] = RPG == 2 ? reinterpret_cast<const float2 *>(radii)[j] : make_float2(radii[j], radii[j]);
+        bits[i] = hist ? depth_bits[j] : 0u;
+    }
+    int64_t v[kScanItems];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int j = j0 + i * kScanThreads;
+        const Rect r = tile_rect(m[i].x, m[i].y, rad[i].x, rad[i].y, ts, tw, th);
+        const int32_t count = j < M ? (r.x1 - r.x0) * (r.y1 - r.y0) : 0;
+        v[i] = count;
+        if (j < M) {
+            tiles_per_gauss[j] = count;
+            if (rects) rects[j] = make_int4(r.x0, r.y0, r.x1 - r.x0, r.y1 - r.y0);
+        }
+    }
+    if (hist) {
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i)
+            if (j0 + i * kScanThreads < M)
+                for (int p = 0; p < hplan.passes; ++p)
+                    atomicAdd(&s_hist[p][(bits[i] >> hplan.shift[p]) & ((1u << hplan.bits[p]) - 1u)], 1u);
+    }
+    const int64_t aggregate = scan_items_exclusive(v, s_part_sums, &s_total);
+    const int64_t before = publish_and_look_back(status, part, aggregate, spin_limit, err);
+    if (threadIdx.x == 0) s_prefix = before;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int j = j0 + i * kScanThreads;
+        if (j < M) gauss_offsets[j] = static_cast<int32_t>(s_prefix + v[i]);
+    }
+    if (threadIdx.x == 0 && static_cast<int64_t>(part + 1) * kScanTile >= M) {
+        const int64_t all = s_prefix + aggregate;
+        *total = all;
+        if (total_host) __hip_atomic_store(total_host, all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (hist) {
+        const int p = threadIdx.x / 256, d = threadIdx.x % 256;
+        const uint32_t c = s_hist[p][d];
+        if (p < hplan.passes && c) atomicAdd(&hist_copy(hist, part)[p * 256 + d], c);
+    }
 }
 
-// Depth order, step 1: position j holds splat perm[j]; its rectangle is gathered once into depth order and its
-// count summed per workgroup. A perm entry outside [0, M) - only possible with a corrupted workspace - gives an
-// empty rectangle.
-__global__ __launch_bounds__(kThreads) void perm_rects_kernel(const int32_t *__restrict__ perm,
-                                                              const int4 *__restrict__ rects, int M,
-                                                              int4 *__restrict__ sorted_rects,
-                                                              int64_t *__restrict__ block_sums) {
-    __shared__ int64_t s_tmp[kThreads / kWave];
-    const int j = blockIdx.x * kThreads + threadIdx.x;
-    int64_t count = 0;
-    if (j < M) {
-        const int i = perm[j];
-        const int4 r = static_cast<unsigned>(i) < static_cast<unsigned>(M) ? rects[i] : make_int4(0, 0, 0, 0);
-        sorted_rects[j] = r;
-        count = static_cast<int64_t>(r.z) * static_cast<int64_t>(r.w);
+// Phase 1b (sorting): position j holds splat perm[j]. Its rectangle is gathered once into depth order
+// (sorted_rects) and the exclusive prefix of the counts in that order gives each position's first output slot
+// (sorted_offsets). A perm entry outside [0, M) - only possible with a corrupted workspace - gives an empty
+// rectangle.
+__global__ __launch_bounds__(kScanThreads) void order_scan_kernel(const int32_t *__restrict__ perm,
+                                                                  const int4 *__restrict__ rects, int M,
+                                                                  int4 *__restrict__ sorted_rects,
+                                                                  int32_t *__restrict__ sorted_offsets,
+                                                                  uint64_t *status, uint32_t *__restrict__ counter,
+                                                                  uint32_t spin_limit, uint32_t *err) {
+    __shared__ int64_t s_part_sums[kScanItems * kScanWaves];
+    __shared__ int64_t s_total;
+    __shared__ int64_t s_prefix;
+    __shared__ uint32_t s_part;
+    take_partition(counter, &s_part);
+    __syncthreads();
+    const uint32_t part = s_part;
+    if (static_cast<int64_t>(part) * kScanTile >= M) return;  // only with a corrupted counter
+    const int j0 = static_cast<int>(part) * kScanTile + static_cast<int>(threadIdx.x);
+    // the permutation entries first, then every gather of the thread's rectangles at once
+    int src[kScanItems];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) src[i] = j0 + i * kScanThreads < M ? perm[j0 + i * kScanThreads] : -1;
+    int4 r[kScanItems];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i)
+        r[i] = static_cast<unsigned>(src[i]) < static_cast<unsigned>(M) ? rects[src[i]] : make_int4(0, 0, 0, 0);
+    int64_t v[kScanItems];
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int j = j0 + i * kScanThreads;
+        v[i] = r[i].z * r[i].w;
+        if (j < M) sorted_rects[j] = r[i];
     }
-    const int64_t sum = block_sum(count, s_tmp);
-    if (threadIdx.x == 0) block_sums[blockIdx.x] = sum;
-}
-
-// Depth order, step 2: first output slot per position = workgroup prefix + exclusive scan within the workgroup.
-__global__ __launch_bounds__(kThreads) void perm_offsets_kernel(const int4 *__restrict__ sorted_rects, int M,
-                                                                const int64_t *__restrict__ block_prefix,
-                                                                int32_t *__restrict__ sorted_offsets) {
-    __shared__ int64_t s_tmp[kThreads / kWave];
-    const int j = blockIdx.x * kThreads + threadIdx.x;
-    int64_t count = 0;
-    if (j < M) {
-        const int4 r = sorted_rects[j];
-        count = static_cast<int64_t>(r.z) * static_cast<int64_t>(r.w);
+    const int64_t aggregate = scan_items_exclusive(v, s_part_sums, &s_total);
+    const int64_t before = publish_and_look_back(status, part, aggregate, spin_limit, err);
+    if (threadIdx.x == 0) s_prefix = before;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int j = j0 + i * kScanThreads;
+        if (j < M) sorted_offsets[j] = static_cast<int32_t>(s_prefix + v[i]);
     }
-    int64_t unused;
-    const int64_t ex = block_exclusive(count, s_tmp, &unused);
-    if (j < M) sorted_offsets[j] = static_cast<int32_t>(block_prefix[blockIdx.x] + ex);
 }
 
 // floor(k / w) for w >= 1, given rcp_w = 1.0f / w correctly rounded. For 0 <= k < 2^22 the float product is within
@@ -287,27 +370,36 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
 }
 
 // Workspace of gs_isect_tiles. The prefix [0, prefix) depends on M and the sort flag only, so phase 1 and phase 2
-// see it at the same offsets: the workgroup sums, the total and, when sorting, the depth order of the splats
-// (two u32/i32 ping-pong pairs of M), the rectangles (row-major and in depth order), the per-position offsets in
-// that order and the depth sort's scratch. Phase 1
-// fills it; phase 2 reads it and adds, when sorting more than one intersection, the alternate intersection buffers
+// see it at the same offsets: the total, the two scans' partition counters and status words, and, when sorting,
+// the depth sort's scratch, the depth order of the splats (two u32/i32 ping-pong pairs of M), the rectangles
+// (row-major and in depth order) and the per-position offsets in that order. [clear_begin, clear_end) is what
+// phase 1 clears before it starts: the counters, the status words and the part of the depth sort's scratch that
+// must start at zero. Phase 2 adds, when sorting more than one intersection, the alternate intersection buffers
 // and the tile sort's scratch.
 struct IsectLayout {
-    size_t block_sums, total, dkeys_a, dids_a, dkeys_b, dids_b, rects, sorted_rects, sorted_offsets, depth_scratch,
-        prefix;
+    size_t total, counters, count_status, order_status, depth_scratch, clear_begin, clear_end;
+    size_t dkeys_a, dids_a, dkeys_b, dids_b, rects, sorted_rects, sorted_offsets, prefix;
     size_t alt_keys, alt_ids, tile_scratch, bytes;
 };
 
 IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     IsectLayout L{};
     Carver c(nullptr);
-    const int64_t blocks = (M + kThreads - 1) / kThreads;
-    L.block_sums = align_up(c.used, 256);
-    c.take<int64_t>(static_cast<size_t>(blocks > 0 ? blocks : 1));
+    const size_t parts = static_cast<size_t>(M > 0 ? (M + kScanTile - 1) / kScanTile : 1);
     L.total = align_up(c.used, 256);
     c.take<int64_t>(1);
+    L.counters = L.clear_begin = align_up(c.used, 256);
+    c.take<uint32_t>(2);  // the two scans' partition counters
+    L.count_status = align_up(c.used, 256);
+    c.take<uint64_t>(parts);
+    L.clear_end = c.used;
     if (sort) {
         const size_t m = static_cast<size_t>(M > 0 ? M : 1);
+        L.order_status = align_up(c.used, 256);
+        c.take<uint64_t>(parts);
+        L.depth_scratch = align_up(c.used, 256);
+        c.take<char>(sort_scratch_layout(static_cast<int64_t>(m)).bytes);
+        L.clear_end = L.depth_scratch + radix_clear_bytes(static_cast<int64_t>(m));
         L.dkeys_a = align_up(c.used, 256);
         c.take<uint32_t>(m);
         L.dids_a = align_up(c.used, 256);
@@ -322,8 +414,6 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
         c.take<int4>(m);
         L.sorted_offsets = align_up(c.used, 256);
         c.take<int32_t>(m);
-        L.depth_scratch = align_up(c.used, 256);
-        c.take<char>(sort_scratch_layout(static_cast<int64_t>(m)).bytes);
     }
     L.prefix = L.bytes = align_up(c.used, 256);
     if (!(sort && n > 1)) return L;
@@ -338,14 +428,15 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     return L;
 }
 
-// Whether p is page-locked host memory the device can write directly (a copy into it does not block the host).
-bool pinned_host(const void *p) {
+// The device-visible address of p when it is page-locked host memory the device can write directly, else null.
+int64_t *pinned_device_address(int64_t *p) {
     hipPointerAttribute_t attr{};
     if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
         (void)hipGetLastError();  // an unknown host pointer is not an error here
-        return false;
+        return nullptr;
     }
-    return attr.type == hipMemoryTypeHost;
+    if (attr.type != hipMemoryTypeHost) return nullptr;
+    return static_cast<int64_t *>(attr.devicePointer);
 }
 
 template <typename T>
@@ -353,23 +444,22 @@ T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
-// count -> workgroup sums -> scan -> per-splat offsets.
-gs_status launch_counts(int rpg, const float2 *m2, const float *radii, int M, float ts, int tw, int th,
-                        int32_t *tiles_per_gauss, int4 *rects, int64_t *block_sums, int64_t *total,
-                        int32_t *offsets, hipStream_t stream) {
-    const int blocks = (M + kThreads - 1) / kThreads;
+// The count scan (hist non-null: with the depth sort's histograms of hplan's passes).
+gs_status launch_count_scan(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, float ts,
+                            int tw, int th, int32_t *tiles_per_gauss, int32_t *offsets, int4 *rects, int64_t *total,
+                            int64_t *total_host, uint64_t *status, uint32_t *counter, uint32_t *hist,
+                            const PassPlan &hplan, uint32_t *err, hipStream_t stream) {
+    const int parts = (M + kScanTile - 1) / kScanTile;
+    const uint32_t spin = spin_limit();
     if (rpg == 2)
-        hipLaunchKernelGGL(count_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
-                           tiles_per_gauss, rects, block_sums);
+        hipLaunchKernelGGL(count_scan_kernel<2>, dim3(parts), dim3(kScanThreads), 0, stream, m2, radii, dbits, M, ts,
+                           tw, th, tiles_per_gauss, offsets, rects, total, total_host, status, counter, hist, hplan,
+                           spin, err);
     else
-        hipLaunchKernelGGL(count_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, M, ts, tw, th,
-                           tiles_per_gauss, rects, block_sums);
-    GS_LAUNCH_TRY("count_kernel");
-    hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks, total);
-    GS_LAUNCH_TRY("scan_block_sums_kernel");
-    hipLaunchKernelGGL(offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream, tiles_per_gauss, M, block_sums,
-                       offsets);
-    GS_LAUNCH_TRY("offsets_kernel");
+        hipLaunchKernelGGL(count_scan_kernel<1>, dim3(parts), dim3(kScanThreads), 0, stream, m2, radii, dbits, M, ts,
+                           tw, th, tiles_per_gauss, offsets, rects, total, total_host, status, counter, hist, hplan,
+                           spin, err);
+    GS_LAUNCH_TRY("count_scan_kernel");
     return ok();
 }
 
@@ -450,55 +540,72 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             *n_isects_out = 0;
             return ok();
         }
-        int64_t *total = at<int64_t>(workspace, L.total);
-        int64_t *block_sums = at<int64_t>(workspace, L.block_sums);
-        int4 *rects = sort ? at<int4>(workspace, L.rects) : nullptr;
-        gs_status st = launch_counts(radii_per_gauss, m2, radii, M, ts, tile_width, tile_height, tiles_per_gauss,
-                                     rects, block_sums, total, gauss_offsets, stream);
+        uint32_t *err = nullptr;
+        gs_status st = device_error_word(&err);
         if (st != GS_OK) return st;
-        // Into page-locked memory the copy is asynchronous, so the depth-order work below is queued before the
-        // host waits; into pageable memory the copy call itself waits for the count.
-        const bool pinned = pinned_host(n_isects_out);
+        if (depth_plan.passes > 4)
+            return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: the depth sort needs %d passes", depth_plan.passes);
+        const uint32_t *dbits = reinterpret_cast<const uint32_t *>(depths);
+        int64_t *total = at<int64_t>(workspace, L.total);
+        uint32_t *counters = at<uint32_t>(workspace, L.counters);
+        char *depth_scratch = sort ? at<char>(workspace, L.depth_scratch) : nullptr;
+        int4 *rects = sort ? at<int4>(workspace, L.rects) : nullptr;
+        // Into page-locked memory the count scan writes the total itself and the host waits for that word alone, so
+        // the depth-order work queued behind the scan runs while the count travels to the host and the caller
+        // prepares phase 2; into pageable memory a copy returns it.
+        int64_t *total_host = pinned_device_address(n_isects_out);
+        volatile int64_t *host_word = n_isects_out;
+        if (total_host) *host_word = -1;
+        GS_HIP_TRY(fill_u32(at<uint32_t>(workspace, L.clear_begin), 0, (L.clear_end - L.clear_begin) / sizeof(uint32_t),
+                            stream));
+        st = launch_count_scan(radii_per_gauss, m2, radii, dbits, M, ts, tile_width, tile_height, tiles_per_gauss,
+                               gauss_offsets, rects, total, total_host, at<uint64_t>(workspace, L.count_status),
+                               counters, sort ? radix_histograms(depth_scratch, M) : nullptr, depth_plan, err, stream);
+        if (st != GS_OK) return st;
         int64_t host_total = 0;
         hipEvent_t copied = nullptr;
-        GS_HIP_TRY(hipEventCreateWithFlags(&copied, hipEventDisableTiming));
-        hipError_t e = hipMemcpyAsync(pinned ? n_isects_out : &host_total, total, sizeof host_total,
-                                      hipMemcpyDeviceToHost, stream);
-        if (e == hipSuccess) e = hipEventRecord(copied, stream);
+        hipError_t e = hipSuccess;
+        if (!total_host) {
+            GS_HIP_TRY(hipEventCreateWithFlags(&copied, hipEventDisableTiming));
+            e = hipMemcpyAsync(&host_total, total, sizeof host_total, hipMemcpyDeviceToHost, stream);
+            if (e == hipSuccess) e = hipEventRecord(copied, stream);
+        }
         if (e == hipSuccess && sort) {
-            // The depth order and the offsets in that order need only the splats: queue them behind the copy so
-            // the device works on them while the count travels to the host and the caller prepares phase 2.
-            const uint32_t *dbits = reinterpret_cast<const uint32_t *>(depths);
+            // the depth order of the splats (histograms from the count scan), then the rectangles and first output
+            // slots in that order
             int in_b = 0;
-            st = radix_sort_pairs<uint32_t>(dbits, nullptr, at<uint32_t>(workspace, L.dkeys_a),
-                                            at<int32_t>(workspace, L.dids_a), at<uint32_t>(workspace, L.dkeys_b),
-                                            at<int32_t>(workspace, L.dids_b), M, depth_plan,
-                                            at<char>(workspace, L.depth_scratch), stream, &in_b);
-            const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
-            const int blocks = (M + kThreads - 1) / kThreads;
+            st = radix_passes<uint32_t>(dbits, nullptr, at<uint32_t>(workspace, L.dkeys_a),
+                                        at<int32_t>(workspace, L.dids_a), at<uint32_t>(workspace, L.dkeys_b),
+                                        at<int32_t>(workspace, L.dids_b), M, depth_plan, depth_scratch, stream, &in_b);
             if (st == GS_OK) {
-                hipLaunchKernelGGL(perm_rects_kernel, dim3(blocks), dim3(kThreads), 0, stream, perm, rects, M,
-                                   at<int4>(workspace, L.sorted_rects), block_sums);
-                e = hipGetLastError();
-            }
-            if (st == GS_OK && e == hipSuccess) {
-                // the scan rewrites the total with the same value (the same counts in another order)
-                hipLaunchKernelGGL(scan_block_sums_kernel, dim3(1), dim3(kThreads), 0, stream, block_sums, blocks,
-                                   total);
-                e = hipGetLastError();
-            }
-            if (st == GS_OK && e == hipSuccess) {
-                hipLaunchKernelGGL(perm_offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                                   at<int4>(workspace, L.sorted_rects), M, block_sums,
-                                   at<int32_t>(workspace, L.sorted_offsets));
+                const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
+                hipLaunchKernelGGL(order_scan_kernel, dim3((M + kScanTile - 1) / kScanTile), dim3(kScanThreads), 0,
+                                   stream, perm, rects, M, at<int4>(workspace, L.sorted_rects),
+                                   at<int32_t>(workspace, L.sorted_offsets), at<uint64_t>(workspace, L.order_status),
+                                   counters + 1, spin_limit(), err);
                 e = hipGetLastError();
             }
         }
-        const hipError_t w = (e == hipSuccess) ? hipEventSynchronize(copied) : e;
-        (void)hipEventDestroy(copied);
+        // wait for the total (also after a failed launch, so no write into the caller's memory is left in flight)
+        hipError_t w = hipSuccess;
+        if (copied) {
+            w = hipEventSynchronize(copied);
+            (void)hipEventDestroy(copied);
+        } else {
+            for (uint64_t polls = 1; *host_word < 0; ++polls) {
+                if (polls % 1024 != 0) continue;
+                const hipError_t q = hipStreamQuery(stream);
+                if (q == hipErrorNotReady) continue;
+                if (q == hipSuccess && *host_word < 0)  // the stream drained without the scan writing the total
+                    return fail(GS_ERR_DEVICE, "gs_isect_tiles: the count scan finished without writing the total");
+                w = q;
+                break;
+            }
+            host_total = *host_word;
+        }
         if (st != GS_OK) return st;
+        if (e != hipSuccess) return fail(GS_ERR_DEVICE, "gs_isect_tiles: %s", hipGetErrorString(e));
         if (w != hipSuccess) return fail(GS_ERR_DEVICE, "gs_isect_tiles: %s", hipGetErrorString(w));
-        if (pinned) host_total = *static_cast<volatile int64_t *>(n_isects_out);
         *n_isects_out = host_total;
         if (host_total >= (int64_t(1) << 31))
             return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: %lld intersections exceed the int32 offsets",

@@ -54,10 +54,10 @@ constexpr int kHistTile = kHistThreads * kHistItems;
 
 }  // namespace
 
-// Device-wide error word of the library (one per GPU): bit kDeviceErrLookBack is set by a digit pass whose
-// look-back wait for a predecessor partition ran past the spin limit. Read and cleared by gs_device_check.
+// Device-wide error word of the library (one per GPU): bit kDeviceErrSortLookBack is set by a digit pass whose
+// look-back wait for a predecessor partition ran past the spin limit, bit kDeviceErrScanLookBack by a single-pass
+// scan of the intersection counts in the same case. Read and cleared by gs_device_check.
 __device__ uint32_t g_device_error = 0;
-constexpr uint32_t kDeviceErrLookBack = 1u;
 
 namespace {
 
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
             }
             if (found) break;
             if (rounds++ >= spin_limit) {
-                atomicOr(&g_device_error, kDeviceErrLookBack);
+                atomicOr(&g_device_error, kDeviceErrSortLookBack);
                 break;
             }
             j -= used;
@@ -408,11 +408,14 @@ SortScratchLayout sort_scratch_layout(int64_t n) {
 }
 
 gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream) {
-    const SortScratchLayout L = sort_scratch_layout(n);
     // histograms, counters and the first look-back array are consecutive: one fill clears all three
-    const size_t words = L.status0 / sizeof(uint32_t) + static_cast<size_t>(L.parts) * kRadix;
-    GS_HIP_TRY(fill_u32(static_cast<uint32_t *>(scratch), 0, words, stream));
+    GS_HIP_TRY(fill_u32(static_cast<uint32_t *>(scratch), 0, radix_clear_bytes(n) / sizeof(uint32_t), stream));
     return ok();
+}
+
+size_t radix_clear_bytes(int64_t n) {
+    const SortScratchLayout L = sort_scratch_layout(n);
+    return L.status0 + static_cast<size_t>(L.parts) * kRadix * sizeof(uint32_t);
 }
 
 uint32_t *radix_histograms(void *scratch, int64_t n) {
@@ -456,7 +459,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
 
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
-    const uint32_t spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    const uint32_t spin = spin_limit();
     for (int p = 0; p < plan.passes; ++p) {
         const bool to_a = (p % 2) == 0;
         KeyT *dk = to_a ? buf_a_keys : buf_b_keys;
@@ -473,7 +476,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
 #define GS_PASS(B)                                                                                                  \
     case B:                                                                                                         \
         hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B>), grid, block, 0, stream, src_k, src_i, dk, di, n,       \
-                           plan.shift[p], h, counters + p, st, st_next, spin_limit);                                \
+                           plan.shift[p], h, counters + p, st, st_next, spin);                                     \
         break;
             GS_PASS(1) GS_PASS(2) GS_PASS(3) GS_PASS(4) GS_PASS(5) GS_PASS(6) GS_PASS(7) GS_PASS(8)
 #undef GS_PASS
@@ -491,6 +494,8 @@ template gs_status radix_sort_pairs<uint32_t>(const uint32_t *, const int32_t *,
                                               int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
 template gs_status radix_sort_pairs<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
                                               int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
+template gs_status radix_passes<uint32_t>(const uint32_t *, const int32_t *, uint32_t *, int32_t *, uint32_t *,
+                                          int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
 template gs_status radix_passes<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
                                           int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
 
@@ -624,6 +629,30 @@ extern "C" gs_status gs_sort_keys_static(uint64_t *keys, int32_t *flatten_ids, i
 
 extern "C" uint32_t gs_set_spin_limit(uint32_t limit) { return g_spin_limit.exchange(limit); }
 
+namespace gs {
+namespace {
+std::mutex g_error_mutex;
+uint32_t *g_error_ptr[kMaxDevices] = {};
+}  // namespace
+
+uint32_t spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
+gs_status device_error_word(uint32_t **out) {
+    int dev = 0;
+    GS_HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GS_ERR_DEVICE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_error_mutex);
+    if (!g_error_ptr[dev]) {
+        void *ptr = nullptr;
+        GS_HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_device_error)));
+        if (!ptr) return fail(GS_ERR_DEVICE, "no address for the device error word");
+        g_error_ptr[dev] = static_cast<uint32_t *>(ptr);
+    }
+    *out = g_error_ptr[dev];
+    return ok();
+}
+}  // namespace gs
+
 extern "C" gs_status gs_device_check(void *stream_handle) {
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
     uint32_t word = 0;
@@ -635,8 +664,12 @@ extern "C" gs_status gs_device_check(void *stream_handle) {
     GS_HIP_TRY(hipMemcpyToSymbolAsync(HIP_SYMBOL(g_device_error), &zero, sizeof zero, 0, hipMemcpyHostToDevice,
                                       stream));
     GS_HIP_TRY(hipStreamSynchronize(stream));
-    if (word & kDeviceErrLookBack)
-        return fail(GS_ERR_DEVICE, "gs_device_check: a radix sort partition stopped waiting for its predecessors "
-                                   "(spin limit reached); that sort's output is invalid");
+    const bool sort = word & kDeviceErrSortLookBack, scan = word & kDeviceErrScanLookBack;
+    if (sort || scan)
+        return fail(GS_ERR_DEVICE, "gs_device_check: a partition of %s stopped waiting for its predecessors (spin limit "
+                                   "reached); that call's output is invalid (device error word 0x%x)",
+                    sort && scan ? "a radix sort and of an intersection-count scan"
+                                 : (sort ? "a radix sort" : "an intersection-count scan"),
+                    word);
     return fail(GS_ERR_DEVICE, "gs_device_check: device error word 0x%x", word);
 }
