@@ -30,23 +30,26 @@ constexpr uint32_t kFlagAggregate = 1u << 30; // partition's own count published
 constexpr uint32_t kFlagInclusive = 2u << 30; // count including every earlier partition published
 constexpr uint32_t kValueMask = (1u << 30) - 1;
 
-// Partition shape of a digit pass per key type. Large partitions shorten the look-back walks (device-coherent
-// loads, ~1 us each under load) as long as the CU keeps 16 waves: one 1024-thread workgroup per CU with 14
-// pairs per thread (128 VGPRs, 130 KB of LDS) holds 14336 pairs; measured on 13M and 157M random 45/47-bit keys it
-// beat 256 threads x 28 pairs (two workgroups per CU) by 12% and 16%, 512 x 14 by 3% and 13%, 768 x 18-20 by 1-4%,
-// and 1024 x 12 by 5%; more than 14 pairs per thread spill past 128 VGPRs. Look-back windows of 2, 3 and 4 were
+// Partition shape of a digit pass: Items pairs per thread of a 1024-thread workgroup. Large partitions shorten the
+// look-back walks (device-coherent loads, ~1 us each under load) as long as the CU keeps 16 waves: one workgroup per
+// CU with 14 pairs per thread (128 VGPRs, 130 KB of LDS) holds 14336 pairs; measured on 13M and 157M random 45/47-bit
+// keys it beat 256 threads x 28 pairs (two workgroups per CU) by 12% and 16%, 512 x 14 by 3% and 13%, 768 x 18-20
+// by 1-4%, and 1024 x 12 by 5%; more than 14 pairs per thread spill past 128 VGPRs. 8-byte keys take 13 or 14 pairs
+// per thread, whichever leaves the fuller last round of partitions over the CUs (pass_items; 13 was 2.5% faster on
+// 13M keys, 912 vs 982 partitions on 256 CUs, and 14 was 1.7% faster on 157M). Look-back windows of 2, 3 and 4 were
 // within 1% (2 best). 4-byte keys sort the splats' depths (about a million, every partition in flight at once):
-// 4 or 8 pairs per thread measured the same there.
-template <typename KeyT>
+// 4, 6 or 8 pairs per thread and windows of 2, 3 or 4 measured the same there, wider windows slower.
+template <typename KeyT, int Items>
 struct Tiling {
-    static constexpr int items = sizeof(KeyT) == 8 ? 14 : 4;   // pairs per thread
+    static constexpr int items = Items;                        // pairs per thread
     static constexpr int tile = kThreads * items;              // pairs per partition
     static constexpr int wave_span = kWave * items;            // contiguous pairs owned by one wave
     static constexpr int window = sizeof(KeyT) == 8 ? 2 : 4;   // predecessors inspected per look-back round
 };
-// the smallest partition of any key type sizes the look-back arrays (one status word per digit and partition)
-constexpr int kMinTile = Tiling<uint32_t>::tile < Tiling<uint64_t>::tile ? Tiling<uint32_t>::tile
-                                                                          : Tiling<uint64_t>::tile;
+constexpr int kItems32 = 4;                  // pairs per thread for 4-byte keys
+constexpr int kItems64Min = 13, kItems64Max = 14;
+// the smallest partition of any shape sizes the look-back arrays (one status word per digit and partition)
+constexpr int kMinTile = kThreads * (kItems32 < kItems64Min ? kItems32 : kItems64Min);
 static_assert(kHistCopyWords == kMaxPasses * kRadix, "one histogram copy holds every pass's digits");
 // histogram kernel: keys per thread and per workgroup step
 constexpr int kHistItems = 16;
@@ -175,21 +178,22 @@ __global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__
     }
 }
 
-// One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling<KeyT>);
+// One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling);
 // wave w owns the contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at
 // w * kWaveSpan + i * 64 + l, so (wave, item, lane) order is input order and the per-wave running counts give a
 // stable rank.
 // ids_in == nullptr means the identity (id = input position). status[part][d] holds this pass's look-back
 // words; status_next[part][d] is cleared for the next pass.
-template <typename KeyT, int kDigitBits>
+template <typename KeyT, int kDigitBits, int kPassItems>
 __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const KeyT *__restrict__ keys_in, const int32_t *__restrict__ ids_in, KeyT *__restrict__ keys_out,
     int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ digit_starts,
     uint32_t *__restrict__ part_counter, uint32_t *status, uint32_t *__restrict__ status_next,
     uint32_t spin_limit) {
     constexpr int digit_bits = kDigitBits;
-    constexpr int kItems = Tiling<KeyT>::items, kTile = Tiling<KeyT>::tile, kWaveSpan = Tiling<KeyT>::wave_span;
-    constexpr int kLookWindow = Tiling<KeyT>::window;
+    using T = Tiling<KeyT, kPassItems>;
+    constexpr int kItems = T::items, kTile = T::tile, kWaveSpan = T::wave_span;
+    constexpr int kLookWindow = T::window;
     __shared__ union {
         KeyT keys[kTile];
         int32_t ids[kTile];
@@ -442,6 +446,53 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
                               result_in_b);
 }
 
+// Launches one digit pass of `bits` bits with Items pairs per thread.
+template <typename KeyT, int Items>
+gs_status launch_pass(int bits, dim3 grid, hipStream_t stream, const KeyT *src_k, const int32_t *src_i, KeyT *dk,
+                      int32_t *di, int64_t n, int shift, const uint32_t *starts, uint32_t *counter, uint32_t *status,
+                      uint32_t *status_next, uint32_t spin) {
+    switch (bits) {
+#define GS_PASS(B)                                                                                                  \
+    case B:                                                                                                         \
+        hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B, Items>), grid, dim3(kThreads), 0, stream, src_k, src_i,  \
+                           dk, di, n, shift, starts, counter, status, status_next, spin);                           \
+        return ok();
+        GS_PASS(1) GS_PASS(2) GS_PASS(3) GS_PASS(4) GS_PASS(5) GS_PASS(6) GS_PASS(7) GS_PASS(8)
+#undef GS_PASS
+        default: return fail(GS_ERR_INVALID_ARG, "radix pass of %d bits", bits);
+    }
+}
+
+// Pairs per thread of the digit passes over n pairs: 4 for 4-byte keys; for 8-byte keys the one of 13 and 14 whose
+// partitions fill the CUs' last round best (cost: rounds of partitions over the CUs times the per-partition work,
+// counted as items plus 3 for the fixed steps of a partition; ties go to 14).
+template <typename KeyT>
+int pass_items(int64_t n) {
+    if (sizeof(KeyT) == 4) return kItems32;
+    static std::atomic<int> cus{0};
+    int c = cus.load(std::memory_order_relaxed);
+    if (c <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                   hipSuccess || c <= 0) {
+            (void)hipGetLastError();
+            c = 256;
+        }
+        cus.store(c, std::memory_order_relaxed);
+    }
+    int best = kItems64Max;
+    int64_t best_cost = -1;
+    for (int items = kItems64Max; items >= kItems64Min; --items) {
+        const int64_t parts = (n + int64_t(kThreads) * items - 1) / (int64_t(kThreads) * items);
+        const int64_t cost = (parts + c - 1) / c * (items + 3);
+        if (best_cost < 0 || cost < best_cost) {
+            best = items;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <typename KeyT>
 gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                        KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
@@ -460,28 +511,31 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
     const uint32_t spin = spin_limit();
+    const int items = pass_items<KeyT>(n);
     for (int p = 0; p < plan.passes; ++p) {
         const bool to_a = (p % 2) == 0;
         KeyT *dk = to_a ? buf_a_keys : buf_b_keys;
         int32_t *di = to_a ? buf_a_ids : buf_b_ids;
         uint32_t *st = status[p & 1];
         uint32_t *st_next = (p + 1 < plan.passes) ? status[(p + 1) & 1] : nullptr;
-        const int64_t parts = (n + Tiling<KeyT>::tile - 1) / Tiling<KeyT>::tile;
+        const int64_t tile = int64_t(kThreads) * items;
+        const int64_t parts = (n + tile - 1) / tile;
         if (parts > L.parts)  // the look-back arrays hold L.parts partitions of 256 words
             return fail(GS_ERR_INVALID_ARG, "radix pass: %lld partitions exceed the look-back arrays (%lld)",
                         (long long)parts, (long long)L.parts);
-        const dim3 grid(static_cast<unsigned>(parts)), block(kThreads);
+        const dim3 grid(static_cast<unsigned>(parts));
         const uint32_t *h = starts + p * kRadix;
-        switch (plan.bits[p]) {
-#define GS_PASS(B)                                                                                                  \
-    case B:                                                                                                         \
-        hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B>), grid, block, 0, stream, src_k, src_i, dk, di, n,       \
-                           plan.shift[p], h, counters + p, st, st_next, spin);                                     \
-        break;
-            GS_PASS(1) GS_PASS(2) GS_PASS(3) GS_PASS(4) GS_PASS(5) GS_PASS(6) GS_PASS(7) GS_PASS(8)
-#undef GS_PASS
-            default: return fail(GS_ERR_INVALID_ARG, "radix pass of %d bits", plan.bits[p]);
-        }
+        gs_status st_launch;
+        if constexpr (sizeof(KeyT) == 4)
+            st_launch = launch_pass<KeyT, kItems32>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n, plan.shift[p],
+                                                    h, counters + p, st, st_next, spin);
+        else if (items == kItems64Min)
+            st_launch = launch_pass<KeyT, kItems64Min>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
+                                                       plan.shift[p], h, counters + p, st, st_next, spin);
+        else
+            st_launch = launch_pass<KeyT, kItems64Max>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
+                                                       plan.shift[p], h, counters + p, st, st_next, spin);
+        if (st_launch != GS_OK) return st_launch;
         GS_LAUNCH_TRY("onesweep_pass_kernel");
         src_k = dk;
         src_i = di;
