@@ -75,6 +75,9 @@ def parse():
                     help="frames in flight at once on separate streams and host threads in the timed steps "
                          "(1 = one at a time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=0,
+                    help="runs per oracle stage in the CPU baseline, median reported (0: 3 for the three smaller "
+                         "workloads, 1 for the two largest)")
     ap.add_argument("--cpu-tile-stride", type=int, default=4,
                     help="CPU baseline composites every k-th tile (then scales to the frame)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -152,10 +155,10 @@ def stage_bytes(scene, n, tile_passes, generic_passes):
     pixels = scene.C * scene.width * scene.height
     K = scene.colors.shape[-1]
     return {
-        # phase 1: counts (means, radii -> counts; counts -> offsets), then the depth order of the splats (one
-        # 4-byte histogram read, 4 passes of 4-byte keys and ids read and written) and the offsets in that order
-        # (the order and two offsets per splat read by each of two kernels, offsets written)
-        "count_depth_order": M * (8 + rb + 4) + M * (4 + 4) + M * (4 + 4 * 16) + M * (2 * (4 + 8) + 4),
+        # phase 1: the count scan (means, radii and depths read once, counts and offsets written), the depth order
+        # of the splats (4 passes of 4-byte keys and ids read and written) and the offsets in that order (the order
+        # read, a count per splat gathered, the offset written)
+        "count_depth_order": M * (8 + rb + 4 + 4 + 4) + M * 4 * 16 + M * (4 + 4 + 4),
         # phase 2: emission in depth order (order, depth bits, offset, mean, radius per splat; 12 bytes per
         # intersection written; the digit histograms are built on the way) and tile_passes passes of 24 B per
         # intersection
@@ -214,51 +217,82 @@ def measured_traffic(config):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(scene, stride):
-    """The oracle as it stands (single thread): intersections, sort and offsets on the whole frame, the composite
-    on every stride-th tile, scaled to the frame."""
+def _cpu_mask():
+    """The host's logical CPU count and this process's affinity mask, as ranges ("0-15")."""
+    try:
+        cpus = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        cpus = list(range(os.cpu_count() or 1))
+    runs, start = [], None
+    for i, c in enumerate(cpus):
+        if start is None:
+            start = c
+        if i + 1 == len(cpus) or cpus[i + 1] != c + 1:
+            runs.append(f"{start}-{c}" if c != start else f"{c}")
+            start = None
+    return os.cpu_count(), ",".join(runs)
+
+
+def _oracle_stages(scene, tiles, openmp, reps):
+    """Per-stage wall times of the oracle on the frame (median over reps runs, each stage timed on its own):
+    count + scan, emission, sort, tile offsets over the whole frame, and the composite on the given tiles."""
     import numpy as np
     import oracle
-    t0 = time.perf_counter()
-    it = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
-                            scene.tile_height, sort=True)
-    off = oracle.tile_offsets(it.keys, scene.C, scene.tile_width, scene.tile_height)
-    t1 = time.perf_counter()
-    tiles = np.arange(0, off.size, stride, dtype=np.int64)
-    ras = oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
-                               scene.width, scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects,
-                               scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold, tiles=tiles)
-    t2 = time.perf_counter()
-    frame_s = (t1 - t0) + (t2 - t1) * off.size / tiles.size
-    pixels = scene.C * scene.width * scene.height
-    return {
-        "value": pixels / frame_s / 1e6, "unit": "Mpix/s", "cores": 1, "kind": "oracle",
-        "sample": f"whole frame for intersections+sort+offsets ({t1 - t0:.2f} s), composite on every {stride}-th "
-                  f"tile ({tiles.size} of {off.size}, {t2 - t1:.2f} s) scaled to all tiles; single thread",
-        "frame_s_estimate": round(frame_s, 3), "isect_sort_offsets_s": round(t1 - t0, 3),
-        "keys_sorted_per_s": it.n_isects / (t1 - t0),
-    }, (it, off, tiles, t1 - t0)
+    runs = []
+    for _ in range(reps):
+        tm = {}
+        it = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                                scene.tile_height, sort=True, openmp=openmp, timings=tm)
+        t0 = time.perf_counter()
+        off = oracle.tile_offsets(it.keys, scene.C, scene.tile_width, scene.tile_height)
+        t1 = time.perf_counter()
+        oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds,
+                             scene.width, scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects,
+                             scene.alpha_cutoff, scene.alpha_clamp, scene.transmittance_threshold,
+                             tiles=tiles if tiles is not None else np.arange(0, off.size, 1, dtype=np.int64),
+                             openmp=openmp)
+        t2 = time.perf_counter()
+        tm.update(offsets_s=t1 - t0, composite_sample_s=t2 - t1)
+        runs.append(tm)
+    return {k: statistics.median(r[k] for r in runs) for k in runs[0]}, it, off
 
 
-def cpu_baseline_openmp(scene, sample):
-    """The same oracle built with OpenMP over the composite's tiles (the pages' CPU parallelisation) on the same
-    tile sample; intersections, sort and offsets stay single-threaded (the single-thread time above is reused)."""
-    import oracle
-    it, off, tiles, isect_s = sample
-    t0 = time.perf_counter()
-    oracle.rasterize_fwd(scene.means2d, scene.conics, scene.colors, scene.opacities, scene.backgrounds, scene.width,
-                         scene.height, scene.tile_size, off, it.flatten_ids, it.n_isects, scene.alpha_cutoff,
-                         scene.alpha_clamp, scene.transmittance_threshold, tiles=tiles, openmp=True)
-    comp_s = time.perf_counter() - t0
-    frame_s = isect_s + comp_s * off.size / tiles.size
-    threads = oracle.threads(openmp=True)
+def _cpu_report(scene, st, it, off, tiles, threads, kind, reps):
+    composite_s = st["composite_sample_s"] * off.size / tiles.size
+    isect_s = st["count_scan_s"] + st["emit_s"] + st["sort_s"] + st["offsets_s"]
+    frame_s = isect_s + composite_s
+    nproc, mask = _cpu_mask()
     return {
         "value": scene.C * scene.width * scene.height / frame_s / 1e6, "unit": "Mpix/s", "cores": threads,
-        "kind": "oracle (OpenMP build)",
-        "sample": f"composite on the same {tiles.size} tiles with {threads} threads ({comp_s:.2f} s) scaled to all "
-                  f"tiles, plus the single-thread intersections+sort+offsets ({isect_s:.2f} s)",
+        "kind": kind,
+        "sample": f"median of {reps} runs per stage: count+scan, emission, sort and tile offsets over the whole frame, "
+                  f"the composite on every {off.size // tiles.size}-th tile ({tiles.size} of {off.size}) scaled to "
+                  f"all tiles; {threads} thread(s)",
         "frame_s_estimate": round(frame_s, 3),
+        "stages_s": {"count_scan": round(st["count_scan_s"], 4), "emit": round(st["emit_s"], 4),
+                     "sort": round(st["sort_s"], 4), "tile_offsets": round(st["offsets_s"], 4),
+                     "composite_scaled": round(composite_s, 3)},
+        "keys_sorted_per_s": it.n_isects / st["sort_s"] if st["sort_s"] > 0 else None,
+        "isect_sort_offsets_s": round(isect_s, 3),
+        "host_nproc": nproc, "affinity": mask, "reps": reps,
     }
+
+
+def cpu_baseline(scene, stride, reps):
+    """The oracle as it stands, single thread: every stage timed, median of reps runs (see _oracle_stages)."""
+    import numpy as np
+    import oracle
+    tiles = np.arange(0, scene.C * scene.tile_width * scene.tile_height, stride, dtype=np.int64)
+    st, it, off = _oracle_stages(scene, tiles, False, reps)
+    return _cpu_report(scene, st, it, off, tiles, oracle.threads(openmp=False), "oracle", reps), tiles
+
+
+def cpu_baseline_openmp(scene, tiles, reps):
+    """The same oracle built with OpenMP (the pages' CPU parallelisation: emission and the sort's merges over
+    splats, the composite over tiles with dynamic scheduling) on the host's threads, same stages and tile sample."""
+    import oracle
+    st, it, off = _oracle_stages(scene, tiles, True, reps)
+    return _cpu_report(scene, st, it, off, tiles, oracle.threads(openmp=True), "oracle (OpenMP build)", reps)
 
 
 def main():
@@ -549,8 +583,9 @@ def main():
     if args.valu_calibration:
         result["valu_calibration"] = valu_calibration(plan.stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], sample = cpu_baseline(scene, args.cpu_tile_stride)
-        result["cpu_baseline_openmp"] = cpu_baseline_openmp(scene, sample)
+        reps = args.cpu_reps if args.cpu_reps > 0 else (3 if args.config in ("config1", "config2", "config3") else 1)
+        result["cpu_baseline"], sample = cpu_baseline(scene, args.cpu_tile_stride, reps)
+        result["cpu_baseline_openmp"] = cpu_baseline_openmp(scene, sample, reps)
     print(json.dumps(result), flush=True)
 
 

@@ -145,9 +145,12 @@ class Isect:
     n_isects: int
 
 
-def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True, openmp=False) -> Isect:
+def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort=True, openmp=False,
+                timings=None) -> Isect:
     """Intersections of every (camera, splat) with the tile grid, as the pages' isect_tiles returns them.
-    openmp: the OpenMP build (emission and the sort's merges on the host's threads; the same result)."""
+    openmp: the OpenMP build (emission and the sort's merges on the host's threads; the same result).
+    timings: a dict that receives the wall time of each step in seconds (count_scan_s, emit_s, sort_s)."""
+    import time
     lib = _load(openmp)
     means2d = _c(means2d, np.float32)
     radii = _c(radii, np.float32)
@@ -156,17 +159,23 @@ def isect_tiles(means2d, radii, depths, tile_size, tile_width, tile_height, sort
     rpg = 2 if radii.ndim == 3 else 1
     tiles_per = np.zeros((C, N), np.int32)
     goff = np.zeros(C * N, np.int64)
+    t0 = time.perf_counter()
     n = int(lib.orc_isect_count(_p(means2d), _p(radii), rpg, C, N, tile_size, tile_width, tile_height,
                                 _p(tiles_per), _p(goff)))
+    t1 = time.perf_counter()
     keys = np.zeros(n, np.uint64)
     ids = np.zeros(n, np.int32)
     if lib.orc_isect_emit(_p(means2d), _p(radii), rpg, _p(depths), C, N, tile_size, tile_width, tile_height,
                           _p(keys), _p(ids)) != OK:
         raise MemoryError("oracle emission allocation failed")
+    t2 = time.perf_counter()
     if sort and n > 1:
         rc = lib.orc_sort_pairs(_p(keys), _p(ids), n)
         if rc != OK:
             raise MemoryError("oracle sort allocation failed")
+    t3 = time.perf_counter()
+    if timings is not None:
+        timings.update(count_scan_s=t1 - t0, emit_s=t2 - t1, sort_s=t3 - t2)
     return Isect(tiles_per, goff, keys, ids, n)
 
 
