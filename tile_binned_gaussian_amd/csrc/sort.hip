@@ -156,26 +156,23 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
 }
 
 // Global start of every digit bucket of every pass: for pass p and digit d, the number of keys whose digit p is
-// below d, summed over the histogram copies. One workgroup, one thread per digit; computed once per sort, so a
-// digit pass's partitions only load their digit's start (off their critical path) instead of each summing the
-// copies and scanning them.
-__global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__restrict__ hist, int passes,
+// below d, summed over the histogram copies. One workgroup of 256 threads per pass (blockIdx.x = p), one thread per
+// digit; computed once per sort, so a digit pass's partitions only load their digit's start (off their critical
+// path) instead of each summing the copies and scanning them.
+__global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__restrict__ hist,
                                                           uint32_t *__restrict__ starts) {
     __shared__ uint32_t s_w[kRadix / kWave];
-    const int d = threadIdx.x, wave = d / kWave, lane = __lane_id();
-    for (int p = 0; p < passes; ++p) {
-        uint32_t c = 0;
+    const int p = blockIdx.x, d = threadIdx.x, wave = d / kWave, lane = __lane_id();
+    uint32_t c = 0;
 #pragma unroll
-        for (int k = 0; k < kHistCopies; ++k) c += hist[k * kHistCopyWords + p * kRadix + d];
-        const uint32_t inc = wave_inclusive_sum(c);
-        __syncthreads();  // the previous pass's reads of s_w are done
-        if (lane == kWave - 1) s_w[wave] = inc;
-        __syncthreads();
-        uint32_t before = 0;
+    for (int k = 0; k < kHistCopies; ++k) c += hist[k * kHistCopyWords + p * kRadix + d];
+    const uint32_t inc = wave_inclusive_sum(c);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
 #pragma unroll
-        for (int w = 0; w < kRadix / kWave; ++w) before += w < wave ? s_w[w] : 0u;
-        starts[p * kRadix + d] = before + inc - c;
-    }
+    for (int w = 0; w < kRadix / kWave; ++w) before += w < wave ? s_w[w] : 0u;
+    starts[p * kRadix + d] = before + inc - c;
 }
 
 // One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling);
@@ -505,7 +502,7 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
     uint32_t *status[2] = {reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1)};
     uint32_t *starts = reinterpret_cast<uint32_t *>(ws + L.starts);
-    hipLaunchKernelGGL(digit_starts_kernel, dim3(1), dim3(kRadix), 0, stream, hist, plan.passes, starts);
+    hipLaunchKernelGGL(digit_starts_kernel, dim3(plan.passes), dim3(kRadix), 0, stream, hist, starts);
     GS_LAUNCH_TRY("digit_starts_kernel");
 
     const KeyT *src_k = keys_in;
