@@ -73,22 +73,24 @@ def test_frame_path_reports_no_error_at_the_default_limit():
 
 
 def test_zero_spin_limit_in_the_count_scans_is_reported():
-    """Phase 1 (the count scan, the depth sort, the scan of the counts in depth order) and the tile sort of a
-    4M-splat frame at a zero limit: some partition gives up and the check says so; every kernel finishes and every
-    write stays in the buffers (the outputs are then meaningless and not compared). The default limit then gives a
-    frame with nothing to report again."""
-    from tile_binned_gaussian_amd import synth
+    """Phase 1 of a 4M-splat frame (the count scan, the depth sort and the scan of the counts in depth order) at a zero
+    limit: some partition gives up and the check says so; every kernel of the phase finishes and every write stays
+    in its buffer (the counts and order are then meaningless and not compared, and nothing is run on them). The
+    default limit then gives a whole frame with nothing to report."""
+    from tile_binned_gaussian_amd import frame, synth
     from gpu_util import gpu_frame
-    ds = synth.random_scene(seed=5, C=1, N=4 << 20, width=1920, height=1080, tile_size=16)
+    scene = synth.random_scene(seed=5, C=1, N=4 << 20, width=1920, height=1080, tile_size=16)
+    plan = frame.FramePlan(frame.to_device(scene))
+    stream = binding._stream(plan.stream)
     binding.gs_device_check()
     prev = binding.gs_set_spin_limit(0)
     gave_up = False
     try:
         for attempt in range(3):
-            print(f"zero-limit frame attempt {attempt}: N={ds.N}", flush=True)
-            gpu_frame(ds)
+            print(f"zero-limit phase 1 attempt {attempt}: N={scene.N}", flush=True)
+            plan._count(stream)
             try:
-                binding.gs_device_check()
+                binding.gs_device_check(plan.stream)
             except binding.GsError as e:
                 assert e.status == binding.GS_ERR_DEVICE
                 assert "spin limit" in str(e)
@@ -96,7 +98,9 @@ def test_zero_spin_limit_in_the_count_scans_is_reported():
                 break
     finally:
         binding.gs_set_spin_limit(prev)
-    assert gave_up, "no partition gave up with a zero spin limit in 3 frames of 4M splats"
+    assert gave_up, "no partition gave up with a zero spin limit in 3 runs of phase 1 over 4M splats"
+    del plan
+    torch.cuda.synchronize()
     binding.gs_device_check()
-    gpu_frame(ds)
+    gpu_frame(scene)
     binding.gs_device_check()

@@ -221,7 +221,8 @@ __global__ __launch_bounds__(kScanThreads) void order_scan_kernel(const int32_t 
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int j = j0 + i * kScanThreads;
-        v[i] = r[i].z * r[i].w;
+        // a rectangle from a workspace that phase 1 did not fill still gives a count >= 0
+        v[i] = static_cast<int64_t>(max(r[i].z, 0)) * static_cast<int64_t>(max(r[i].w, 0));
         if (j < M) sorted_rects[j] = r[i];
     }
     const int64_t aggregate = scan_items_exclusive(v, s_part_sums, &s_total);
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
             const int w = max(s_w[threadIdx.x], 1);
             s_w[threadIdx.x] = w;
             s_rcp_w[threadIdx.x] = 1.0f / static_cast<float>(w);
-            s_start[threadIdx.x] = gauss_offsets[j];
+            s_start[threadIdx.x] = min(max(gauss_offsets[j], 0), n);
             s_depth[threadIdx.x] = sorted_depth ? sorted_depth[j] : depth_bits[i];
             s_upper_cam[threadIdx.x] = static_cast<uint32_t>(i / N) << tile_bits;
             s_id[threadIdx.x] = i;
@@ -311,10 +312,14 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
             s_depth[threadIdx.x] = s_upper_cam[threadIdx.x] = 0;
             s_id[threadIdx.x] = 0;
         }
-        if (threadIdx.x == 0) s_start[kThreads] = (g0 + kThreads < M) ? gauss_offsets[g0 + kThreads] : n;
+        if (threadIdx.x == 0)
+            s_start[kThreads] = (g0 + kThreads < M) ? min(max(gauss_offsets[g0 + kThreads], 0), n) : n;
         __syncthreads();
-        // clamped to [0, n] so that offsets inconsistent with n can never address past the outputs
-        const int out_end = min(s_start[kThreads], n);
+        // Every start is clamped to [0, n] as it is loaded, so offsets inconsistent with n (a workspace that phase 1
+        // did not fill, or a wait that gave up) can never address outside the outputs: every slot written lies in
+        // [out_begin, out_end), within [0, n). They are then not ordered either, so the search below may land on any
+        // position of the chunk; it still reads only s_start[0 .. 255] and the key it builds is merely wrong.
+        const int out_end = s_start[kThreads];
         const int out_begin = min(s_start[0], out_end);
         // every lane runs every round (the histogram's neighbour exchange needs the whole wave)
         for (int round = out_begin; round < out_end; round += kThreads) {
