@@ -16,6 +16,38 @@ __device__ __forceinline__ uint32_t *hist_copy(uint32_t *hist, unsigned block) {
     return hist + static_cast<size_t>(block % kHistCopies) * kHistCopyWords;
 }
 
+// Digit counting by runs. Lanes holding consecutive keys compare a digit with the previous lane's, and each run
+// of equal digits is added to an LDS histogram once, by its first lane, as its length: keys that share a digit
+// (one splat's intersections share their depth bits) then cost one LDS atomic per run instead of one per key.
+// The two halves of the wave (lanes 0-31 and 32-63) are counted apart, so a run's length is found in one 32-bit
+// word: its first lane shifts the 64-bit mask of run starts right by lane + 1, which puts lane (lane + 1 + k) at
+// bit k. A lower-half run ends at the latest at lane 32 (always marked a start); an upper-half run ends at the
+// latest at the wave's end, which a per-lane sentinel bit at the position of lane 64 marks.
+struct RunLanes {
+    uint32_t shift;     // lane + 1, and 63 for lane 63 (its own start bit, set whenever it counts, lands at bit 0)
+    uint32_t sentinel;  // 1 << (63 - lane) in lanes 32..63, 0 in lanes 0..31
+    bool first;         // lanes 0 and 32 start a run whatever their digit
+};
+__device__ __forceinline__ RunLanes run_lanes() {
+    const uint32_t lane = __lane_id();
+    return {lane < 63u ? lane + 1u : 63u, lane >= 32u ? 1u << (63u - lane) : 0u, lane == 0u || lane == 32u};
+}
+// Adds the wave's digits d to the LDS histogram hist. The whole wave must call it together (it reads the previous
+// lane's digit); a lane with in == false holds no key, adds nothing and must hold a digit no key can have
+// (0xffffffff), so that it never extends a run.
+__device__ __forceinline__ void wave_add_runs(uint32_t *hist, uint32_t d, bool in, const RunLanes &rl) {
+    // the previous lane's digit (a whole-wave shift right by one lane; lane 0 reads 0 and is a start anyway)
+    const uint32_t prev = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d), 0x138, 0xf, 0xf, true));
+    const bool differs = d != prev;
+    // the ballot of the comparison alone stays one compare; lanes 0 and 32 are or-ed in as constants
+    const uint64_t starts = __builtin_amdgcn_ballot_w64(differs) | 0x0000000100000001ull;
+    if ((differs | rl.first) & in) {  // bitwise: a short-circuit turns into branches
+        // nonzero: bit 32 of starts (lower half) or the sentinel (upper half) bounds the run
+        const uint32_t later = static_cast<uint32_t>(starts >> rl.shift) | rl.sentinel;
+        atomicAdd(&hist[d], static_cast<uint32_t>(__builtin_ctz(later)) + 1u);
+    }
+}
+
 // Digit passes over bits [begin_bit, end_bit): pass p sorts `bits[p]` bits starting at `shift[p]`.
 struct PassPlan {
     int passes;

@@ -272,8 +272,7 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
     __shared__ int s_x0[kThreads], s_y0[kThreads], s_w[kThreads], s_id[kThreads];
     __shared__ float s_rcp_w[kThreads];
     __shared__ uint32_t s_upper_cam[kThreads], s_depth[kThreads];
-    const int lane = __lane_id();
-    const uint64_t above_mask = lane == kWave - 1 ? 0ull : (~0ull << (lane + 1));
+    const RunLanes rl = run_lanes();
     if (hist)
         for (int p = 0; p < hplan.passes; ++p) s_hist[p][threadIdx.x] = 0;
     const int chunks = (M + kThreads - 1) / kThreads;
@@ -345,20 +344,15 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                 ids[slot] = s_id[lo];
             }
             if (hist) {
-                // consecutive lanes hold consecutive slots: a run of equal digits adds its length once
+                // consecutive lanes hold consecutive slots: a run of equal digits adds its length once; every
+                // digit of hplan lies in the key's upper word (its shifts are at least 32, checked on the host)
+                const uint32_t upper32 = static_cast<uint32_t>(upper);
 #pragma unroll
                 for (int p = 0; p < kMaxPasses; ++p) {
                     if (p >= hplan.passes) break;
                     const uint32_t d =
-                        in ? static_cast<uint32_t>(key >> hplan.shift[p]) & ((1u << hplan.bits[p]) - 1u) : 0xffffffffu;
-                    const uint32_t prev = __builtin_amdgcn_update_dpp(0xffffffffu, d, 0x138, 0xf, 0xf, false);
-                    const bool start = lane == 0 || d != prev;
-                    const uint64_t starts = __ballot(start);
-                    if (start && in) {
-                        const uint64_t later = starts & above_mask;
-                        const int next = later ? __builtin_ctzll(later) : kWave;
-                        atomicAdd(&s_hist[p][d], static_cast<uint32_t>(next - lane));
-                    }
+                        in ? (upper32 >> (hplan.shift[p] - 32)) & ((1u << hplan.bits[p]) - 1u) : 0xffffffffu;
+                    wave_add_runs(s_hist[p], d, in, rl);
                 }
             }
         }
@@ -468,11 +462,17 @@ gs_status launch_count_scan(int rpg, const float2 *m2, const float *radii, const
     return ok();
 }
 
-// hist (nullable): accumulate the digit histograms of the emitted keys for the passes of hplan.
+// hist (nullable): accumulate the digit histograms of the emitted keys for the passes of hplan, whose digits must
+// all lie in the keys' upper words (bits 32..63).
 gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
                       int tw, int th, int tile_bits, const int32_t *perm, const uint32_t *sorted_depth,
                       const int4 *sorted_rects, const int32_t *offsets, int n, uint64_t *keys, int32_t *ids,
                       uint32_t *hist, const PassPlan &hplan, hipStream_t stream) {
+    if (hist)
+        for (int p = 0; p < hplan.passes; ++p)
+            if (hplan.shift[p] < 32 || hplan.shift[p] + hplan.bits[p] > 64)
+                return fail(GS_ERR_INVALID_ARG, "emission histogram pass %d over bits [%d, %d) outside the upper word", p,
+                            hplan.shift[p], hplan.shift[p] + hplan.bits[p]);
     const int chunks = (M + kThreads - 1) / kThreads;
     const int blocks = chunks < kEmitBlocks ? chunks : kEmitBlocks;
     if (rpg == 2)

@@ -106,17 +106,30 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t *s_
 constexpr int64_t kHistBlocksMin = 2048, kHistBlocksMax = 4096, kHistTilesPerBlock = 8;
 
 // Digit histograms of every pass. Each thread holds 16 keys read lane-contiguous (consecutive lanes hold
-// consecutive keys). Per pass, a lane whose digit differs from the previous lane's starts a run, and only run
-// starts add to the LDS histogram (the run length), so keys that share digits - one splat's intersections share
-// their depth bits - cost one LDS atomic per run.
+// consecutive keys), and every pass's digits are counted by runs (wave_add_runs), so keys that share digits - one
+// splat's intersections share their depth bits - cost one LDS atomic per run. Every tile but the last is full and
+// is counted without the per-key bounds test.
+template <typename KeyT, bool kFull>
+__device__ __forceinline__ void count_tile_digits(const KeyT (&k)[kHistItems], int valid, const PassPlan &plan,
+                                                  uint32_t (&s_hist)[kMaxPasses][kRadix], const RunLanes &rl) {
+    for (int p = 0; p < plan.passes; ++p) {
+        const int shift = plan.shift[p];
+        const uint32_t mask = (1u << plan.bits[p]) - 1u;
+#pragma unroll
+        for (int i = 0; i < kHistItems; ++i) {
+            const bool in = kFull || i * kHistThreads + static_cast<int>(threadIdx.x) < valid;
+            const uint32_t d = in ? digit_of(k[i], shift, mask) : 0xffffffffu;
+            wave_add_runs(s_hist[p], d, in, rl);
+        }
+    }
+}
+
 template <typename KeyT>
 __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__restrict__ keys, int64_t n,
                                                              PassPlan plan, uint32_t *__restrict__ hist) {
     __shared__ uint32_t s_hist[kMaxPasses][kRadix];
     for (int p = 0; p < plan.passes; ++p) s_hist[p][threadIdx.x] = 0;
-    const int lane = __lane_id();
-    // bits above this lane, for the distance to the next run start
-    const uint64_t above_mask = lane == kWave - 1 ? 0ull : (~0ull << (lane + 1));
+    const RunLanes rl = run_lanes();
     const int64_t tiles = (n + kHistTile - 1) / kHistTile;
     __syncthreads();
     for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
@@ -128,24 +141,10 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
             const int q = i * kHistThreads + threadIdx.x;
             k[i] = q < valid ? keys[base + q] : KeyT(0);
         }
-        for (int p = 0; p < plan.passes; ++p) {
-            const int shift = plan.shift[p];
-            const uint32_t mask = (1u << plan.bits[p]) - 1u;
-#pragma unroll
-            for (int i = 0; i < kHistItems; ++i) {
-                const bool in = i * kHistThreads + static_cast<int>(threadIdx.x) < valid;
-                const uint32_t d = in ? digit_of(k[i], shift, mask) : 0xffffffffu;
-                // the previous lane's digit (a whole-wave shift right by one lane; lane 0 keeps the all-ones value)
-                const uint32_t prev = __builtin_amdgcn_update_dpp(0xffffffffu, d, 0x138, 0xf, 0xf, false);
-                const bool start = lane == 0 || d != prev;
-                const uint64_t starts = __ballot(start);
-                if (start && in) {
-                    const uint64_t later = starts & above_mask;
-                    const int next = later ? __builtin_ctzll(later) : kWave;
-                    atomicAdd(&s_hist[p][d], static_cast<uint32_t>(next - lane));
-                }
-            }
-        }
+        if (valid == kHistTile)
+            count_tile_digits<KeyT, true>(k, valid, plan, s_hist, rl);
+        else
+            count_tile_digits<KeyT, false>(k, valid, plan, s_hist, rl);
     }
     __syncthreads();
     uint32_t *copy = hist_copy(hist, blockIdx.x);
