@@ -208,22 +208,20 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     if (tid == 0) s_part = atomicAdd(part_counter, 1u);
     for (int i = tid; i < kWaves * kRadix; i += kThreads) (&s_wave_hist[0][0])[i] = 0;
     __syncthreads();
-    const uint32_t part = s_part;
+    const uint32_t part = __builtin_amdgcn_readfirstlane(s_part);  // uniform: the load paths below branch on it
     // the host launches exactly one workgroup per partition; a counter left inconsistent by a corrupted workspace
     // must not address past the arrays (the result is then wrong, but every access stays in bounds)
     if (static_cast<int64_t>(part) * kTile >= n) return;
     // threads [0, kRadix) own digit d = tid for the per-digit steps; the other waves only rank and move pairs
     const bool digit_thread = tid < kRadix;
     const int d = digit_thread ? tid : 0;
-    if (status_next && digit_thread) status_next[static_cast<size_t>(part) * kRadix + d] = 0;
-
-    // global start of this thread's digit bucket for the pass (precomputed once per sort); used only when the
-    // pairs are written, so its load is in flight with the key loads
-    const uint32_t digit_global_start = digit_thread ? digit_starts[d] : 0u;
 
     // load this wave's span of keys (ids are loaded after the keys are written, to keep registers free)
     const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan + lane;
     const bool full = static_cast<int64_t>(part + 1) * kTile <= n;
+    // Both kinds of partition issue the same kItems loads in the same order (a partial one clamps its addresses to
+    // the last pair, then replaces what lies past the end), so the ranking of each item waits for its own load
+    // only, not for the whole span.
     KeyT k[kItems];
     if (full) {
 #pragma unroll
@@ -232,9 +230,19 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
 #pragma unroll
         for (int i = 0; i < kItems; ++i) {
             const int64_t pos = base + i * kWave;
-            k[i] = pos < n ? keys_in[pos] : ~KeyT(0);  // past the end: largest digit, ranked after every real pair
+            k[i] = keys_in[pos < n ? pos : n - 1];
         }
     }
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < kItems; ++i)
+            if (base + i * kWave >= n) k[i] = ~KeyT(0);  // past the end: largest digit, ranked after every real pair
+    }
+    // issued after the key loads, so that nothing waits for them before the keys are requested
+    if (status_next && digit_thread) status_next[static_cast<size_t>(part) * kRadix + d] = 0;
+    // global start of this thread's digit bucket for the pass (precomputed once per sort); used only when the
+    // pairs are written, so its load is in flight with the key loads
+    const uint32_t digit_global_start = digit_thread ? digit_starts[d] : 0u;
 
 
     // stable rank within the wave: the lanes holding the same digit, from one ballot per digit bit. A lane's
