@@ -308,7 +308,35 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         lp[i] = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
         s_buf.keys[lp[i]] = k[i];
     }
-    // the ids travel with the keys; load them while the look-back is in flight
+    // decoupled look-back for digit d: walk back over the predecessors' published counts, a window of kLookWindow
+    // at a time, until one carries an inclusive count (partition 0 always does). The wait is bounded: after
+    // spin_limit rounds without finding one the partition gives up, flags the device error word and publishes
+    // what it has, so that every later partition also finishes (the pass's output is then invalid, and every
+    // write still stays inside the arrays).
+    // Adds the window's published counts up to the first unpublished word or the inclusive one; `used` = words
+    // consumed, the result = whether an inclusive count was among them.
+    auto consume = [&](uint32_t &sum, int &used) {
+        bool found = false;
+        used = 0;
+#pragma unroll
+        for (int w = 0; w < kLookWindow; ++w) {
+            if (found || used < w) continue;
+            const uint32_t flag = s[w] & ~kValueMask;
+            if (flag == 0) continue;
+            sum += s[w] & kValueMask;
+            used = w + 1;
+            if (flag == kFlagInclusive) found = true;
+        }
+        return found;
+    };
+    uint32_t before = 0;
+    const bool looks_back = part > 0 && digit_thread;
+    int used = 0;
+    // The first window (requested before the local scan) is inspected before the ids are requested, so that this
+    // inspection waits for the status words only; a wait placed after the id loads would also wait for them.
+    bool found = !looks_back || consume(before, used);
+
+    // the ids travel with the keys; load them while the rest of the look-back is in flight
     int32_t v[kItems];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
@@ -317,27 +345,9 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         else v[i] = static_cast<int32_t>(pos);
     }
 
-    // decoupled look-back for digit d: walk back over the predecessors' published counts, a window of kLookWindow
-    // at a time, until one carries an inclusive count (partition 0 always does). The wait is bounded: after
-    // spin_limit rounds without finding one the partition gives up, flags the device error word and publishes
-    // what it has, so that every later partition also finishes (the pass's output is then invalid, and every
-    // write still stays inside the arrays).
-    uint32_t before = 0;
-    if (part > 0 && digit_thread) {
+    if (looks_back) {
         uint32_t rounds = 0;
-        while (true) {
-            int used = 0;
-            bool found = false;
-#pragma unroll
-            for (int w = 0; w < kLookWindow; ++w) {
-                if (found || used < w) continue;  // stop at the first unpublished word or the inclusive one
-                const uint32_t flag = s[w] & ~kValueMask;
-                if (flag == 0) continue;
-                before += s[w] & kValueMask;
-                used = w + 1;
-                if (flag == kFlagInclusive) found = true;
-            }
-            if (found) break;
+        while (!found) {
             if (rounds++ >= spin_limit) {
                 atomicOr(&g_device_error, kDeviceErrSortLookBack);
                 break;
@@ -348,6 +358,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
             for (int w = 0; w < kLookWindow; ++w)
                 s[w] = (j - w >= 0) ? atomic_load_agent(status + static_cast<size_t>(j - w) * kRadix + d)
                                     : kFlagInclusive;
+            found = consume(before, used);
         }
         atomic_store_agent(my_status, kFlagInclusive | (before + part_count));
     }
