@@ -10,7 +10,8 @@ Frames are independent, so the timed steps keep --frames-in-flight frames in fli
 by its own host thread (each frame whole, on its own buffers): one frame's latency-bound intersection chain
 overlaps another's compositing. The
 per-frame latency with one frame at a time is measured first and reported beside the throughput, with the
-per-stage times.
+per-stage times. Before each timed part the frame runs untimed for a quarter of a second (settle), so that a short
+run measures the settled device rather than its first frames after an idle start.
 
     python bench.py [--steps K] [--warmup W] [--config config3] [--frames-in-flight F] [--no-cpu-baseline]
 
@@ -146,6 +147,23 @@ def valu_calibration(stream):
             "wave_instructions_per_simd_cycle": round(16 * 1024 * waves / simds / (dt * shader_hz), 4),
             "shader_clock_GHz": round(shader_hz / 1e9, 4)}
     return res
+
+
+SETTLE_S = 0.25
+
+
+def settle(run):
+    """Untimed frames for at least SETTLE_S seconds before a warm-up and its timed steps: the device idles while
+    the process starts and allocates, and its first ~20 ms of frames after an idle period run up to 15% slower (a
+    kernel trace shows the composite falling from ~430 to ~380 us over them), so a short timed run would otherwise
+    measure that transition. Returns the milliseconds spent."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        run()
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
 
 
 def stage_bytes(scene, n, tile_passes, generic_passes):
@@ -319,9 +337,12 @@ def main():
     torch.cuda.synchronize()
     n_eval, n_pass, n_comp, n_exec, n_staged = (int(v) for v in counts.cpu())
 
+    # the timing events exist before the warm-up, so that nothing leaves the device idle between the warm-up and
+    # the timed frames
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    settle_ms = settle(plan.run)
     for _ in range(args.warmup):
         plan.run()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -341,6 +362,7 @@ def main():
         ms_per_step = latency_ms
     else:
         flight = [frame.FramePlan(ds, stream=torch.cuda.Stream()) for _ in range(F)]
+        settle(lambda: [p.run() for p in flight])
         for k in range(max(args.warmup, F)):
             flight[k % F].run()
         torch.cuda.synchronize()
@@ -523,6 +545,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
         "ms_per_step": round(ms_per_step, 4),
         "frames_in_flight": F,
         "latency_ms_per_frame": round(latency_ms, 4),

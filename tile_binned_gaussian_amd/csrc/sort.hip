@@ -180,8 +180,9 @@ __global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__
 // w * kWaveSpan + i * 64 + l, so (wave, item, lane) order is input order and the per-wave running counts give a
 // stable rank.
 // ids_in == nullptr means the identity (id = input position). status[part][d] holds this pass's look-back
-// words; status_next[part][d] is cleared for the next pass.
-template <typename KeyT, int kDigitBits, int kPassItems>
+// words; status_next[part][d] is cleared for the next pass. kStream: the pass reads its keys and ids with
+// non-temporal loads (see stream_loads).
+template <typename KeyT, int kDigitBits, int kPassItems, bool kStream>
 __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const KeyT *__restrict__ keys_in, const int32_t *__restrict__ ids_in, KeyT *__restrict__ keys_out,
     int32_t *__restrict__ ids_out, int64_t n, int shift, const uint32_t *__restrict__ digit_starts,
@@ -238,7 +239,8 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     KeyT k[kItems];
     if (full) {
 #pragma unroll
-        for (int i = 0; i < kItems; ++i) k[i] = keys_in[base + i * kWave];
+        for (int i = 0; i < kItems; ++i)
+            k[i] = kStream ? __builtin_nontemporal_load(keys_in + base + i * kWave) : keys_in[base + i * kWave];
     } else {
 #pragma unroll
         for (int i = 0; i < kItems; ++i) {
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const int64_t pos = base + i * kWave;
-        if (ids_in) v[i] = (full || pos < n) ? ids_in[pos] : 0;
+        if (ids_in) v[i] = (full || pos < n) ? (kStream ? __builtin_nontemporal_load(ids_in + pos) : ids_in[pos]) : 0;
         else v[i] = static_cast<int32_t>(pos);
     }
 
@@ -478,16 +480,31 @@ gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
                               result_in_b);
 }
 
+// Whether the passes over n pairs read them with non-temporal loads: for 8-byte keys up to 2^25 pairs (12 bytes
+// each, 402 MB per buffer). A pass's reads then do not displace the pairs the previous pass has just written from
+// the caches, so more of them are still there when this pass's successor reads them. Measured on random 45-bit
+// keys, whole sort: 6% faster at 13M pairs, 10% at 20M, 3% at 32M, and 1% slower at 38M, 4-6% slower at 44-192M
+// (the crossover lies between 32M and 38M); 4-byte keys (1-6M depth keys) within 1% either way, so they stay plain.
+template <typename KeyT>
+bool stream_loads(int64_t n) {
+    return sizeof(KeyT) == 8 && n <= (int64_t(1) << 25);
+}
+
 // Launches one digit pass of `bits` bits with Items pairs per thread.
 template <typename KeyT, int Items>
 gs_status launch_pass(int bits, dim3 grid, hipStream_t stream, const KeyT *src_k, const int32_t *src_i, KeyT *dk,
                       int32_t *di, int64_t n, int shift, const uint32_t *starts, uint32_t *counter, uint32_t *status,
                       uint32_t *status_next, uint32_t spin) {
+    const bool nt = stream_loads<KeyT>(n);
     switch (bits) {
 #define GS_PASS(B)                                                                                                  \
     case B:                                                                                                         \
-        hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B, Items>), grid, dim3(kThreads), 0, stream, src_k, src_i,  \
-                           dk, di, n, shift, starts, counter, status, status_next, spin);                           \
+        if (nt)                                                                                                     \
+            hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B, Items, sizeof(KeyT) == 8>), grid, dim3(kThreads), 0, \
+                               stream, src_k, src_i, dk, di, n, shift, starts, counter, status, status_next, spin); \
+        else                                                                                                        \
+            hipLaunchKernelGGL((onesweep_pass_kernel<KeyT, B, Items, false>), grid, dim3(kThreads), 0, stream,     \
+                               src_k, src_i, dk, di, n, shift, starts, counter, status, status_next, spin);         \
         return ok();
         GS_PASS(1) GS_PASS(2) GS_PASS(3) GS_PASS(4) GS_PASS(5) GS_PASS(6) GS_PASS(7) GS_PASS(8)
 #undef GS_PASS
