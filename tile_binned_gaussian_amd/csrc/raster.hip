@@ -21,6 +21,8 @@ constexpr int kMaxThreads = 256;
 // 4 spills past the 64 registers of 8 waves per SIMD; 4 channels take 2, which fits)
 template <int K>
 constexpr int kUnroll = K > 3 ? 2 : 3;
+// cull word bit of a staged splat that may not take the composite's short step (bits 0-3: the waves it reaches)
+constexpr uint32_t kNotShort = 0x80000000u;
 
 struct RasterArgs {
     const float2 *means;
@@ -46,6 +48,7 @@ struct RasterArgs {
     int trace_vec;                    // trace_ids is 16-byte aligned and max_steps a multiple of 4
     const int32_t *bin_counts;        // nullable: ranges from fixed-capacity bins instead of offsets
     int capacity;                     // bin capacity (bin t occupies ids[t * capacity, (t + 1) * capacity))
+    int short_step;                   // alpha_cutoff >= 1e-20: batches of well-conditioned splats take the short step
 };
 
 // Traced kernels stage each pixel's trace in LDS, kTraceChunk ids per thread, and store a full chunk as four
@@ -270,10 +273,11 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
     const float px = static_cast<float>(x) + 0.5f, py = static_cast<float>(y) + 0.5f;
     const int64_t p = (static_cast<int64_t>(camera) * a.height + y) * a.width + x;
 
-    // pixel-centre boxes of every wave's region (for the cull bits), in pixel coordinates
-    float rx0[kMaxThreads / kWave], rx1[kMaxThreads / kWave], ry0[kMaxThreads / kWave], ry1[kMaxThreads / kWave];
-#pragma unroll
-    for (int w = 0; w < kMaxThreads / kWave; ++w) {
+    // The pixel-centre box of wave w's region (for the cull bits), in pixel coordinates. It is rebuilt from the tile's
+    // origin where it is used rather than kept for all four waves: the 16 floats held across the loop cost the step
+    // its registers (the kernel then spilled).
+    const int tile_x0 = tx * ts, tile_y0 = ty * ts;
+    auto region = [ts, quadrants, tile_x0, tile_y0](int w, float &x0, float &x1, float &y0, float &y1) {
         int qx0, qx1, qy0, qy1;
         if (quadrants) {
             qx0 = (w & 1) * 8;
@@ -286,11 +290,11 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             qy0 = (w * kWave) / ts;
             qy1 = (w * kWave + kWave - 1) / ts;
         }
-        rx0[w] = static_cast<float>(tx * ts + qx0) + 0.5f;
-        rx1[w] = static_cast<float>(tx * ts + qx1) + 0.5f;
-        ry0[w] = static_cast<float>(ty * ts + qy0) + 0.5f;
-        ry1[w] = static_cast<float>(ty * ts + qy1) + 0.5f;
-    }
+        x0 = static_cast<float>(tile_x0 + qx0) + 0.5f;
+        x1 = static_cast<float>(tile_x0 + qx1) + 0.5f;
+        y0 = static_cast<float>(tile_y0 + qy0) + 0.5f;
+        y1 = static_cast<float>(tile_y0 + qy1) + 0.5f;
+    };
 
     float T = 1.0f, acc[K];
 #pragma unroll
@@ -323,13 +327,19 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             s_rec[threadIdx.x * 3 + 1] = make_float4(cc, o, __int_as_float(idx), __int_as_float(g));
             s_rec[threadIdx.x * 3 + 2] = col;
             const CullBox box = cull_box(m, ca, cb, cc, o, a.alpha_cutoff, a.log_cutoff);
-            uint32_t bits = 0;
+            // bit 31: the splat may not take the short step (its conic is not a well-conditioned positive-definite
+            // one within the cull's bounds, or a colour is not finite)
+            const bool well = box.exact && __builtin_isfinite(col.x) && __builtin_isfinite(col.y) &&
+                              __builtin_isfinite(col.z) && __builtin_isfinite(col.w);
+            uint32_t bits = well ? 0u : kNotShort;
             if (!box.never) {
 #pragma unroll
                 for (int w = 0; w < kMaxThreads / kWave; ++w) {
-                    bool touch = box.x1 >= rx0[w] && box.x0 <= rx1[w] && box.y1 >= ry0[w] && box.y0 <= ry1[w];
+                    float qx0, qx1, qy0, qy1;
+                    region(w, qx0, qx1, qy0, qy1);
+                    bool touch = box.x1 >= qx0 && box.x0 <= qx1 && box.y1 >= qy0 && box.y0 <= qy1;
                     if (touch && box.exact)
-                        touch = region_reach(m, ca, cb, cc, box.ra, box.rc, box.thr, rx0[w], rx1[w], ry0[w], ry1[w]);
+                        touch = region_reach(m, ca, cb, cc, box.ra, box.rc, box.thr, qx0, qx1, qy0, qy1);
                     bits |= (touch ? 1u : 0u) << w;
                 }
             }
@@ -339,11 +349,15 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
         }
         __syncthreads();
         const int count = end - base < nthreads ? end - base : nthreads;
-        // this wave's splats of the batch, in order, as byte offsets of their records
+        // this wave's splats of the batch, in order, as byte offsets of their records; whether all of them may take
+        // the short step
         int listed = 0;
+        bool long_step = !a.short_step;
         for (int c0 = 0; c0 < count; c0 += kWave) {
             const int j = c0 + lane;
-            const bool keep = j < count && ((s_mask[j] >> wave) & 1u);
+            const uint32_t mj = j < count ? s_mask[j] : 0u;
+            const bool keep = (mj >> wave) & 1u;
+            long_step = long_step || __ballot(keep && (mj & kNotShort)) != 0;
             const uint64_t ballot = __ballot(keep);
             if (keep) s_list[wave][listed + __popcll(ballot & lt_mask)] = static_cast<uint16_t>(j * kRec * 4);
             listed += __popcll(ballot);
@@ -353,6 +367,65 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             // kUnroll records per iteration: their quadratic forms and exponentials are independent chains, and the
             // steps then apply in list order (written out here and below rather than shared through a lambda, whose
             // by-reference captures cost registers)
+            // The short step, for a batch whose listed splats all have well-conditioned positive-definite conics
+            // (the cull's exact case: a > 0, c > 0, det > 0, trace^2 <= 1000 det, opacity in [cutoff, 1e6], mean
+            // within 1e6 px) and finite colours, with alpha_cutoff >= 1e-20. It gives the bits of the step below:
+            //  - such a conic's computed sigma is within 0.15% of the exact quadratic form at the same dx, dy (the
+            //    cull's bound), so it is never negative and the sign test can go; an overflow gives +inf or NaN,
+            //    never -inf (the cross term is at most half the diagonal terms);
+            //  - sigma <= 80 takes the same polynomial; above 80, or NaN, the polynomial at min(sigma, 100) is below
+            //    2e-35, so alpha (at most 1e6 times that) fails the cutoff exactly as the specified alpha of 0 does,
+            //    and alpha is used nowhere else;
+            //  - E <= 1 keeps alpha finite, so min(alpha, clamp) is the clamp's select;
+            //  - a splat that does not composite adds colour * 0 = +-0 to every accumulator, which changes none:
+            //    they start at +0, and a round-to-nearest sum is -0 only when both terms are, so none is ever -0.
+            if (!long_step) {
+                for (; jj + kUnroll<K> <= listed; jj += kUnroll<K>) {
+                    if (__ballot(!done) == 0) break;
+                    float4 q0[kUnroll<K>], col[kUnroll<K>];
+                    float2 q1[kUnroll<K>];
+                    int at[kUnroll<K>];
+                    float al[kUnroll<K>];
+#pragma unroll
+                    for (int h = 0; h < kUnroll<K>; ++h) {
+                        const char *r = rec_base + s_list[wave][jj + h];
+                        q0[h] = *reinterpret_cast<const float4 *>(r);
+                        q1[h] = *reinterpret_cast<const float2 *>(r + 16);
+                        col[h] = *reinterpret_cast<const float4 *>(r + 32);
+                        at[h] = __float_as_int(*reinterpret_cast<const float *>(r + 24));
+                    }
+#pragma unroll
+                    for (int h = 0; h < kUnroll<K>; ++h) {
+                        const float dx = q0[h].x - px;
+                        const float dy = q0[h].y - py;
+                        const float sigma = 0.5f * (q0[h].z * dx * dx + q1[h].x * dy * dy) + q0[h].w * dx * dy;
+                        const float e = q1[h].y * (HWEXP ? exp_neg_hw(sigma) : exp_neg_poly(fminf(sigma, 100.0f)));
+                        al[h] = fminf(e, a.alpha_clamp);
+                    }
+#pragma unroll
+                    for (int h = 0; h < kUnroll<K>; ++h) {
+                        const float alpha = al[h];
+                        if (COUNT && !done) ++n_exec;
+                        const bool pass = !done && !(alpha < a.alpha_cutoff);
+                        const float t_next = T * (1.0f - alpha);
+                        const bool halt = pass && t_next <= a.transmittance_threshold;
+                        const bool comp = pass && !halt;
+                        const float v = comp ? alpha * T : 0.0f;
+                        acc[0] = acc[0] + col[h].x * v;
+                        if (K > 1) acc[1] = acc[1] + col[h].y * v;
+                        if (K > 2) acc[2] = acc[2] + col[h].z * v;
+                        if (K > 3) acc[3] = acc[3] + col[h].w * v;
+                        T = comp ? t_next : T;
+                        last = comp ? at[h] : last;
+                        done = done || halt;
+                        if (COUNT) {
+                            n_pass += pass ? 1u : 0u;
+                            n_comp += comp ? 1u : 0u;
+                            if (halt) stop = at[h] + 1;
+                        }
+                    }
+                }
+            }
             for (; jj + kUnroll<K> <= listed; jj += kUnroll<K>) {
                 if (__ballot(!done) == 0) break;
                 float4 q0[kUnroll<K>], col[kUnroll<K>];
@@ -600,6 +673,7 @@ gs_status rasterize(const char *fn, const float *means2d, const float *conics, c
     args.trace_vec = (max_splat_steps % 4 == 0 && (reinterpret_cast<uintptr_t>(trace_ids) & 15) == 0) ? 1 : 0;
     args.bin_counts = bin_counts;
     args.capacity = capacity;
+    args.short_step = alpha_cutoff >= 1.0e-20f ? 1 : 0;
     const bool trace = max_splat_steps >= 0;
     if (exp_mode != 0 && exp_mode != 1) return fail(GS_ERR_INVALID_ARG, "%s: exp_mode %d is not 0 or 1", fn, exp_mode);
     if (exp_mode == 1 && trace) return fail(GS_ERR_INVALID_ARG, "%s: the hardware exponential has no traced build", fn);

@@ -29,12 +29,11 @@ __device__ __forceinline__ float exp_neg(float sigma) {
     return __builtin_ldexpf(q, static_cast<int>(k));
 }
 
-// The same function without branches (a select replaces the early return), for lock-step loops where every lane
-// evaluates it anyway. Identical bits: the polynomial path is the one above, and any sigma that is not <= 80
-// (including NaN) selects 0.
-__device__ __forceinline__ float exp_neg_select(float sigma) {
+// The reduction and polynomial of exp_neg without its range test: Cody and Waite's reduction and the degree-7
+// Taylor polynomial, q = e^r with -sigma = k ln 2 + r.
+__device__ __forceinline__ float exp_neg_parts(float sigma, float &k) {
     const float t = -sigma;
-    const float k = __builtin_rintf(t * 0x1.715476p+0f);
+    k = __builtin_rintf(t * 0x1.715476p+0f);  // 1 / ln 2
     float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);
     r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);
     float q = 0x1.a01a02p-13f;
@@ -45,9 +44,26 @@ __device__ __forceinline__ float exp_neg_select(float sigma) {
     q = __builtin_fmaf(q, r, 0.5f);
     q = __builtin_fmaf(q, r, 1.0f);
     q = __builtin_fmaf(q, r, 1.0f);
+    return q;
+}
+
+// The same function without branches (a select replaces the early return), for lock-step loops where every lane
+// evaluates it anyway. Identical bits: the polynomial path is the one above, and any sigma that is not <= 80
+// (including NaN) selects 0.
+__device__ __forceinline__ float exp_neg_select(float sigma) {
+    float k;
+    const float q = exp_neg_parts(sigma, k);
     const int ki = (sigma <= 80.0f) ? static_cast<int>(k) : 0;
     const float e = __builtin_ldexpf(q, ki);
     return (sigma <= 80.0f) ? e : 0.0f;
+}
+
+// The polynomial path alone, for sigma <= 100 (k then lies in [-145, 116], so the conversion and scale are exact):
+// equal to exp_neg for sigma <= 80, and below 2e-35 on (80, 100].
+__device__ __forceinline__ float exp_neg_poly(float sigma) {
+    float k;
+    const float q = exp_neg_parts(sigma, k);
+    return __builtin_ldexpf(q, static_cast<int>(k));
 }
 
 // e^-sigma by the hardware base-2 exponential (v_exp_f32, about 1 ulp) of -sigma log2(e): a product and one
