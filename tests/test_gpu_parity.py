@@ -70,8 +70,43 @@ def _cull_edges():
     return s
 
 
+def _step_mix():
+    # splats outside the composite's short step beside ordinary ones, so that some batches of a wave take the full
+    # step and others the short one: ill-conditioned conics (axis ratio 2000-5000), indefinite conics (sigma < 0 in
+    # places), opacities above 1e6, and infinite or NaN colour channels
+    rng = np.random.default_rng(45)
+    s = synth.random_scene(45, 1, 3000, 96, 64, 16, r_range=(1.0, 16.0), background=True)
+    n = s.N
+    pick = lambda frac: rng.uniform(size=n) < frac  # noqa: E731
+    ill = pick(0.08)
+    l1 = rng.uniform(1.0, 30.0, n)
+    l2 = l1 / rng.uniform(2000.0, 5000.0, n)
+    th = rng.uniform(0, np.pi, n)
+    cs, sn = np.cos(th), np.sin(th)
+    sxx, syy, sxy = l1 * cs * cs + l2 * sn * sn, l1 * sn * sn + l2 * cs * cs, (l1 - l2) * cs * sn
+    det = l1 * l2
+    ill_conic = np.stack([syy / det, -sxy / det, sxx / det], -1).astype(np.float32)
+    s.conics[0][ill] = ill_conic[ill]
+    indef = pick(0.04)
+    a = rng.uniform(0.05, 0.5, n)
+    s.conics[0][indef] = np.stack([a, 1.5 * a, a], -1).astype(np.float32)[indef]
+    s.opacities[0][pick(0.02)] = np.float32(2.0e6)
+    s.colors[0][pick(0.02), 1] = np.float32(np.inf)
+    s.colors[0][pick(0.01), 2] = np.float32(np.nan)
+    return s
+
+
+def _cutoff(value):
+    s = synth.random_scene(46, 1, 800, 80, 48, 16, r_range=(1.0, 14.0))
+    s.alpha_cutoff = float(value)
+    return s
+
+
 SCENES = {
     "cull-edges": _cull_edges,
+    "step-mix": _step_mix,
+    "cutoff-zero": lambda: _cutoff(0.0),
+    "cutoff-1e-20": lambda: _cutoff(np.float32(1e-20)),
     "tiny": lambda: synth.tiny(),
     "tiny-aniso": lambda: synth.tiny(anisotropic=True),
     "multicam-ragged-elliptical": lambda: synth.random_scene(35, 3, 700, 150, 90, 16, elliptical=True,
