@@ -93,6 +93,20 @@ __device__ __forceinline__ void tile_range(const RasterArgs &a, int tile, int &s
     if (a.max_list >= 0 && end - start > a.max_list) end = start + a.max_list;
 }
 
+// The tile of workgroup b. Workgroups are dealt to the 8 XCDs round-robin (b on XCD b mod 8), each XCD with its own
+// L2; tiles side by side stage mostly the same splats. So the grid is cut into stripes of two tile rows, stripe s
+// going to XCD s mod 8: the i-th workgroup an XCD receives takes the i-th tile of its stripes, in order, and the
+// tiles past the last whole round of 8 stripes go round-robin. A bijection of [0, tiles). Measured against the
+// plain order on the composite alone: 1M-splat 1080p frame unchanged (0.327 vs 0.329 ms) with 31% fewer bytes
+// fetched (469 vs 684 MB per launch), 6M-splat frame 6% faster, 4-camera frame 3% faster; one contiguous band per
+// XCD fetched less (412 MB) but was 3% slower on the 1M-splat frame, where the splats cluster.
+__device__ __forceinline__ int tile_of_block(int b, int tiles, int tile_width) {
+    const int xcd = b & 7, i = b >> 3;
+    const int stripe = 2 * tile_width;
+    const int full = tiles / (8 * stripe);
+    return i < full * stripe ? (i / stripe) * (8 * stripe) + xcd * stripe + (i % stripe) : b;
+}
+
 template <int K, int PPT, bool COUNT, bool TRACE, bool HWEXP>
 __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float2 s_xy[kMaxThreads];
@@ -100,7 +114,7 @@ __global__ __launch_bounds__(kMaxThreads) void raster_fwd_kernel(RasterArgs a) {
     __shared__ float s_rgb[kMaxThreads * K];
     __shared__ int32_t s_g[kMaxThreads];  // the staged ids (-1: outside [0, n_splats), e.g. an empty bin slot)
 
-    const int tile = static_cast<int>(blockIdx.x);
+    const int tile = tile_of_block(static_cast<int>(blockIdx.x), a.total_tiles, a.tile_width);
     const int per_camera = a.tile_width * a.tile_height;
     const int camera = tile / per_camera;
     const int local = tile - camera * per_camera;
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
     __shared__ uint16_t s_list[kMaxThreads / kWave][kMaxThreads];
     __shared__ int32_t s_trace[TRACE ? kMaxThreads * kTraceStride : 1];
 
-    const int tile = static_cast<int>(blockIdx.x);
+    const int tile = tile_of_block(static_cast<int>(blockIdx.x), a.total_tiles, a.tile_width);
     const int per_camera = a.tile_width * a.tile_height;
     const int camera = tile / per_camera;
     const int local = tile - camera * per_camera;

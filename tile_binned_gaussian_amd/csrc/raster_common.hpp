@@ -109,9 +109,14 @@ __device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c,
     if (!(o >= alpha_cutoff) || !(o <= 1.0e6f) || !(det > 0.0f) || !(a > 0.0f) || !(c > 0.0f) ||
         !(tr * tr <= 1.0e3f * det) || !(fabsf(m.x) < 1.0e6f) || !(fabsf(m.y) < 1.0e6f))
         return box;
-    const float L = logf(o) - log_cutoff + 0.05f;
-    float rx = sqrtf(2.0f * L * (c / det)) * 1.0001f;
-    float ry = sqrtf(2.0f * L * (a / det)) * 1.0001f;
+    // The hardware logarithm, reciprocal and square root (within a few ulp) stand in for the correctly rounded
+    // functions: their errors, below 1e-6 absolute in L and a few 2^-24 relative in rx, ry and 1/a, 1/c, are far
+    // inside the margins (0.05 in L, 1e-4 relative in rx, ry); a reciprocal or logarithm flushed to 0 or infinity
+    // leaves rx or ry infinite or NaN, and the splat is then never culled.
+    const float L = __logf(o) - log_cutoff + 0.05f;
+    const float rdet = __builtin_amdgcn_rcpf(det);
+    float rx = __builtin_amdgcn_sqrtf(2.0f * L * (c * rdet)) * 1.0001f;
+    float ry = __builtin_amdgcn_sqrtf(2.0f * L * (a * rdet)) * 1.0001f;
     if (!(rx < 1.0e6f) || !(ry < 1.0e6f)) return box;
     rx += 2.0e-3f + 1.0e-6f * (fabsf(m.x) + rx);
     ry += 2.0e-3f + 1.0e-6f * (fabsf(m.y) + ry);
@@ -120,8 +125,8 @@ __device__ __forceinline__ CullBox cull_box(float2 m, float a, float b, float c,
     box.y0 = m.y - ry;
     box.y1 = m.y + ry;
     box.thr = 1.004f * L + 1.0e-3f;
-    box.ra = 1.0f / a;
-    box.rc = 1.0f / c;
+    box.ra = __builtin_amdgcn_rcpf(a);
+    box.rc = __builtin_amdgcn_rcpf(c);
     box.exact = true;
     return box;
 }
