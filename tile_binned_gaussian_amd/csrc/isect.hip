@@ -16,9 +16,10 @@ constexpr int kThreads = 256;
 constexpr int kEmitBlocks = 4096;
 
 // ------------------------------------------------------------------------------------------------------------
-// Phase 1. Two single-pass scans over partitions of kScanTile consecutive positions: the tile counts in splat order
-// (each splat's first output slot, and the total) and, when sorting, the counts in depth order. Item i of thread t
-// is position i * kScanThreads + t of the partition, so every load and store of a wave is contiguous.
+// Phase 1. A single-pass scan of the tile counts in splat order over partitions of kScanTile consecutive positions
+// (each splat's first output slot, and the total); when sorting, the depth sort that follows it also scans the
+// counts in depth order, in its last pass. Item i of thread t is position i * kScanThreads + t of the partition, so
+// every load and store of a wave is contiguous.
 // A partition takes its index from a counter (so every predecessor is already running), publishes its sum in its
 // status word, and finds the sum over all predecessors by a decoupled look-back in which the 64 lanes of the first
 // wave each inspect one predecessor per round. A status word holds a flag in its top two bits (the partition's own
@@ -119,8 +120,8 @@ __device__ int64_t publish_and_look_back(uint64_t *status, uint32_t part, int64_
 // Phase 1a: per-splat tile count (tiles_per_gauss), its exclusive prefix in splat order (gauss_offsets) and the total
 // (*total; also *total_host when non-null, a device-visible address of page-locked host memory). When sorting,
 // rects receives each splat's rectangle as (x0, y0, width, height) in tiles, and the depth sort's digit histograms
-// (hplan's passes over the depth bits) are accumulated, so neither the rectangles nor the depths are read again
-// for them.
+// (hplan's passes over the depth bits) are accumulated, with the tile counts summed by the last pass's digit in
+// the row after them, so neither the rectangles nor the depths are read again for them.
 static_assert(kScanThreads == 4 * 256, "one thread per digit of the depth sort's four 8-bit passes");
 template <int RPG>
 __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
@@ -129,12 +130,17 @@ __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
     int4 *__restrict__ rects, int64_t *__restrict__ total, int64_t *total_host, uint64_t *status,
     uint32_t *__restrict__ counter, uint32_t *__restrict__ hist, PassPlan hplan, uint32_t spin_limit, uint32_t *err) {
     __shared__ uint32_t s_hist[4][256];
+    // the last pass's digits: key count (low word) and tile count sum (high word), one 64-bit LDS atomic per splat
+    __shared__ uint64_t s_top[256];
     __shared__ int64_t s_part_sums[kScanItems * kScanWaves];
     __shared__ int64_t s_total;
     __shared__ int64_t s_prefix;
     __shared__ uint32_t s_part;
     take_partition(counter, &s_part);
-    if (hist) (&s_hist[0][0])[threadIdx.x] = 0;
+    if (hist) {
+        (&s_hist[0][0])[threadIdx.x] = 0;
+        if (threadIdx.x < 256) s_top[threadIdx.x] = 0;
+    }
     __syncthreads();
     const uint32_t part = s_part;
     if (static_cast<int64_t>(part) * kScanTile >= M) return;  // only with a corrupted counter
@@ -163,11 +169,15 @@ __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
         }
     }
     if (hist) {
+        const int last = hplan.passes - 1;
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i)
-            if (j0 + i * kScanThreads < M)
-                for (int p = 0; p < hplan.passes; ++p)
+            if (j0 + i * kScanThreads < M) {
+                for (int p = 0; p < last; ++p)
                     atomicAdd(&s_hist[p][(bits[i] >> hplan.shift[p]) & ((1u << hplan.bits[p]) - 1u)], 1u);
+                atomicAdd(&s_top[(bits[i] >> hplan.shift[last]) & ((1u << hplan.bits[last]) - 1u)],
+                          (static_cast<uint64_t>(v[i]) << 32) | 1u);
+            }
     }
     const int64_t aggregate = scan_items_exclusive(v, s_part_sums, &s_total);
     const int64_t before = publish_and_look_back(status, part, aggregate, spin_limit, err);
@@ -184,55 +194,11 @@ __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
         if (total_host) __hip_atomic_store(total_host, all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     if (hist) {
-        const int p = threadIdx.x / 256, d = threadIdx.x % 256;
-        const uint32_t c = s_hist[p][d];
-        if (p < hplan.passes && c) atomicAdd(&hist_copy(hist, part)[p * 256 + d], c);
-    }
-}
-
-// Phase 1b (sorting): position j holds splat perm[j]. Its rectangle is gathered once into depth order
-// (sorted_rects) and the exclusive prefix of the counts in that order gives each position's first output slot
-// (sorted_offsets). A perm entry outside [0, M) - only possible with a corrupted workspace - gives an empty
-// rectangle.
-__global__ __launch_bounds__(kScanThreads) void order_scan_kernel(const int32_t *__restrict__ perm,
-                                                                  const int4 *__restrict__ rects, int M,
-                                                                  int4 *__restrict__ sorted_rects,
-                                                                  int32_t *__restrict__ sorted_offsets,
-                                                                  uint64_t *status, uint32_t *__restrict__ counter,
-                                                                  uint32_t spin_limit, uint32_t *err) {
-    __shared__ int64_t s_part_sums[kScanItems * kScanWaves];
-    __shared__ int64_t s_total;
-    __shared__ int64_t s_prefix;
-    __shared__ uint32_t s_part;
-    take_partition(counter, &s_part);
-    __syncthreads();
-    const uint32_t part = s_part;
-    if (static_cast<int64_t>(part) * kScanTile >= M) return;  // only with a corrupted counter
-    const int j0 = static_cast<int>(part) * kScanTile + static_cast<int>(threadIdx.x);
-    // the permutation entries first, then every gather of the thread's rectangles at once
-    int src[kScanItems];
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) src[i] = j0 + i * kScanThreads < M ? perm[j0 + i * kScanThreads] : -1;
-    int4 r[kScanItems];
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i)
-        r[i] = static_cast<unsigned>(src[i]) < static_cast<unsigned>(M) ? rects[src[i]] : make_int4(0, 0, 0, 0);
-    int64_t v[kScanItems];
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int j = j0 + i * kScanThreads;
-        // a rectangle from a workspace that phase 1 did not fill still gives a count >= 0
-        v[i] = static_cast<int64_t>(max(r[i].z, 0)) * static_cast<int64_t>(max(r[i].w, 0));
-        if (j < M) sorted_rects[j] = r[i];
-    }
-    const int64_t aggregate = scan_items_exclusive(v, s_part_sums, &s_total);
-    const int64_t before = publish_and_look_back(status, part, aggregate, spin_limit, err);
-    if (threadIdx.x == 0) s_prefix = before;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int j = j0 + i * kScanThreads;
-        if (j < M) sorted_offsets[j] = static_cast<int32_t>(s_prefix + v[i]);
+        const int p = threadIdx.x / 256, d = threadIdx.x % 256, last = hplan.passes - 1;
+        const uint32_t c = p < last ? s_hist[p][d] : (p == last ? static_cast<uint32_t>(s_top[d]) : 0u);
+        if (c) atomicAdd(&hist_copy(hist, part)[p * 256 + d], c);
+        const uint32_t w = p == 0 ? static_cast<uint32_t>(s_top[d] >> 32) : 0u;
+        if (w) atomicAdd(&hist_copy(hist, part)[hplan.passes * 256 + d], w);
     }
 }
 
@@ -369,11 +335,11 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
 }
 
 // Workspace of gs_isect_tiles. The prefix [0, prefix) depends on M and the sort flag only, so phase 1 and phase 2
-// see it at the same offsets: the total, the two scans' partition counters and status words, and, when sorting,
-// the depth sort's scratch, the depth order of the splats (two u32/i32 ping-pong pairs of M), the rectangles
-// (row-major and in depth order) and the per-position offsets in that order. [clear_begin, clear_end) is what
-// phase 1 clears before it starts: the counters, the status words and the part of the depth sort's scratch that
-// must start at zero. Phase 2 adds, when sorting more than one intersection, the alternate intersection buffers
+// see it at the same offsets: the total, the count scan's partition counter and status words, and, when sorting,
+// the look-back words of the depth sort's last pass, the depth sort's scratch, the depth order of the splats (two
+// ping-pong triples of M depth keys, ids and tile counts), the rectangles (row-major and in depth order) and the
+// per-position offsets in that order. [clear_begin, clear_end) is what phase 1 clears before it starts: the counter, the status and
+// look-back words and the part of the depth sort's scratch that must start at zero. Phase 2 adds, when sorting more than one intersection, the alternate intersection buffers
 // and the tile sort's scratch.
 struct IsectLayout {
     size_t total, counters, count_status, order_status, depth_scratch, clear_begin, clear_end;
@@ -388,14 +354,14 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     L.total = align_up(c.used, 256);
     c.take<int64_t>(1);
     L.counters = L.clear_begin = align_up(c.used, 256);
-    c.take<uint32_t>(2);  // the two scans' partition counters
+    c.take<uint32_t>(1);  // the count scan's partition counter
     L.count_status = align_up(c.used, 256);
     c.take<uint64_t>(parts);
     L.clear_end = c.used;
     if (sort) {
         const size_t m = static_cast<size_t>(M > 0 ? M : 1);
         L.order_status = align_up(c.used, 256);
-        c.take<uint64_t>(parts);
+        c.take<char>(depth_order_status_bytes(static_cast<int64_t>(m)));
         L.depth_scratch = align_up(c.used, 256);
         c.take<char>(sort_scratch_layout(static_cast<int64_t>(m)).bytes);
         L.clear_end = L.depth_scratch + radix_clear_bytes(static_cast<int64_t>(m));
@@ -576,20 +542,16 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             if (e == hipSuccess) e = hipEventRecord(copied, stream);
         }
         if (e == hipSuccess && sort) {
-            // the depth order of the splats (histograms from the count scan), then the rectangles and first output
-            // slots in that order
+            // the depth order of the splats (histograms from the count scan), whose last pass also writes the
+            // rectangles and first output slots in that order
             int in_b = 0;
-            st = radix_passes<uint32_t>(dbits, nullptr, at<uint32_t>(workspace, L.dkeys_a),
-                                        at<int32_t>(workspace, L.dids_a), at<uint32_t>(workspace, L.dkeys_b),
-                                        at<int32_t>(workspace, L.dids_b), M, depth_plan, depth_scratch, stream, &in_b);
-            if (st == GS_OK) {
-                const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
-                hipLaunchKernelGGL(order_scan_kernel, dim3((M + kScanTile - 1) / kScanTile), dim3(kScanThreads), 0,
-                                   stream, perm, rects, M, at<int4>(workspace, L.sorted_rects),
-                                   at<int32_t>(workspace, L.sorted_offsets), at<uint64_t>(workspace, L.order_status),
-                                   counters + 1, spin_limit(), err);
-                e = hipGetLastError();
-            }
+            st = depth_order_passes(dbits, at<uint32_t>(workspace, L.dkeys_a), at<int32_t>(workspace, L.dids_a),
+                                    at<uint32_t>(workspace, L.dkeys_b), at<int32_t>(workspace, L.dids_b), M,
+                                    depth_plan, depth_scratch, rects, at<int4>(workspace, L.sorted_rects),
+                                    at<int32_t>(workspace, L.sorted_offsets), at<uint64_t>(workspace, L.order_status),
+                                    stream, &in_b);
+            if (st == GS_OK && (in_b != 0) != depth_in_b)
+                st = fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: the depth order landed in the other buffer pair");
         }
         // wait for the total (also after a failed launch, so no write into the caller's memory is left in flight)
         hipError_t w = hipSuccess;

@@ -78,6 +78,12 @@ __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
 __device__ __forceinline__ void atomic_store_agent(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t atomic_load_agent64(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <typename KeyT>
 __device__ __forceinline__ uint32_t digit_of(KeyT k, int shift, uint32_t mask) {
@@ -175,6 +181,40 @@ __global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__
     starts[p * kRadix + d] = before + inc - c;
 }
 
+// Stable rank of each of a wave's items among the wave's items of the same digit (digit_bits bits at shift), item
+// i of every lane coming after items 0..i-1 of all lanes and after item i of lower lanes; wave_hist (this wave's
+// LDS counts per digit, zero before the first call) advances by the wave's count of each digit. The lanes holding
+// the same digit come from one ballot per digit bit: a lane's mismatch set gathers, for every bit, the lanes whose
+// bit differs from its own (ballot XOR the lane's bit spread over 32 bits, ORed in by one three-input bit operation
+// per half of the 64-lane mask); its complement is the set of lanes with the same digit.
+template <typename KeyT, int kItems, int kDigitBits>
+__device__ __forceinline__ void rank_in_wave(const KeyT (&k)[kItems], int shift, uint32_t *wave_hist,
+                                             uint32_t (&rank)[kItems]) {
+    const int lane = __lane_id();
+    const uint32_t digit_mask = (1u << kDigitBits) - 1u;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const uint32_t d = digit_of(k[i], shift, digit_mask);
+        uint32_t miss_lo = 0u, miss_hi = 0u;
+#pragma unroll
+        for (int b = 0; b < kDigitBits; ++b) {
+            const uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), b, 1));
+            const uint64_t ballot = __ballot(spread != 0u);
+            // truth table 0xF6: first | (second ^ third), the first operand being the table's high index bit
+            miss_lo = __builtin_amdgcn_bitop3_b32(miss_lo, static_cast<uint32_t>(ballot), spread, 0xF6);
+            miss_hi = __builtin_amdgcn_bitop3_b32(miss_hi, static_cast<uint32_t>(ballot >> 32), spread, 0xF6);
+        }
+        const uint32_t same_lo = ~miss_lo, same_hi = ~miss_hi;
+        const uint64_t same = (static_cast<uint64_t>(same_hi) << 32) | same_lo;
+        const uint32_t below = static_cast<uint32_t>(__popcll(same & lt_mask));
+        const uint32_t run = wave_hist[d];
+        rank[i] = run + below;
+        const int leader = 63 - __clzll(same);
+        if (lane == leader) wave_hist[d] = run + static_cast<uint32_t>(__popcll(same));
+    }
+}
+
 // One digit pass. Partition `part` covers pairs [part * kTile, part * kTile + kTile) (kTile from Tiling);
 // wave w owns the contiguous span [w * kWaveSpan, (w + 1) * kWaveSpan) of it, item i of lane l sitting at
 // w * kWaveSpan + i * 64 + l, so (wave, item, lane) order is input order and the per-wave running counts give a
@@ -264,32 +304,8 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
     const uint32_t digit_global_start = digit_thread ? digit_starts[d] : 0u;
 
 
-    // stable rank within the wave: the lanes holding the same digit, from one ballot per digit bit. A lane's
-    // mismatch set gathers, for every bit, the lanes whose bit differs from its own (ballot XOR the lane's bit spread
-    // over 32 bits, ORed in by one three-input bit operation per half of the 64-lane mask); its complement is the set
-    // of lanes with the same digit.
     uint32_t rank[kItems];
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const uint32_t d = digit_of(k[i], shift, digit_mask);
-        uint32_t miss_lo = 0u, miss_hi = 0u;
-#pragma unroll
-        for (int b = 0; b < digit_bits; ++b) {
-            const uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), b, 1));
-            const uint64_t ballot = __ballot(spread != 0u);
-            // truth table 0xF6: first | (second ^ third), the first operand being the table's high index bit
-            miss_lo = __builtin_amdgcn_bitop3_b32(miss_lo, static_cast<uint32_t>(ballot), spread, 0xF6);
-            miss_hi = __builtin_amdgcn_bitop3_b32(miss_hi, static_cast<uint32_t>(ballot >> 32), spread, 0xF6);
-        }
-        const uint32_t same_lo = ~miss_lo, same_hi = ~miss_hi;
-        const uint64_t same = (static_cast<uint64_t>(same_hi) << 32) | same_lo;
-        const uint32_t below = static_cast<uint32_t>(__popcll(same & lt_mask));
-        const uint32_t run = s_wave_hist[wave][d];
-        rank[i] = run + below;
-        const int leader = 63 - __clzll(same);
-        if (lane == leader) s_wave_hist[wave][d] = run + static_cast<uint32_t>(__popcll(same));
-    }
+    rank_in_wave<KeyT, kItems, digit_bits>(k, shift, s_wave_hist[wave], rank);
     __syncthreads();
 
     // per digit (thread d): counts of the waves -> exclusive prefix over waves, and the partition total
@@ -398,6 +414,200 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
         if ((full || q < valid) && dst[i] < n) keys_out[dst[i]] = key;
     }
     // the ids follow through the same LDS bytes
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) s_buf.ids[lp[i]] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int q = i * kThreads + tid;
+        if ((full || q < valid) && dst[i] < n) ids_out[dst[i]] = s_buf.ids[q];
+    }
+}
+
+// The last pass of the splats' depth sort (4-byte keys, 8-bit digits, partitions indexed by block), which also
+// produces what the emission reads in depth order: besides the sorted (key, id) pairs, for every output position
+// the rectangle of its splat (gathered by id from rects, which is in splat order) and the splat's first output
+// slot, the sum of the tile counts (width x height of the rectangles) of every splat placed before it. That sum has
+// three parts: the counts of the splats whose digit is smaller (weight_starts: the exclusive scan over digits of a
+// histogram of counts by this pass's digit), of the earlier partitions' splats with the same digit (the look-back,
+// whose words carry each partition's count sum beside its key count), and of the partition's own earlier splats
+// with that digit (an exclusive scan of the counts in the partition's reordered sequence). A 64-bit status word
+// holds 2 flag bits, the count sum in bits [30, 62) and the key count in bits [0, 30); both fields add as one
+// integer while the counts stay below 2^30 keys and 2^32 tiles, and the flags are masked off every published sum.
+constexpr uint64_t kFlag64Aggregate = 1ull << 62;
+constexpr uint64_t kFlag64Inclusive = 2ull << 62;
+constexpr uint64_t kValue64Mask = (1ull << 62) - 1;
+constexpr int kPackShift = 30;
+constexpr uint64_t kPackKeysMask = (1ull << kPackShift) - 1;
+
+__global__ __launch_bounds__(kThreads) void depth_order_pass_kernel(
+    const uint32_t *__restrict__ keys_in, const int32_t *__restrict__ ids_in, const int4 *__restrict__ rects,
+    uint32_t *__restrict__ keys_out, int32_t *__restrict__ ids_out,
+    int4 *__restrict__ sorted_rects, int32_t *__restrict__ sorted_offsets, int64_t n, int shift, const uint32_t *__restrict__ digit_starts,
+    const uint32_t *__restrict__ weight_starts, uint64_t *status, uint32_t spin_limit) {
+    constexpr int kItems = kItems32, kTile = kThreads * kItems, kWaveSpan = kWave * kItems;
+    constexpr int kLookWindow = 4;
+    constexpr uint32_t kMask = kRadix - 1;
+    __shared__ union {
+        uint32_t keys[kTile];
+        int32_t ids[kTile];
+    } s_buf;
+    // tile counts in the partition's reordered sequence, then their exclusive prefix (entry kTile: the total)
+    __shared__ union {
+        uint4 quad[kTile / 4 + 1];
+        uint32_t word[kTile + 4];
+    } s_count;
+    __shared__ int4 s_rect[kTile];
+    __shared__ uint32_t s_wave_hist[kWaves][kRadix];
+    __shared__ uint32_t s_local_start[kRadix];
+    __shared__ uint32_t s_global_base[kRadix];
+    __shared__ uint32_t s_count_base[kRadix];
+    __shared__ uint32_t s_tmp[kWaves];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = __lane_id();
+    const uint32_t part = blockIdx.x;
+    if (static_cast<int64_t>(part) * kTile >= n) return;
+    const bool digit_thread = tid < kRadix;
+    const int d = digit_thread ? tid : 0;
+    const int64_t base = static_cast<int64_t>(part) * kTile + static_cast<int64_t>(wave) * kWaveSpan + lane;
+    const bool full = static_cast<int64_t>(part + 1) * kTile <= n;
+
+    // keys and ids at once; the ids address the gather of the rectangles, issued as soon as they arrive
+    uint32_t k[kItems];
+    int32_t v[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int64_t at = base + i * kWave < n ? base + i * kWave : n - 1;
+        k[i] = keys_in[at];
+        v[i] = ids_in[at];
+    }
+    for (int i = tid; i < kWaves * kRadix; i += kThreads) (&s_wave_hist[0][0])[i] = 0;
+    // a position past the end, and an id outside [0, n) (only from a corrupted workspace), take an empty rectangle
+    int4 r[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const bool real = (full || base + i * kWave < n) && static_cast<uint64_t>(v[i]) < static_cast<uint64_t>(n);
+        r[i] = real ? rects[v[i]] : make_int4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < kItems; ++i)
+            if (base + i * kWave >= n) k[i] = ~0u;  // past the end: largest digit, ranked after every real pair
+    }
+    const uint32_t digit_global_start = digit_thread ? digit_starts[d] : 0u;
+    const uint32_t digit_count_start = digit_thread ? weight_starts[d] : 0u;
+
+    uint32_t rank[kItems];
+    rank_in_wave<uint32_t, kItems, 8>(k, shift, s_wave_hist[wave], rank);
+    __syncthreads();
+    uint32_t running = 0;
+    if (digit_thread) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t c = s_wave_hist[w][d];
+            s_wave_hist[w][d] = running;
+            running += c;
+        }
+    }
+    const uint32_t part_keys = running;
+    uint32_t local_total;
+    const uint32_t local_start = block_exclusive_u32(part_keys, s_tmp, &local_total);
+    if (digit_thread) s_local_start[d] = local_start;
+    __syncthreads();
+
+    // reorder keys, rectangles and tile counts by digit through LDS
+    uint32_t lp[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const uint32_t dd = (k[i] >> shift) & kMask;
+        lp[i] = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
+        s_buf.keys[lp[i]] = k[i];
+        s_rect[lp[i]] = r[i];
+        // a rectangle from a workspace the count scan did not fill still counts >= 0
+        s_count.word[lp[i]] = static_cast<uint32_t>(max(r[i].z, 0)) * static_cast<uint32_t>(max(r[i].w, 0));
+    }
+    __syncthreads();
+    // exclusive prefix of the counts in reordered sequence: thread t takes positions 4t .. 4t + 3
+    {
+        const uint4 c = s_count.quad[tid];
+        uint32_t total;
+        const uint32_t before_t = block_exclusive_u32(c.x + c.y + c.z + c.w, s_tmp, &total);
+        s_count.quad[tid] = make_uint4(before_t, before_t + c.x, before_t + c.x + c.y, before_t + c.x + c.y + c.z);
+        if (tid == 0) s_count.word[kTile] = total;
+    }
+    __syncthreads();
+
+    // per digit: publish the key count and count sum, then find those of all earlier partitions by a decoupled
+    // look-back (a window of predecessors per round, bounded by spin_limit as in the other passes)
+    uint64_t mine = 0;
+    if (digit_thread) {
+        const uint32_t sum = s_count.word[local_start + part_keys] - s_count.word[local_start];
+        mine = (static_cast<uint64_t>(sum) << kPackShift) | part_keys;
+        atomic_store_agent64(status + static_cast<size_t>(part) * kRadix + d,
+                             (part == 0 ? kFlag64Inclusive : kFlag64Aggregate) | mine);
+    }
+    uint64_t before = 0;
+    if (digit_thread && part > 0) {
+        int64_t j = static_cast<int64_t>(part) - 1;  // the newest predecessor not yet added
+        uint32_t rounds = 0;
+        while (true) {
+            uint64_t s[kLookWindow];
+#pragma unroll
+            for (int w = 0; w < kLookWindow; ++w)
+                s[w] = j - w >= 0 ? atomic_load_agent64(status + static_cast<size_t>(j - w) * kRadix + d)
+                                  : kFlag64Inclusive;
+            // add the window's published words up to the first unpublished one, or through the inclusive one
+            bool found = false;
+            int used = 0;
+#pragma unroll
+            for (int w = 0; w < kLookWindow; ++w) {
+                if (found || used < w) continue;
+                const uint64_t flag = s[w] & ~kValue64Mask;
+                if (flag == 0) continue;
+                before += s[w] & kValue64Mask;
+                used = w + 1;
+                if (flag == kFlag64Inclusive) found = true;
+            }
+            if (found) break;
+            if (rounds++ >= spin_limit) {
+                atomicOr(&g_device_error, kDeviceErrSortLookBack);
+                break;
+            }
+            j -= used;
+            if (used < kLookWindow) __builtin_amdgcn_s_sleep(1);
+        }
+        atomic_store_agent64(status + static_cast<size_t>(part) * kRadix + d,
+                             kFlag64Inclusive | ((before + mine) & kValue64Mask));
+    }
+    if (digit_thread) {
+        s_global_base[d] = digit_global_start + static_cast<uint32_t>(before & kPackKeysMask);
+        s_count_base[d] = digit_count_start + static_cast<uint32_t>(before >> kPackShift);
+    }
+    __syncthreads();
+
+    // keys, rectangles and first slots: consecutive local positions of one digit go to consecutive positions
+    const int64_t valid64 = n - static_cast<int64_t>(part) * kTile;
+    const int valid = valid64 < kTile ? static_cast<int>(valid64) : kTile;
+    uint32_t dst[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int q = i * kThreads + tid;
+        const uint32_t key = s_buf.keys[q];
+        const uint32_t dd = (key >> shift) & kMask;
+        const uint32_t ls = s_local_start[dd];
+        dst[i] = s_global_base[dd] + (static_cast<uint32_t>(q) - ls);
+        // dst < n always holds when the histograms match the keys; the test keeps a corrupted one in bounds
+        if ((full || q < valid) && dst[i] < n) {
+            keys_out[dst[i]] = key;
+            sorted_rects[dst[i]] = s_rect[q];
+            sorted_offsets[dst[i]] = static_cast<int32_t>(s_count_base[dd] + (s_count.word[q] - s_count.word[ls]));
+        }
+    }
+    // the ids follow through the keys' LDS bytes
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) s_buf.ids[lp[i]] = v[i];
@@ -542,31 +752,30 @@ int pass_items(int64_t n) {
     return best;
 }
 
+namespace {
+
+// Digit passes [0, count) of plan (count <= plan.passes), after digit_starts_kernel: pass p reads the previous
+// pass's output (the input for p = 0) and writes buffer A when p is even, B when odd. Each pass clears the look-back
+// array of the next pass it runs; the pass at count - 1 clears none.
 template <typename KeyT>
-gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
-                       KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
-                       hipStream_t stream, int *result_in_b) {
-    *result_in_b = 0;
-    if (plan.passes == 0 || n < 1) return ok();
+gs_status run_digit_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                           KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, int count,
+                           void *scratch, hipStream_t stream) {
     const SortScratchLayout L = sort_scratch_layout(n);
     char *ws = static_cast<char *>(scratch);
-    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
     uint32_t *status[2] = {reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1)};
-    uint32_t *starts = reinterpret_cast<uint32_t *>(ws + L.starts);
-    hipLaunchKernelGGL(digit_starts_kernel, dim3(plan.passes), dim3(kRadix), 0, stream, hist, starts);
-    GS_LAUNCH_TRY("digit_starts_kernel");
-
+    const uint32_t *starts = reinterpret_cast<const uint32_t *>(ws + L.starts);
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
     const uint32_t spin = spin_limit();
     const int items = pass_items<KeyT>(n);
-    for (int p = 0; p < plan.passes; ++p) {
+    for (int p = 0; p < count; ++p) {
         const bool to_a = (p % 2) == 0;
         KeyT *dk = to_a ? buf_a_keys : buf_b_keys;
         int32_t *di = to_a ? buf_a_ids : buf_b_ids;
         uint32_t *st = status[p & 1];
-        uint32_t *st_next = (p + 1 < plan.passes) ? status[(p + 1) & 1] : nullptr;
+        uint32_t *st_next = (p + 1 < count) ? status[(p + 1) & 1] : nullptr;
         const int64_t tile = int64_t(kThreads) * items;
         const int64_t parts = (n + tile - 1) / tile;
         if (parts > L.parts)  // the look-back arrays hold L.parts partitions of 256 words
@@ -575,21 +784,84 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
         const dim3 grid(static_cast<unsigned>(parts));
         const uint32_t *h = starts + p * kRadix;
         gs_status st_launch;
-        if constexpr (sizeof(KeyT) == 4)
+        if constexpr (sizeof(KeyT) == 4) {
             st_launch = launch_pass<KeyT, kItems32>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n, plan.shift[p],
                                                     h, counters + p, st, st_next, spin);
-        else if (items == kItems64Min)
+        } else if (items == kItems64Min) {
             st_launch = launch_pass<KeyT, kItems64Min>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
                                                        plan.shift[p], h, counters + p, st, st_next, spin);
-        else
+        } else {
             st_launch = launch_pass<KeyT, kItems64Max>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
                                                        plan.shift[p], h, counters + p, st, st_next, spin);
+        }
         if (st_launch != GS_OK) return st_launch;
         GS_LAUNCH_TRY("onesweep_pass_kernel");
         src_k = dk;
         src_i = di;
     }
+    return ok();
+}
+
+// The global digit starts of `rows` rows of the histogram copies (one workgroup per row).
+gs_status launch_digit_starts(void *scratch, int64_t n, int rows, hipStream_t stream) {
+    const SortScratchLayout L = sort_scratch_layout(n);
+    char *ws = static_cast<char *>(scratch);
+    hipLaunchKernelGGL(digit_starts_kernel, dim3(rows), dim3(kRadix), 0, stream,
+                       reinterpret_cast<const uint32_t *>(ws + L.hist), reinterpret_cast<uint32_t *>(ws + L.starts));
+    GS_LAUNCH_TRY("digit_starts_kernel");
+    return ok();
+}
+
+}  // namespace
+
+template <typename KeyT>
+gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                       KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
+                       hipStream_t stream, int *result_in_b) {
+    *result_in_b = 0;
+    if (plan.passes == 0 || n < 1) return ok();
+    gs_status st = launch_digit_starts(scratch, n, plan.passes, stream);
+    if (st != GS_OK) return st;
+    st = run_digit_passes<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, plan.passes,
+                                scratch, stream);
+    if (st != GS_OK) return st;
     *result_in_b = (plan.passes % 2) == 0;
+    return ok();
+}
+
+size_t depth_order_status_bytes(int64_t n) {
+    const int64_t parts = (n + kThreads * kItems32 - 1) / (kThreads * kItems32);
+    return static_cast<size_t>(parts > 0 ? parts : 1) * kRadix * sizeof(uint64_t);
+}
+
+gs_status depth_order_passes(const uint32_t *depth_bits, uint32_t *buf_a_keys, int32_t *buf_a_ids,
+                             uint32_t *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,
+                             void *scratch, const int4 *rects, int4 *sorted_rects, int32_t *sorted_offsets,
+                             uint64_t *order_status, hipStream_t stream, int *result_in_b) {
+    *result_in_b = 0;
+    const int last = plan.passes - 1;
+    if (last < 1 || last + 1 >= kMaxPasses || plan.bits[last] != 8)
+        return fail(GS_ERR_INVALID_ARG, "depth order: %d passes (need 2 to %d, the last of 8 bits)", plan.passes,
+                    kMaxPasses - 1);
+    if (n < 1) return ok();
+    // row plan.passes of the histogram copies holds the tile counts by the last pass's digit
+    gs_status st = launch_digit_starts(scratch, n, plan.passes + 1, stream);
+    if (st != GS_OK) return st;
+    st = run_digit_passes<uint32_t>(depth_bits, nullptr, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, last,
+                                    scratch, stream);
+    if (st != GS_OK) return st;
+    // pass `last` reads what pass last - 1 wrote
+    const bool to_a = (last % 2) == 0;
+    const SortScratchLayout L = sort_scratch_layout(n);
+    const uint32_t *starts = reinterpret_cast<const uint32_t *>(static_cast<char *>(scratch) + L.starts);
+    const int64_t parts = (n + kThreads * kItems32 - 1) / (kThreads * kItems32);
+    hipLaunchKernelGGL(depth_order_pass_kernel, dim3(static_cast<unsigned>(parts)), dim3(kThreads), 0, stream,
+                       to_a ? buf_b_keys : buf_a_keys, to_a ? buf_b_ids : buf_a_ids, rects,
+                       to_a ? buf_a_keys : buf_b_keys, to_a ? buf_a_ids : buf_b_ids, sorted_rects, sorted_offsets, n,
+                       plan.shift[last], starts + last * kRadix, starts + plan.passes * kRadix, order_status,
+                       spin_limit());
+    GS_LAUNCH_TRY("depth_order_pass_kernel");
+    *result_in_b = to_a ? 0 : 1;
     return ok();
 }
 
