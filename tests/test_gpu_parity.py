@@ -151,6 +151,38 @@ def test_isect_rectangle_past_2_pow_22_tiles():
         assert_isect_equal(s, gpu_isect(s, sort), it_o, sort)
 
 
+def _bit_pattern_depths(rng, m):
+    """Depth bit patterns over the whole 32-bit range: negative floats, -0, infinities, NaN payloads and
+    denormals beside ordinary positive depths, many sharing a top byte of 0xff (the last depth pass's largest
+    digit) and many repeated exactly."""
+    bits = rng.integers(0, 1 << 32, m, dtype=np.uint64).astype(np.uint32)
+    kind = rng.integers(0, 6, m)
+    bits = np.where(kind == 0, np.uint32(0xFF000000) | (bits & np.uint32(0x00FFFFFF)), bits)
+    bits = np.where(kind == 1, np.float32(rng.uniform(0.5, 10.0, m)).view(np.uint32), bits)
+    bits = np.where(kind == 2, bits & np.uint32(0x007FFFFF), bits)  # +0 and positive denormals
+    special = np.array([0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFFFFFFF, 0x00000000], np.uint32)
+    bits = np.where(kind == 3, special[rng.integers(0, len(special), m)], bits)
+    dup = rng.uniform(size=m) < 0.2
+    bits[dup] = bits[rng.integers(0, m, int(dup.sum()))]
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("n_per_camera", [1, 2047, 5000, 6144])
+def test_isect_sorted_depth_bit_patterns(n_per_camera):
+    # The depth sort orders the splats by the depths' bit patterns alone, over ragged partitions of 4096 splats
+    # (2 cameras: 2, 4094, 10000 and 12288 splats); the last pass also scans the tile counts in that order, so
+    # splats without tiles and the largest digit (top byte 0xff) next to the padding past the last splat are
+    # covered. Keys, ids, counts and offsets must equal the oracle's bit for bit.
+    rng = np.random.default_rng(n_per_camera)
+    s = synth.random_scene(46 + n_per_camera, 2, n_per_camera, 96, 80, 16, r_range=(0.25, 20.0),
+                           zero_radius_frac=0.25)
+    s.depths[...] = _bit_pattern_depths(rng, s.C * s.N).reshape(s.C, s.N)
+    s.depths[:, -min(n_per_camera, 64):] = np.uint32(0xFFFFFFF0).view(np.float32)
+    it_o = oracle.isect_tiles(s.means2d, s.radii, s.depths, s.tile_size, s.tile_width, s.tile_height, sort=True)
+    assert it_o.n_isects > 0
+    assert_isect_equal(s, gpu_isect(s, True), it_o, True)
+
+
 @pytest.mark.parametrize("name", list(SCENES))
 def test_ranges_on_oracle_keys(name):
     scene = SCENES[name]()
