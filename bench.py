@@ -174,9 +174,9 @@ def stage_bytes(scene, n, tile_passes, generic_passes):
     K = scene.colors.shape[-1]
     return {
         # phase 1: the count scan (means, radii and depths read once, counts and offsets written), the depth order
-        # of the splats (4 passes of 4-byte keys and ids read and written) and the offsets in that order (the order
-        # read, a count per splat gathered, the offset written)
-        "count_depth_order": M * (8 + rb + 4 + 4 + 4) + M * 4 * 16 + M * (4 + 4 + 4),
+        # of the splats (4 passes of 4-byte keys and ids read and written) and the offsets in that order (a count per
+        # splat gathered, the offset written; the last depth pass computes them)
+        "count_depth_order": M * (8 + rb + 4 + 4 + 4) + M * 4 * 16 + M * (4 + 4),
         # phase 2: emission in depth order (order, depth bits, offset, mean, radius per splat; 12 bytes per
         # intersection written; the digit histograms are built on the way) and tile_passes passes of 24 B per
         # intersection
