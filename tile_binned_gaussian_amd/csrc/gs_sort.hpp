@@ -1,7 +1,7 @@
 // Internal interface of the onesweep radix sort (sort.hip), shared with the intersection step.
 #pragma once
 
-#include "gs_internal.hpp"
+#include "gs_rect.hpp"
 
 namespace gs {
 
@@ -80,15 +80,15 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
 
 // The splats' depth order for the emission: the passes of plan (histograms already accumulated by the caller, and
 // in row plan.passes of the histogram copies the tile counts by the last pass's digit), the last one (8 bits) also
-// writing, for every position of the order, the rectangle of its splat (gathered from rects, in splat order) and
-// its first output slot (the exclusive prefix of the tile counts in that order). Pass p writes buffer A when p is
+// writing, for every position of the order, the rectangle of its splat (gathered from rects, in splat order; int4,
+// or one packed word when pk.cx is nonzero) and its first output slot (the exclusive prefix of the tile counts in that order). Pass p writes buffer A when p is
 // even and B when odd; *result_in_b tells where the order lands. order_status holds depth_order_status_bytes(n)
 // bytes, zero before the call.
 size_t depth_order_status_bytes(int64_t n);
 gs_status depth_order_passes(const uint32_t *depth_bits, uint32_t *buf_a_keys, int32_t *buf_a_ids,
                              uint32_t *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,
-                             void *scratch, const int4 *rects, int4 *sorted_rects, int32_t *sorted_offsets,
-                             uint64_t *order_status, hipStream_t stream, int *result_in_b);
+                             void *scratch, const void *rects, void *sorted_rects, RectPacking pk,
+                             int32_t *sorted_offsets, uint64_t *order_status, hipStream_t stream, int *result_in_b);
 
 // Stable LSD sort of n (key, id) pairs (prepare + histograms + passes). Pass 0 reads (keys_in, ids_in)
 // (ids_in == nullptr: ids are the input positions); pass p writes buffer A when p is even and B when odd, so the

@@ -119,7 +119,8 @@ __device__ int64_t publish_and_look_back(uint64_t *status, uint32_t part, int64_
 
 // Phase 1a: per-splat tile count (tiles_per_gauss), its exclusive prefix in splat order (gauss_offsets) and the total
 // (*total; also *total_host when non-null, a device-visible address of page-locked host memory). When sorting,
-// rects receives each splat's rectangle as (x0, y0, width, height) in tiles, and the depth sort's digit histograms
+// rects receives each splat's rectangle as (x0, y0, width, height) in tiles (int4, or one packed word when pk.cx is
+// nonzero), and the depth sort's digit histograms
 // (hplan's passes over the depth bits) are accumulated, with the tile counts summed by the last pass's digit in
 // the row after them, so neither the rectangles nor the depths are read again for them.
 static_assert(kScanThreads == 4 * 256, "one thread per digit of the depth sort's four 8-bit passes");
@@ -127,7 +128,7 @@ template <int RPG>
 __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
     const float2 *__restrict__ means, const float *__restrict__ radii, const uint32_t *__restrict__ depth_bits, int M,
     float ts, int tw, int th, int32_t *__restrict__ tiles_per_gauss, int32_t *__restrict__ gauss_offsets,
-    int4 *__restrict__ rects, int64_t *__restrict__ total, int64_t *total_host, uint64_t *status,
+    void *__restrict__ rects, RectPacking pk, int64_t *__restrict__ total, int64_t *total_host, uint64_t *status,
     uint32_t *__restrict__ counter, uint32_t *__restrict__ hist, PassPlan hplan, uint32_t spin_limit, uint32_t *err) {
     __shared__ uint32_t s_hist[4][256];
     // the last pass's digits: key count (low word) and tile count sum (high word), one 64-bit LDS atomic per splat
@@ -165,7 +166,8 @@ __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
         v[i] = count;
         if (j < M) {
             tiles_per_gauss[j] = count;
-            if (rects) rects[j] = make_int4(r.x0, r.y0, r.x1 - r.x0, r.y1 - r.y0);
+            if (rects && pk.cx) static_cast<uint32_t *>(rects)[j] = pack_rect(r.x0, r.y0, r.x1 - r.x0, r.y1 - r.y0, pk);
+            else if (rects) static_cast<int4 *>(rects)[j] = make_int4(r.x0, r.y0, r.x1 - r.x0, r.y1 - r.y0);
         }
     }
     if (hist) {
@@ -218,7 +220,8 @@ __device__ __forceinline__ int floor_div(int k, int w, float rcp_w) {
 // position (the last one whose start is <= slot) by an unrolled branchless binary search in LDS, and writes key and
 // id for tile k of that splat's rectangle in row-major order (row = k / width by a float reciprocal kept per
 // position, corrected to the exact quotient). With a permutation, sorted_depth[j] holds the depth bits of splat
-// perm[j] (read in order instead of gathered), and sorted_rects[j] its rectangle, so no splat data is gathered.
+// perm[j] (read in order instead of gathered), and sorted_rects[j] its rectangle (int4, or one packed word when
+// pk.cx is nonzero), so no splat data is gathered.
 // Workgroups stride over chunks, so the digit histograms (hist non-null) are flushed to global memory once per
 // workgroup, into the histogram copy of that workgroup.
 static_assert(kThreads * kMaxPasses == kHistCopyWords, "one emission thread per digit of the histograms");
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                                                         float ts, int tw, int th, int tile_bits,
                                                         const int32_t *__restrict__ perm,
                                                         const uint32_t *__restrict__ sorted_depth,
-                                                        const int4 *__restrict__ sorted_rects,
+                                                        const void *__restrict__ sorted_rects, RectPacking pk,
                                                         const int32_t *__restrict__ gauss_offsets, int n,
                                                         uint64_t *__restrict__ keys, int32_t *__restrict__ ids,
                                                         uint32_t *__restrict__ hist, PassPlan hplan) {
@@ -250,7 +253,8 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
             int i = perm ? perm[j] : j;
             if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) i = 0;  // only with a corrupted workspace
             if (sorted_rects) {
-                const int4 r = sorted_rects[j];
+                const int4 r = pk.cx ? unpack_rect(static_cast<const uint32_t *>(sorted_rects)[j], pk)
+                                     : static_cast<const int4 *>(sorted_rects)[j];
                 s_x0[threadIdx.x] = r.x;
                 s_y0[threadIdx.x] = r.y;
                 s_w[threadIdx.x] = r.z;
@@ -411,18 +415,19 @@ T *at(void *ws, size_t off) {
 
 // The count scan (hist non-null: with the depth sort's histograms of hplan's passes).
 gs_status launch_count_scan(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, float ts,
-                            int tw, int th, int32_t *tiles_per_gauss, int32_t *offsets, int4 *rects, int64_t *total,
+                            int tw, int th, int32_t *tiles_per_gauss, int32_t *offsets, void *rects,
+                            RectPacking pk, int64_t *total,
                             int64_t *total_host, uint64_t *status, uint32_t *counter, uint32_t *hist,
                             const PassPlan &hplan, uint32_t *err, hipStream_t stream) {
     const int parts = (M + kScanTile - 1) / kScanTile;
     const uint32_t spin = spin_limit();
     if (rpg == 2)
         hipLaunchKernelGGL(count_scan_kernel<2>, dim3(parts), dim3(kScanThreads), 0, stream, m2, radii, dbits, M, ts,
-                           tw, th, tiles_per_gauss, offsets, rects, total, total_host, status, counter, hist, hplan,
+                           tw, th, tiles_per_gauss, offsets, rects, pk, total, total_host, status, counter, hist, hplan,
                            spin, err);
     else
         hipLaunchKernelGGL(count_scan_kernel<1>, dim3(parts), dim3(kScanThreads), 0, stream, m2, radii, dbits, M, ts,
-                           tw, th, tiles_per_gauss, offsets, rects, total, total_host, status, counter, hist, hplan,
+                           tw, th, tiles_per_gauss, offsets, rects, pk, total, total_host, status, counter, hist, hplan,
                            spin, err);
     GS_LAUNCH_TRY("count_scan_kernel");
     return ok();
@@ -432,7 +437,8 @@ gs_status launch_count_scan(int rpg, const float2 *m2, const float *radii, const
 // all lie in the keys' upper words (bits 32..63).
 gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
                       int tw, int th, int tile_bits, const int32_t *perm, const uint32_t *sorted_depth,
-                      const int4 *sorted_rects, const int32_t *offsets, int n, uint64_t *keys, int32_t *ids,
+                      const void *sorted_rects, RectPacking pk, const int32_t *offsets, int n, uint64_t *keys,
+                      int32_t *ids,
                       uint32_t *hist, const PassPlan &hplan, hipStream_t stream) {
     if (hist)
         for (int p = 0; p < hplan.passes; ++p)
@@ -443,10 +449,10 @@ gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint3
     const int blocks = chunks < kEmitBlocks ? chunks : kEmitBlocks;
     if (rpg == 2)
         hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, sorted_depth, sorted_rects, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, sorted_rects, pk, offsets, n, keys, ids, hist, hplan);
     else
         hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, sorted_depth, sorted_rects, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, sorted_rects, pk, offsets, n, keys, ids, hist, hplan);
     GS_LAUNCH_TRY("emit_kernel");
     return ok();
 }
@@ -497,6 +503,8 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
 
     // the depth order of the splats lands in the B pair after an even number of 8-bit passes over 32 bits
     const PassPlan depth_plan = make_pass_plan(0, 32);
+    // rectangles stored for the depth order take one word each when the grid allows it
+    const RectPacking pk = rect_packing(tile_width, tile_height);
     const bool depth_in_b = depth_plan.passes % 2 == 0;
 
     if (keys == nullptr) {  // ---------------------------------------------------------------- phase 1: count
@@ -520,7 +528,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         int64_t *total = at<int64_t>(workspace, L.total);
         uint32_t *counters = at<uint32_t>(workspace, L.counters);
         char *depth_scratch = sort ? at<char>(workspace, L.depth_scratch) : nullptr;
-        int4 *rects = sort ? at<int4>(workspace, L.rects) : nullptr;
+        void *rects = sort ? at<void>(workspace, L.rects) : nullptr;
         // Into page-locked memory the count scan writes the total itself and the host waits for that word alone, so
         // the depth-order work queued behind the scan runs while the count travels to the host and the caller
         // prepares phase 2; into pageable memory a copy returns it.
@@ -530,7 +538,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
         GS_HIP_TRY(fill_u32(at<uint32_t>(workspace, L.clear_begin), 0, (L.clear_end - L.clear_begin) / sizeof(uint32_t),
                             stream));
         st = launch_count_scan(radii_per_gauss, m2, radii, dbits, M, ts, tile_width, tile_height, tiles_per_gauss,
-                               gauss_offsets, rects, total, total_host, at<uint64_t>(workspace, L.count_status),
+                               gauss_offsets, rects, pk, total, total_host, at<uint64_t>(workspace, L.count_status),
                                counters, sort ? radix_histograms(depth_scratch, M) : nullptr, depth_plan, err, stream);
         if (st != GS_OK) return st;
         int64_t host_total = 0;
@@ -547,7 +555,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             int in_b = 0;
             st = depth_order_passes(dbits, at<uint32_t>(workspace, L.dkeys_a), at<int32_t>(workspace, L.dids_a),
                                     at<uint32_t>(workspace, L.dkeys_b), at<int32_t>(workspace, L.dids_b), M,
-                                    depth_plan, depth_scratch, rects, at<int4>(workspace, L.sorted_rects),
+                                    depth_plan, depth_scratch, rects, at<void>(workspace, L.sorted_rects), pk,
                                     at<int32_t>(workspace, L.sorted_offsets), at<uint64_t>(workspace, L.order_status),
                                     stream, &in_b);
             if (st == GS_OK && (in_b != 0) != depth_in_b)
@@ -595,7 +603,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const int n = static_cast<int>(n_isects);
     if (!(sort && n > 1))  // emission in (camera, splat, tile row, tile column) order
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, nullptr, nullptr, nullptr, gauss_offsets, n, keys, flatten_ids, nullptr,
+                           tile_bits, nullptr, nullptr, nullptr, pk, gauss_offsets, n, keys, flatten_ids, nullptr,
                            PassPlan{}, stream);
 
     // Sorted output. Phase 1 put the splats in stable (depth bits, flat id) order and computed each position's
@@ -605,7 +613,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const int32_t *perm = at<int32_t>(workspace, depth_in_b ? L.dids_b : L.dids_a);
     const uint32_t *sorted_depth = at<uint32_t>(workspace, depth_in_b ? L.dkeys_b : L.dkeys_a);
     const int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
-    const int4 *sorted_rects = at<int4>(workspace, L.sorted_rects);
+    const void *sorted_rects = at<void>(workspace, L.sorted_rects);
     void *scratch = at<char>(workspace, L.tile_scratch);
     const PassPlan tile_plan = make_pass_plan(32, 32 + tile_bits + cam_bits);
     uint64_t *alt_keys = at<uint64_t>(workspace, L.alt_keys);
@@ -616,13 +624,13 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     int32_t *emit_ids = odd ? alt_ids : flatten_ids;
     if (tile_plan.passes == 0)
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
-                           tile_bits, perm, sorted_depth, sorted_rects, sorted_offsets, n, emit_keys, emit_ids,
+                           tile_bits, perm, sorted_depth, sorted_rects, pk, sorted_offsets, n, emit_keys, emit_ids,
                            nullptr, PassPlan{}, stream);
     // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them
     gs_status st = radix_prepare(n, scratch, stream);
     if (st != GS_OK) return st;
     st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
-                     perm, sorted_depth, sorted_rects, sorted_offsets, n, emit_keys, emit_ids,
+                     perm, sorted_depth, sorted_rects, pk, sorted_offsets, n, emit_keys, emit_ids,
                      radix_histograms(scratch, n), tile_plan, stream);
     if (st != GS_OK) return st;
     int in_b = 0;

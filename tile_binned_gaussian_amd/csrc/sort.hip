@@ -427,7 +427,8 @@ __global__ __launch_bounds__(kThreads) void onesweep_pass_kernel(
 
 // The last pass of the splats' depth sort (4-byte keys, 8-bit digits, partitions indexed by block), which also
 // produces what the emission reads in depth order: besides the sorted (key, id) pairs, for every output position
-// the rectangle of its splat (gathered by id from rects, which is in splat order) and the splat's first output
+// the rectangle of its splat (gathered by id from rects, which is in splat order: int4, or one packed word when
+// pk.cx is nonzero, which keeps the gathered array small enough to stay mostly in L2) and the splat's first output
 // slot, the sum of the tile counts (width x height of the rectangles) of every splat placed before it. That sum has
 // three parts: the counts of the splats whose digit is smaller (weight_starts: the exclusive scan over digits of a
 // histogram of counts by this pass's digit), of the earlier partitions' splats with the same digit (the look-back,
@@ -442,9 +443,9 @@ constexpr int kPackShift = 30;
 constexpr uint64_t kPackKeysMask = (1ull << kPackShift) - 1;
 
 __global__ __launch_bounds__(kThreads) void depth_order_pass_kernel(
-    const uint32_t *__restrict__ keys_in, const int32_t *__restrict__ ids_in, const int4 *__restrict__ rects,
-    uint32_t *__restrict__ keys_out, int32_t *__restrict__ ids_out,
-    int4 *__restrict__ sorted_rects, int32_t *__restrict__ sorted_offsets, int64_t n, int shift, const uint32_t *__restrict__ digit_starts,
+    const uint32_t *__restrict__ keys_in, const int32_t *__restrict__ ids_in, const void *__restrict__ rects,
+    RectPacking pk, uint32_t *__restrict__ keys_out, int32_t *__restrict__ ids_out, void *__restrict__ sorted_rects,
+    int32_t *__restrict__ sorted_offsets, int64_t n, int shift, const uint32_t *__restrict__ digit_starts,
     const uint32_t *__restrict__ weight_starts, uint64_t *status, uint32_t spin_limit) {
     constexpr int kItems = kItems32, kTile = kThreads * kItems, kWaveSpan = kWave * kItems;
     constexpr int kLookWindow = 4;
@@ -458,7 +459,10 @@ __global__ __launch_bounds__(kThreads) void depth_order_pass_kernel(
         uint4 quad[kTile / 4 + 1];
         uint32_t word[kTile + 4];
     } s_count;
-    __shared__ int4 s_rect[kTile];
+    __shared__ union {
+        int4 full[kTile];
+        uint32_t packed[kTile];
+    } s_rect;
     __shared__ uint32_t s_wave_hist[kWaves][kRadix];
     __shared__ uint32_t s_local_start[kRadix];
     __shared__ uint32_t s_global_base[kRadix];
@@ -486,11 +490,15 @@ __global__ __launch_bounds__(kThreads) void depth_order_pass_kernel(
     }
     for (int i = tid; i < kWaves * kRadix; i += kThreads) (&s_wave_hist[0][0])[i] = 0;
     // a position past the end, and an id outside [0, n) (only from a corrupted workspace), take an empty rectangle
+    // (packed: the zero word)
     int4 r[kItems];
+    uint32_t rp[kItems];
+    const bool packed = pk.cx != 0;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const bool real = (full || base + i * kWave < n) && static_cast<uint64_t>(v[i]) < static_cast<uint64_t>(n);
-        r[i] = real ? rects[v[i]] : make_int4(0, 0, 0, 0);
+        if (packed) rp[i] = real ? static_cast<const uint32_t *>(rects)[v[i]] : 0u;
+        else r[i] = real ? static_cast<const int4 *>(rects)[v[i]] : make_int4(0, 0, 0, 0);
     }
     __syncthreads();
     if (!full) {
@@ -526,9 +534,15 @@ __global__ __launch_bounds__(kThreads) void depth_order_pass_kernel(
         const uint32_t dd = (k[i] >> shift) & kMask;
         lp[i] = s_local_start[dd] + s_wave_hist[wave][dd] + rank[i];
         s_buf.keys[lp[i]] = k[i];
-        s_rect[lp[i]] = r[i];
-        // a rectangle from a workspace the count scan did not fill still counts >= 0
-        s_count.word[lp[i]] = static_cast<uint32_t>(max(r[i].z, 0)) * static_cast<uint32_t>(max(r[i].w, 0));
+        if (packed) {
+            s_rect.packed[lp[i]] = rp[i];
+            const int4 u = unpack_rect(rp[i], pk);
+            s_count.word[lp[i]] = static_cast<uint32_t>(u.z) * static_cast<uint32_t>(u.w);
+        } else {
+            s_rect.full[lp[i]] = r[i];
+            // a rectangle from a workspace the count scan did not fill still counts >= 0
+            s_count.word[lp[i]] = static_cast<uint32_t>(max(r[i].z, 0)) * static_cast<uint32_t>(max(r[i].w, 0));
+        }
     }
     __syncthreads();
     // exclusive prefix of the counts in reordered sequence: thread t takes positions 4t .. 4t + 3
@@ -603,7 +617,8 @@ __global__ __launch_bounds__(kThreads) void depth_order_pass_kernel(
         // dst < n always holds when the histograms match the keys; the test keeps a corrupted one in bounds
         if ((full || q < valid) && dst[i] < n) {
             keys_out[dst[i]] = key;
-            sorted_rects[dst[i]] = s_rect[q];
+            if (packed) static_cast<uint32_t *>(sorted_rects)[dst[i]] = s_rect.packed[q];
+            else static_cast<int4 *>(sorted_rects)[dst[i]] = s_rect.full[q];
             sorted_offsets[dst[i]] = static_cast<int32_t>(s_count_base[dd] + (s_count.word[q] - s_count.word[ls]));
         }
     }
@@ -836,8 +851,8 @@ size_t depth_order_status_bytes(int64_t n) {
 
 gs_status depth_order_passes(const uint32_t *depth_bits, uint32_t *buf_a_keys, int32_t *buf_a_ids,
                              uint32_t *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,
-                             void *scratch, const int4 *rects, int4 *sorted_rects, int32_t *sorted_offsets,
-                             uint64_t *order_status, hipStream_t stream, int *result_in_b) {
+                             void *scratch, const void *rects, void *sorted_rects, RectPacking pk,
+                             int32_t *sorted_offsets, uint64_t *order_status, hipStream_t stream, int *result_in_b) {
     *result_in_b = 0;
     const int last = plan.passes - 1;
     if (last < 1 || last + 1 >= kMaxPasses || plan.bits[last] != 8)
@@ -856,7 +871,7 @@ gs_status depth_order_passes(const uint32_t *depth_bits, uint32_t *buf_a_keys, i
     const uint32_t *starts = reinterpret_cast<const uint32_t *>(static_cast<char *>(scratch) + L.starts);
     const int64_t parts = (n + kThreads * kItems32 - 1) / (kThreads * kItems32);
     hipLaunchKernelGGL(depth_order_pass_kernel, dim3(static_cast<unsigned>(parts)), dim3(kThreads), 0, stream,
-                       to_a ? buf_b_keys : buf_a_keys, to_a ? buf_b_ids : buf_a_ids, rects,
+                       to_a ? buf_b_keys : buf_a_keys, to_a ? buf_b_ids : buf_a_ids, rects, pk,
                        to_a ? buf_a_keys : buf_b_keys, to_a ? buf_a_ids : buf_b_ids, sorted_rects, sorted_offsets, n,
                        plan.shift[last], starts + last * kRadix, starts + plan.passes * kRadix, order_status,
                        spin_limit());
