@@ -132,9 +132,9 @@ gs_status gs_sort_keys_static(uint64_t *keys, int32_t *flatten_ids, int64_t n, i
  * Device-side failure of the sort and the count scans ([gsplat] gs_isect_tiles turns a failure of its sort into
  * an error status, NoMemError; here the only device-side failure is a wait that does not end).
  *
- * Each digit pass of the sort (gs_sort_keys, and gs_isect_tiles with sort != 0) and the two scans of
- * gs_isect_tiles' phase 1 (the counts in splat order, and with sort != 0 in depth order) let a partition wait for
- * the counts of the partitions before it. The wait is bounded: after `limit` rounds (one round is one
+ * Each digit pass of the sort (gs_sort_keys, and gs_isect_tiles with sort != 0, whose last depth pass also scans
+ * the counts in depth order) and the scan of the counts in splat order in gs_isect_tiles' phase 1 let a partition
+ * wait for the counts of the partitions before it. The wait is bounded: after `limit` rounds (one round is one
  * device-coherent load plus a short sleep; the default, 2^20, is about a second) the partition gives up, sets the
  * library's device error word of the current GPU and finishes, so the kernel always completes; that call's output
  * is then invalid (every access still stays inside the caller's buffers).

@@ -20,10 +20,11 @@ constexpr int kEmitBlocks = 4096;
 // (each splat's first output slot, and the total); when sorting, the depth sort that follows it also scans the
 // counts in depth order, in its last pass. Item i of thread t is position i * kScanThreads + t of the partition, so
 // every load and store of a wave is contiguous.
-// A partition takes its index from a counter (so every predecessor is already running), publishes its sum in its
-// status word, and finds the sum over all predecessors by a decoupled look-back in which the 64 lanes of the first
-// wave each inspect one predecessor per round. A status word holds a flag in its top two bits (the partition's own
-// sum published, or its inclusive prefix published) and the value below.
+// Partition p is workgroup p: workgroups start in block order on each XCD, so every predecessor of a running
+// partition is running or done (the bounded look-back turns any violation into a reported error, not a hang). It
+// publishes its sum in its status word, and finds the sum over all predecessors by a decoupled look-back in which
+// the 64 lanes of the first wave each inspect one predecessor per round. A status word holds a flag in its top two
+// bits (the partition's own sum published, or its inclusive prefix published) and the value below.
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 4;
 constexpr int kScanTile = kScanThreads * kScanItems;
@@ -70,11 +71,6 @@ __device__ __forceinline__ int64_t scan_items_exclusive(int64_t (&v)[kScanItems]
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) v[i] = s_part_sums[i * kScanWaves + wave] + inc[i] - v[i];
     return *s_total;
-}
-
-// The partition index from the counter (thread 0 asks; valid in every thread after the next barrier).
-__device__ __forceinline__ void take_partition(uint32_t *counter, uint32_t *s_part) {
-    if (threadIdx.x == 0) *s_part = atomicAdd(counter, 1u);
 }
 
 // Publishes the partition's sum and returns the sum over partitions [0, part) (wave 0 only; the other waves get 0).
@@ -129,22 +125,19 @@ __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(
     const float2 *__restrict__ means, const float *__restrict__ radii, const uint32_t *__restrict__ depth_bits, int M,
     float ts, int tw, int th, int32_t *__restrict__ tiles_per_gauss, int32_t *__restrict__ gauss_offsets,
     void *__restrict__ rects, RectPacking pk, int64_t *__restrict__ total, int64_t *total_host, uint64_t *status,
-    uint32_t *__restrict__ counter, uint32_t *__restrict__ hist, PassPlan hplan, uint32_t spin_limit, uint32_t *err) {
+    uint32_t *__restrict__ hist, PassPlan hplan, uint32_t spin_limit, uint32_t *err) {
     __shared__ uint32_t s_hist[4][256];
     // the last pass's digits: key count (low word) and tile count sum (high word), one 64-bit LDS atomic per splat
     __shared__ uint64_t s_top[256];
     __shared__ int64_t s_part_sums[kScanItems * kScanWaves];
     __shared__ int64_t s_total;
     __shared__ int64_t s_prefix;
-    __shared__ uint32_t s_part;
-    take_partition(counter, &s_part);
     if (hist) {
         (&s_hist[0][0])[threadIdx.x] = 0;
         if (threadIdx.x < 256) s_top[threadIdx.x] = 0;
     }
     __syncthreads();
-    const uint32_t part = s_part;
-    if (static_cast<int64_t>(part) * kScanTile >= M) return;  // only with a corrupted counter
+    const uint32_t part = blockIdx.x;
     const int j0 = static_cast<int>(part) * kScanTile + static_cast<int>(threadIdx.x);
     // every load of the thread's splats is issued before any result is used
     float2 m[kScanItems];
@@ -339,14 +332,14 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
 }
 
 // Workspace of gs_isect_tiles. The prefix [0, prefix) depends on M and the sort flag only, so phase 1 and phase 2
-// see it at the same offsets: the total, the count scan's partition counter and status words, and, when sorting,
-// the look-back words of the depth sort's last pass, the depth sort's scratch, the depth order of the splats (two
-// ping-pong triples of M depth keys, ids and tile counts), the rectangles (row-major and in depth order) and the
-// per-position offsets in that order. [clear_begin, clear_end) is what phase 1 clears before it starts: the counter, the status and
-// look-back words and the part of the depth sort's scratch that must start at zero. Phase 2 adds, when sorting more than one intersection, the alternate intersection buffers
-// and the tile sort's scratch.
+// see it at the same offsets: the total, the count scan's status words, and, when sorting, the look-back words of
+// the depth sort's last pass, the depth sort's scratch, the depth order of the splats (two u32/i32 ping-pong pairs
+// of M), the rectangles (in splat order and in depth order; 4 or 16 bytes each) and the per-position offsets in
+// that order. [clear_begin, clear_end) is what phase 1 clears before it starts: the status and look-back words and
+// the part of the depth sort's scratch that must start at zero. Phase 2 adds, when sorting more than one
+// intersection, the alternate intersection buffers and the tile sort's scratch.
 struct IsectLayout {
-    size_t total, counters, count_status, order_status, depth_scratch, clear_begin, clear_end;
+    size_t total, count_status, order_status, depth_scratch, clear_begin, clear_end;
     size_t dkeys_a, dids_a, dkeys_b, dids_b, rects, sorted_rects, sorted_offsets, prefix;
     size_t alt_keys, alt_ids, tile_scratch, bytes;
 };
@@ -357,9 +350,7 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     const size_t parts = static_cast<size_t>(M > 0 ? (M + kScanTile - 1) / kScanTile : 1);
     L.total = align_up(c.used, 256);
     c.take<int64_t>(1);
-    L.counters = L.clear_begin = align_up(c.used, 256);
-    c.take<uint32_t>(1);  // the count scan's partition counter
-    L.count_status = align_up(c.used, 256);
+    L.count_status = L.clear_begin = align_up(c.used, 256);
     c.take<uint64_t>(parts);
     L.clear_end = c.used;
     if (sort) {
@@ -417,17 +408,17 @@ T *at(void *ws, size_t off) {
 gs_status launch_count_scan(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, float ts,
                             int tw, int th, int32_t *tiles_per_gauss, int32_t *offsets, void *rects,
                             RectPacking pk, int64_t *total,
-                            int64_t *total_host, uint64_t *status, uint32_t *counter, uint32_t *hist,
+                            int64_t *total_host, uint64_t *status, uint32_t *hist,
                             const PassPlan &hplan, uint32_t *err, hipStream_t stream) {
     const int parts = (M + kScanTile - 1) / kScanTile;
     const uint32_t spin = spin_limit();
     if (rpg == 2)
         hipLaunchKernelGGL(count_scan_kernel<2>, dim3(parts), dim3(kScanThreads), 0, stream, m2, radii, dbits, M, ts,
-                           tw, th, tiles_per_gauss, offsets, rects, pk, total, total_host, status, counter, hist, hplan,
+                           tw, th, tiles_per_gauss, offsets, rects, pk, total, total_host, status, hist, hplan,
                            spin, err);
     else
         hipLaunchKernelGGL(count_scan_kernel<1>, dim3(parts), dim3(kScanThreads), 0, stream, m2, radii, dbits, M, ts,
-                           tw, th, tiles_per_gauss, offsets, rects, pk, total, total_host, status, counter, hist, hplan,
+                           tw, th, tiles_per_gauss, offsets, rects, pk, total, total_host, status, hist, hplan,
                            spin, err);
     GS_LAUNCH_TRY("count_scan_kernel");
     return ok();
@@ -526,7 +517,6 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
             return fail(GS_ERR_INVALID_ARG, "gs_isect_tiles: the depth sort needs %d passes", depth_plan.passes);
         const uint32_t *dbits = reinterpret_cast<const uint32_t *>(depths);
         int64_t *total = at<int64_t>(workspace, L.total);
-        uint32_t *counters = at<uint32_t>(workspace, L.counters);
         char *depth_scratch = sort ? at<char>(workspace, L.depth_scratch) : nullptr;
         void *rects = sort ? at<void>(workspace, L.rects) : nullptr;
         // Into page-locked memory the count scan writes the total itself and the host waits for that word alone, so
@@ -539,7 +529,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
                             stream));
         st = launch_count_scan(radii_per_gauss, m2, radii, dbits, M, ts, tile_width, tile_height, tiles_per_gauss,
                                gauss_offsets, rects, pk, total, total_host, at<uint64_t>(workspace, L.count_status),
-                               counters, sort ? radix_histograms(depth_scratch, M) : nullptr, depth_plan, err, stream);
+                               sort ? radix_histograms(depth_scratch, M) : nullptr, depth_plan, err, stream);
         if (st != GS_OK) return st;
         int64_t host_total = 0;
         hipEvent_t copied = nullptr;
