@@ -23,6 +23,20 @@ template <int K>
 constexpr int kUnroll = K > 3 ? 2 : 3;
 // cull word bit of a staged splat that may not take the composite's short step (bits 0-3: the waves it reaches)
 constexpr uint32_t kNotShort = 0x80000000u;
+// Index-word bit of a staged record that holds the conic's a and c themselves. The other records hold a / 2 and
+// c / 2, which is exact, and so is every product of the quadratic form then: a, c >= 2^-60 (and, within the cull's
+// exact case, a, c < 6e20 with |dx|, |dy| < 2.1e6 for any pixel of a region the splat is listed for), so with
+// |dx| >= 2^-26 whenever it is not 0 each product stays normal and finite, and halving commutes with rounding. The
+// sum a/2 dx^2 + c/2 dy^2 is then bit for bit 0.5 (a dx^2 + c dy^2), the specified form, one multiplication
+// shorter.
+constexpr int32_t kWholeConic = INT32_MIN;
+
+// The quadratic form of a staged record at (dx, dy), in the specified operation order; `whole`: the record holds a
+// and c themselves, else their halves.
+__device__ __forceinline__ float record_sigma(float a, float b, float c, bool whole, float dx, float dy) {
+    const float s = a * dx * dx + c * dy * dy;
+    return (whole ? 0.5f * s : s) + b * dx * dy;
+}
 
 struct RasterArgs {
     const float2 *means;
@@ -319,6 +333,10 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
     unsigned long long n_pass = 0, n_comp = 0, n_exec = 0, n_staged = 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const char *rec_base = reinterpret_cast<const char *>(s_rec);
+    // the transmittance threshold as a bit pattern ordered against non-negative finite floats as the threshold is
+    // (0 for +-0, below every such pattern when negative, above every one when NaN)
+    const float thr = a.transmittance_threshold;
+    const int thr_bits = thr > 0.0f ? __float_as_int(thr) : (thr == 0.0f ? 0 : (thr < 0.0f ? -1 : INT_MAX));
 
     for (int base = start; base < end; base += nthreads) {
         if (__syncthreads_and(done)) break;  // also orders the previous batch's LDS reads before refilling
@@ -337,14 +355,16 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             if (K > 1) col.y = cs[1];
             if (K > 2) col.z = cs[2];
             if (K > 3) col.w = cs[3];
-            s_rec[threadIdx.x * 3 + 0] = make_float4(m.x, m.y, ca, cb);
-            s_rec[threadIdx.x * 3 + 1] = make_float4(cc, o, __int_as_float(idx), __int_as_float(g));
-            s_rec[threadIdx.x * 3 + 2] = col;
             const CullBox box = cull_box(m, ca, cb, cc, o, a.alpha_cutoff, a.log_cutoff);
             // bit 31: the splat may not take the short step (its conic is not a well-conditioned positive-definite
-            // one within the cull's bounds, or a colour is not finite)
-            const bool well = box.exact && __builtin_isfinite(col.x) && __builtin_isfinite(col.y) &&
-                              __builtin_isfinite(col.z) && __builtin_isfinite(col.w);
+            // one within the cull's bounds with a, c >= 2^-60, or a colour is not finite); the others hold a / 2 and
+            // c / 2 (kWholeConic)
+            const bool well = box.exact && ca >= 0x1p-60f && cc >= 0x1p-60f && __builtin_isfinite(col.x) &&
+                              __builtin_isfinite(col.y) && __builtin_isfinite(col.z) && __builtin_isfinite(col.w);
+            s_rec[threadIdx.x * 3 + 0] = make_float4(m.x, m.y, well ? 0.5f * ca : ca, cb);
+            s_rec[threadIdx.x * 3 + 1] =
+                make_float4(well ? 0.5f * cc : cc, o, __int_as_float(well ? idx : (idx | kWholeConic)), __int_as_float(g));
+            s_rec[threadIdx.x * 3 + 2] = col;
             uint32_t bits = well ? 0u : kNotShort;
             if (!box.never) {
 #pragma unroll
@@ -383,7 +403,8 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             // by-reference captures cost registers)
             // The short step, for a batch whose listed splats all have well-conditioned positive-definite conics
             // (the cull's exact case: a > 0, c > 0, det > 0, trace^2 <= 1000 det, opacity in [cutoff, 1e6], mean
-            // within 1e6 px) and finite colours, with alpha_cutoff >= 1e-20. It gives the bits of the step below:
+            // within 1e6 px; and a, c >= 2^-60, so the records hold their halves) and finite colours, with
+            // alpha_cutoff >= 1e-20. It gives the bits of the step below:
             //  - such a conic's computed sigma is within 0.15% of the exact quadratic form at the same dx, dy (the
             //    cull's bound), so it is never negative and the sign test can go; an overflow gives +inf or NaN,
             //    never -inf (the cross term is at most half the diagonal terms);
@@ -392,7 +413,9 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             //    and alpha is used nowhere else;
             //  - E <= 1 keeps alpha finite, so min(alpha, clamp) is the clamp's select;
             //  - a splat that does not composite adds colour * 0 = +-0 to every accumulator, which changes none:
-            //    they start at +0, and a round-to-nearest sum is -0 only when both terms are, so none is ever -0.
+            //    they start at +0, and a round-to-nearest sum is -0 only when both terms are, so none is ever -0;
+            //  - t_next is finite and not negative, so its order against the threshold is that of the bit patterns,
+            //    and one comparison (as a wave mask and its complement) decides both halting and compositing.
             if (!long_step) {
                 for (; jj + kUnroll<K> <= listed; jj += kUnroll<K>) {
                     if (__ballot(!done) == 0) break;
@@ -412,7 +435,7 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                     for (int h = 0; h < kUnroll<K>; ++h) {
                         const float dx = q0[h].x - px;
                         const float dy = q0[h].y - py;
-                        const float sigma = 0.5f * (q0[h].z * dx * dx + q1[h].x * dy * dy) + q0[h].w * dx * dy;
+                        const float sigma = record_sigma(q0[h].z, q0[h].w, q1[h].x, false, dx, dy);
                         const float e = q1[h].y * (HWEXP ? exp_neg_hw(sigma) : exp_neg_poly(fminf(sigma, 100.0f)));
                         al[h] = fminf(e, a.alpha_clamp);
                     }
@@ -421,9 +444,14 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                         const float alpha = al[h];
                         if (COUNT && !done) ++n_exec;
                         const bool pass = !done && !(alpha < a.alpha_cutoff);
+                        // t_next is finite and not negative here (alpha in [0, clamp], T in [0, 1]), so its order against
+                        // the threshold is that of the bit patterns, and one comparison decides both outcomes
                         const float t_next = T * (1.0f - alpha);
-                        const bool halt = pass && t_next <= a.transmittance_threshold;
-                        const bool comp = pass && !halt;
+                        const uint64_t above_m = __ballot(__float_as_int(t_next) > thr_bits);
+                        const bool above = __builtin_amdgcn_inverse_ballot_w64(above_m);
+                        const bool below = __builtin_amdgcn_inverse_ballot_w64(~above_m);
+                        const bool halt = pass && below;
+                        const bool comp = pass && above;
                         const float v = comp ? alpha * T : 0.0f;
                         acc[0] = acc[0] + col[h].x * v;
                         if (K > 1) acc[1] = acc[1] + col[h].y * v;
@@ -458,7 +486,8 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                 for (int h = 0; h < kUnroll<K>; ++h) {
                     const float dx = q0[h].x - px;
                     const float dy = q0[h].y - py;
-                    sg[h] = 0.5f * (q0[h].z * dx * dx + q1[h].x * dy * dy) + q0[h].w * dx * dy;
+                    sg[h] = record_sigma(q0[h].z, q0[h].w, q1[h].x, at[h] < 0, dx, dy);
+                    at[h] &= INT32_MAX;
                     const float e = q1[h].y * (HWEXP ? exp_neg_hw(sg[h]) : exp_neg_select(sg[h]));
                     al[h] = e > a.alpha_clamp ? a.alpha_clamp : e;
                 }
@@ -491,9 +520,11 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             const char *rec = rec_base + s_list[wave][jj];
             const float4 r0 = *reinterpret_cast<const float4 *>(rec);
             const float2 r1 = *reinterpret_cast<const float2 *>(rec + 16);
+            const int word = __float_as_int(*reinterpret_cast<const float *>(rec + 24));
             const float dx = r0.x - px;
             const float dy = r0.y - py;
-            const float sigma = 0.5f * (r0.z * dx * dx + r1.x * dy * dy) + r0.w * dx * dy;
+            const float sigma = record_sigma(r0.z, r0.w, r1.x, word < 0, dx, dy);
+            const int at = word & INT32_MAX;
             float alpha = r1.y * (HWEXP ? exp_neg_hw(sigma) : exp_neg_select(sigma));
             alpha = alpha > a.alpha_clamp ? a.alpha_clamp : alpha;
             if constexpr (!TRACE) {
@@ -503,7 +534,6 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                 const bool halt = pass && t_next <= a.transmittance_threshold;
                 const bool comp = pass && !halt;
                 const float4 col = *reinterpret_cast<const float4 *>(rec + 32);
-                const int at = __float_as_int(*reinterpret_cast<const float *>(rec + 24));
                 const float v = alpha * T;
                 acc[0] = comp ? acc[0] + col.x * v : acc[0];
                 if (K > 1) acc[1] = comp ? acc[1] + col.y * v : acc[1];
@@ -524,7 +554,7 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                     const float t_next = T * (1.0f - alpha);
                     if (t_next <= a.transmittance_threshold) {
                         done = true;
-                        if (COUNT) stop = __float_as_int(*reinterpret_cast<const float *>(rec + 24)) + 1;
+                        if (COUNT) stop = at + 1;
                     } else {
                         if (COUNT) ++n_comp;
                         const float4 col = *reinterpret_cast<const float4 *>(rec + 32);
@@ -534,7 +564,7 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                         if (K > 2) acc[2] = acc[2] + col.z * v;
                         if (K > 3) acc[3] = acc[3] + col.w * v;
                         T = t_next;
-                        last = __float_as_int(*reinterpret_cast<const float *>(rec + 24));
+                        last = at;
                         my_trace[steps & (kTraceChunk - 1)] =
                             __float_as_int(*reinterpret_cast<const float *>(rec + 28));
                         ++steps;
