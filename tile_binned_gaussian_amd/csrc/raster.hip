@@ -408,9 +408,9 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
             //  - such a conic's computed sigma is within 0.15% of the exact quadratic form at the same dx, dy (the
             //    cull's bound), so it is never negative and the sign test can go; an overflow gives +inf or NaN,
             //    never -inf (the cross term is at most half the diagonal terms);
-            //  - sigma <= 80 takes the same polynomial; above 80, or NaN, the polynomial at min(sigma, 100) is below
-            //    2e-35, so alpha (at most 1e6 times that) fails the cutoff exactly as the specified alpha of 0 does,
-            //    and alpha is used nowhere else;
+            //  - sigma <= 80 takes the same polynomial (exp_neg_short, exact there); above 80, or NaN, it is taken at
+            //    min(sigma, 80), which gives e^-80 < 2e-35, so alpha (at most 1e6 times that) fails the cutoff exactly
+            //    as the specified alpha of 0 does, and alpha is used nowhere else;
             //  - E <= 1 keeps alpha finite, so min(alpha, clamp) is the clamp's select;
             //  - a splat that does not composite adds colour * 0 = +-0 to every accumulator, which changes none:
             //    they start at +0, and a round-to-nearest sum is -0 only when both terms are, so none is ever -0;
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                         const float dx = q0[h].x - px;
                         const float dy = q0[h].y - py;
                         const float sigma = record_sigma(q0[h].z, q0[h].w, q1[h].x, false, dx, dy);
-                        const float e = q1[h].y * (HWEXP ? exp_neg_hw(sigma) : exp_neg_poly(fminf(sigma, 100.0f)));
+                        const float e = q1[h].y * (HWEXP ? exp_neg_hw(sigma) : exp_neg_short(fminf(sigma, 80.0f)));
                         al[h] = fminf(e, a.alpha_clamp);
                     }
 #pragma unroll

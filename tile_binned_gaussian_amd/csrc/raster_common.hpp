@@ -29,11 +29,9 @@ __device__ __forceinline__ float exp_neg(float sigma) {
     return __builtin_ldexpf(q, static_cast<int>(k));
 }
 
-// The reduction and polynomial of exp_neg without its range test: Cody and Waite's reduction and the degree-7
-// Taylor polynomial, q = e^r with -sigma = k ln 2 + r.
-__device__ __forceinline__ float exp_neg_parts(float sigma, float &k) {
-    const float t = -sigma;
-    k = __builtin_rintf(t * 0x1.715476p+0f);  // 1 / ln 2
+// Cody and Waite's reduction r = t - k ln 2 (ln 2 split as in exp_neg) and the degree-7 Taylor polynomial q = e^r,
+// for t = -sigma and k = rint(t / ln 2) given.
+__device__ __forceinline__ float exp_reduced_poly(float t, float k) {
     float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);
     r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);
     float q = 0x1.a01a02p-13f;
@@ -47,6 +45,13 @@ __device__ __forceinline__ float exp_neg_parts(float sigma, float &k) {
     return q;
 }
 
+// The reduction and polynomial of exp_neg without its range test: q = e^r with -sigma = k ln 2 + r.
+__device__ __forceinline__ float exp_neg_parts(float sigma, float &k) {
+    const float t = -sigma;
+    k = __builtin_rintf(t * 0x1.715476p+0f);  // 1 / ln 2
+    return exp_reduced_poly(t, k);
+}
+
 // The same function without branches (a select replaces the early return), for lock-step loops where every lane
 // evaluates it anyway. Identical bits: the polynomial path is the one above, and any sigma that is not <= 80
 // (including NaN) selects 0.
@@ -58,12 +63,17 @@ __device__ __forceinline__ float exp_neg_select(float sigma) {
     return (sigma <= 80.0f) ? e : 0.0f;
 }
 
-// The polynomial path alone, for sigma <= 100 (k then lies in [-145, 116], so the conversion and scale are exact):
-// equal to exp_neg for sigma <= 80, and below 2e-35 on (80, 100].
-__device__ __forceinline__ float exp_neg_poly(float sigma) {
-    float k;
-    const float q = exp_neg_parts(sigma, k);
-    return __builtin_ldexpf(q, static_cast<int>(k));
+// exp_neg for 0 <= sigma <= 80 (the polynomial path), with k = rint(-sigma / ln 2) formed by adding and subtracting
+// 1.5 * 2^23 (which rounds the already rounded product to the nearest integer, ties to even, as rintf does, since
+// |k| <= 116) and 2^k applied by adding k to the exponent field of q (in [0.7, 1.42]): the result's exponent stays
+// at 2^-117 or above, so the sum is the exact scaling, and the bits are exp_neg's. Both steps are plain adds, which
+// issue in pairs where the rounding, conversion and ldexp instructions do not.
+__device__ __forceinline__ float exp_neg_short(float sigma) {
+    const float t = -sigma;
+    const float shifted = t * 0x1.715476p+0f + 0x1.8p+23f;  // 1 / ln 2; k in the low bits
+    const float q = exp_reduced_poly(t, shifted - 0x1.8p+23f);
+    // (bits(shifted) << 23) is k << 23 modulo 2^32: the constant's own bits lie at positions 22 and up
+    return __int_as_float(__float_as_int(q) + static_cast<int>(static_cast<uint32_t>(__float_as_int(shifted)) << 23));
 }
 
 // e^-sigma by the hardware base-2 exponential (v_exp_f32, about 1 ulp) of -sigma log2(e): a product and one
