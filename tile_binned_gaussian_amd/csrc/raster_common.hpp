@@ -147,16 +147,18 @@ __device__ __forceinline__ float quad_form(float a, float b, float c, float dx, 
 }
 
 // Whether sigma can be <= thr somewhere in the box [x0, x1] x [y0, y1]: yes if the mean is inside; otherwise the
-// minimum of the convex quadratic lies on an edge, where it is a one-dimensional quadratic minimised at the
-// clamped stationary point.
+// minimum of the convex quadratic lies on the boundary, on an edge that faces the mean (at a minimiser inside the
+// top edge the gradient is (0, -t), t >= 0, which for a positive-definite form means the mean lies on or above the
+// top edge's line, and likewise for the other edges), so only the edge nearest the mean in x and the one nearest
+// in y are searched, each a one-dimensional quadratic minimised at the clamped stationary point. A nearest edge
+// with the mean within its range is merely one more point of the box, which leaves the minimum found unchanged.
 __device__ __forceinline__ bool region_reach(float2 m, float a, float b, float c, float ra, float rc, float thr,
                                              float x0, float x1, float y0, float y1) {
     if (m.x >= x0 && m.x <= x1 && m.y >= y0 && m.y <= y1) return true;
     const float lx = x0 - m.x, hx = x1 - m.x, ly = y0 - m.y, hy = y1 - m.y;
-    float best = quad_form(a, b, c, lx, fminf(fmaxf(-b * lx * rc, ly), hy));
-    best = fminf(best, quad_form(a, b, c, hx, fminf(fmaxf(-b * hx * rc, ly), hy)));
-    best = fminf(best, quad_form(a, b, c, fminf(fmaxf(-b * ly * ra, lx), hx), ly));
-    best = fminf(best, quad_form(a, b, c, fminf(fmaxf(-b * hy * ra, lx), hx), hy));
+    const float ex = m.x < x0 ? lx : hx, ey = m.y < y0 ? ly : hy;
+    const float best = fminf(quad_form(a, b, c, ex, fminf(fmaxf(-b * ex * rc, ly), hy)),
+                             quad_form(a, b, c, fminf(fmaxf(-b * ey * ra, lx), hx), ey));
     return best <= thr;
 }
 
