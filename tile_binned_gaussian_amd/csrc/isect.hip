@@ -210,9 +210,9 @@ __device__ __forceinline__ int floor_div(int k, int w, float rcp_w) {
 
 // Phase 2: a chunk is 256 consecutive positions (splat perm[j], or j without a permutation); their outputs occupy
 // the contiguous slots [start(g0), start(g0 + 256)). Each thread walks slots with stride 256, finds the owning
-// position (the last one whose start is <= slot) by an unrolled branchless binary search in LDS, and writes key and
-// id for tile k of that splat's rectangle in row-major order (row = k / width by a float reciprocal kept per
-// position, corrected to the exact quotient). With a permutation, sorted_depth[j] holds the depth bits of splat
+// position (the last one whose start is <= slot) by an unrolled branchless binary search in LDS, reads that
+// position's two 16-byte LDS records, and writes key and id for tile k of that splat's rectangle in row-major order
+// (row = k / width by a float reciprocal kept per position, corrected to the exact quotient). With a permutation, sorted_depth[j] holds the depth bits of splat
 // perm[j] (read in order instead of gathered), and sorted_rects[j] its rectangle (int4, or one packed word when
 // pk.cx is nonzero), so no splat data is gathered.
 // Workgroups stride over chunks, so the digit histograms (hist non-null) are flushed to global memory once per
@@ -231,9 +231,9 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                                                         uint32_t *__restrict__ hist, PassPlan hplan) {
     __shared__ uint32_t s_hist[kMaxPasses][kThreads];
     __shared__ int s_start[kThreads + 1];
-    __shared__ int s_x0[kThreads], s_y0[kThreads], s_w[kThreads], s_id[kThreads];
-    __shared__ float s_rcp_w[kThreads];
-    __shared__ uint32_t s_upper_cam[kThreads], s_depth[kThreads];
+    // per position: (start, x0, y0, width) and (1 / width, camera bits, depth bits, id), two 16-byte LDS reads
+    __shared__ int4 s_pa[kThreads];
+    __shared__ uint4 s_pb[kThreads];
     const RunLanes rl = run_lanes();
     if (hist)
         for (int p = 0; p < hplan.passes; ++p) s_hist[p][threadIdx.x] = 0;
@@ -245,34 +245,32 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
         if (j < M) {
             int i = perm ? perm[j] : j;
             if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) i = 0;  // only with a corrupted workspace
+            int x0, y0, w;
             if (sorted_rects) {
                 const int4 r = pk.cx ? unpack_rect(static_cast<const uint32_t *>(sorted_rects)[j], pk)
                                      : static_cast<const int4 *>(sorted_rects)[j];
-                s_x0[threadIdx.x] = r.x;
-                s_y0[threadIdx.x] = r.y;
-                s_w[threadIdx.x] = r.z;
+                x0 = r.x;
+                y0 = r.y;
+                w = r.z;
             } else {
                 const Rect r = rect_of<RPG>(means, radii, i, ts, tw, th);
-                s_x0[threadIdx.x] = r.x0;
-                s_y0[threadIdx.x] = r.y0;
-                s_w[threadIdx.x] = r.x1 - r.x0;
+                x0 = r.x0;
+                y0 = r.y0;
+                w = r.x1 - r.x0;
             }
             // a slot never maps to an empty rectangle unless the offsets are corrupt; width 1 keeps the division
             // defined
-            const int w = max(s_w[threadIdx.x], 1);
-            s_w[threadIdx.x] = w;
-            s_rcp_w[threadIdx.x] = 1.0f / static_cast<float>(w);
-            s_start[threadIdx.x] = min(max(gauss_offsets[j], 0), n);
-            s_depth[threadIdx.x] = sorted_depth ? sorted_depth[j] : depth_bits[i];
-            s_upper_cam[threadIdx.x] = static_cast<uint32_t>(i / N) << tile_bits;
-            s_id[threadIdx.x] = i;
+            w = max(w, 1);
+            const int start = min(max(gauss_offsets[j], 0), n);
+            s_start[threadIdx.x] = start;
+            s_pa[threadIdx.x] = make_int4(start, x0, y0, w);
+            s_pb[threadIdx.x] = make_uint4(__float_as_uint(1.0f / static_cast<float>(w)),
+                                           static_cast<uint32_t>(i / N) << tile_bits,
+                                           sorted_depth ? sorted_depth[j] : depth_bits[i], static_cast<uint32_t>(i));
         } else {
             s_start[threadIdx.x] = n;
-            s_w[threadIdx.x] = 1;
-            s_rcp_w[threadIdx.x] = 1.0f;
-            s_x0[threadIdx.x] = s_y0[threadIdx.x] = 0;
-            s_depth[threadIdx.x] = s_upper_cam[threadIdx.x] = 0;
-            s_id[threadIdx.x] = 0;
+            s_pa[threadIdx.x] = make_int4(n, 0, 0, 1);
+            s_pb[threadIdx.x] = make_uint4(__float_as_uint(1.0f), 0u, 0u, 0u);
         }
         if (threadIdx.x == 0)
             s_start[kThreads] = (g0 + kThreads < M) ? min(max(gauss_offsets[g0 + kThreads], 0), n) : n;
@@ -294,17 +292,19 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
 #pragma unroll
             for (int step = kThreads / 2; step > 0; step >>= 1)
                 if (s_start[lo + step] <= sl) lo += step;
-            const int k = sl - s_start[lo];
-            const int w = s_w[lo];
-            const int ry = floor_div(k, w, s_rcp_w[lo]);
+            const int4 pa = s_pa[lo];
+            const uint4 pb = s_pb[lo];
+            const int k = sl - pa.x;
+            const int w = pa.w;
+            const int ry = floor_div(k, w, __uint_as_float(pb.x));
             const int rx = k - ry * w;
-            const uint32_t tile = static_cast<uint32_t>(s_y0[lo] + ry) * static_cast<uint32_t>(tw) +
-                                  static_cast<uint32_t>(s_x0[lo] + rx);
-            const uint64_t upper = static_cast<uint64_t>(s_upper_cam[lo] | tile);
-            const uint64_t key = (upper << 32) | static_cast<uint64_t>(s_depth[lo]);
+            const uint32_t tile = static_cast<uint32_t>(pa.z + ry) * static_cast<uint32_t>(tw) +
+                                  static_cast<uint32_t>(pa.y + rx);
+            const uint64_t upper = static_cast<uint64_t>(pb.y | tile);
+            const uint64_t key = (upper << 32) | static_cast<uint64_t>(pb.z);
             if (in) {
                 keys[slot] = key;
-                ids[slot] = s_id[lo];
+                ids[slot] = static_cast<int32_t>(pb.w);
             }
             if (hist) {
                 // consecutive lanes hold consecutive slots: a run of equal digits adds its length once; every
