@@ -366,7 +366,9 @@ __global__ __launch_bounds__(kMaxThreads, (TRACE || COUNT) ? 1 : 8) void raster_
                 make_float4(well ? 0.5f * cc : cc, o, __int_as_float(well ? idx : (idx | kWholeConic)), __int_as_float(g));
             s_rec[threadIdx.x * 3 + 2] = col;
             uint32_t bits = well ? 0u : kNotShort;
-            if (!box.never) {
+            if (!box.never && quadrants && box.exact) {
+                bits |= quadrant_reach(m, ca, cb, cc, box, static_cast<float>(tile_x0), static_cast<float>(tile_y0));
+            } else if (!box.never) {
 #pragma unroll
                 for (int w = 0; w < kMaxThreads / kWave; ++w) {
                     float qx0, qx1, qy0, qy1;

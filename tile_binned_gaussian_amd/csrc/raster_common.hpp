@@ -162,5 +162,49 @@ __device__ __forceinline__ bool region_reach(float2 m, float a, float b, float c
     return best <= thr;
 }
 
+// region_reach for the four 8 x 8 quadrants of a 16 x 16 tile at once: quadrant w covers the pixel-centre box
+// [ox + 8 (w & 1) + 0.5, ox + 8 (w & 1) + 7.5] x [oy + 8 (w >> 1) + 0.5, oy + 8 (w >> 1) + 7.5] (ox, oy: the tile's
+// first pixel). Bit w is set when the splat's box overlaps quadrant w and the region test passes for it, with the
+// values region_reach computes (so the same decisions): the quadrants share two x ranges and two y ranges, so each
+// range's edge offsets, nearest edge, stationary-point product and a ex^2 (c ey^2) term are computed once.
+__device__ __forceinline__ uint32_t quadrant_reach(float2 m, float a, float b, float c, const CullBox &box, float ox,
+                                                   float oy) {
+    float lx[2], hx[2], ex[2], sx[2], ax[2], ly[2], hy[2], ey[2], sy[2], cy[2];
+    bool xo[2], xin[2], yo[2], yin[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float x0 = ox + (i ? 8.5f : 0.5f), x1 = ox + (i ? 15.5f : 7.5f);
+        xo[i] = box.x1 >= x0 && box.x0 <= x1;
+        xin[i] = m.x >= x0 && m.x <= x1;
+        lx[i] = x0 - m.x;
+        hx[i] = x1 - m.x;
+        ex[i] = m.x < x0 ? lx[i] : hx[i];
+        sx[i] = -b * ex[i] * box.rc;
+        ax[i] = a * ex[i] * ex[i];
+        const float y0 = oy + (i ? 8.5f : 0.5f), y1 = oy + (i ? 15.5f : 7.5f);
+        yo[i] = box.y1 >= y0 && box.y0 <= y1;
+        yin[i] = m.y >= y0 && m.y <= y1;
+        ly[i] = y0 - m.y;
+        hy[i] = y1 - m.y;
+        ey[i] = m.y < y0 ? ly[i] : hy[i];
+        sy[i] = -b * ey[i] * box.ra;
+        cy[i] = c * ey[i] * ey[i];
+    }
+    uint32_t bits = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int i = w & 1, j = w >> 1;
+        // the nearest x edge at its clamped stationary y, and the nearest y edge at its clamped stationary x, as
+        // quad_form evaluates them
+        const float dyx = fminf(fmaxf(sx[i], ly[j]), hy[j]);
+        const float dxy = fminf(fmaxf(sy[j], lx[i]), hx[i]);
+        const float qx = 0.5f * (ax[i] + c * dyx * dyx) + b * ex[i] * dyx;
+        const float qy = 0.5f * (a * dxy * dxy + cy[j]) + b * dxy * ey[j];
+        const bool reach = (xin[i] && yin[j]) || fminf(qx, qy) <= box.thr;
+        bits |= (xo[i] && yo[j] && reach ? 1u : 0u) << w;
+    }
+    return bits;
+}
+
 }  // namespace
 }  // namespace gs
