@@ -81,9 +81,9 @@ gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_k
 // The splats' depth order for the emission: the passes of plan (histograms already accumulated by the caller, and
 // in row plan.passes of the histogram copies the tile counts by the last pass's digit), the last one (8 bits) also
 // writing, for every position of the order, the rectangle of its splat (gathered from rects, in splat order; int4,
-// or one packed word when pk.cx is nonzero) and its first output slot (the exclusive prefix of the tile counts in that order). Pass p writes buffer A when p is
-// even and B when odd; *result_in_b tells where the order lands. order_status holds depth_order_status_bytes(n)
-// bytes, zero before the call.
+// or one packed word when pk.cx is nonzero) and its first output slot (the exclusive prefix of the tile counts in
+// that order). Pass p writes buffer A when p is even and B when odd; *result_in_b tells where the order lands.
+// order_status holds depth_order_status_bytes(n) bytes, zero before the call.
 size_t depth_order_status_bytes(int64_t n);
 gs_status depth_order_passes(const uint32_t *depth_bits, uint32_t *buf_a_keys, int32_t *buf_a_ids,
                              uint32_t *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,

@@ -212,11 +212,11 @@ __device__ __forceinline__ int floor_div(int k, int w, float rcp_w) {
 // the contiguous slots [start(g0), start(g0 + 256)). Each thread walks slots with stride 256, finds the owning
 // position (the last one whose start is <= slot) by an unrolled branchless binary search in LDS, reads that
 // position's two 16-byte LDS records, and writes key and id for tile k of that splat's rectangle in row-major order
-// (row = k / width by a float reciprocal kept per position, corrected to the exact quotient). With a permutation, sorted_depth[j] holds the depth bits of splat
-// perm[j] (read in order instead of gathered), and sorted_rects[j] its rectangle (int4, or one packed word when
-// pk.cx is nonzero), so no splat data is gathered.
-// Workgroups stride over chunks, so the digit histograms (hist non-null) are flushed to global memory once per
-// workgroup, into the histogram copy of that workgroup.
+// (row = k / width by a float reciprocal kept per position, corrected to the exact quotient). With a permutation,
+// sorted_depth[j] holds the depth bits of splat perm[j] (read in order instead of gathered), and sorted_rects[j]
+// its rectangle (int4, or one packed word when pk.cx is nonzero), so no splat data is gathered. Workgroups stride
+// over chunks, so the digit histograms (hist non-null) are flushed to global memory once per workgroup, into the
+// histogram copy of that workgroup.
 static_assert(kThreads * kMaxPasses == kHistCopyWords, "one emission thread per digit of the histograms");
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict__ means,
