@@ -93,7 +93,8 @@ const char *gs_last_error(void);
  *   behind the count, runs while the host returns; with pageable memory a copy call waits for the count first.
  *   Phase 2 must then receive a workspace that starts with those bytes unchanged: the same buffer (sized for
  *   phase 2 from the start), or a larger one into which the caller copied them on the same stream. A workspace
- *   without them gives a wrong order (never an access outside the buffers).
+ *   without them gives a wrong order (never an access outside the buffers). Phase 2 accumulates the tile sort's
+ *   digit counts in those bytes and zeroes them again as it reads them, so they serve a later phase 2 too.
  */
 size_t gs_isect_workspace_bytes(int64_t C, int64_t N, int64_t n_isects, int tile_width, int tile_height, int sort);
 

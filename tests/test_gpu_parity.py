@@ -266,6 +266,42 @@ def test_count_into_pageable_and_pinned_memory_agree():
     assert int(pinned[0]) == expected
 
 
+@pytest.mark.parametrize("name", ["multicam-ragged-elliptical", "two-tile-passes"])
+def test_isect_phase2_repeats_on_one_prefix(name):
+    """Phase 2 run three times on the prefix one phase 1 left: the tile sort keeps its digit counts in that prefix
+    and zeroes them as it reads them, so every run gives the oracle's sorted intersections."""
+    import ctypes
+    scene = (synth.random_scene(43, 3, 3000, 640, 360, 8, elliptical=True) if name == "two-tile-passes"
+             else SCENES[name]())
+    lib = binding.load_library()
+    m, r, d = dev(scene.means2d), dev(scene.radii), dev(scene.depths)
+    C, N = scene.C, scene.N
+    rpg = 2 if scene.radii.ndim == 3 else 1
+    expected = oracle.isect_tiles(scene.means2d, scene.radii, scene.depths, scene.tile_size, scene.tile_width,
+                                  scene.tile_height, sort=True)
+    n = expected.n_isects
+    ws = torch.empty(lib.gs_isect_workspace_bytes(C, N, n, scene.tile_width, scene.tile_height, 1),
+                     dtype=torch.uint8, device="cuda")
+    tpg = torch.empty((C, N), dtype=torch.int32, device="cuda")
+    goff = torch.empty(C * N, dtype=torch.int32, device="cuda")
+    s = binding._stream(None)
+    count = ctypes.c_int64(-1)
+    binding._check(lib.gs_isect_tiles(binding._ptr(m), binding._ptr(r), rpg, binding._ptr(d), C, N, scene.tile_size,
+                                      scene.tile_width, scene.tile_height, 1, binding._ptr(tpg), binding._ptr(goff),
+                                      ctypes.byref(count), None, None, 0, binding._ptr(ws), ws.numel(), s))
+    assert count.value == n
+    for _ in range(3):
+        keys = torch.full((n,), -1, dtype=torch.int64, device="cuda")
+        ids = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        binding._check(lib.gs_isect_tiles(binding._ptr(m), binding._ptr(r), rpg, binding._ptr(d), C, N,
+                                          scene.tile_size, scene.tile_width, scene.tile_height, 1, None,
+                                          binding._ptr(goff), None, binding._ptr(keys), binding._ptr(ids), n,
+                                          binding._ptr(ws), ws.numel(), s))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(keys_u64(keys), expected.keys)
+        np.testing.assert_array_equal(host(ids), expected.flatten_ids)
+
+
 def test_frame_is_deterministic():
     scene = SCENES["multicam-ragged-elliptical"]()
     a, b = gpu_frame(scene), gpu_frame(scene)

@@ -65,6 +65,23 @@ struct SortScratchLayout {
 };
 SortScratchLayout sort_scratch_layout(int64_t n);
 
+// The scratch of one sort as separate regions (the contiguous layout above, or regions a caller places itself):
+// histogram copies (kHistCopies x kHistCopyWords words), partition counters (kMaxPasses words), two look-back arrays
+// of parts x 256 words and the digit starts (kMaxPasses x 256 words).
+struct SortScratch {
+    uint32_t *hist, *counters, *status0, *status1, *starts;
+    int64_t parts;
+};
+SortScratch sort_scratch(void *scratch, int64_t n);
+// The contiguous layout in two pieces: the head (histogram copies and counters, the same size for every n) and the
+// tail (look-back arrays and digit starts), each at its own address.
+size_t sort_scratch_head_bytes();
+size_t sort_scratch_tail_bytes(int64_t n);
+SortScratch sort_scratch_split(void *head, void *tail, int64_t n);
+// Partitions of one digit pass over n pairs of KeyT keys: its look-back array spans that many times 256 words.
+template <typename KeyT>
+int64_t radix_partitions(int64_t n);
+
 // Clears the scratch's histograms, partition counters and first look-back array for a sort of n pairs.
 gs_status radix_prepare(int64_t n, void *scratch, hipStream_t stream);
 // Bytes at the start of the scratch that radix_prepare clears (a caller may clear them itself instead).
@@ -77,6 +94,14 @@ template <typename KeyT>
 gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                        KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
                        hipStream_t stream, int *result_in_b);
+// The same with the scratch in separate regions. The histogram copies must be zero before the caller accumulates
+// the histograms and the first look-back array zero when the passes start; the digit starts step zeroes the
+// histogram entries once it has read them and resets the passes' partition counters itself, so after a sort the
+// histogram copies are ready for the next one.
+template <typename KeyT>
+gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                       KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,
+                       const SortScratch &scratch, hipStream_t stream, int *result_in_b);
 
 // The splats' depth order for the emission: the passes of plan (histograms already accumulated by the caller, and
 // in row plan.passes of the histogram copies the tile counts by the last pass's digit), the last one (8 bits) also

@@ -216,7 +216,8 @@ __device__ __forceinline__ int floor_div(int k, int w, float rcp_w) {
 // sorted_depth[j] holds the depth bits of splat perm[j] (read in order instead of gathered), and sorted_rects[j]
 // its rectangle (int4, or one packed word when pk.cx is nonzero), so no splat data is gathered. Workgroups stride
 // over chunks, so the digit histograms (hist non-null) are flushed to global memory once per workgroup, into the
-// histogram copy of that workgroup.
+// histogram copy of that workgroup. The workgroups also zero clear[0, 4 * clear_quads) (the first look-back array
+// of the sort that follows), so no separate clearing launch precedes it.
 static_assert(kThreads * kMaxPasses == kHistCopyWords, "one emission thread per digit of the histograms");
 template <int RPG>
 __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict__ means,
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
                                                         const void *__restrict__ sorted_rects, RectPacking pk,
                                                         const int32_t *__restrict__ gauss_offsets, int n,
                                                         uint64_t *__restrict__ keys, int32_t *__restrict__ ids,
-                                                        uint32_t *__restrict__ hist, PassPlan hplan) {
+                                                        uint32_t *__restrict__ hist, PassPlan hplan,
+                                                        uint4 *__restrict__ clear, int clear_quads) {
     __shared__ uint32_t s_hist[kMaxPasses][kThreads];
     __shared__ int s_start[kThreads + 1];
     // per position: (start, x0, y0, width) and (1 / width, camera bits, depth bits, id), two 16-byte LDS reads
@@ -237,6 +239,8 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
     const RunLanes rl = run_lanes();
     if (hist)
         for (int p = 0; p < hplan.passes; ++p) s_hist[p][threadIdx.x] = 0;
+    for (int q = blockIdx.x * kThreads + threadIdx.x; q < clear_quads; q += gridDim.x * kThreads)
+        clear[q] = make_uint4(0u, 0u, 0u, 0u);
     const int chunks = (M + kThreads - 1) / kThreads;
     for (int chunk = blockIdx.x; chunk < chunks; chunk += gridDim.x) {
         const int g0 = chunk * kThreads;
@@ -335,11 +339,12 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const float2 *__restrict
 // see it at the same offsets: the total, the count scan's status words, and, when sorting, the look-back words of
 // the depth sort's last pass, the depth sort's scratch, the depth order of the splats (two u32/i32 ping-pong pairs
 // of M), the rectangles (in splat order and in depth order; 4 or 16 bytes each) and the per-position offsets in
-// that order. [clear_begin, clear_end) is what phase 1 clears before it starts: the status and look-back words and
-// the part of the depth sort's scratch that must start at zero. Phase 2 adds, when sorting more than one
-// intersection, the alternate intersection buffers and the tile sort's scratch.
+// that order. [clear_begin, clear_end) is what phase 1 clears before it starts: the status and look-back words, the
+// tile sort's histogram copies and partition counters, and the part of the depth sort's scratch that must start at
+// zero. Phase 2 adds, when sorting more than one intersection, the alternate intersection buffers and the rest of
+// the tile sort's scratch (its look-back arrays and digit starts).
 struct IsectLayout {
-    size_t total, count_status, order_status, depth_scratch, clear_begin, clear_end;
+    size_t total, count_status, order_status, tile_head, depth_scratch, clear_begin, clear_end;
     size_t dkeys_a, dids_a, dkeys_b, dids_b, rects, sorted_rects, sorted_offsets, prefix;
     size_t alt_keys, alt_ids, tile_scratch, bytes;
 };
@@ -357,6 +362,8 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
         const size_t m = static_cast<size_t>(M > 0 ? M : 1);
         L.order_status = align_up(c.used, 256);
         c.take<char>(depth_order_status_bytes(static_cast<int64_t>(m)));
+        L.tile_head = align_up(c.used, 256);
+        c.take<char>(sort_scratch_head_bytes());
         L.depth_scratch = align_up(c.used, 256);
         c.take<char>(sort_scratch_layout(static_cast<int64_t>(m)).bytes);
         L.clear_end = L.depth_scratch + radix_clear_bytes(static_cast<int64_t>(m));
@@ -383,7 +390,7 @@ IsectLayout isect_layout(int64_t M, int64_t n, int sort) {
     L.alt_ids = align_up(c.used, 256);
     c.take<int32_t>(nn);
     L.tile_scratch = align_up(c.used, 256);
-    c.take<char>(sort_scratch_layout(n).bytes);
+    c.take<char>(sort_scratch_tail_bytes(n));
     L.bytes = align_up(c.used, 256);
     return L;
 }
@@ -425,25 +432,36 @@ gs_status launch_count_scan(int rpg, const float2 *m2, const float *radii, const
 }
 
 // hist (nullable): accumulate the digit histograms of the emitted keys for the passes of hplan, whose digits must
-// all lie in the keys' upper words (bits 32..63).
+// all lie in the keys' upper words (bits 32..63). clear (nullable, 16-byte aligned): clear_words words (a multiple
+// of 4) the emission zeroes.
 gs_status launch_emit(int rpg, const float2 *m2, const float *radii, const uint32_t *dbits, int M, int N, float ts,
                       int tw, int th, int tile_bits, const int32_t *perm, const uint32_t *sorted_depth,
                       const void *sorted_rects, RectPacking pk, const int32_t *offsets, int n, uint64_t *keys,
                       int32_t *ids,
-                      uint32_t *hist, const PassPlan &hplan, hipStream_t stream) {
+                      uint32_t *hist, const PassPlan &hplan, uint32_t *clear, int64_t clear_words,
+                      hipStream_t stream) {
     if (hist)
         for (int p = 0; p < hplan.passes; ++p)
             if (hplan.shift[p] < 32 || hplan.shift[p] + hplan.bits[p] > 64)
                 return fail(GS_ERR_INVALID_ARG, "emission histogram pass %d over bits [%d, %d) outside the upper word", p,
                             hplan.shift[p], hplan.shift[p] + hplan.bits[p]);
+    if (!clear) clear_words = 0;
+    if (clear_words % 4 != 0 || clear_words / 4 >= (int64_t(1) << 31) ||
+        reinterpret_cast<uintptr_t>(clear) % alignof(uint4) != 0)
+        return fail(GS_ERR_INVALID_ARG, "emission: %lld words to clear are not whole aligned 16-byte units",
+                    (long long)clear_words);
+    uint4 *cq = reinterpret_cast<uint4 *>(clear);
+    const int quads = static_cast<int>(clear_words / 4);
     const int chunks = (M + kThreads - 1) / kThreads;
     const int blocks = chunks < kEmitBlocks ? chunks : kEmitBlocks;
     if (rpg == 2)
         hipLaunchKernelGGL(emit_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, sorted_depth, sorted_rects, pk, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, sorted_rects, pk, offsets, n, keys, ids, hist, hplan, cq,
+                           quads);
     else
         hipLaunchKernelGGL(emit_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, m2, radii, dbits, M, N, ts, tw,
-                           th, tile_bits, perm, sorted_depth, sorted_rects, pk, offsets, n, keys, ids, hist, hplan);
+                           th, tile_bits, perm, sorted_depth, sorted_rects, pk, offsets, n, keys, ids, hist, hplan, cq,
+                           quads);
     GS_LAUNCH_TRY("emit_kernel");
     return ok();
 }
@@ -594,7 +612,7 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     if (!(sort && n > 1))  // emission in (camera, splat, tile row, tile column) order
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
                            tile_bits, nullptr, nullptr, nullptr, pk, gauss_offsets, n, keys, flatten_ids, nullptr,
-                           PassPlan{}, stream);
+                           PassPlan{}, nullptr, 0, stream);
 
     // Sorted output. Phase 1 put the splats in stable (depth bits, flat id) order and computed each position's
     // first output slot in that order; emitting each splat's tiles in that order makes the intersections ordered
@@ -604,7 +622,10 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     const uint32_t *sorted_depth = at<uint32_t>(workspace, depth_in_b ? L.dkeys_b : L.dkeys_a);
     const int32_t *sorted_offsets = at<int32_t>(workspace, L.sorted_offsets);
     const void *sorted_rects = at<void>(workspace, L.sorted_rects);
-    void *scratch = at<char>(workspace, L.tile_scratch);
+    // the tile sort's histogram copies and counters sit in the prefix (zero after phase 1, and again after every
+    // tile sort); its look-back arrays and digit starts follow the alternate buffers
+    const SortScratch scratch =
+        sort_scratch_split(at<char>(workspace, L.tile_head), at<char>(workspace, L.tile_scratch), n);
     const PassPlan tile_plan = make_pass_plan(32, 32 + tile_bits + cam_bits);
     uint64_t *alt_keys = at<uint64_t>(workspace, L.alt_keys);
     int32_t *alt_ids = at<int32_t>(workspace, L.alt_ids);
@@ -615,13 +636,12 @@ extern "C" gs_status gs_isect_tiles(const float *means2d, const float *radii, in
     if (tile_plan.passes == 0)
         return launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
                            tile_bits, perm, sorted_depth, sorted_rects, pk, sorted_offsets, n, emit_keys, emit_ids,
-                           nullptr, PassPlan{}, stream);
-    // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them
-    gs_status st = radix_prepare(n, scratch, stream);
-    if (st != GS_OK) return st;
-    st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height, tile_bits,
-                     perm, sorted_depth, sorted_rects, pk, sorted_offsets, n, emit_keys, emit_ids,
-                     radix_histograms(scratch, n), tile_plan, stream);
+                           nullptr, PassPlan{}, nullptr, 0, stream);
+    // the emission also accumulates the tile passes' digit histograms, so the keys are not read again for them,
+    // and zeroes the first pass's look-back array
+    gs_status st = launch_emit(radii_per_gauss, m2, radii, dbits, M, static_cast<int>(N), ts, tile_width, tile_height,
+                               tile_bits, perm, sorted_depth, sorted_rects, pk, sorted_offsets, n, emit_keys, emit_ids,
+                               scratch.hist, tile_plan, scratch.status0, radix_partitions<uint64_t>(n) * 256, stream);
     if (st != GS_OK) return st;
     int in_b = 0;
     if (odd)

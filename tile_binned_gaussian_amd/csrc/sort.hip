@@ -164,14 +164,21 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const KeyT *__r
 // Global start of every digit bucket of every pass: for pass p and digit d, the number of keys whose digit p is
 // below d, summed over the histogram copies. One workgroup of 256 threads per pass (blockIdx.x = p), one thread per
 // digit; computed once per sort, so a digit pass's partitions only load their digit's start (off their critical
-// path) instead of each summing the copies and scanning them.
-__global__ __launch_bounds__(kRadix) void digit_starts_kernel(const uint32_t *__restrict__ hist,
-                                                          uint32_t *__restrict__ starts) {
+// path) instead of each summing the copies and scanning them. With counters non-null the step also readies the
+// scratch for the next sort: it zeroes the histogram entries it has read and resets pass p's partition counter.
+__global__ __launch_bounds__(kRadix) void digit_starts_kernel(uint32_t *__restrict__ hist,
+                                                          uint32_t *__restrict__ starts,
+                                                          uint32_t *__restrict__ counters) {
     __shared__ uint32_t s_w[kRadix / kWave];
     const int p = blockIdx.x, d = threadIdx.x, wave = d / kWave, lane = __lane_id();
     uint32_t c = 0;
 #pragma unroll
     for (int k = 0; k < kHistCopies; ++k) c += hist[k * kHistCopyWords + p * kRadix + d];
+    if (counters) {
+#pragma unroll
+        for (int k = 0; k < kHistCopies; ++k) hist[k * kHistCopyWords + p * kRadix + d] = 0;
+        if (d == 0) counters[p] = 0;
+    }
     const uint32_t inc = wave_inclusive_sum(c);
     if (lane == kWave - 1) s_w[wave] = inc;
     __syncthreads();
@@ -685,6 +692,29 @@ uint32_t *radix_histograms(void *scratch, int64_t n) {
     return reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + sort_scratch_layout(n).hist);
 }
 
+SortScratch sort_scratch(void *scratch, int64_t n) {
+    const SortScratchLayout L = sort_scratch_layout(n);
+    char *ws = static_cast<char *>(scratch);
+    return SortScratch{reinterpret_cast<uint32_t *>(ws + L.hist), reinterpret_cast<uint32_t *>(ws + L.counters),
+                       reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1),
+                       reinterpret_cast<uint32_t *>(ws + L.starts), L.parts};
+}
+
+size_t sort_scratch_head_bytes() { return sort_scratch_layout(1).status0; }
+
+size_t sort_scratch_tail_bytes(int64_t n) {
+    const SortScratchLayout L = sort_scratch_layout(n);
+    return L.bytes - L.status0;
+}
+
+SortScratch sort_scratch_split(void *head, void *tail, int64_t n) {
+    const SortScratchLayout L = sort_scratch_layout(n);
+    char *h = static_cast<char *>(head), *t = static_cast<char *>(tail) - L.status0;
+    return SortScratch{reinterpret_cast<uint32_t *>(h + L.hist), reinterpret_cast<uint32_t *>(h + L.counters),
+                       reinterpret_cast<uint32_t *>(t + L.status0), reinterpret_cast<uint32_t *>(t + L.status1),
+                       reinterpret_cast<uint32_t *>(t + L.starts), L.parts};
+}
+
 template <typename KeyT>
 gs_status radix_sort_pairs(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                            KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
@@ -767,6 +797,14 @@ int pass_items(int64_t n) {
     return best;
 }
 
+template <typename KeyT>
+int64_t radix_partitions(int64_t n) {
+    const int64_t tile = int64_t(kThreads) * pass_items<KeyT>(n);
+    return (n + tile - 1) / tile;
+}
+template int64_t radix_partitions<uint32_t>(int64_t);
+template int64_t radix_partitions<uint64_t>(int64_t);
+
 namespace {
 
 // Digit passes [0, count) of plan (count <= plan.passes), after digit_starts_kernel: pass p reads the previous
@@ -775,12 +813,10 @@ namespace {
 template <typename KeyT>
 gs_status run_digit_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                            KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, int count,
-                           void *scratch, hipStream_t stream) {
-    const SortScratchLayout L = sort_scratch_layout(n);
-    char *ws = static_cast<char *>(scratch);
-    uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
-    uint32_t *status[2] = {reinterpret_cast<uint32_t *>(ws + L.status0), reinterpret_cast<uint32_t *>(ws + L.status1)};
-    const uint32_t *starts = reinterpret_cast<const uint32_t *>(ws + L.starts);
+                           const SortScratch &S, hipStream_t stream) {
+    uint32_t *counters = S.counters;
+    uint32_t *status[2] = {S.status0, S.status1};
+    const uint32_t *starts = S.starts;
     const KeyT *src_k = keys_in;
     const int32_t *src_i = ids_in;
     const uint32_t spin = spin_limit();
@@ -793,9 +829,9 @@ gs_status run_digit_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
         uint32_t *st_next = (p + 1 < count) ? status[(p + 1) & 1] : nullptr;
         const int64_t tile = int64_t(kThreads) * items;
         const int64_t parts = (n + tile - 1) / tile;
-        if (parts > L.parts)  // the look-back arrays hold L.parts partitions of 256 words
+        if (parts > S.parts)  // the look-back arrays hold S.parts partitions of 256 words
             return fail(GS_ERR_INVALID_ARG, "radix pass: %lld partitions exceed the look-back arrays (%lld)",
-                        (long long)parts, (long long)L.parts);
+                        (long long)parts, (long long)S.parts);
         const dim3 grid(static_cast<unsigned>(parts));
         const uint32_t *h = starts + p * kRadix;
         gs_status st_launch;
@@ -817,13 +853,27 @@ gs_status run_digit_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
     return ok();
 }
 
-// The global digit starts of `rows` rows of the histogram copies (one workgroup per row).
-gs_status launch_digit_starts(void *scratch, int64_t n, int rows, hipStream_t stream) {
-    const SortScratchLayout L = sort_scratch_layout(n);
-    char *ws = static_cast<char *>(scratch);
-    hipLaunchKernelGGL(digit_starts_kernel, dim3(rows), dim3(kRadix), 0, stream,
-                       reinterpret_cast<const uint32_t *>(ws + L.hist), reinterpret_cast<uint32_t *>(ws + L.starts));
+// The global digit starts of `rows` rows of the histogram copies (one workgroup per row); with recycle, the rows
+// read are zeroed and the partition counters of those passes reset.
+gs_status launch_digit_starts(const SortScratch &S, int rows, bool recycle, hipStream_t stream) {
+    hipLaunchKernelGGL(digit_starts_kernel, dim3(rows), dim3(kRadix), 0, stream, S.hist, S.starts,
+                       recycle ? S.counters : nullptr);
     GS_LAUNCH_TRY("digit_starts_kernel");
+    return ok();
+}
+
+template <typename KeyT>
+gs_status passes_after_histograms(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                                  KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,
+                                  const SortScratch &S, bool recycle, hipStream_t stream, int *result_in_b) {
+    *result_in_b = 0;
+    if (plan.passes == 0 || n < 1) return ok();
+    gs_status st = launch_digit_starts(S, plan.passes, recycle, stream);
+    if (st != GS_OK) return st;
+    st = run_digit_passes<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, plan.passes,
+                                S, stream);
+    if (st != GS_OK) return st;
+    *result_in_b = (plan.passes % 2) == 0;
     return ok();
 }
 
@@ -833,15 +883,16 @@ template <typename KeyT>
 gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
                        KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan, void *scratch,
                        hipStream_t stream, int *result_in_b) {
-    *result_in_b = 0;
-    if (plan.passes == 0 || n < 1) return ok();
-    gs_status st = launch_digit_starts(scratch, n, plan.passes, stream);
-    if (st != GS_OK) return st;
-    st = run_digit_passes<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, plan.passes,
-                                scratch, stream);
-    if (st != GS_OK) return st;
-    *result_in_b = (plan.passes % 2) == 0;
-    return ok();
+    return passes_after_histograms<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan,
+                                         sort_scratch(scratch, n), false, stream, result_in_b);
+}
+
+template <typename KeyT>
+gs_status radix_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf_a_keys, int32_t *buf_a_ids,
+                       KeyT *buf_b_keys, int32_t *buf_b_ids, int64_t n, const PassPlan &plan,
+                       const SortScratch &scratch, hipStream_t stream, int *result_in_b) {
+    return passes_after_histograms<KeyT>(keys_in, ids_in, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan,
+                                         scratch, true, stream, result_in_b);
 }
 
 size_t depth_order_status_bytes(int64_t n) {
@@ -860,15 +911,15 @@ gs_status depth_order_passes(const uint32_t *depth_bits, uint32_t *buf_a_keys, i
                     kMaxPasses - 1);
     if (n < 1) return ok();
     // row plan.passes of the histogram copies holds the tile counts by the last pass's digit
-    gs_status st = launch_digit_starts(scratch, n, plan.passes + 1, stream);
+    const SortScratch S = sort_scratch(scratch, n);
+    gs_status st = launch_digit_starts(S, plan.passes + 1, false, stream);
     if (st != GS_OK) return st;
     st = run_digit_passes<uint32_t>(depth_bits, nullptr, buf_a_keys, buf_a_ids, buf_b_keys, buf_b_ids, n, plan, last,
-                                    scratch, stream);
+                                    S, stream);
     if (st != GS_OK) return st;
     // pass `last` reads what pass last - 1 wrote
     const bool to_a = (last % 2) == 0;
-    const SortScratchLayout L = sort_scratch_layout(n);
-    const uint32_t *starts = reinterpret_cast<const uint32_t *>(static_cast<char *>(scratch) + L.starts);
+    const uint32_t *starts = S.starts;
     const int64_t parts = (n + kThreads * kItems32 - 1) / (kThreads * kItems32);
     hipLaunchKernelGGL(depth_order_pass_kernel, dim3(static_cast<unsigned>(parts)), dim3(kThreads), 0, stream,
                        to_a ? buf_b_keys : buf_a_keys, to_a ? buf_b_ids : buf_a_ids, rects, pk,
@@ -888,6 +939,9 @@ template gs_status radix_passes<uint32_t>(const uint32_t *, const int32_t *, uin
                                           int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
 template gs_status radix_passes<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
                                           int32_t *, int64_t, const PassPlan &, void *, hipStream_t, int *);
+template gs_status radix_passes<uint64_t>(const uint64_t *, const int32_t *, uint64_t *, int32_t *, uint64_t *,
+                                          int32_t *, int64_t, const PassPlan &, const SortScratch &, hipStream_t,
+                                          int *);
 
 namespace {
 
