@@ -362,34 +362,38 @@ def main():
         ms_per_step = latency_ms
     else:
         flight = [frame.FramePlan(ds, stream=torch.cuda.Stream()) for _ in range(F)]
-        settle(lambda: [p.run() for p in flight])
-        for k in range(max(args.warmup, F)):
-            flight[k % F].run()
-        torch.cuda.synchronize()
-        share = [args.steps // F + (1 if i < args.steps % F else 0) for i in range(F)]  # exactly K steps in all
-        gate = threading.Barrier(F + 1)
 
-        errors = []
+        def pipelined(steps):
+            """`steps` frames in all, spread over the F plans, each plan fed by its own host thread; returns the
+            seconds from the threads' common start to the device's last frame (synchronized on both sides)."""
+            share = [steps // F + (1 if i < steps % F else 0) for i in range(F)]
+            gate = threading.Barrier(F + 1)
+            errors = []
 
-        def feed(p, count):
+            def feed(p, count):
+                gate.wait()
+                try:
+                    for _ in range(count):
+                        p.run()
+                except Exception as e:  # re-raised on the main thread below
+                    errors.append(e)
+            workers = [threading.Thread(target=feed, args=(p, c)) for p, c in zip(flight, share)]
+            for w in workers:
+                w.start()
+            torch.cuda.synchronize()
             gate.wait()
-            try:
-                for _ in range(count):
-                    p.run()
-            except Exception as e:  # re-raised on the main thread below
-                errors.append(e)
-        workers = [threading.Thread(target=feed, args=(p, c)) for p, c in zip(flight, share)]
-        for w in workers:
-            w.start()
-        torch.cuda.synchronize()
-        gate.wait()
-        t0 = time.perf_counter()
-        for w in workers:
-            w.join()
-        torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        if errors:
-            raise errors[0]
+            t0 = time.perf_counter()
+            for w in workers:
+                w.join()
+            torch.cuda.synchronize()
+            if errors:
+                raise errors[0]
+            return time.perf_counter() - t0
+        settle(lambda: [p.run() for p in flight])
+        # the warm-up steps run the same way as the timed ones (threads, streams and all), so the timed steps are
+        # not the first the threaded path runs in this process
+        pipelined(max(args.warmup, F))
+        ms_per_step = pipelined(args.steps) * 1e3 / args.steps  # exactly K steps
         assert all(p.n_isects == plan.n_isects for p in flight)
         del flight
     # outside the frame: the composite's backward on the last frame (seeded output gradients)
