@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="config3", choices=sorted(WORKLOADS))
-    ap.add_argument("--frames-in-flight", type=int, default=3,
+    ap.add_argument("--frames-in-flight", type=int, default=2,
                     help="frames in flight at once on separate streams and host threads in the timed steps "
                          "(1 = one at a time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -389,9 +389,9 @@ def main():
             if errors:
                 raise errors[0]
             return time.perf_counter() - t0
-        settle(lambda: [p.run() for p in flight])
-        # the warm-up steps run the same way as the timed ones (threads, streams and all), so the timed steps are
-        # not the first the threaded path runs in this process
+        # the settle and the warm-up steps run the same way as the timed ones (threads, streams and all), so the
+        # timed steps are not the first the threaded path runs in this process
+        settle(lambda: pipelined(2 * F))
         pipelined(max(args.warmup, F))
         ms_per_step = pipelined(args.steps) * 1e3 / args.steps  # exactly K steps
         assert all(p.n_isects == plan.n_isects for p in flight)
