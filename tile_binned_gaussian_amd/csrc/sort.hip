@@ -48,6 +48,8 @@ struct Tiling {
     static constexpr int window = sizeof(KeyT) == 8 ? 2 : 4;   // predecessors inspected per look-back round
 };
 constexpr int kItems32 = 4;                  // pairs per thread for 4-byte keys
+constexpr int kItems32Big = 16;              // ... from kItems32BigMin pairs on (one workgroup per CU)
+constexpr int64_t kItems32BigMin = int64_t(1) << 21;
 constexpr int kItems64Min = 13, kItems64Max = 14;
 // the smallest partition of any shape sizes the look-back arrays (one status word per digit and partition)
 constexpr int kMinTile = kThreads * (kItems32 < kItems64Min ? kItems32 : kItems64Min);
@@ -767,12 +769,13 @@ gs_status launch_pass(int bits, dim3 grid, hipStream_t stream, const KeyT *src_k
     }
 }
 
-// Pairs per thread of the digit passes over n pairs: 4 for 4-byte keys; for 8-byte keys the one of 13 and 14 whose
-// partitions fill the CUs' last round best (cost: rounds of partitions over the CUs times the per-partition work,
-// counted as items plus 3 for the fixed steps of a partition; ties go to 14).
+// Pairs per thread of the digit passes over n pairs: for 4-byte keys 4, or 16 from 2^21 pairs on (fewer, larger
+// partitions shorten the look-back once there are several rounds of them); for 8-byte keys the one of 13 and 14
+// whose partitions fill the CUs' last round best (cost: rounds of partitions over the CUs times the per-partition
+// work, counted as items plus 3 for the fixed steps of a partition; ties go to 14).
 template <typename KeyT>
 int pass_items(int64_t n) {
-    if (sizeof(KeyT) == 4) return kItems32;
+    if (sizeof(KeyT) == 4) return n >= kItems32BigMin ? kItems32Big : kItems32;
     static std::atomic<int> cus{0};
     int c = cus.load(std::memory_order_relaxed);
     if (c <= 0) {
@@ -836,8 +839,12 @@ gs_status run_digit_passes(const KeyT *keys_in, const int32_t *ids_in, KeyT *buf
         const uint32_t *h = starts + p * kRadix;
         gs_status st_launch;
         if constexpr (sizeof(KeyT) == 4) {
-            st_launch = launch_pass<KeyT, kItems32>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n, plan.shift[p],
-                                                    h, counters + p, st, st_next, spin);
+            if (items == kItems32Big)
+                st_launch = launch_pass<KeyT, kItems32Big>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
+                                                           plan.shift[p], h, counters + p, st, st_next, spin);
+            else
+                st_launch = launch_pass<KeyT, kItems32>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
+                                                        plan.shift[p], h, counters + p, st, st_next, spin);
         } else if (items == kItems64Min) {
             st_launch = launch_pass<KeyT, kItems64Min>(plan.bits[p], grid, stream, src_k, src_i, dk, di, n,
                                                        plan.shift[p], h, counters + p, st, st_next, spin);
